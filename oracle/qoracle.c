@@ -1,0 +1,207 @@
+/*
+ * qoracle.c -- plain CPU oracle for the weight-only-quantized decode products.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the bench's CPU
+ * baseline leg load this file's library.  It shares no source, header, table
+ * or helper with the HIP library; the two meet only in the seeded inputs.
+ *
+ * Every function is the plain definition of what the pages compute, written
+ * out in double precision (fp64) except the activation quantiser, whose
+ * integer outputs are decided in IEEE binary32 exactly as the page fixes it.
+ * No blocking, no reordering beyond a single left-to-right loop.
+ *
+ * Sources (cited by page and function, no line numbers):
+ *  [Q8]  cortiq-engine 0.5.43 gpu_wgpu.rs page, module doc and the q8_matvec /
+ *        q8_matmat shaders; cortiq-engine 0.3.7 gpu_metal.rs page, q8_matvec /
+ *        q8_matmat kernels: y[o] = rs[o] * sum_i q[o,i] * xs[i], xs already
+ *        prescaled, batched y[b,o] with xs [nb][K] and y [nb][M] row-major.
+ *  [Q2]  qxmx qxmx_gpu.cpp page, dequant_embd: code k of a block is
+ *        (qs[k/4] >> 2*(k%4)) & 3, weight = d * (code - 1); blocks are 18 B
+ *        per 64 weights or 34 B per 128 (upload_q2), d a binary16 scale.
+ *  [AQ]  qxmx qxmx_gpu.cpp page, gpu_rmsnorm_quant: act_scale = amax/127,
+ *        inv = 1/act_scale (0 when act_scale is 0), v = round(x*inv) with
+ *        round-half-away-from-zero, clamped to [-128, 127]; suma = sum of the
+ *        int8 values of each 64-wide group.
+ *  [GV]  qxmx qxmx_gpu.cpp page, gemv_dpas8 and gemv_reduce: per 64-wide
+ *        group the integer dot of codes with the int8 activations, corrected
+ *        by suma to sum (code-1)*xq, scaled by d, summed over groups and
+ *        multiplied by act_scale.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *  - binary16 is decoded per IEEE 754 (subnormal = m * 2^-24); the page's
+ *    host helper f16_to_f32 uses 2^-14 for subnormals, its device code uses
+ *    native half.
+ *  - a block is the 2-byte little-endian d followed by the code bytes.
+ *  - the quantiser acts on the given f32 vector (no fused norm).
+ *  - the Q2 reference result is built from sc*xq, the quantised activations.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared qoracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+/* ---- binary16 -> double, IEEE 754 definition ---------------------------- */
+double qo_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                /* 0.m * 2^-14 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);    /* 1.m * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* ---- q8_row: y[o] = rs[o] * sum_i q[o,i] * xs[i]  [Q8] ------------------- */
+/* rows == NULL: all M rows, y[o]; else y[j] for o = rows[j], j < nrows.
+ * mass[.] = sum_i |rs[o] q[o,i] xs[i]|, the per-output error yardstick.   */
+void qo_q8row_gemv(const int8_t *q, const float *rs, const float *xs,
+                   int64_t M, int64_t K, const int64_t *rows, int64_t nrows,
+                   double *y, double *mass)
+{
+    int64_t n = rows ? nrows : M;
+    for (int64_t j = 0; j < n; j++) {
+        int64_t o = rows ? rows[j] : j;
+        const int8_t *qr = q + o * K;
+        double acc = 0.0, am = 0.0;
+        for (int64_t i = 0; i < K; i++) {
+            double t = (double)qr[i] * (double)xs[i];
+            acc += t;
+            am += fabs(t);
+        }
+        y[j] = (double)rs[o] * acc;
+        if (mass) mass[j] = fabs((double)rs[o]) * am;
+    }
+}
+
+/* ---- batched q8_row: y[b,o] = rs[o] * sum_i q[o,i] * xs[b,i]  [Q8] ------- */
+/* bs/os == NULL: the full [nb][M] output; else the n listed (b, o) entries. */
+void qo_q8row_gemm(const int8_t *q, const float *rs, const float *xs,
+                   int64_t nb, int64_t M, int64_t K,
+                   const int64_t *bs, const int64_t *os, int64_t n,
+                   double *y, double *mass)
+{
+    int64_t total = bs ? n : nb * M;
+    for (int64_t j = 0; j < total; j++) {
+        int64_t b = bs ? bs[j] : j / M;
+        int64_t o = bs ? os[j] : j % M;
+        const int8_t *qr = q + o * K;
+        const float *xr = xs + b * K;
+        double acc = 0.0, am = 0.0;
+        for (int64_t i = 0; i < K; i++) {
+            double t = (double)qr[i] * (double)xr[i];
+            acc += t;
+            am += fabs(t);
+        }
+        y[j] = (double)rs[o] * acc;
+        if (mass) mass[j] = fabs((double)rs[o]) * am;
+    }
+}
+
+/* ---- Q2 blocks [Q2] ------------------------------------------------------ */
+static int64_t blk_bytes(int group) { return 2 + group / 4; }
+
+static const uint8_t *q2_blk(const uint8_t *blob, int64_t K, int group,
+                             int64_t o, int64_t g)
+{
+    return blob + (o * (K / group) + g) * blk_bytes(group);
+}
+
+static double q2_d(const uint8_t *blk)
+{
+    return qo_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+static int q2_code(const uint8_t *blk, int k)
+{
+    return (blk[2 + k / 4] >> (2 * (k % 4))) & 3;
+}
+
+/* Dense dequantisation w[o][i] = d * (code - 1) of the whole matrix. */
+void qo_q2_dequant(const uint8_t *blob, int64_t M, int64_t K, int group,
+                   double *w)
+{
+    for (int64_t o = 0; o < M; o++)
+        for (int64_t i = 0; i < K; i++) {
+            const uint8_t *blk = q2_blk(blob, K, group, o, i / group);
+            w[o * K + i] = q2_d(blk) * (double)(q2_code(blk, (int)(i % group)) - 1);
+        }
+}
+
+/* ---- activation int8 quantisation, in IEEE binary32  [AQ] --------------- */
+/* suma may be NULL; else K/64 entries (K % 64 == 0 is the caller's job). */
+void qo_act_quant_i8(const float *x, int64_t K, int8_t *xq, float *act_scale,
+                     int32_t *suma)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < K; i++) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    float sc = amax / 127.0f;
+    float inv = sc > 0.0f ? 1.0f / sc : 0.0f;
+    for (int64_t i = 0; i < K; i++) {
+        float v = roundf(x[i] * inv);
+        if (v > 127.0f) v = 127.0f;
+        if (v < -128.0f) v = -128.0f;
+        xq[i] = (int8_t)v;
+    }
+    if (suma)
+        for (int64_t g = 0; g < K / 64; g++) {
+            int32_t s = 0;
+            for (int k = 0; k < 64; k++) s += xq[g * 64 + k];
+            suma[g] = s;
+        }
+    *act_scale = sc;
+}
+
+/* ---- Q2 x int8 group dots  [GV] ----------------------------------------- */
+/* dots[o][u] = sum over the 64 weights of 64-wide unit u of (code-1)*xq.
+ * A 128-wide block is two 64-wide units sharing d.                        */
+void qo_q2_dots(const uint8_t *blob, int64_t M, int64_t K, int group,
+                const int8_t *xq, int32_t *dots)
+{
+    int64_t nu = K / 64;
+    for (int64_t o = 0; o < M; o++)
+        for (int64_t u = 0; u < nu; u++) {
+            int32_t s = 0;
+            for (int64_t i = u * 64; i < u * 64 + 64; i++) {
+                const uint8_t *blk = q2_blk(blob, K, group, o, i / group);
+                s += (q2_code(blk, (int)(i % group)) - 1) * (int32_t)xq[i];
+            }
+            dots[o * nu + u] = s;
+        }
+}
+
+/* y[o] = sc * sum_u d(u) * dots[o][u], fp64  [GV]
+ * rows == NULL: all rows; mass[.] = sum_i |d (code-1)| * |sc xq_i|.       */
+void qo_q2_gemv(const uint8_t *blob, int64_t M, int64_t K, int group,
+                const int8_t *xq, float sc, const int64_t *rows, int64_t nrows,
+                double *y, double *mass)
+{
+    int64_t n = rows ? nrows : M;
+    int64_t nu = K / 64;
+    for (int64_t j = 0; j < n; j++) {
+        int64_t o = rows ? rows[j] : j;
+        double acc = 0.0, am = 0.0;
+        for (int64_t u = 0; u < nu; u++) {
+            const uint8_t *blk = q2_blk(blob, K, group, o, (u * 64) / group);
+            double d = q2_d(blk);
+            int64_t dot = 0, adot = 0;
+            for (int64_t i = u * 64; i < u * 64 + 64; i++) {
+                int c = q2_code(blk, (int)(i % group)) - 1;
+                dot += (int64_t)c * xq[i];
+                adot += (int64_t)(c < 0 ? -c : c) * (xq[i] < 0 ? -xq[i] : xq[i]);
+            }
+            acc += d * (double)dot;
+            am += fabs(d) * (double)adot;
+        }
+        y[j] = (double)sc * acc;
+        if (mass) mass[j] = fabs((double)sc) * am;
+    }
+}

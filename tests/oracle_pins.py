@@ -1,0 +1,294 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with what the pages or the mathematics fix: hand-worked examples
+(``tests/golden``), library routines (numpy's binary16 decoder, numpy fp64
+matmul), an independent encoder, brute force on tiny inputs, closed-form
+special cases and exact invariants.  ``test_oracle.py`` runs them on the
+oracle; ``test_oracle_mutants.py`` runs them on deliberately broken copies of
+the oracle and requires that every copy fails at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close(a, b, rel=1e-12, abs_=0.0):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    err = np.abs(a - b)
+    lim = rel * np.abs(b) + abs_
+    assert np.all(err <= lim), f"max err {err.max()} (limit {lim.flat[np.argmax(err - lim)]})"
+
+
+# ---- independent encoder of GGUF-style Q2 blocks (test side) -------------
+def encode_q2(codes: np.ndarray, d_bits: np.ndarray, group: int) -> np.ndarray:
+    """codes uint8 [M][K] in 0..3, d_bits uint16 [M][K/group] -> block blob.
+
+    Byte j of a block holds codes 4j..4j+3 at bit offsets 0, 2, 4, 6.
+    """
+    M, K = codes.shape
+    ng = K // group
+    c = codes.reshape(M, ng, group // 4, 4).astype(np.uint8)
+    qs = c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)
+    blob = np.empty((M, ng, 2 + group // 4), np.uint8)
+    blob[:, :, 0] = (d_bits & 0xFF).astype(np.uint8)
+    blob[:, :, 1] = (d_bits >> 8).astype(np.uint8)
+    blob[:, :, 2:] = qs
+    return blob.reshape(-1)
+
+
+def f16_values(d_bits):
+    return np.asarray(d_bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+# ---- binary16 -------------------------------------------------------------
+def pin_f16_all_vs_numpy(orc):
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.f16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_f16_golden(orc):
+    for bits, val in _golden("f16_points.json")["points"]:
+        got = orc.f16_to_f64(bits)
+        assert got == val and np.signbit(got) == np.signbit(val), (bits, got, val)
+
+
+# ---- q8_row ---------------------------------------------------------------
+def pin_q8row_hand(orc):
+    g = _golden("q8row_hand.json")
+    y, m = orc.q8row_gemv(np.array(g["q"], np.int8), np.array(g["rs"], np.float32),
+                          np.array(g["xs"], np.float32))
+    assert np.array_equal(y, np.array(g["y"])), y
+    assert np.array_equal(m, np.array(g["mass"])), m
+
+
+def pin_q8row_vs_numpy_matmul(orc):
+    rng = np.random.Generator(np.random.PCG64(11))
+    for M, K in [(1, 4), (7, 36), (33, 260)]:
+        q = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+        rs = rng.uniform(0.001, 0.01, M).astype(np.float32)
+        xs = rng.standard_normal(K, dtype=np.float32)
+        W = rs.astype(np.float64)[:, None] * q.astype(np.float64)
+        ref = W @ xs.astype(np.float64)
+        y, m = orc.q8row_gemv(q, rs, xs)
+        _close(y, ref, rel=1e-12, abs_=1e-12)
+        _close(m, np.abs(W) @ np.abs(xs.astype(np.float64)), rel=1e-12)
+
+
+def pin_q8row_rows_subset(orc):
+    rng = np.random.Generator(np.random.PCG64(12))
+    q = rng.integers(-127, 128, size=(20, 16), dtype=np.int8)
+    rs = rng.uniform(0.001, 0.01, 20).astype(np.float32)
+    xs = rng.standard_normal(16, dtype=np.float32)
+    y, _ = orc.q8row_gemv(q, rs, xs)
+    rows = np.array([19, 0, 7, 7])
+    ys, _ = orc.q8row_gemv(q, rs, xs, rows=rows)
+    assert np.array_equal(ys, y[rows])
+
+
+def pin_q8gemm_hand(orc):
+    g = _golden("q8gemm_hand.json")
+    y, _ = orc.q8row_gemm(np.array(g["q"], np.int8), np.array(g["rs"], np.float32),
+                          np.array(g["xs"], np.float32))
+    assert np.array_equal(y, np.array(g["y"])), y
+
+
+def pin_q8gemm_vs_numpy(orc):
+    rng = np.random.Generator(np.random.PCG64(13))
+    nb, M, K = 5, 9, 68
+    q = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    rs = rng.uniform(0.001, 0.01, M).astype(np.float32)
+    xs = rng.standard_normal((nb, K), dtype=np.float32)
+    W = rs.astype(np.float64)[:, None] * q.astype(np.float64)
+    ref = xs.astype(np.float64) @ W.T
+    y, m = orc.q8row_gemm(q, rs, xs)
+    _close(y, ref, rel=1e-12, abs_=1e-12)
+    _close(m, np.abs(xs.astype(np.float64)) @ np.abs(W).T, rel=1e-12)
+    bs = np.array([4, 0, 2])
+    os_ = np.array([8, 3, 0])
+    ye, _ = orc.q8row_gemm(q, rs, xs, entries=(bs, os_))
+    assert np.array_equal(ye, y[bs, os_])
+    for b in range(nb):
+        yb, _ = orc.q8row_gemv(q, rs, xs[b])
+        _close(y[b], yb, rel=1e-14, abs_=1e-14)
+
+
+# ---- activation quantisation ---------------------------------------------
+def pin_act_quant_tie(orc):
+    g = _golden("act_quant_tie.json")
+    x = np.zeros(g["K"], np.float32)
+    x[: len(g["x_head"])] = g["x_head"]
+    xq, sc, suma = orc.act_quant_i8(x)
+    assert list(xq[: len(g["xq_head"])]) == g["xq_head"], xq[:8]
+    assert np.all(xq[len(g["xq_head"]):] == 0)
+    assert sc == np.float32(g["act_scale"])
+    assert list(suma) == g["suma"]
+
+
+def pin_act_quant_invariants(orc):
+    rng = np.random.Generator(np.random.PCG64(14))
+    for K, scale in [(64, 1.0), (128, 3e-3), (4096, 1.0), (5120, 250.0), (17408, 1.0)]:
+        x = (rng.standard_normal(K) * scale).astype(np.float32)
+        xq, sc, suma = orc.act_quant_i8(x)
+        amax = np.max(np.abs(x))
+        assert sc == np.float32(amax) / np.float32(127.0)
+        j = int(np.argmax(np.abs(x)))
+        assert abs(int(xq[j])) == 127 and np.sign(xq[j]) == np.sign(x[j])
+        assert np.max(np.abs(xq.astype(np.int32))) == 127
+        r = np.abs(xq.astype(np.float64) - x.astype(np.float64) / np.float64(sc))
+        assert np.all(r <= 0.5 + 1e-5), r.max()
+        assert np.array_equal(suma, xq.astype(np.int32).reshape(-1, 64).sum(axis=1))
+
+
+def pin_act_quant_pow2(orc):
+    rng = np.random.Generator(np.random.PCG64(15))
+    x = rng.standard_normal(1024).astype(np.float32)
+    xq0, sc0, s0 = orc.act_quant_i8(x)
+    for k in (-20, -3, -1, 1, 5, 30):
+        xq, sc, s = orc.act_quant_i8((x * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(xq, xq0) and np.array_equal(s, s0)
+        assert sc == np.float32(sc0 * np.float32(2.0 ** k))
+
+
+def pin_act_quant_zero(orc):
+    xq, sc, suma = orc.act_quant_i8(np.zeros(128, np.float32))
+    assert sc == 0.0 and not np.isnan(sc)
+    assert np.all(xq == 0) and np.all(suma == 0)
+
+
+# ---- Q2 -----------------------------------------------------------------
+def _hand_block(case):
+    group = case["group"]
+    qs = np.full(group // 4, case["qs_fill"], np.uint8)
+    for k, v in case["qs_set"].items():
+        qs[int(k)] = v
+    blob = np.empty(2 + group // 4, np.uint8)
+    blob[0] = case["d_bits"] & 0xFF
+    blob[1] = case["d_bits"] >> 8
+    blob[2:] = qs
+    return blob
+
+
+def pin_q2_blocks_hand(orc):
+    tie = _golden("act_quant_tie.json")
+    for case in _golden("q2_blocks_hand.json")["cases"]:
+        group = case["group"]
+        blob = _hand_block(case)
+        w = orc.q2_dequant(blob, 1, group, group)[0]
+        if "w_head" in case:
+            assert list(w[: len(case["w_head"])]) == case["w_head"], (case["name"], w[:8])
+        for k, v in case.get("w_at", {}).items():
+            assert w[int(k)] == v, (case["name"], k, w[int(k)])
+        if "dot" in case:
+            x = np.zeros(group, np.float32)
+            x[: len(tie["x_head"])] = tie["x_head"]
+            xq, sc, _ = orc.act_quant_i8(x)
+            dots = orc.q2_dots(blob, 1, group, group, xq)
+            assert dots[0, 0] == case["dot"], dots
+            y, _ = orc.q2_gemv(blob, 1, group, group, xq, sc)
+            assert y[0] == case["y"], y
+
+
+def pin_q2_roundtrip_encoder(orc):
+    rng = np.random.Generator(np.random.PCG64(16))
+    for group, M, K in [(64, 3, 192), (128, 2, 384)]:
+        codes = rng.integers(0, 4, size=(M, K), dtype=np.uint8)
+        d_bits = np.abs(rng.normal(0, 0.02, size=(M, K // group))).astype(np.float16).view(np.uint16)
+        d_bits[0, 0] = 0x0001  # a subnormal scale
+        blob = encode_q2(codes, d_bits, group)
+        w = orc.q2_dequant(blob, M, K, group)
+        ref = np.repeat(f16_values(d_bits), group, axis=1) * (codes.astype(np.float64) - 1.0)
+        assert np.array_equal(w, ref)
+
+
+def _q2_case(rng, M, K, group):
+    codes = rng.integers(0, 4, size=(M, K), dtype=np.uint8)
+    d_bits = np.abs(rng.normal(0, 0.02, size=(M, K // group))).astype(np.float16).view(np.uint16)
+    return codes, d_bits, encode_q2(codes, d_bits, group)
+
+
+def pin_q2_dots_brute(orc):
+    rng = np.random.Generator(np.random.PCG64(17))
+    for group, M, K in [(64, 4, 256), (128, 3, 384)]:
+        codes, _, _ = _q2_case(rng, M, K, group)
+        ones = np.full((M, K // group), 0x3C00, np.uint16)  # d = 1.0
+        blob = encode_q2(codes, ones, group)
+        x = rng.standard_normal(K).astype(np.float32)
+        xq, _, _ = orc.act_quant_i8(x)
+        dots = orc.q2_dots(blob, M, K, group, xq)
+        ref = ((codes.astype(np.int64) - 1) * xq.astype(np.int64)).reshape(M, K // 64, 64).sum(-1)
+        assert np.array_equal(dots, ref)
+
+
+def pin_q2_gemv_vs_dense(orc):
+    rng = np.random.Generator(np.random.PCG64(18))
+    for group, M, K in [(64, 5, 320), (128, 6, 640)]:
+        codes, d_bits, blob = _q2_case(rng, M, K, group)
+        x = rng.standard_normal(K).astype(np.float32)
+        xq, sc, _ = orc.act_quant_i8(x)
+        W = np.repeat(f16_values(d_bits), group, axis=1) * (codes.astype(np.float64) - 1.0)
+        xd = np.float64(sc) * xq.astype(np.float64)
+        y, m = orc.q2_gemv(blob, M, K, group, xq, sc)
+        _close(y, W @ xd, rel=1e-12, abs_=1e-15)
+        _close(m, np.abs(W) @ np.abs(xd), rel=1e-12)
+        rows = np.array([M - 1, 0])
+        yr, _ = orc.q2_gemv(blob, M, K, group, xq, sc, rows=rows)
+        assert np.array_equal(yr, y[rows])
+
+
+def pin_q2_g128_is_two_g64(orc):
+    rng = np.random.Generator(np.random.PCG64(19))
+    M, K = 3, 512
+    codes, d128, blob128 = _q2_case(rng, M, K, 128)
+    blob64 = encode_q2(codes, np.repeat(d128, 2, axis=1), 64)
+    x = rng.standard_normal(K).astype(np.float32)
+    xq, sc, _ = orc.act_quant_i8(x)
+    assert np.array_equal(orc.q2_dequant(blob128, M, K, 128), orc.q2_dequant(blob64, M, K, 64))
+    assert np.array_equal(orc.q2_dots(blob128, M, K, 128, xq), orc.q2_dots(blob64, M, K, 64, xq))
+    assert np.array_equal(orc.q2_gemv(blob128, M, K, 128, xq, sc)[0],
+                          orc.q2_gemv(blob64, M, K, 64, xq, sc)[0])
+
+
+def pin_q2_codes_one_zero(orc):
+    rng = np.random.Generator(np.random.PCG64(20))
+    M, K = 4, 256
+    codes = np.ones((M, K), np.uint8)
+    d_bits = np.abs(rng.normal(0, 0.02, size=(M, K // 64))).astype(np.float16).view(np.uint16)
+    blob = encode_q2(codes, d_bits, 64)
+    xq, sc, _ = orc.act_quant_i8(rng.standard_normal(K).astype(np.float32))
+    y, _ = orc.q2_gemv(blob, M, K, 64, xq, sc)
+    assert np.all(y == 0.0)
+    assert np.all(orc.q2_dots(blob, M, K, 64, xq) == 0)
+
+
+def pin_q2_pow2(orc):
+    rng = np.random.Generator(np.random.PCG64(21))
+    M, K = 6, 384
+    _, _, blob = _q2_case(rng, M, K, 128)
+    x = rng.standard_normal(K).astype(np.float32)
+    xq0, sc0, _ = orc.act_quant_i8(x)
+    y0, _ = orc.q2_gemv(blob, M, K, 128, xq0, sc0)
+    for k in (-7, 3, 12):
+        xq, sc, _ = orc.act_quant_i8((x * np.float32(2.0 ** k)).astype(np.float32))
+        y, _ = orc.q2_gemv(blob, M, K, 128, xq, sc)
+        assert np.array_equal(y, y0 * 2.0 ** k)
+
+
+ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

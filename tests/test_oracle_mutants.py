@@ -1,0 +1,62 @@
+"""Every plausible slip in the oracle must be caught by at least one pin.
+
+Each case copies ``oracle/qoracle.c``, plants one mistake in the copy (a wrong
+sign, index, constant, rounding mode or dropped term), builds it with gcc in a
+temporary folder and runs all pins against it.  The planted mistakes live
+only in this file and in the temporary copies.  CPU only.
+
+(Dropping the zero guard of the quantiser's reciprocal is not listed: on
+x86-64 the resulting NaN converts to int8 0, the same output as the guard.)
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTANTS = {
+    "f16 subnormal as 2^-14": ("ldexp((double)m, -24)", "ldexp((double)m, -14)"),
+    "f16 exponent bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
+    "q8 row scale dropped": ("y[j] = (double)rs[o] * acc;\n        if (mass) mass[j] = fabs((double)rs[o]) * am;\n    }\n}\n\n/* ---- batched",
+                             "y[j] = acc;\n        if (mass) mass[j] = fabs((double)rs[o]) * am;\n    }\n}\n\n/* ---- batched"),
+    "q8 activation reversed": ("double t = (double)qr[i] * (double)xs[i];", "double t = (double)qr[i] * (double)xs[K - 1 - i];"),
+    "q8 sign": ("            acc += t;\n            am += fabs(t);\n        }\n        y[j] = (double)rs[o] * acc;\n        if (mass) mass[j] = fabs((double)rs[o]) * am;\n    }\n}\n\n/* ---- batched",
+                "            acc -= t;\n            am += fabs(t);\n        }\n        y[j] = (double)rs[o] * acc;\n        if (mass) mass[j] = fabs((double)rs[o]) * am;\n    }\n}\n\n/* ---- batched"),
+    "gemm ignores batch row": ("const float *xr = xs + b * K;", "const float *xr = xs;"),
+    "gemm transposed scale": ("y[j] = (double)rs[o] * acc;\n        if (mass) mass[j] = fabs((double)rs[o]) * am;\n    }\n}\n\n/* ---- Q2",
+                              "y[j] = (double)rs[b % M] * acc;\n        if (mass) mass[j] = fabs((double)rs[o]) * am;\n    }\n}\n\n/* ---- Q2"),
+    "quant half-to-even": ("float v = roundf(x[i] * inv);", "float v = rintf(x[i] * inv);"),
+    "quant truncation": ("float v = roundf(x[i] * inv);", "float v = truncf(x[i] * inv);"),
+    "quant /128": ("float sc = amax / 127.0f;", "float sc = amax / 128.0f;"),
+    "quant suma index": ("for (int k = 0; k < 64; k++) s += xq[g * 64 + k];", "for (int k = 0; k < 64; k++) s += xq[k];"),
+    "q2 code bit order": ("return (blk[2 + k / 4] >> (2 * (k % 4))) & 3;", "return (blk[2 + k / 4] >> (2 * (3 - k % 4))) & 3;"),
+    "q2 code byte index": ("return (blk[2 + k / 4] >> (2 * (k % 4))) & 3;", "return (blk[2 + (k / 4) % 16] >> (2 * (k % 4))) & 3;"),
+    "q2 value offset dropped": ("w[o * K + i] = q2_d(blk) * (double)(q2_code(blk, (int)(i % group)) - 1);",
+                                "w[o * K + i] = q2_d(blk) * (double)(q2_code(blk, (int)(i % group)));"),
+    "q2 scale byte order": ("return qo_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));",
+                            "return qo_f16_to_f64((uint16_t)(blk[1] | (blk[0] << 8)));"),
+    "q2 dots offset dropped": ("s += (q2_code(blk, (int)(i % group)) - 1) * (int32_t)xq[i];",
+                               "s += (q2_code(blk, (int)(i % group))) * (int32_t)xq[i];"),
+    "q2 gemv group index": ("const uint8_t *blk = q2_blk(blob, K, group, o, (u * 64) / group);",
+                            "const uint8_t *blk = q2_blk(blob, K, group, o, u % (K / group));"),
+    "q2 gemv act scale dropped": ("y[j] = (double)sc * acc;", "y[j] = acc;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "qoracle.c")).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {name}"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.build(str(mpath), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin_name, pin in ALL_PINS.items():
+        try:
+            pin(orc)
+        except Exception:  # a failed assertion or a crash both expose the slip
+            caught.append(pin_name)
+    assert caught, f"no pin catches mutant '{name}'"
