@@ -1,0 +1,192 @@
+/*
+ * qgemv.h -- C-ABI of the weight-only-quantized decode library for MI355X
+ * (gfx950).  Plain C: pointers, sizes and status codes; no C++ or framework
+ * types.  Library: weight_quantized_decode_q8_amd/libqgemv.so.
+ *
+ * Conventions shared by every entry point
+ *  - "device" pointers are HIP device memory on the current device; "host"
+ *    pointers are ordinary CPU memory.  The caller owns every buffer.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Device entry
+ *    points only enqueue work on it: they never synchronise, never allocate
+ *    and never copy between host and device.
+ *  - Every argument is validated before anything is launched.  A bad
+ *    argument returns QG_EINVAL and enqueues nothing; qg_last_error() then
+ *    names the argument.  A failed kernel launch returns QG_ELAUNCH.  There
+ *    is no fallback path of any kind.
+ *  - Sizes are int64_t element counts unless the name says bytes.
+ *  - Entry points are re-entrant and keep no global state besides the
+ *    thread-local error message.
+ *
+ * Sources of the operations (page and function; the pages are third-party
+ * source files of LLM inference engines):
+ *  [Q8]  cortiq-engine 0.5.43 gpu_wgpu.rs page: module doc, shaders
+ *        q8_matvec and q8_matmat; cortiq-engine 0.3.7 gpu_metal.rs page:
+ *        kernels q8_matvec / q8_matmat, host q8_matvec / q8_matvec_range /
+ *        q8_matmat.
+ *  [Q2]  qxmx qxmx_gpu.cpp page: dequant_embd (code and value rule),
+ *        repack_q2_g64 / repack_q2_g128 (host repack, g128 = two g64 halves
+ *        sharing d), upload_q2 (block footprints, padded rows).
+ *  [AQ]  qxmx qxmx_gpu.cpp page: gpu_rmsnorm_quant (per-vector int8
+ *        activation quantisation with per-64 group sums).
+ *  [GV]  qxmx qxmx_gpu.cpp page: gemv_dpas8 (int8-activation Q2 GEMV,
+ *        split-K partials, the suma correction) and gemv_reduce.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qg_status {
+    QG_OK = 0,
+    QG_EINVAL = 1,   /* bad argument; nothing was enqueued */
+    QG_ELAUNCH = 2,  /* a kernel launch failed */
+} qg_status;
+
+/* Human-readable name of a status. */
+const char *qg_status_string(qg_status s);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char *qg_last_error(void);
+
+/* Version of this ABI (bumped on any incompatible change). */
+int qg_abi_version(void);
+
+/* ======================================================================
+ * q8_row weights  [Q8]
+ *
+ * Source format (the pages' q8_row): int8 q[M][K] row-major, K % 4 == 0,
+ * plus one f32 row scale rs[M] kept separately.
+ *
+ * Device format "T64" (this library): rows in tiles of 64, K in chunks of
+ * 16 bytes; byte (o, i) lives at
+ *     ((o/64) * (Kp/16) + i/16) * 1024 + (o%64) * 16 + i%16
+ * with Mp = M rounded up to 64 and Kp = K rounded up to 16; padding bytes
+ * are zero.  A wavefront load of one chunk of a tile is 1 KiB contiguous.
+ * ==================================================================== */
+
+/* Bytes of the T64 image of an M x K q8_row matrix (0 if M<1, K<4 or K%4). */
+size_t qg_q8row_packed_bytes(int64_t M, int64_t K);
+
+/* Host: repack row-major q[M][K] (host) into the T64 image dst (host,
+ * dst_bytes >= qg_q8row_packed_bytes).  The caller uploads dst.
+ * QG_EINVAL: null pointer, M < 1, K < 4, K % 4 != 0, dst too small.      */
+qg_status qg_repack_q8row(const int8_t *q, int64_t M, int64_t K,
+                          void *dst, size_t dst_bytes);
+
+/* Host: inverse of qg_repack_q8row (for tests and export).              */
+qg_status qg_unpack_q8row(const void *packed, size_t packed_bytes,
+                          int64_t M, int64_t K, int8_t *q);
+
+/* Device: y[o] = rs[o] * sum_i q[o,i] * xs[i]   [Q8, q8_matvec]
+ *   qpacked: device, T64 image of q (qg_q8row_packed_bytes(M, K) bytes)
+ *   rs:      device, f32[M];  xs: device, f32[K] (already prescaled by the
+ *            caller, as on the pages);  y: device, f32[M], written.
+ * Accumulation in f32 (no activation quantisation).  A row range of a
+ * larger matrix is a call on a pointer offset by whole 64-row tiles.
+ * QG_EINVAL: null pointer, M < 1, K < 4, K % 4 != 0.                     */
+qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs,
+                      float *y, int64_t M, int64_t K, void *stream);
+
+/* ======================================================================
+ * Q2 weights  [Q2]
+ *
+ * Source format (GGUF-style, as the pages read it): per row, K/group blocks
+ * of (2 + group/4) bytes -- an IEEE binary16 scale d (little-endian), then
+ * group/4 code bytes; code k of a block is (qs[k/4] >> 2*(k%4)) & 3 and the
+ * weight is d * (code - 1).  group is 64 (18-byte blocks) or 128 (34-byte
+ * blocks); a 128 block is two 64-wide units sharing d.
+ *
+ * Device format "T64" (this library), two planes:
+ *  codes:  [Mp/64 tiles][K/64 units][64 rows][16 bytes]; inside the 16
+ *          bytes of (row, unit), 32-bit word j covers weights 16j..16j+15
+ *          and weight 16j + 4a + b sits at bits 8b + 2a of that word, so
+ *          (word >> 2a) & 0x03030303 yields the codes of weights
+ *          16j+4a .. 16j+4a+3 as four bytes.
+ *  scales: [Mp/64 tiles][K/group][64 rows] binary16, one per group (not
+ *          duplicated for 128-wide groups).
+ * Padding rows (M..Mp) have zero codes and zero scales.
+ * ==================================================================== */
+
+typedef struct qg_q2_weight {
+    const void *codes;    /* device, qg_q2_codes_bytes(M, K) bytes        */
+    const void *scales;   /* device, qg_q2_scales_bytes(M, K, group) bytes */
+    int64_t M;            /* rows (outputs)                               */
+    int64_t K;            /* columns (inputs), K % group == 0             */
+    int32_t group;        /* 64 or 128                                    */
+    int32_t reserved;     /* must be 0                                    */
+} qg_q2_weight;
+
+/* Size of the GGUF-style block blob: M * (K/group) * (2 + group/4). */
+size_t qg_q2_blocks_bytes(int64_t M, int64_t K, int group);
+/* Sizes of the two device planes (0 on bad shape). */
+size_t qg_q2_codes_bytes(int64_t M, int64_t K);
+size_t qg_q2_scales_bytes(int64_t M, int64_t K, int group);
+
+/* Host: repack a GGUF-style block blob (host, src_bytes must equal
+ * qg_q2_blocks_bytes) into the two T64 planes (host).  The scales are
+ * copied bit for bit.  QG_EINVAL: null pointer, M < 1, group not 64/128,
+ * K % group != 0, wrong src_bytes, destination too small.                */
+qg_status qg_repack_q2(const void *blocks, size_t src_bytes,
+                       int64_t M, int64_t K, int group,
+                       void *codes, size_t codes_bytes,
+                       void *scales, size_t scales_bytes);
+
+/* Host: inverse of qg_repack_q2 (for tests and export). */
+qg_status qg_unpack_q2(const void *codes, size_t codes_bytes,
+                       const void *scales, size_t scales_bytes,
+                       int64_t M, int64_t K, int group,
+                       void *blocks, size_t blocks_bytes);
+
+/* Device: per-vector int8 activation quantisation   [AQ]
+ *   x:         device, f32[K], finite.
+ *   xq:        device, int8[K], written: clamp(round(x * inv), -128, 127),
+ *              round half away from zero, inv = 1/act_scale (0 if
+ *              act_scale is 0), all in IEEE binary32.
+ *   act_scale: device, f32[1], written: max|x| / 127.
+ *   suma:      device, int32[K/64], written: sum of xq over each 64-wide
+ *              group (the correction term of the Q2 GEMV).
+ * QG_EINVAL: null pointer, K < 64, K % 64 != 0, K > 1 << 24.             */
+qg_status qquant_act_i8(const float *x, int64_t K, int8_t *xq,
+                        float *act_scale, int32_t *suma, void *stream);
+
+/* Bytes of split-K workspace qgemv_q2 needs for this shape and split
+ * (split_k 0 = the library's choice).                                    */
+size_t qgemv_q2_ws_bytes(int64_t M, int64_t K, int group, int split_k);
+
+/* Split factor qgemv_q2 uses for split_k = 0 (auto) on this shape.       */
+int qgemv_q2_auto_split(int64_t M, int64_t K, int group);
+
+/* Device: y[o] = act_scale * sum_u d(o,u) * sum_{i in unit u} (code-1)*xq_i
+ *   [GV, gemv_dpas8 + gemv_reduce]
+ *   w:         host struct describing the device planes.
+ *   xq, suma, act_scale: device, as written by qquant_act_i8 (K entries,
+ *              K/64 entries, 1 entry).
+ *   y:         device, f32[M], written.
+ *   ws:        device workspace of >= qgemv_q2_ws_bytes(M, K, group,
+ *              split_k) bytes (may be NULL when that is 0); holds the f32
+ *              split-K partials [split][Mp]; contents on entry are ignored.
+ *   split_k:   0 = auto, else 1..16 contiguous ranges of 64-wide units.
+ * The int32 unit dots are exact; y is accumulated in f32 from d * dot.
+ * QG_EINVAL: null pointer, bad weight struct, split_k out of range,
+ * workspace too small.                                                    */
+qg_status qgemv_q2(const qg_q2_weight *w, const int8_t *xq,
+                   const int32_t *suma, const float *act_scale, float *y,
+                   void *ws, size_t ws_bytes, int split_k, void *stream);
+
+/* Test entry: qgemv_q2 that also writes the exact int32 unit dots
+ *   dots[o][u] = sum_{i in unit u} (code - 1) * xq_i   (device,
+ *   int32[M][K/64]) from the same kernel, to prove them bit-exact.        */
+qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq,
+                        const int32_t *suma, const float *act_scale,
+                        float *y, int32_t *dots, void *ws, size_t ws_bytes,
+                        int split_k, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMV_H */

@@ -1,0 +1,162 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared
+symbol, its repacks place every byte where the header says, and invalid
+arguments are rejected before anything is launched.  No GPU needed: the
+device entry points are only called with arguments that fail validation."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import weight_quantized_decode_q8_amd as qg
+from oracle_pins import encode_q2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M):
+            if m.group(1) not in ("if", "sizeof"):
+                names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("qgemv_q8row", "qgemv_q2", "qquant_act_i8", "qg_repack_q2", "qg_repack_q8row"):
+        assert n in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports(name):
+    assert hasattr(ctypes.CDLL(qg.LIB_PATH), name), name
+
+
+def test_abi_and_status_strings():
+    L = qg.lib()
+    assert L.qg_abi_version() == 1
+    assert L.qg_status_string(0) == b"QG_OK"
+    assert L.qg_status_string(1) == b"QG_EINVAL"
+    assert L.qg_status_string(2) == b"QG_ELAUNCH"
+
+
+def test_sizes():
+    L = qg.lib()
+    assert L.qg_q8row_packed_bytes(256, 512) == 256 * 512
+    assert L.qg_q8row_packed_bytes(65, 20) == 128 * 32
+    assert L.qg_q8row_packed_bytes(10, 6) == 0
+    assert L.qg_q2_blocks_bytes(4096, 4096, 64) == 4096 * 64 * 18
+    assert L.qg_q2_blocks_bytes(17408, 5120, 128) == 17408 * 40 * 34
+    assert L.qg_q2_codes_bytes(100, 256) == 128 * 64
+    assert L.qg_q2_scales_bytes(100, 256, 128) == 128 * 2 * 2
+    assert L.qg_q2_scales_bytes(100, 200, 128) == 0
+    for M, K, g in [(4096, 4096, 64), (17408, 5120, 128), (5120, 17408, 128), (1, 64, 64)]:
+        S = L.qgemv_q2_auto_split(M, K, g)
+        assert 1 <= S <= 16
+        ws = L.qgemv_q2_ws_bytes(M, K, g, 0)
+        assert ws == (0 if S == 1 else S * ((M + 63) // 64 * 64) * 4)
+    assert L.qgemv_q2_ws_bytes(100, 256, 64, 1) == 0
+    assert L.qgemv_q2_ws_bytes(100, 256, 64, 4) == 4 * 128 * 4
+
+
+@pytest.mark.parametrize("M,K", [(1, 4), (63, 16), (64, 20), (70, 36), (130, 1028)])
+def test_q8_repack_layout(M, K):
+    rng = np.random.Generator(np.random.PCG64(M * 1000 + K))
+    q = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    p = qg.repack_q8row(q)
+    Mp, Kp = -(-M // 64) * 64, -(-K // 16) * 16
+    assert p.size == Mp * Kp
+    o, i = np.meshgrid(np.arange(M), np.arange(K), indexing="ij")
+    where = ((o // 64) * (Kp // 16) + i // 16) * 1024 + (o % 64) * 16 + i % 16
+    assert np.array_equal(p[where].view(np.int8), q)
+    mask = np.ones(p.size, bool)
+    mask[where.reshape(-1)] = False
+    assert np.all(p[mask] == 0)  # padding is zero
+    assert np.array_equal(qg.unpack_q8row(p, M, K), q)
+
+
+def decode_t64_codes(codes, M, K):
+    """Codes [M][K] read back from the T64 code plane per the header's layout."""
+    tiles = -(-M // 64)
+    nu = K // 64
+    u8 = codes.reshape(tiles, nu, 64, 4, 4)            # [tile][unit][row][word j][byte]
+    words = u8.astype(np.uint32)
+    w = words[..., 0] | (words[..., 1] << 8) | (words[..., 2] << 16) | (words[..., 3] << 24)
+    out = np.empty((tiles, 64, nu, 4, 4, 4), np.uint8)  # [tile][row][unit][j][a][b]
+    for a in range(4):
+        for b in range(4):
+            out[:, :, :, :, a, b] = ((w >> (8 * b + 2 * a)) & 3).transpose(0, 2, 1, 3)
+    return out.reshape(tiles * 64, K)[:M]
+
+
+@pytest.mark.parametrize("M,K,group", [(1, 64, 64), (65, 192, 64), (100, 256, 128), (64, 1024, 128)])
+def test_q2_repack_layout(M, K, group):
+    rng = np.random.Generator(np.random.PCG64(M + K + group))
+    codes = rng.integers(0, 4, size=(M, K), dtype=np.uint8)
+    d_bits = rng.integers(0, 1 << 15, size=(M, K // group), dtype=np.uint16)
+    blob = encode_q2(codes, d_bits, group)
+    cplane, splane = qg.repack_q2(blob, M, K, group)
+    tiles = -(-M // 64)
+    assert cplane.size == tiles * 64 * K // 4
+    assert np.array_equal(decode_t64_codes(cplane, M, K), codes)
+    s = splane.reshape(tiles, K // group, 64).transpose(0, 2, 1).reshape(tiles * 64, K // group)
+    assert np.array_equal(s[:M], d_bits)
+    assert np.all(s[M:] == 0)
+    assert np.all(decode_t64_codes(cplane, tiles * 64, K)[M:] == 0)
+    assert np.array_equal(qg.unpack_q2(cplane, splane, M, K, group), blob)
+
+
+def _einval(status):
+    assert status == qg.QG_EINVAL
+    assert qg.lib().qg_last_error()
+
+
+def test_einval_paths():
+    L = qg.lib()
+    P = ctypes.c_void_p
+    a16 = P(0x10000)  # never dereferenced: every call below fails validation
+    # q8_row GEMV
+    _einval(L.qgemv_q8row(None, a16, a16, a16, 64, 64, None))
+    _einval(L.qgemv_q8row(a16, a16, a16, a16, 0, 64, None))
+    _einval(L.qgemv_q8row(a16, a16, a16, a16, 64, 62, None))
+    _einval(L.qgemv_q8row(P(0x10004), a16, a16, a16, 64, 64, None))
+    _einval(L.qgemv_q8row(a16, a16, P(0x10004), a16, 64, 64, None))
+    # activation quantiser
+    _einval(L.qquant_act_i8(a16, 100, a16, a16, a16, None))
+    _einval(L.qquant_act_i8(a16, 0, a16, a16, a16, None))
+    _einval(L.qquant_act_i8(None, 64, a16, a16, a16, None))
+    _einval(L.qquant_act_i8(P(0x10008), 64, a16, a16, a16, None))
+    # Q2 GEMV
+    w = qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 64, 0)
+    bad = [qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 96, 0),
+           qg.qg_q2_weight(0x10000, 0x20000, 128, 200, 64, 0),
+           qg.qg_q2_weight(0x10000, 0x20000, 0, 256, 64, 0),
+           qg.qg_q2_weight(0, 0x20000, 128, 256, 64, 0),
+           qg.qg_q2_weight(0x10008, 0x20000, 128, 256, 64, 0),
+           qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 64, 7)]
+    for b in bad:
+        _einval(L.qgemv_q2(ctypes.byref(b), a16, a16, a16, a16, None, 0, 1, None))
+    _einval(L.qgemv_q2(None, a16, a16, a16, a16, None, 0, 1, None))
+    _einval(L.qgemv_q2(ctypes.byref(w), a16, a16, a16, a16, None, 0, 17, None))
+    _einval(L.qgemv_q2(ctypes.byref(w), a16, a16, a16, a16, None, 0, -1, None))
+    _einval(L.qgemv_q2(ctypes.byref(w), a16, a16, a16, a16, None, 0, 4, None))        # no workspace
+    _einval(L.qgemv_q2(ctypes.byref(w), a16, a16, a16, a16, a16, 100, 4, None))       # too small
+    _einval(L.qgemv_q2(ctypes.byref(w), P(0x10004), a16, a16, a16, None, 0, 1, None))  # xq misaligned
+    _einval(L.qgemv_q2_dots(ctypes.byref(w), a16, a16, a16, a16, None, None, 0, 1, None))
+    # host repacks
+    z = np.zeros(64, np.uint8)
+    _einval(L.qg_repack_q8row(None, 4, 4, z.ctypes.data, 64))
+    _einval(L.qg_repack_q8row(z.ctypes.data, 4, 4, z.ctypes.data, 10))
+    _einval(L.qg_repack_q2(z.ctypes.data, 17, 1, 64, 64, z.ctypes.data, 64, z.ctypes.data, 64))
+    _einval(L.qg_repack_q2(z.ctypes.data, 18, 1, 64, 32, z.ctypes.data, 64, z.ctypes.data, 64))
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(qg.QGError):
+        qg.repack_q2(np.zeros(10, np.uint8), 1, 64, 64)

@@ -1,0 +1,243 @@
+"""Python binding of libqgemv.so, the weight-only-quantized decode library.
+
+Argument marshalling only: every step of the computation runs in the
+library's HIP kernels (device entry points) or its C++ host repack.  Device
+tensors are torch tensors used as plain device memory; the stream is torch's
+current stream unless one is given.  Nothing here falls back to any other
+implementation: if the library is missing, or an entry point returns an
+error, a ``QGError`` is raised.
+
+Entry points mirror ``include/qgemv.h`` one for one, with the same names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+QG_OK, QG_EINVAL, QG_ELAUNCH = 0, 1, 2
+
+
+class QGError(RuntimeError):
+    """A non-OK status from the library (or the library is not built)."""
+
+    def __init__(self, fn, status, message):
+        super().__init__(f"{fn}: status {status}: {message}")
+        self.status = status
+
+
+class qg_q2_weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+_SIGS = {
+    "qg_status_string": (ctypes.c_char_p, [_I]),
+    "qg_last_error": (ctypes.c_char_p, []),
+    "qg_abi_version": (_I, []),
+    "qg_q8row_packed_bytes": (_SZ, [_I64, _I64]),
+    "qg_repack_q8row": (_I, [_P, _I64, _I64, _P, _SZ]),
+    "qg_unpack_q8row": (_I, [_P, _SZ, _I64, _I64, _P]),
+    "qgemv_q8row": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "qg_q2_blocks_bytes": (_SZ, [_I64, _I64, _I]),
+    "qg_q2_codes_bytes": (_SZ, [_I64, _I64]),
+    "qg_q2_scales_bytes": (_SZ, [_I64, _I64, _I]),
+    "qg_repack_q2": (_I, [_P, _SZ, _I64, _I64, _I, _P, _SZ, _P, _SZ]),
+    "qg_unpack_q2": (_I, [_P, _SZ, _P, _SZ, _I64, _I64, _I, _P, _SZ]),
+    "qquant_act_i8": (_I, [_P, _I64, _P, _P, _P, _P]),
+    "qgemv_q2_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
+    "qgemv_q2_auto_split": (_I, [_I64, _I64, _I]),
+    "qgemv_q2": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _SZ, _I, _P]),
+    "qgemv_q2_dots": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P, _SZ, _I, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises QGError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QGError("load", -1, f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != QG_OK:
+        raise QGError(fn, status, lib().qg_last_error().decode())
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev(t, dtype, name):
+    """Device pointer of a contiguous torch tensor of the given dtype."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise QGError(name, QG_EINVAL, "tensor is not on a HIP device")
+    if t.dtype != dtype:
+        raise QGError(name, QG_EINVAL, f"dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise QGError(name, QG_EINVAL, "tensor is not contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------- q8_row --
+def q8row_packed_bytes(M: int, K: int) -> int:
+    return lib().qg_q8row_packed_bytes(M, K)
+
+
+def repack_q8row(q: np.ndarray) -> np.ndarray:
+    """Host: row-major int8 [M][K] -> T64 image (uint8, flat)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    M, K = q.shape
+    n = lib().qg_q8row_packed_bytes(M, K)
+    if n == 0:
+        raise QGError("qg_repack_q8row", QG_EINVAL, f"bad shape {q.shape}")
+    out = np.empty(n, np.uint8)
+    _check("qg_repack_q8row", lib().qg_repack_q8row(_np_ptr(q), M, K, _np_ptr(out), n))
+    return out
+
+
+def unpack_q8row(packed: np.ndarray, M: int, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    q = np.empty((M, K), np.int8)
+    _check("qg_unpack_q8row", lib().qg_unpack_q8row(_np_ptr(packed), packed.nbytes, M, K, _np_ptr(q)))
+    return q
+
+
+def qgemv_q8row(qpacked, rs, xs, y, M: int, K: int, stream=None):
+    """y[o] = rs[o] * sum_i q[o,i] xs[i] on the device (all torch tensors)."""
+    import torch
+    _check("qgemv_q8row", lib().qgemv_q8row(
+        _dev(qpacked, torch.uint8, "qpacked"), _dev(rs, torch.float32, "rs"),
+        _dev(xs, torch.float32, "xs"), _dev(y, torch.float32, "y"), M, K, _stream(stream)))
+
+
+@dataclass
+class Q8RowWeight:
+    """A q8_row matrix resident on the device: T64 image + row scales."""
+    packed: object  # torch.uint8 device tensor
+    rs: object      # torch.float32 device tensor [M]
+    M: int
+    K: int
+
+    @classmethod
+    def from_host(cls, q: np.ndarray, rs: np.ndarray, device="cuda"):
+        import torch
+        packed = torch.from_numpy(repack_q8row(q)).to(device)
+        rs_t = torch.from_numpy(np.ascontiguousarray(rs, np.float32)).to(device)
+        return cls(packed, rs_t, q.shape[0], q.shape[1])
+
+    def gemv(self, xs, y, stream=None):
+        qgemv_q8row(self.packed, self.rs, xs, y, self.M, self.K, stream)
+
+
+# -------------------------------------------------------------------- Q2 --
+def q2_blocks_bytes(M, K, group):
+    return lib().qg_q2_blocks_bytes(M, K, group)
+
+
+def repack_q2(blocks: np.ndarray, M: int, K: int, group: int):
+    """Host: GGUF-style block blob -> (codes uint8 plane, scales uint16 plane)."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1)
+    nc = lib().qg_q2_codes_bytes(M, K)
+    ns = lib().qg_q2_scales_bytes(M, K, group)
+    if nc == 0 or ns == 0:
+        raise QGError("qg_repack_q2", QG_EINVAL, f"bad shape M={M} K={K} group={group}")
+    codes = np.empty(nc, np.uint8)
+    scales = np.empty(ns // 2, np.uint16)
+    _check("qg_repack_q2", lib().qg_repack_q2(_np_ptr(blocks), blocks.nbytes, M, K, group,
+                                              _np_ptr(codes), nc, _np_ptr(scales), ns))
+    return codes, scales
+
+
+def unpack_q2(codes: np.ndarray, scales: np.ndarray, M: int, K: int, group: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    out = np.empty(lib().qg_q2_blocks_bytes(M, K, group), np.uint8)
+    _check("qg_unpack_q2", lib().qg_unpack_q2(_np_ptr(codes), codes.nbytes, _np_ptr(scales), scales.nbytes,
+                                              M, K, group, _np_ptr(out), out.nbytes))
+    return out
+
+
+def qquant_act_i8(x, xq, act_scale, suma, stream=None):
+    """Per-vector int8 quantisation of x (f32[K]) into xq, act_scale[1], suma[K/64]."""
+    import torch
+    _check("qquant_act_i8", lib().qquant_act_i8(
+        _dev(x, torch.float32, "x"), x.numel(), _dev(xq, torch.int8, "xq"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
+
+
+def qgemv_q2_ws_bytes(M, K, group, split_k=0) -> int:
+    return lib().qgemv_q2_ws_bytes(M, K, group, split_k)
+
+
+def qgemv_q2_auto_split(M, K, group) -> int:
+    return lib().qgemv_q2_auto_split(M, K, group)
+
+
+@dataclass
+class Q2Weight:
+    """A Q2 matrix resident on the device: the two T64 planes."""
+    codes: object   # torch.uint8 device tensor
+    scales: object  # torch.int16 device tensor (binary16 bit patterns)
+    M: int
+    K: int
+    group: int
+
+    @classmethod
+    def from_blocks(cls, blocks: np.ndarray, M: int, K: int, group: int, device="cuda"):
+        import torch
+        c, s = repack_q2(blocks, M, K, group)
+        return cls(torch.from_numpy(c).to(device), torch.from_numpy(s.view(np.int16)).to(device), M, K, group)
+
+    def desc(self) -> qg_q2_weight:
+        import torch
+        return qg_q2_weight(_dev(self.codes, torch.uint8, "codes").value,
+                            _dev(self.scales, torch.int16, "scales").value,
+                            self.M, self.K, self.group, 0)
+
+
+def qgemv_q2(w: Q2Weight, xq, suma, act_scale, y, ws=None, split_k=0, stream=None):
+    """y = act_scale * sum_u d * dot_u on the device; ws is a uint8 tensor or None."""
+    import torch
+    d = w.desc()
+    wsp = _dev(ws, torch.uint8, "ws")
+    _check("qgemv_q2", lib().qgemv_q2(
+        ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(y, torch.float32, "y"),
+        wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
+
+
+def qgemv_q2_dots(w: Q2Weight, xq, suma, act_scale, y, dots, ws=None, split_k=0, stream=None):
+    """qgemv_q2 that also writes the exact int32 unit dots [M][K/64]."""
+    import torch
+    d = w.desc()
+    wsp = _dev(ws, torch.uint8, "ws")
+    _check("qgemv_q2_dots", lib().qgemv_q2_dots(
+        ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(y, torch.float32, "y"),
+        _dev(dots, torch.int32, "dots"), wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))

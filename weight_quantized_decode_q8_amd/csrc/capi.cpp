@@ -1,0 +1,127 @@
+// capi.cpp -- the C-ABI entry points: argument validation, then the launch.
+// Nothing is enqueued unless every argument checks out; there is no fallback.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qg_internal.h"
+
+namespace qg {
+
+namespace {
+thread_local char g_msg[512] = "";
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+qg_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(QG_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return QG_OK;
+}
+
+qg_status check_q2_weight(const qg_q2_weight *w, const char *fn) {
+  if (!w) return fail(QG_EINVAL, "%s: null weight descriptor", fn);
+  if (!w->codes || !w->scales) return fail(QG_EINVAL, "%s: null weight plane", fn);
+  if (w->reserved != 0) return fail(QG_EINVAL, "%s: reserved field must be 0", fn);
+  if (w->group != 64 && w->group != 128) return fail(QG_EINVAL, "%s: group %d is not 64 or 128", fn, w->group);
+  if (w->M < 1 || w->M > (1LL << 31) - 64) return fail(QG_EINVAL, "%s: bad M=%lld", fn, (long long)w->M);
+  if (w->K < w->group || w->K % w->group != 0 || w->K > (1 << 24))
+    return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of group %d (at most 2^24)", fn, (long long)w->K, w->group);
+  if (!aligned(w->codes, 16)) return fail(QG_EINVAL, "%s: codes plane not 16-byte aligned", fn);
+  if (!aligned(w->scales, 2)) return fail(QG_EINVAL, "%s: scales plane not 2-byte aligned", fn);
+  return QG_OK;
+}
+}  // namespace
+
+qg_status fail(qg_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+}  // namespace qg
+
+using qg::aligned;
+using qg::fail;
+
+extern "C" {
+
+const char *qg_status_string(qg_status s) {
+  switch (s) {
+    case QG_OK: return "QG_OK";
+    case QG_EINVAL: return "QG_EINVAL";
+    case QG_ELAUNCH: return "QG_ELAUNCH";
+  }
+  return "QG_UNKNOWN";
+}
+
+const char *qg_last_error(void) { return qg::g_msg; }
+
+int qg_abi_version(void) { return 1; }
+
+qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
+                      int64_t K, void *stream) {
+  const char *fn = "qgemv_q8row";
+  if (!qpacked || !rs || !xs || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (M < 1 || M > (1LL << 31) - 64) return fail(QG_EINVAL, "%s: bad M=%lld", fn, (long long)M);
+  if (K < 4 || K % 4 != 0 || K > (1 << 30)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 4", fn, (long long)K);
+  if (!aligned(qpacked, 16)) return fail(QG_EINVAL, "%s: weight image not 16-byte aligned", fn);
+  if (!aligned(xs, 16)) return fail(QG_EINVAL, "%s: xs not 16-byte aligned", fn);
+  if (!aligned(rs, 4) || !aligned(y, 4)) return fail(QG_EINVAL, "%s: rs/y not 4-byte aligned", fn);
+  return qg::launched(qg::launch_q8row_gemv(qpacked, rs, xs, y, (int)M, (int)K, (hipStream_t)stream), fn);
+}
+
+qg_status qquant_act_i8(const float *x, int64_t K, int8_t *xq, float *act_scale, int32_t *suma,
+                        void *stream) {
+  const char *fn = "qquant_act_i8";
+  if (!x || !xq || !act_scale || !suma) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (K < 64 || K % 64 != 0 || K > (1 << 24)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
+  if (!aligned(x, 16)) return fail(QG_EINVAL, "%s: x not 16-byte aligned", fn);
+  if (!aligned(xq, 4) || !aligned(act_scale, 4) || !aligned(suma, 4)) return fail(QG_EINVAL, "%s: misaligned output", fn);
+  return qg::launched(qg::launch_act_quant(x, (int)K, xq, act_scale, suma, (hipStream_t)stream), fn);
+}
+
+int qgemv_q2_auto_split(int64_t M, int64_t K, int group) {
+  if (M < 1 || (group != 64 && group != 128) || K < group || K % group) return 1;
+  return qg::q2_auto_split(M, K, group);
+}
+
+size_t qgemv_q2_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
+  if (M < 1 || (group != 64 && group != 128) || K < group || K % group) return 0;
+  const int S = split_k == 0 ? qg::q2_auto_split(M, K, group) : split_k;
+  if (S <= 1 || S > qg::kMaxSplit) return 0;
+  return (size_t)S * (size_t)qg::round_up(M, 64) * sizeof(float);
+}
+
+static qg_status q2_common(const char *fn, const qg_q2_weight *w, const int8_t *xq, const int32_t *suma,
+                           const float *act_scale, float *y, int32_t *dots, void *ws, size_t ws_bytes,
+                           int split_k, void *stream) {
+  qg_status st = qg::check_q2_weight(w, fn);
+  if (st != QG_OK) return st;
+  if (!xq || !suma || !act_scale || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!aligned(xq, 16)) return fail(QG_EINVAL, "%s: xq not 16-byte aligned", fn);
+  if (!aligned(suma, 4) || !aligned(act_scale, 4) || !aligned(y, 4) || (dots && !aligned(dots, 4)))
+    return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  if (split_k < 0 || split_k > qg::kMaxSplit) return fail(QG_EINVAL, "%s: split_k=%d outside 0..16", fn, split_k);
+  const int S = split_k == 0 ? qg::q2_auto_split(w->M, w->K, w->group) : split_k;
+  const size_t need = qgemv_q2_ws_bytes(w->M, w->K, w->group, S);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed for split %d", fn, ws ? ws_bytes : (size_t)0, need, S);
+  if (need > 0 && !aligned(ws, 4)) return fail(QG_EINVAL, "%s: workspace not 4-byte aligned", fn);
+  return qg::launched(qg::launch_q2_gemv(w->codes, w->scales, (int)w->M, (int)w->K, w->group, xq, suma, act_scale,
+                                         y, dots, static_cast<float *>(ws), S, (hipStream_t)stream),
+                      fn);
+}
+
+qg_status qgemv_q2(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
+                   float *y, void *ws, size_t ws_bytes, int split_k, void *stream) {
+  return q2_common("qgemv_q2", w, xq, suma, act_scale, y, nullptr, ws, ws_bytes, split_k, stream);
+}
+
+qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
+                        float *y, int32_t *dots, void *ws, size_t ws_bytes, int split_k, void *stream) {
+  if (!dots) return fail(QG_EINVAL, "qgemv_q2_dots: null dots");
+  return q2_common("qgemv_q2_dots", w, xq, suma, act_scale, y, dots, ws, ws_bytes, split_k, stream);
+}
+
+}  // extern "C"

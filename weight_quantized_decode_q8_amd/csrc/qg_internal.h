@@ -1,0 +1,39 @@
+// qg_internal.h -- private declarations shared by the library's translation
+// units: launchers (one per kernel family) and the error-message helper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qgemv.h"
+
+namespace qg {
+
+// Tiles of the T64 device formats: 64 rows, one row per lane of a wavefront.
+constexpr int kTileRows = 64;
+// q8_row chunk: 16 bytes of one row (one 128-bit load per lane).
+constexpr int kQ8Chunk = 16;
+// Q2 unit: 64 weights = 16 code bytes of one row.
+constexpr int kQ2Unit = 64;
+constexpr int kMaxSplit = 16;
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Records a formatted message for qg_last_error() and returns `s`.
+qg_status fail(qg_status s, const char *fmt, ...);
+
+// Launchers.  Arguments are validated by the C-ABI layer before any call.
+hipError_t launch_act_quant(const float *x, int K, int8_t *xq, float *act_scale,
+                            int32_t *suma, hipStream_t stream);
+
+hipError_t launch_q8row_gemv(const void *qpacked, const float *rs, const float *xs,
+                             float *y, int M, int K, hipStream_t stream);
+
+hipError_t launch_q2_gemv(const void *codes, const void *scales, int M, int K, int group,
+                          const int8_t *xq, const int32_t *suma, const float *act_scale,
+                          float *y, int32_t *dots, float *partials, int split,
+                          hipStream_t stream);
+
+int q2_auto_split(int64_t M, int64_t K, int group);
+
+}  // namespace qg
