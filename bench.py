@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-only-quantized decode hot path on one MI355X.
+
+A step is one pass of the batch-1 decode path at the pages' model shapes,
+captured once in a HIP graph and replayed:
+    quantise x (K=5120) -> Q2 g128 gate GEMV 17408x5120 -> Q2 g128 up GEMV
+    -> quantise h (K=17408) -> Q2 g128 down GEMV 5120x17408
+    -> q8_row lm_head GEMV 248320x5120.
+`value` is the weight bytes the step streams (the formats' own bytes: 34 B
+per 128 Q2 weights, K+4 bytes per q8_row row) divided by the step time:
+batch-1 quantized GEMV weight GB/s.  Inputs are synthetic and seeded, already
+resident in HBM when timing starts.  The lm_head stream (1.27 GB) evicts the
+256 MB last-level cache every step, so the FFN weights also come from HBM.
+
+Also reported: per-kernel times and roofline fractions, the dominant
+kernel's roofline (HIP events on the launch stream), and the CPU oracle timed
+on this host over the same step (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "q8row_gemv_lm_head_248320x5120_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "weight_quantized_decode_q8_amd", "csrc", "q8row_gemv.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel timing table (for counter runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    return ap.parse_args()
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """Bytes per lm_head launch from the committed counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != src_sha(KERNEL_SRC):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(row sharding across GPUs is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_quantized_decode_q8_amd as qg
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    # ---------------- inputs (seeded, synthetic; shapes of the pages' model)
+    t0 = time.time()
+    host = {}
+    for name in ("C3_gate", "C3_up", "C3_down"):
+        host[name] = synth.config_inputs(name)
+    q4, rs4, xs4 = synth.config_inputs("C4")
+    x_dn = host["C3_down"][1]
+    x_gu = host["C3_gate"][1]
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    W = {}
+    for name in ("C3_gate", "C3_up", "C3_down"):
+        c = synth.CONFIGS[name]
+        W[name] = qg.Q2Weight.from_blocks(host[name][0], c["M"], c["K"], c["group"], dev)
+    L4 = qg.Q8RowWeight.from_host(q4, rs4, dev)
+    M4, K4 = q4.shape
+    xs4_d = torch.from_numpy(xs4).to(dev)
+    xgu_d = torch.from_numpy(x_gu).to(dev)
+    xdn_d = torch.from_numpy(x_dn).to(dev)
+    Kgu, Kdn = x_gu.size, x_dn.size
+    xq_gu = torch.empty(Kgu, dtype=torch.int8, device=dev)
+    xq_dn = torch.empty(Kdn, dtype=torch.int8, device=dev)
+    sc_gu = torch.empty(1, dtype=torch.float32, device=dev)
+    sc_dn = torch.empty(1, dtype=torch.float32, device=dev)
+    su_gu = torch.empty(Kgu // 64, dtype=torch.int32, device=dev)
+    su_dn = torch.empty(Kdn // 64, dtype=torch.int32, device=dev)
+    y = {n: torch.empty(W[n].M, dtype=torch.float32, device=dev) for n in W}
+    y4 = torch.empty(M4, dtype=torch.float32, device=dev)
+    ws = {n: torch.zeros(max(1, qg.qgemv_q2_ws_bytes(W[n].M, W[n].K, W[n].group, 0)),
+                         dtype=torch.uint8, device=dev) for n in W}
+    log(f"inputs resident in HBM after {time.time() - t0:.1f}s")
+
+    def k_quant_gu():
+        qg.qquant_act_i8(xgu_d, xq_gu, sc_gu, su_gu)
+
+    def k_quant_dn():
+        qg.qquant_act_i8(xdn_d, xq_dn, sc_dn, su_dn)
+
+    def k_gate():
+        qg.qgemv_q2(W["C3_gate"], xq_gu, su_gu, sc_gu, y["C3_gate"], ws["C3_gate"])
+
+    def k_up():
+        qg.qgemv_q2(W["C3_up"], xq_gu, su_gu, sc_gu, y["C3_up"], ws["C3_up"])
+
+    def k_down():
+        qg.qgemv_q2(W["C3_down"], xq_dn, su_dn, sc_dn, y["C3_down"], ws["C3_down"])
+
+    def k_lm_head():
+        L4.gemv(xs4_d, y4)
+
+    def step():
+        k_quant_gu()
+        k_gate()
+        k_up()
+        k_quant_dn()
+        k_down()
+        k_lm_head()
+
+    q2_bytes = {n: W[n].M * (W[n].K // W[n].group) * (2 + W[n].group // 4) for n in W}
+    lm_bytes = M4 * (K4 + 4)
+    step_bytes = sum(q2_bytes.values()) + lm_bytes
+
+    # ---------------- eager reference run, then graph capture
+    step()
+    torch.cuda.synchronize()
+    ref = {n: y[n].clone() for n in y}
+    ref4 = y4.clone()
+
+    def capture(fn, n=1):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        return g
+
+    g_step = capture(step)
+    for _ in range(3):
+        g_step.replay()
+        torch.cuda.synchronize()
+        for n in y:
+            assert torch.equal(y[n], ref[n]), f"graph replay of {n} differs from eager"
+        assert torch.equal(y4, ref4), "graph replay of lm_head differs from eager"
+
+    # ---------------- timed region: K steps
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        g_step.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s (wall {wall * 1e6 / args.steps:.1f} us/step)")
+
+    # ---------------- per-kernel times (graph of n back-to-back launches)
+    def kernel_us(fn, n):
+        g = capture(fn, n)
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * n)
+
+    kernels = {}
+    for name, fn, nbytes, n in [] if args.no_breakdown else [("act_quant_K5120", k_quant_gu, None, 50),
+                                ("q2_gate_17408x5120_g128", k_gate, q2_bytes["C3_gate"], 20),
+                                ("q2_up_17408x5120_g128", k_up, q2_bytes["C3_up"], 20),
+                                ("act_quant_K17408", k_quant_dn, None, 50),
+                                ("q2_down_5120x17408_g128", k_down, q2_bytes["C3_down"], 20),
+                                ("q8row_lm_head_248320x5120", k_lm_head, lm_bytes, 10)]:
+        us = kernel_us(fn, n)
+        ent = {"us": round(us, 3)}
+        if nbytes:
+            gbs = nbytes / us / 1e3
+            ent.update({"weight_bytes": nbytes, "GB/s": round(gbs, 1),
+                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        kernels[name] = ent
+        log(f"  {name}: {ent}")
+
+    # ---------------- dominant kernel roofline: HIP events on its stream
+    n_dom = 20
+    k_lm_head()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n_dom):
+        k_lm_head()
+    b.record(stream)
+    torch.cuda.synchronize()
+    dom_us = a.elapsed_time(b) * 1e3 / n_dom
+    achieved = lm_bytes / dom_us / 1e3
+    roofline = {"bound": "hbm", "kernel": "q8row_gemv_t64 (lm_head 248320x5120)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                "avg_launch_us": round(dom_us, 2), "algorithmic_bytes_per_launch": lm_bytes}
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---------------- CPU oracle over the same step, on this host
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        def oracle_step():
+            rq, rsc, _ = oracle.act_quant_i8(x_gu)
+            for name in ("C3_gate", "C3_up"):
+                c = synth.CONFIGS[name]
+                oracle.q2_gemv(host[name][0], c["M"], c["K"], c["group"], rq, rsc)
+            rq, rsc, _ = oracle.act_quant_i8(x_dn)
+            c = synth.CONFIGS["C3_down"]
+            oracle.q2_gemv(host["C3_down"][0], c["M"], c["K"], c["group"], rq, rsc)
+            oracle.q8row_gemv(q4, rs4, xs4)
+
+        # whole steps until about 10 s of CPU work (at least one)
+        c0 = time.perf_counter()
+        passes = 0
+        while passes == 0 or time.perf_counter() - c0 < 10.0:
+            oracle_step()
+            passes += 1
+        cpu_s = (time.perf_counter() - c0) / passes
+        cpu = {"value": round(step_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "seconds_per_step": round(cpu_s, 3), "passes": passes,
+               "sample": f"{passes} whole decode steps (all six kernels' work) by the fp64 C oracle, "
+                         "single thread, mean per step"}
+        log(f"cpu oracle: {cpu}")
+
+    out = {
+        "metric": "batch-1 quantized GEMV weight GB/s (% of HBM peak); prefill GEMM TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "dtype": "f32",
+        "dtype_detail": "q8_row: int8 weights x f32 activations, f32 accumulate; Q2: 2-bit codes x int8 "
+                        "activations, exact int32 unit dots, f32 scale accumulate",
+        "data": "synthetic",
+        "config": {"workload": "decode_step_batch1: act-quant + Q2 g128 FFN (gate, up 17408x5120; "
+                               "down 5120x17408) + q8_row lm_head 248320x5120",
+                   "step_weight_bytes": step_bytes, "graph": "hipGraph of the six launches",
+                   "parallelism": "single GPU"},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
