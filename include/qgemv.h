@@ -186,6 +186,39 @@ qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq,
                         float *y, int32_t *dots, void *ws, size_t ws_bytes,
                         int split_k, void *stream);
 
+/* ======================================================================
+ * Batched prefill q8_row GEMM  [Q8, q8_matmat / q8_mul_mm]
+ *
+ *   y[b, o] = rs[o] * sum_i q[o, i] * xs[b, i]
+ *
+ * The weights are exact int8 in the T64 image (the same image qgemv_q8row
+ * reads).  The f32 activations are split exactly into int8 limbs of a
+ * per-row fixed-point value, xs[b, i] ~= 2^e_b * (h*65536 + m*256 + l)
+ * (24 bits, rounded to nearest; 2^e_b the smallest power of two bringing
+ * max_i |xs[b, i]| to at most 126*65536), and each limb is an exact int8
+ * MFMA product with int32 accumulation.  xs_limbs selects the form:
+ *   3  all three limbs (24-bit activations);
+ *   2  the two upper limbs only (16-bit activations, 2/3 of the work);
+ *   0  auto: per 128 rows of xs, 2 limbs when every row satisfies
+ *      2^(e_b+8) <= 0.9e-5 * sum_i |xs[b,i]| / sqrt(K) (the 16-bit error
+ *      then stays well inside 2e-5 * sum_i |w_i xs_i| for q8_row weights),
+ *      else 3 limbs.
+ * Arguments:
+ *   qpacked: device, T64 image of q [M][K] (16-byte aligned);
+ *   rs: device f32[M];  xs: device f32[nb][K] row-major (16-byte aligned);
+ *   y: device f32[nb][M] row-major, written;
+ *   ws: device workspace, 256-byte aligned, >= qgemm_q8row_batched_ws_bytes
+ *       (nb, K) bytes; holds the limbs and per-row exponents; contents on
+ *       entry are ignored.
+ * QG_EINVAL: null pointer, nb < 1, M < 1, K < 4 or K % 4 != 0, xs_limbs
+ * not 0/2/3, misalignment, workspace too small.                          */
+size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K);
+
+qg_status qgemm_q8row_batched(const void *qpacked, const float *rs,
+                              const float *xs, float *y, int64_t nb,
+                              int64_t M, int64_t K, int xs_limbs, void *ws,
+                              size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,8 @@ _SIGS = {
     "qgemv_q2_auto_split": (_I, [_I64, _I64, _I]),
     "qgemv_q2": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qgemv_q2_dots": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P, _SZ, _I, _P]),
+    "qgemm_q8row_batched_ws_bytes": (_SZ, [_I64, _I64]),
+    "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -65,6 +67,13 @@ def lib():
     """The loaded library (raises QGError when it has not been built)."""
     global _lib
     if _lib is None:
+        # Load torch first so that the HIP runtime soname the library needs
+        # resolves to the runtime torch already uses: one runtime per process,
+        # so torch's streams and allocations are valid handles here.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise QGError("load", -1, f"{LIB_PATH} is not built (run __graft_entry__.build())")
         L = ctypes.CDLL(LIB_PATH)
@@ -241,3 +250,17 @@ def qgemv_q2_dots(w: Q2Weight, xq, suma, act_scale, y, dots, ws=None, split_k=0,
         ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(y, torch.float32, "y"),
         _dev(dots, torch.int32, "dots"), wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
+
+
+# ------------------------------------------------------ batched q8_row GEMM --
+def qgemm_q8row_batched_ws_bytes(nb: int, K: int) -> int:
+    return lib().qgemm_q8row_batched_ws_bytes(nb, K)
+
+
+def qgemm_q8row_batched(qpacked, rs, xs, y, nb: int, M: int, K: int, ws, xs_limbs: int = 0, stream=None):
+    """y[b,o] = rs[o] * sum_i q[o,i] xs[b,i] (xs [nb][K], y [nb][M]); ws a uint8 tensor."""
+    import torch
+    _check("qgemm_q8row_batched", lib().qgemm_q8row_batched(
+        _dev(qpacked, torch.uint8, "qpacked"), _dev(rs, torch.float32, "rs"),
+        _dev(xs, torch.float32, "xs"), _dev(y, torch.float32, "y"), nb, M, K, xs_limbs,
+        _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)))

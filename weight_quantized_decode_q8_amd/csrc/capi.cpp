@@ -124,4 +124,30 @@ qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq, const int32_t *
   return q2_common("qgemv_q2_dots", w, xq, suma, act_scale, y, dots, ws, ws_bytes, split_k, stream);
 }
 
+size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K) {
+  if (nb < 1 || K < 4 || K % 4 != 0) return 0;
+  size_t a, b;
+  return qg::gemm_ws_layout(nb, K, &a, &b);
+}
+
+qg_status qgemm_q8row_batched(const void *qpacked, const float *rs, const float *xs, float *y,
+                              int64_t nb, int64_t M, int64_t K, int xs_limbs, void *ws,
+                              size_t ws_bytes, void *stream) {
+  const char *fn = "qgemm_q8row_batched";
+  if (!qpacked || !rs || !xs || !y || !ws) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (nb < 1 || nb > (1 << 24)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
+  if (M < 1 || M > (1LL << 31) - 256) return fail(QG_EINVAL, "%s: bad M=%lld", fn, (long long)M);
+  if (K < 4 || K % 4 != 0 || K > (1 << 24)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 4", fn, (long long)K);
+  if (nb * M > (1LL << 40) || qg::round_up(nb, 128) * qg::round_up(K, 64) * 3 > (1LL << 40))
+    return fail(QG_EINVAL, "%s: problem too large", fn);
+  if (xs_limbs != 0 && xs_limbs != 2 && xs_limbs != 3) return fail(QG_EINVAL, "%s: xs_limbs=%d must be 0, 2 or 3", fn, xs_limbs);
+  if (!aligned(qpacked, 16) || !aligned(xs, 16) || !aligned(ws, 256))
+    return fail(QG_EINVAL, "%s: qpacked and xs must be 16-byte aligned, ws 256-byte aligned", fn);
+  if (!aligned(rs, 4) || !aligned(y, 4)) return fail(QG_EINVAL, "%s: rs/y not 4-byte aligned", fn);
+  const size_t need = qgemm_q8row_batched_ws_bytes(nb, K);
+  if (ws_bytes < need) return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  return qg::launched(qg::launch_q8row_gemm(qpacked, rs, xs, y, (int)nb, (int)M, (int)K, xs_limbs, ws,
+                                            (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

@@ -1,0 +1,311 @@
+// q8row_gemm.hip -- batched prefill q8_row product on int8 MFMA.
+//
+// What is computed (cortiq-engine 0.5.43 gpu_wgpu.rs page, q8_matmat and
+// q8_mul_mm; cortiq-engine 0.3.7 gpu_metal.rs page, q8_matmat / q8_mul_mm):
+//     y[b, o] = rs[o] * sum_i q[o, i] * xs[b, i]
+// with xs [nb][K] and y [nb][M] row-major and the weights in the T64 image.
+//
+// Precision scheme (differs from the Metal page, whose fast kernel rounds
+// w*rs and xs to half): the weights stay exact int8 and the f32 activations
+// are split exactly into int8 limbs of a per-row fixed-point value:
+//     xs[b, i] ~= 2^e_b * (h * 65536 + m * 256 + l),  h, m, l in [-128, 127]
+// where 2^e_b is the smallest power of two that brings max_i |xs[b, i]| to
+// at most 126 * 65536 (a 24-bit value rounded to nearest).  Each limb is a
+// separate exact int8 x int8 -> int32 MFMA product; the limbs' int32 sums
+// are combined in f32 and scaled by rs[o] and 2^e_b at the end.  Dropping
+// the lowest limb gives the 2-limb (16-bit) form at 2/3 of the MFMA work;
+// its rounding is then 0.5 * 2^(e_b + 8) per element.
+//
+// The limb count is 3, 2, or chosen per 64-row tile of xs ("auto"): a tile
+// uses 2 limbs only when, for every row, 2^(e_b + 8) <= 0.9e-5 * sum|xs_b| /
+// sqrt(K).  With weights of the q8_row distribution (E|q| / sqrt(E q^2) >=
+// 0.8) this keeps the 16-bit rounding error of every output below 1/6 of
+// 2e-5 * sum_i |w_i x_i| at six standard deviations; rows with a large
+// max/mean ratio (activation outliers) get the 24-bit form.
+//
+// gfx950 kernel: v_mfma_i32_16x16x64_i8 (A row and B column = lane % 16, the
+// 16-byte k chunk = lane / 16, D[4 * (lane / 16) + v][lane % 16]), a 256 x 128
+// (2 limbs) or 256 x 64 (3 limbs) output tile per 4-wave workgroup with
+// 256 accumulator registers per lane, operands staged through LDS in two
+// buffers, and a block order that puts the workgroups sharing one weight
+// tile on the same XCD (the same L2) at the same time.
+#include "qg_internal.h"
+
+namespace qg {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTM = 256;       // weight rows (outputs o) per workgroup
+constexpr int kKS = 64;        // K bytes per pipeline stage (one MFMA depth)
+constexpr int kCPS = kKS / 16; // 16-byte chunks per stage
+constexpr int kLimbMax = 3;
+constexpr int kR3 = 126 * 65536;  // largest |fixed-point value|, 3 limbs
+
+// ------------------------------------------------------------- prep kernel
+// One workgroup per (padded) row b of xs.  Writes the three limbs in the
+// same tiled form as the weights: limb l, row b, 16-byte chunk c at
+//   ((l * nbt + b / 64) * nchunk + c) * 64 + b % 64        (16-byte units)
+// plus the row's exponent e_b and whether it needs the third limb.
+__global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict__ xs, int nb, int K,
+                                                        int nchunk, int nbt, i32x4 *__restrict__ xl,
+                                                        int *__restrict__ xexp, int *__restrict__ need3) {
+  __shared__ float red_max[4], red_sum[4];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const bool live = b < nb;
+  const float *row = xs + (size_t)b * K;
+
+  float amax = 0.0f, asum = 0.0f;
+  if (live) {
+    for (int k = tid * 4; k < K; k += 256 * 4) {  // K % 4 == 0, rows 16-byte aligned
+      const float4 v = *reinterpret_cast<const float4 *>(row + k);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      asum += (fabsf(v.x) + fabsf(v.y)) + (fabsf(v.z) + fabsf(v.w));
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, off));
+    asum += __shfl_xor(asum, off);
+  }
+  if ((tid & 63) == 0) {
+    red_max[tid >> 6] = amax;
+    red_sum[tid >> 6] = asum;
+  }
+  __syncthreads();
+  amax = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+  asum = (red_sum[0] + red_sum[1]) + (red_sum[2] + red_sum[3]);
+
+  // Smallest e with amax <= kR3 * 2^e (kR3 * 2^e is exact in f32).
+  int e = 0;
+  if (amax > 0.0f) {
+    e = ilogbf(amax) - 22;
+    while (amax > ldexpf((float)kR3, e)) e++;
+    while (amax <= ldexpf((float)kR3, e - 1)) e--;
+  }
+  if (tid == 0) {
+    xexp[b] = e;
+    const float thresh = 0.9e-5f * asum / sqrtf((float)K);
+    need3[b] = (amax > 0.0f && ldexpf(1.0f, e + 8) > thresh) ? 1 : 0;
+  }
+
+  for (int c = tid; c < nchunk; c += 256) {
+    int lim[kLimbMax][4];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      lim[0][w] = lim[1][w] = lim[2][w] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int k = c * 16 + w * 4 + j;
+        const float x = (live && k < K) ? row[k] : 0.0f;
+        int v = (int)rintf(ldexpf(x, -e));  // exact scaling, then nearest
+        const int lo = ((v + 128) & 255) - 128;
+        v = (v - lo) >> 8;
+        const int mi = ((v + 128) & 255) - 128;
+        const int hi = (v - mi) >> 8;
+        lim[0][w] |= (hi & 255) << (8 * j);
+        lim[1][w] |= (mi & 255) << (8 * j);
+        lim[2][w] |= (lo & 255) << (8 * j);
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < kLimbMax; l++)
+      xl[((size_t)(l * nbt + b / 64) * nchunk + c) * 64 + (b & 63)] =
+          i32x4{lim[l][0], lim[l][1], lim[l][2], lim[l][3]};
+  }
+}
+
+// ------------------------------------------------------------- GEMM kernel
+// L limbs, TN rows of xs (outputs b) per workgroup; 4 waves as 2 (o) x 2 (b).
+template <int L, int TN>
+struct GemmShape {
+  static constexpr int kWaveO = kTM / 2;               // 128 outputs o per wave
+  static constexpr int kWaveB = TN / 2;                // outputs b per wave
+  static constexpr int kOB = kWaveO / 16;              // 16-row MFMA blocks along o
+  static constexpr int kBB = kWaveB / 16;              // 16-column blocks along b
+  static constexpr int kAPieces = kTM / 64 * kCPS * 64;  // 16-byte pieces per stage
+  static constexpr int kBPieces = L * (TN / 64) * kCPS * 64;
+};
+
+template <int L, int TN>
+__global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
+    const i32x4 *__restrict__ w, const float *__restrict__ rs, const i32x4 *__restrict__ xl,
+    const int *__restrict__ xexp, const int *__restrict__ need3, float *__restrict__ y, int nb,
+    int M, int nchunk_w, int nchunk, int nbt64, int n_ot, int n_bt, int mode) {
+  using S = GemmShape<L, TN>;
+  __shared__ i32x4 As[2][S::kAPieces];
+  __shared__ i32x4 Bs[2][S::kBPieces];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wo = wave >> 1, wb = wave & 1;
+
+  // Block order: the n_bt workgroups of one weight tile get ids 8 apart, so
+  // the round-robin dispatch over the 8 XCDs puts them on one XCD together.
+  const int id = blockIdx.x;
+  const int per_grp = 8 * n_bt;
+  const int ot = (id / per_grp) * 8 + (id % per_grp) % 8;
+  const int bt = (id % per_grp) / 8;
+  if (ot >= n_ot) return;
+
+  // Auto mode: a 128-row group of xs rows goes to the 3-limb kernel if any
+  // of its rows needs the third limb, else to the 2-limb kernel.
+  if (mode == 1) {
+    const int g0 = (bt * TN) / 128 * 128;
+    const int f = need3[g0 + lane] | need3[g0 + 64 + lane];
+    const bool grp3 = __builtin_amdgcn_ballot_w64(f != 0) != 0;
+    if (grp3 != (L == 3)) return;
+  }
+
+  const int o_tile0 = ot * (kTM / 64);  // first 64-row weight tile
+  const int m_tiles = (M + 63) / 64;
+  const int b_tile0 = bt * (TN / 64);   // first 64-row limb tile
+
+  // Global -> register staging for one stage (k chunks c0 .. c0+3).
+  i32x4 ra[S::kAPieces / 256];
+  i32x4 rb[S::kBPieces / 256];
+  auto load_stage = [&](int step) {
+    const int c0 = step * kCPS;
+#pragma unroll
+    for (int i = 0; i < S::kAPieces / 256; i++) {
+      const int p = tid + 256 * i;
+      const int rt = p / (kCPS * 64), kc = (p / 64) % kCPS, r = p % 64;
+      const int t = o_tile0 + rt, c = c0 + kc;
+      ra[i] = (t < m_tiles && c < nchunk_w)
+                  ? __builtin_nontemporal_load(w + ((size_t)t * nchunk_w + c) * 64 + r)
+                  : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < S::kBPieces / 256; i++) {
+      const int p = tid + 256 * i;
+      const int l = p / ((TN / 64) * kCPS * 64);
+      const int q = p % ((TN / 64) * kCPS * 64);
+      const int bt64 = q / (kCPS * 64), kc = (q / 64) % kCPS, r = q % 64;
+      rb[i] = xl[((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + c0 + kc) * 64 + r];
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < S::kAPieces / 256; i++) As[buf][tid + 256 * i] = ra[i];
+#pragma unroll
+    for (int i = 0; i < S::kBPieces / 256; i++) Bs[buf][tid + 256 * i] = rb[i];
+  };
+
+  i32x4 acc[S::kOB][S::kBB][L];
+#pragma unroll
+  for (int a = 0; a < S::kOB; a++)
+#pragma unroll
+    for (int c = 0; c < S::kBB; c++)
+#pragma unroll
+      for (int l = 0; l < L; l++) acc[a][c][l] = i32x4{0, 0, 0, 0};
+
+  const int nsteps = nchunk / kCPS;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+
+  const int kc = lane >> 4, r16 = lane & 15;
+  for (int step = 0; step < nsteps; step++) {
+    const int buf = step & 1;
+    if (step + 1 < nsteps) load_stage(step + 1);
+
+    i32x4 bf[S::kBB][L];
+#pragma unroll
+    for (int c = 0; c < S::kBB; c++) {
+      const int bcol = wb * S::kWaveB + c * 16 + r16;  // 0 .. TN-1
+#pragma unroll
+      for (int l = 0; l < L; l++)
+        bf[c][l] = Bs[buf][((l * (TN / 64) + bcol / 64) * kCPS + kc) * 64 + (bcol & 63)];
+    }
+#pragma unroll
+    for (int a = 0; a < S::kOB; a++) {
+      const int orow = wo * S::kWaveO + a * 16 + r16;  // 0 .. 255
+      const i32x4 af = As[buf][((orow / 64) * kCPS + kc) * 64 + (orow & 63)];
+#pragma unroll
+      for (int c = 0; c < S::kBB; c++)
+#pragma unroll
+        for (int l = 0; l < L; l++)
+          acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c][l], acc[a][c][l], 0, 0, 0);
+    }
+
+    if (step + 1 < nsteps) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: combine the limbs in f32, apply rs[o] and 2^e_b.
+#pragma unroll
+  for (int c = 0; c < S::kBB; c++) {
+    const int b = bt * TN + wb * S::kWaveB + c * 16 + r16;
+    if (b >= nb) continue;
+    const int e = xexp[b] + (L == 2 ? 8 : 0);
+#pragma unroll
+    for (int a = 0; a < S::kOB; a++) {
+      const int o0 = ot * kTM + wo * S::kWaveO + a * 16 + 4 * kc;
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int o = o0 + v;
+        if (o >= M) continue;
+        float val;
+        if (L == 2)
+          val = (float)acc[a][c][0][v] * 256.0f + (float)acc[a][c][1][v];
+        else
+          val = ((float)acc[a][c][0][v] * 65536.0f + (float)acc[a][c][1][v] * 256.0f) +
+                (float)acc[a][c][2][v];
+        y[(size_t)b * M + o] = ldexpf(val * rs[o], e);
+      }
+    }
+  }
+}
+
+template <int L, int TN>
+hipError_t launch_gemm(const void *w, const float *rs, const i32x4 *xl, const int *xexp,
+                       const int *need3, float *y, int nb, int nbp, int M, int nchunk_w,
+                       int nchunk, int mode, hipStream_t stream) {
+  const int n_ot = (M + kTM - 1) / kTM;
+  const int n_bt = nbp / TN;
+  const int grid = (n_ot + 7) / 8 * 8 * n_bt;
+  q8row_gemm_kernel<L, TN><<<grid, 256, 0, stream>>>(
+      reinterpret_cast<const i32x4 *>(w), rs, xl, xexp, need3, y, nb, M, nchunk_w, nchunk,
+      nbp / 64, n_ot, n_bt, mode);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need) {
+  const int64_t nbp = round_up(nb, 128);
+  const int64_t kp = round_up(K, kKS);
+  const size_t limbs = (size_t)kLimbMax * nbp * kp;
+  *off_exp = (size_t)round_up(limbs, 256);
+  *off_need = *off_exp + (size_t)round_up(nbp * 4, 256);
+  return *off_need + (size_t)round_up(nbp * 4, 256);
+}
+
+hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, float *y, int nb,
+                             int M, int K, int limbs, void *ws, hipStream_t stream) {
+  size_t off_exp, off_need;
+  gemm_ws_layout(nb, K, &off_exp, &off_need);
+  const int nbp = (int)round_up(nb, 128);
+  const int nchunk = (int)(round_up(K, kKS) / 16);
+  const int nchunk_w = (int)(round_up(K, 16) / 16);
+  char *base = static_cast<char *>(ws);
+  i32x4 *xl = reinterpret_cast<i32x4 *>(base);
+  int *xexp = reinterpret_cast<int *>(base + off_exp);
+  int *need3 = reinterpret_cast<int *>(base + off_need);
+
+  gemm_prep_kernel<<<nbp, 256, 0, stream>>>(xs, nb, K, nchunk, nbp / 64, xl, xexp, need3);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (limbs == 2 || limbs == 0) {
+    err = launch_gemm<2, 128>(w, rs, xl, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
+                              limbs == 0 ? 1 : 0, stream);
+    if (err != hipSuccess) return err;
+  }
+  if (limbs == 3 || limbs == 0)
+    err = launch_gemm<3, 64>(w, rs, xl, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
+                             limbs == 0 ? 1 : 0, stream);
+  return err;
+}
+
+}  // namespace qg
