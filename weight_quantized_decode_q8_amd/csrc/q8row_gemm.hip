@@ -36,7 +36,6 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTM = 256;       // weight rows (outputs o) per workgroup
 constexpr int kKS = 64;        // K bytes per pipeline stage (one MFMA depth)
 constexpr int kCPS = kKS / 16; // 16-byte chunks per stage
 constexpr int kLimbMax = 3;
@@ -90,14 +89,24 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict_
   }
 
   for (int c = tid; c < nchunk; c += 256) {
+    float xv[16];
+    if (live && c * 16 + 16 <= K) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float4 v = *reinterpret_cast<const float4 *>(row + c * 16 + 4 * q);
+        xv[4 * q] = v.x, xv[4 * q + 1] = v.y, xv[4 * q + 2] = v.z, xv[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; j++) xv[j] = (live && c * 16 + j < K) ? row[c * 16 + j] : 0.0f;
+    }
     int lim[kLimbMax][4];
 #pragma unroll
     for (int w = 0; w < 4; w++) {
       lim[0][w] = lim[1][w] = lim[2][w] = 0;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const int k = c * 16 + w * 4 + j;
-        const float x = (live && k < K) ? row[k] : 0.0f;
+        const float x = xv[w * 4 + j];
         int v = (int)rintf(ldexpf(x, -e));  // exact scaling, then nearest
         const int lo = ((v + 128) & 255) - 128;
         v = (v - lo) >> 8;
@@ -116,15 +125,26 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict_
 }
 
 // ------------------------------------------------------------- GEMM kernel
-// L limbs, TN rows of xs (outputs b) per workgroup; 4 waves as 2 (o) x 2 (b).
+// One workgroup of 4 waves computes a kTM x TN block of y^T: kTM = 272 weight
+// rows (17 MFMA row blocks; 17408 = 64 * 272, so the pages' FFN width gives
+// exactly 256 blocks per 128 xs rows, one per CU) by TN rows of xs.  Every
+// wave owns all 272 weight rows and TN/4 xs rows, so the A fragments are
+// shared through LDS and each wave keeps 17 x (TN/64) x L accumulator tiles.
+constexpr int kOB = 17;
+constexpr int kTM = 16 * kOB;  // 272
+
 template <int L, int TN>
 struct GemmShape {
-  static constexpr int kWaveO = kTM / 2;               // 128 outputs o per wave
-  static constexpr int kWaveB = TN / 2;                // outputs b per wave
-  static constexpr int kOB = kWaveO / 16;              // 16-row MFMA blocks along o
-  static constexpr int kBB = kWaveB / 16;              // 16-column blocks along b
-  static constexpr int kAPieces = kTM / 64 * kCPS * 64;  // 16-byte pieces per stage
-  static constexpr int kBPieces = L * (TN / 64) * kCPS * 64;
+  static constexpr int kWB = TN / 4;                  // xs rows per wave
+  static constexpr int kBB = kWB / 16;                // 16-column MFMA blocks per wave
+  static constexpr int kAPieces = kTM * kCPS;         // 16-byte pieces of A per stage
+  static constexpr int kBPieces = L * TN * kCPS;      // 16-byte pieces of B per stage
+  static constexpr int kAPerT = (kAPieces + 255) / 256;
+  static constexpr int kBPerT = kBPieces / 256;
+  static constexpr int kStageBytes = (kAPieces + kBPieces) * 16;
+  static constexpr int kRowStride = kTM + 4;          // epilogue row stride (floats)
+  static constexpr int kEpiBytes = 64 * kRowStride * 4;
+  static constexpr int kLdsBytes = 2 * kStageBytes > kEpiBytes ? 2 * kStageBytes : kEpiBytes;
 };
 
 template <int L, int TN>
@@ -133,15 +153,16 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
     const int *__restrict__ xexp, const int *__restrict__ need3, float *__restrict__ y, int nb,
     int M, int nchunk_w, int nchunk, int nbt64, int n_ot, int n_bt, int mode) {
   using S = GemmShape<L, TN>;
-  __shared__ i32x4 As[2][S::kAPieces];
-  __shared__ i32x4 Bs[2][S::kBPieces];
+  __shared__ __attribute__((aligned(16))) char lds[S::kLdsBytes];
+  // Stage buffer `buf` holds the A pieces, then the B pieces.
+  auto As = [&](int buf) { return reinterpret_cast<i32x4 *>(lds + buf * S::kStageBytes); };
+  auto Bs = [&](int buf) { return As(buf) + S::kAPieces; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wo = wave >> 1, wb = wave & 1;
 
-  // Block order: the n_bt workgroups of one weight tile get ids 8 apart, so
+  // Block order: the n_bt workgroups of one weight block get ids 8 apart, so
   // the round-robin dispatch over the 8 XCDs puts them on one XCD together.
   const int id = blockIdx.x;
   const int per_grp = 8 * n_bt;
@@ -158,26 +179,27 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
     if (grp3 != (L == 3)) return;
   }
 
-  const int o_tile0 = ot * (kTM / 64);  // first 64-row weight tile
+  const int o0 = ot * kTM;
   const int m_tiles = (M + 63) / 64;
-  const int b_tile0 = bt * (TN / 64);   // first 64-row limb tile
+  const int b_tile0 = bt * (TN / 64);
 
-  // Global -> register staging for one stage (k chunks c0 .. c0+3).
-  i32x4 ra[S::kAPieces / 256];
-  i32x4 rb[S::kBPieces / 256];
-  auto load_stage = [&](int step) {
+  // Global -> register staging of one stage (k chunks c0 .. c0+3).
+  auto load_stage = [&](int step, i32x4 (&ra)[S::kAPerT], i32x4 (&rb)[S::kBPerT]) {
     const int c0 = step * kCPS;
 #pragma unroll
-    for (int i = 0; i < S::kAPieces / 256; i++) {
+    for (int i = 0; i < S::kAPerT; i++) {
+      // Branch-free guard: an out-of-range piece reads piece 0 of the image
+      // (always valid) and is replaced by zeros.
       const int p = tid + 256 * i;
-      const int rt = p / (kCPS * 64), kc = (p / 64) % kCPS, r = p % 64;
-      const int t = o_tile0 + rt, c = c0 + kc;
-      ra[i] = (t < m_tiles && c < nchunk_w)
-                  ? __builtin_nontemporal_load(w + ((size_t)t * nchunk_w + c) * 64 + r)
-                  : i32x4{0, 0, 0, 0};
+      const int kc = p / kTM, row = p % kTM;
+      const int o = o0 + row, t = o >> 6, c = c0 + kc;
+      const bool ok = p < S::kAPieces && t < m_tiles && c < nchunk_w;
+      const size_t idx = ok ? ((size_t)t * nchunk_w + c) * 64 + (o & 63) : 0;
+      const i32x4 v = __builtin_nontemporal_load(w + idx);
+      ra[i] = ok ? v : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < S::kBPieces / 256; i++) {
+    for (int i = 0; i < S::kBPerT; i++) {
       const int p = tid + 256 * i;
       const int l = p / ((TN / 64) * kCPS * 64);
       const int q = p % ((TN / 64) * kCPS * 64);
@@ -185,76 +207,109 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
       rb[i] = xl[((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + c0 + kc) * 64 + r];
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, const i32x4 (&ra)[S::kAPerT], const i32x4 (&rb)[S::kBPerT]) {
 #pragma unroll
-    for (int i = 0; i < S::kAPieces / 256; i++) As[buf][tid + 256 * i] = ra[i];
+    for (int i = 0; i < S::kAPerT; i++) {
+      const int p = tid + 256 * i;
+      if (p < S::kAPieces) As(buf)[p] = ra[i];
+    }
 #pragma unroll
-    for (int i = 0; i < S::kBPieces / 256; i++) Bs[buf][tid + 256 * i] = rb[i];
+    for (int i = 0; i < S::kBPerT; i++) Bs(buf)[tid + 256 * i] = rb[i];
   };
 
-  i32x4 acc[S::kOB][S::kBB][L];
+  i32x4 acc[kOB][S::kBB][L];
 #pragma unroll
-  for (int a = 0; a < S::kOB; a++)
+  for (int a = 0; a < kOB; a++)
 #pragma unroll
     for (int c = 0; c < S::kBB; c++)
 #pragma unroll
       for (int l = 0; l < L; l++) acc[a][c][l] = i32x4{0, 0, 0, 0};
 
-  const int nsteps = nchunk / kCPS;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
   const int kc = lane >> 4, r16 = lane & 15;
-  for (int step = 0; step < nsteps; step++) {
-    const int buf = step & 1;
-    if (step + 1 < nsteps) load_stage(step + 1);
-
+  auto compute = [&](int buf) {
     i32x4 bf[S::kBB][L];
 #pragma unroll
     for (int c = 0; c < S::kBB; c++) {
-      const int bcol = wb * S::kWaveB + c * 16 + r16;  // 0 .. TN-1
+      const int bcol = wave * S::kWB + c * 16 + r16;  // 0 .. TN-1
 #pragma unroll
       for (int l = 0; l < L; l++)
-        bf[c][l] = Bs[buf][((l * (TN / 64) + bcol / 64) * kCPS + kc) * 64 + (bcol & 63)];
+        bf[c][l] = Bs(buf)[((l * (TN / 64) + bcol / 64) * kCPS + kc) * 64 + (bcol & 63)];
     }
+    // A fragments double-buffered in registers: the read of block a+1 is in
+    // flight while the MFMAs of block a issue.
+    i32x4 af[2];
+    af[0] = As(buf)[kc * kTM + r16];
 #pragma unroll
-    for (int a = 0; a < S::kOB; a++) {
-      const int orow = wo * S::kWaveO + a * 16 + r16;  // 0 .. 255
-      const i32x4 af = As[buf][((orow / 64) * kCPS + kc) * 64 + (orow & 63)];
+    for (int a = 0; a < kOB; a++) {
+      if (a + 1 < kOB) af[(a + 1) & 1] = As(buf)[kc * kTM + (a + 1) * 16 + r16];
 #pragma unroll
       for (int c = 0; c < S::kBB; c++)
 #pragma unroll
         for (int l = 0; l < L; l++)
-          acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c][l], acc[a][c][l], 0, 0, 0);
+          acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[a & 1], bf[c][l], acc[a][c][l], 0, 0, 0);
     }
+  };
 
-    if (step + 1 < nsteps) store_stage(buf ^ 1);
+  // K loop: LDS double buffer; the next stage's global loads are in flight
+  // while this stage's MFMAs run.
+  const int nsteps = nchunk / kCPS;
+  i32x4 ra[S::kAPerT], rb[S::kBPerT];
+  load_stage(0, ra, rb);
+  store_stage(0, ra, rb);
+  __syncthreads();
+  for (int step = 0; step < nsteps; step++) {
+    const int buf = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) load_stage(step + 1, ra, rb);
+    compute(buf);
+    if (more) store_stage(buf ^ 1, ra, rb);
     __syncthreads();
   }
 
-  // Epilogue: combine the limbs in f32, apply rs[o] and 2^e_b.
+  // Epilogue: limbs combined in f32 per output, transposed through LDS in
+  // groups of 64 xs rows, then written as whole rows of y (272 consecutive
+  // outputs each) with rs[o] and 2^e_b applied on the way out.
+  float *ep = reinterpret_cast<float *>(lds);
+  const bool vec = (M & 3) == 0;
 #pragma unroll
   for (int c = 0; c < S::kBB; c++) {
-    const int b = bt * TN + wb * S::kWaveB + c * 16 + r16;
-    if (b >= nb) continue;
-    const int e = xexp[b] + (L == 2 ? 8 : 0);
+    const int row = wave * 16 + r16;  // 0..63 within the group
 #pragma unroll
-    for (int a = 0; a < S::kOB; a++) {
-      const int o0 = ot * kTM + wo * S::kWaveO + a * 16 + 4 * kc;
+    for (int a = 0; a < kOB; a++) {
+      float vv[4];
 #pragma unroll
       for (int v = 0; v < 4; v++) {
-        const int o = o0 + v;
-        if (o >= M) continue;
-        float val;
         if (L == 2)
-          val = (float)acc[a][c][0][v] * 256.0f + (float)acc[a][c][1][v];
+          vv[v] = (float)acc[a][c][0][v] * 256.0f + (float)acc[a][c][1][v];
         else
-          val = ((float)acc[a][c][0][v] * 65536.0f + (float)acc[a][c][1][v] * 256.0f) +
-                (float)acc[a][c][2][v];
-        y[(size_t)b * M + o] = ldexpf(val * rs[o], e);
+          vv[v] = ((float)acc[a][c][0][v] * 65536.0f + (float)acc[a][c][1][v] * 256.0f) +
+                  (float)acc[a][c][L - 1][v];
+      }
+      *reinterpret_cast<float4 *>(ep + row * S::kRowStride + a * 16 + 4 * kc) =
+          make_float4(vv[0], vv[1], vv[2], vv[3]);
+    }
+    __syncthreads();
+    // 64 rows x 68 float4 per group.
+    for (int f = tid; f < 64 * (kTM / 4); f += 256) {
+      const int gr = f / (kTM / 4), col = (f % (kTM / 4)) * 4;
+      const int b = bt * TN + (gr / 16) * S::kWB + c * 16 + (gr % 16);
+      const int o = o0 + col;
+      if (b >= nb || o >= M) continue;
+      const float4 v4 = *reinterpret_cast<const float4 *>(ep + gr * S::kRowStride + col);
+      const int e = xexp[b] + (L == 2 ? 8 : 0);
+      float *dst = y + (size_t)b * M + o;
+      if (vec && o + 3 < M) {
+        const float4 r4 = *reinterpret_cast<const float4 *>(rs + o);
+        *reinterpret_cast<float4 *>(dst) = make_float4(ldexpf(v4.x * r4.x, e), ldexpf(v4.y * r4.y, e),
+                                                       ldexpf(v4.z * r4.z, e), ldexpf(v4.w * r4.w, e));
+      } else {
+        if (o < M) dst[0] = ldexpf(v4.x * rs[o], e);
+        if (o + 1 < M) dst[1] = ldexpf(v4.y * rs[o + 1], e);
+        if (o + 2 < M) dst[2] = ldexpf(v4.z * rs[o + 2], e);
+        if (o + 3 < M) dst[3] = ldexpf(v4.w * rs[o + 3], e);
       }
     }
+    __syncthreads();
   }
 }
 
