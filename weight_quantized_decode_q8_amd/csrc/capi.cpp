@@ -126,8 +126,8 @@ qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq, const int32_t *
 
 size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K) {
   if (nb < 1 || K < 4 || K % 4 != 0) return 0;
-  size_t a, b;
-  return qg::gemm_ws_layout(nb, K, &a, &b);
+  size_t a, b, c;
+  return qg::gemm_ws_layout(nb, K, &a, &b, &c);
 }
 
 qg_status qgemm_q8row_batched(const void *qpacked, const float *rs, const float *xs, float *y,

@@ -48,10 +48,12 @@ constexpr int kR3 = 126 * 65536;  // largest |fixed-point value|, 3 limbs
 // plus the row's exponent e_b and whether it needs the third limb.
 __global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict__ xs, int nb, int K,
                                                         int nchunk, int nbt, i32x4 *__restrict__ xl,
-                                                        int *__restrict__ xexp, int *__restrict__ need3) {
+                                                        int *__restrict__ xexp, int *__restrict__ need3,
+                                                        i32x4 *__restrict__ zero_blk) {
   __shared__ float red_max[4], red_sum[4];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  if (b == 0 && tid < 64) zero_blk[tid] = i32x4{0, 0, 0, 0};
   const bool live = b < nb;
   const float *row = xs + (size_t)b * K;
 
@@ -139,19 +141,32 @@ struct GemmShape {
   static constexpr int kBB = kWB / 16;                // 16-column MFMA blocks per wave
   static constexpr int kAPieces = kTM * kCPS;         // 16-byte pieces of A per stage
   static constexpr int kBPieces = L * TN * kCPS;      // 16-byte pieces of B per stage
-  static constexpr int kAPerT = (kAPieces + 255) / 256;
-  static constexpr int kBPerT = kBPieces / 256;
+  static constexpr int kAWaveLoads = kAPieces / 64;   // 1 KiB wave loads of A (17)
+  static constexpr int kBWaveLoads = kBPieces / 64;
+  static constexpr int kAPerWave = (kAWaveLoads + 3) / 4;  // at most, per wave
+  static constexpr int kBPerWave = kBWaveLoads / 4;
+  static constexpr int kMinLoadsPerWave = kAWaveLoads / 4 + kBPerWave;
+  static constexpr int kStages = 4;                   // LDS ring depth
   static constexpr int kStageBytes = (kAPieces + kBPieces) * 16;
   static constexpr int kRowStride = kTM + 4;          // epilogue row stride (floats)
   static constexpr int kEpiBytes = 64 * kRowStride * 4;
-  static constexpr int kLdsBytes = 2 * kStageBytes > kEpiBytes ? 2 * kStageBytes : kEpiBytes;
+  static constexpr int kLdsBytes =
+      kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
 };
+
+// s_waitcnt immediate for vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt and lgkmcnt left at their maxima, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
 
 template <int L, int TN>
 __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
     const i32x4 *__restrict__ w, const float *__restrict__ rs, const i32x4 *__restrict__ xl,
-    const int *__restrict__ xexp, const int *__restrict__ need3, float *__restrict__ y, int nb,
-    int M, int nchunk_w, int nchunk, int nbt64, int n_ot, int n_bt, int mode) {
+    const i32x4 *__restrict__ zero_blk, const int *__restrict__ xexp,
+    const int *__restrict__ need3, float *__restrict__ y, int nb, int M, int nchunk_w, int nchunk,
+    int nbt64, int n_ot, int n_bt, int mode) {
   using S = GemmShape<L, TN>;
   __shared__ __attribute__((aligned(16))) char lds[S::kLdsBytes];
   // Stage buffer `buf` holds the A pieces, then the B pieces.
@@ -183,38 +198,33 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
   const int m_tiles = (M + 63) / 64;
   const int b_tile0 = bt * (TN / 64);
 
-  // Global -> register staging of one stage (k chunks c0 .. c0+3).
-  auto load_stage = [&](int step, i32x4 (&ra)[S::kAPerT], i32x4 (&rb)[S::kBPerT]) {
+  // One stage = wave loads of 1 KiB that go straight from global memory into
+  // LDS (lane i's 16 bytes land at base + 16 i); wave w issues wave loads
+  // w, w + 4, ...  Pieces outside the weight image read the zero block.
+  auto issue_stage = [&](int step) {
+    const int buf = step % S::kStages;
     const int c0 = step * kCPS;
 #pragma unroll
-    for (int i = 0; i < S::kAPerT; i++) {
-      // Branch-free guard: an out-of-range piece reads piece 0 of the image
-      // (always valid) and is replaced by zeros.
-      const int p = tid + 256 * i;
-      const int kc = p / kTM, row = p % kTM;
-      const int o = o0 + row, t = o >> 6, c = c0 + kc;
-      const bool ok = p < S::kAPieces && t < m_tiles && c < nchunk_w;
-      const size_t idx = ok ? ((size_t)t * nchunk_w + c) * 64 + (o & 63) : 0;
-      const i32x4 v = __builtin_nontemporal_load(w + idx);
-      ra[i] = ok ? v : i32x4{0, 0, 0, 0};
+    for (int i = 0; i < S::kAPerWave; i++) {
+      const int j = wave + 4 * i;
+      if (j < S::kAWaveLoads) {
+        const int p = 64 * j + lane;
+        const int kc = p / kTM, row = p % kTM;
+        const int o = o0 + row, t = o >> 6, c = c0 + kc;
+        const i32x4 *src = (t < m_tiles && c < nchunk_w) ? w + ((size_t)t * nchunk_w + c) * 64 + (o & 63)
+                                                        : zero_blk + lane;
+        __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)(As(buf) + 64 * j), 16, 0, 0);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < S::kBPerT; i++) {
-      const int p = tid + 256 * i;
-      const int l = p / ((TN / 64) * kCPS * 64);
-      const int q = p % ((TN / 64) * kCPS * 64);
-      const int bt64 = q / (kCPS * 64), kc = (q / 64) % kCPS, r = q % 64;
-      rb[i] = xl[((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + c0 + kc) * 64 + r];
+    for (int i = 0; i < S::kBPerWave; i++) {
+      const int j = wave + 4 * i;
+      const int l = j / ((TN / 64) * kCPS);
+      const int q = j % ((TN / 64) * kCPS);
+      const int bt64 = q / kCPS, kc = q % kCPS;
+      const i32x4 *src = xl + ((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + c0 + kc) * 64 + lane;
+      __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)(Bs(buf) + 64 * j), 16, 0, 0);
     }
-  };
-  auto store_stage = [&](int buf, const i32x4 (&ra)[S::kAPerT], const i32x4 (&rb)[S::kBPerT]) {
-#pragma unroll
-    for (int i = 0; i < S::kAPerT; i++) {
-      const int p = tid + 256 * i;
-      if (p < S::kAPieces) As(buf)[p] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::kBPerT; i++) Bs(buf)[tid + 256 * i] = rb[i];
   };
 
   i32x4 acc[kOB][S::kBB][L];
@@ -250,21 +260,29 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
     }
   };
 
-  // K loop: LDS double buffer; the next stage's global loads are in flight
-  // while this stage's MFMAs run.
+  // K loop over an LDS ring of kStages buffers: kStages - 1 stages are in
+  // flight ahead of the one being multiplied.
   const int nsteps = nchunk / kCPS;
-  i32x4 ra[S::kAPerT], rb[S::kBPerT];
-  load_stage(0, ra, rb);
-  store_stage(0, ra, rb);
-  __syncthreads();
+#pragma unroll
+  for (int s0 = 0; s0 < S::kStages - 1; s0++)
+    if (s0 < nsteps) issue_stage(s0);
   for (int step = 0; step < nsteps; step++) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) load_stage(step + 1, ra, rb);
-    compute(buf);
-    if (more) store_stage(buf ^ 1, ra, rb);
+    // Wait for this wave's loads of `step`: later stages may stay in flight.
+    // (Every wave issues at least kMinLoadsPerWave loads per stage.)
+    const int ahead = min(S::kStages - 2, nsteps - 1 - step);
+    static_assert(S::kStages == 4, "waits below assume two stages in flight");
+    if (ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kMinLoadsPerWave));
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::kMinLoadsPerWave));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
+    if (step + S::kStages - 1 < nsteps) issue_stage(step + S::kStages - 1);
+    compute(step % S::kStages);
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
 
   // Epilogue: limbs combined in f32 per output, transposed through LDS in
   // groups of 64 xs rows, then written as whole rows of y (272 consecutive
@@ -314,33 +332,36 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
 }
 
 template <int L, int TN>
-hipError_t launch_gemm(const void *w, const float *rs, const i32x4 *xl, const int *xexp,
-                       const int *need3, float *y, int nb, int nbp, int M, int nchunk_w,
-                       int nchunk, int mode, hipStream_t stream) {
+hipError_t launch_gemm(const void *w, const float *rs, const i32x4 *xl, const i32x4 *zero_blk,
+                       const int *xexp, const int *need3, float *y, int nb, int nbp, int M,
+                       int nchunk_w, int nchunk, int mode, hipStream_t stream) {
   const int n_ot = (M + kTM - 1) / kTM;
   const int n_bt = nbp / TN;
   const int grid = (n_ot + 7) / 8 * 8 * n_bt;
   q8row_gemm_kernel<L, TN><<<grid, 256, 0, stream>>>(
-      reinterpret_cast<const i32x4 *>(w), rs, xl, xexp, need3, y, nb, M, nchunk_w, nchunk,
+      reinterpret_cast<const i32x4 *>(w), rs, xl, zero_blk, xexp, need3, y, nb, M, nchunk_w, nchunk,
       nbp / 64, n_ot, n_bt, mode);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need) {
+// Workspace: limbs [3][nbp/64][Kp/16][64][16 B], then e_b [nbp], need3
+// [nbp], then a 1 KiB block of zeros (the source of out-of-range pieces).
+size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need, size_t *off_zero) {
   const int64_t nbp = round_up(nb, 128);
   const int64_t kp = round_up(K, kKS);
   const size_t limbs = (size_t)kLimbMax * nbp * kp;
   *off_exp = (size_t)round_up(limbs, 256);
   *off_need = *off_exp + (size_t)round_up(nbp * 4, 256);
-  return *off_need + (size_t)round_up(nbp * 4, 256);
+  *off_zero = *off_need + (size_t)round_up(nbp * 4, 256);
+  return *off_zero + 1024;
 }
 
 hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, float *y, int nb,
                              int M, int K, int limbs, void *ws, hipStream_t stream) {
-  size_t off_exp, off_need;
-  gemm_ws_layout(nb, K, &off_exp, &off_need);
+  size_t off_exp, off_need, off_zero;
+  gemm_ws_layout(nb, K, &off_exp, &off_need, &off_zero);
   const int nbp = (int)round_up(nb, 128);
   const int nchunk = (int)(round_up(K, kKS) / 16);
   const int nchunk_w = (int)(round_up(K, 16) / 16);
@@ -348,17 +369,18 @@ hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, fl
   i32x4 *xl = reinterpret_cast<i32x4 *>(base);
   int *xexp = reinterpret_cast<int *>(base + off_exp);
   int *need3 = reinterpret_cast<int *>(base + off_need);
+  i32x4 *zero_blk = reinterpret_cast<i32x4 *>(base + off_zero);
 
-  gemm_prep_kernel<<<nbp, 256, 0, stream>>>(xs, nb, K, nchunk, nbp / 64, xl, xexp, need3);
+  gemm_prep_kernel<<<nbp, 256, 0, stream>>>(xs, nb, K, nchunk, nbp / 64, xl, xexp, need3, zero_blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (limbs == 2 || limbs == 0) {
-    err = launch_gemm<2, 128>(w, rs, xl, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
+    err = launch_gemm<2, 128>(w, rs, xl, zero_blk, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
                               limbs == 0 ? 1 : 0, stream);
     if (err != hipSuccess) return err;
   }
   if (limbs == 3 || limbs == 0)
-    err = launch_gemm<3, 64>(w, rs, xl, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
+    err = launch_gemm<3, 64>(w, rs, xl, zero_blk, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
                              limbs == 0 ? 1 : 0, stream);
   return err;
 }

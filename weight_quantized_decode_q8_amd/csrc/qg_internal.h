@@ -37,7 +37,7 @@ hipError_t launch_q2_gemv(const void *codes, const void *scales, int M, int K, i
 int q2_auto_split(int64_t M, int64_t K, int group);
 
 // Batched q8_row GEMM: workspace layout (limbs, exponents, flags) and launch.
-size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need);
+size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need, size_t *off_zero);
 hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, float *y, int nb,
                              int M, int K, int limbs, void *ws, hipStream_t stream);
 
