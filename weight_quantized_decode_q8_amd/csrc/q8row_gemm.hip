@@ -127,32 +127,16 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict_
 }
 
 // ------------------------------------------------------------- GEMM kernel
-// One workgroup of 4 waves computes a kTM x TN block of y^T: kTM = 272 weight
-// rows (17 MFMA row blocks; 17408 = 64 * 272, so the pages' FFN width gives
-// exactly 256 blocks per 128 xs rows, one per CU) by TN rows of xs.  Every
-// wave owns all 272 weight rows and TN/4 xs rows, so the A fragments are
-// shared through LDS and each wave keeps 17 x (TN/64) x L accumulator tiles.
+// One workgroup of 8 waves (2 per SIMD) computes a kTM x TN block of y^T:
+// kTM = 272 weight rows (17 MFMA row blocks; 17408 = 64 * 272, so the pages'
+// FFN width gives exactly 256 blocks per 128 xs rows, one per CU) by TN rows
+// of xs.  Waves are 2 (weight rows: blocks 0-8 and 9-16) x 4 (xs rows), so a
+// wave holds at most 9 x (TN/64) x L accumulator tiles and the two waves of a
+// SIMD overlap each other's LDS reads with MFMAs.
 constexpr int kOB = 17;
+constexpr int kOBW = 9;        // row blocks of the first wave half (the second has 8)
 constexpr int kTM = 16 * kOB;  // 272
-
-template <int L, int TN>
-struct GemmShape {
-  static constexpr int kWB = TN / 4;                  // xs rows per wave
-  static constexpr int kBB = kWB / 16;                // 16-column MFMA blocks per wave
-  static constexpr int kAPieces = kTM * kCPS;         // 16-byte pieces of A per stage
-  static constexpr int kBPieces = L * TN * kCPS;      // 16-byte pieces of B per stage
-  static constexpr int kAWaveLoads = kAPieces / 64;   // 1 KiB wave loads of A (17)
-  static constexpr int kBWaveLoads = kBPieces / 64;
-  static constexpr int kAPerWave = (kAWaveLoads + 3) / 4;  // at most, per wave
-  static constexpr int kBPerWave = kBWaveLoads / 4;
-  static constexpr int kMinLoadsPerWave = kAWaveLoads / 4 + kBPerWave;
-  static constexpr int kStages = 4;                   // LDS ring depth
-  static constexpr int kStageBytes = (kAPieces + kBPieces) * 16;
-  static constexpr int kRowStride = kTM + 4;          // epilogue row stride (floats)
-  static constexpr int kEpiBytes = 64 * kRowStride * 4;
-  static constexpr int kLdsBytes =
-      kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
-};
+constexpr int kThreads = 512;
 
 // s_waitcnt immediate for vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14; expcnt and lgkmcnt left at their maxima, i.e. not waited for).
@@ -162,7 +146,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void global_void;
 
 template <int L, int TN>
-__global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
+struct GemmShape {
+  static constexpr int kWB = TN / 4;                  // xs rows per wave
+  static constexpr int kBB = kWB / 16;                // 16-column MFMA blocks per wave
+  static constexpr int kAPieces = kTM * kCPS;         // 16-byte pieces of A per stage
+  static constexpr int kBPieces = L * TN * kCPS;      // 16-byte pieces of B per stage
+  static constexpr int kAWaveLoads = kAPieces / 64;   // 1 KiB wave loads of A (17)
+  static constexpr int kBWaveLoads = kBPieces / 64;
+  static constexpr int kAPerWave = (kAWaveLoads + 7) / 8;  // at most, per wave
+  static constexpr int kBPerWave = (kBWaveLoads + 7) / 8;
+  static constexpr int kMinLoadsPerWave = kAWaveLoads / 8 + kBWaveLoads / 8;
+  static constexpr int kStages = 4;                   // LDS ring depth
+  static constexpr int kStageBytes = (kAPieces + kBPieces) * 16;
+  static constexpr int kRowStride = kTM + 4;          // epilogue row stride (floats)
+  static constexpr int kEpiBytes = 64 * kRowStride * 4;
+  static constexpr int kLdsBytes =
+      kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
+};
+
+template <int L, int TN>
+__global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
     const i32x4 *__restrict__ w, const float *__restrict__ rs, const i32x4 *__restrict__ xl,
     const i32x4 *__restrict__ zero_blk, const int *__restrict__ xexp,
     const int *__restrict__ need3, float *__restrict__ y, int nb, int M, int nchunk_w, int nchunk,
@@ -176,6 +179,10 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave & 3;         // xs-row quarter
+  const int wh = wave >> 2;        // weight-row half
+  const int ob0 = wh * kOBW;       // first row block of this wave
+  const int nob = wh == 0 ? kOBW : kOB - kOBW;
 
   // Block order: the n_bt workgroups of one weight block get ids 8 apart, so
   // the round-robin dispatch over the 8 XCDs puts them on one XCD together.
@@ -200,13 +207,13 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
 
   // One stage = wave loads of 1 KiB that go straight from global memory into
   // LDS (lane i's 16 bytes land at base + 16 i); wave w issues wave loads
-  // w, w + 4, ...  Pieces outside the weight image read the zero block.
+  // w, w + 8, ...  Pieces outside the weight image read the zero block.
   auto issue_stage = [&](int step) {
     const int buf = step % S::kStages;
     const int c0 = step * kCPS;
 #pragma unroll
     for (int i = 0; i < S::kAPerWave; i++) {
-      const int j = wave + 4 * i;
+      const int j = wave + 8 * i;
       if (j < S::kAWaveLoads) {
         const int p = 64 * j + lane;
         const int kc = p / kTM, row = p % kTM;
@@ -218,18 +225,20 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
     }
 #pragma unroll
     for (int i = 0; i < S::kBPerWave; i++) {
-      const int j = wave + 4 * i;
-      const int l = j / ((TN / 64) * kCPS);
-      const int q = j % ((TN / 64) * kCPS);
-      const int bt64 = q / kCPS, kc = q % kCPS;
-      const i32x4 *src = xl + ((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + c0 + kc) * 64 + lane;
-      __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)(Bs(buf) + 64 * j), 16, 0, 0);
+      const int j = wave + 8 * i;
+      if (j < S::kBWaveLoads) {
+        const int l = j / ((TN / 64) * kCPS);
+        const int q = j % ((TN / 64) * kCPS);
+        const int bt64 = q / kCPS, kc = q % kCPS;
+        const i32x4 *src = xl + ((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + c0 + kc) * 64 + lane;
+        __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)(Bs(buf) + 64 * j), 16, 0, 0);
+      }
     }
   };
 
-  i32x4 acc[kOB][S::kBB][L];
+  i32x4 acc[kOBW][S::kBB][L];
 #pragma unroll
-  for (int a = 0; a < kOB; a++)
+  for (int a = 0; a < kOBW; a++)
 #pragma unroll
     for (int c = 0; c < S::kBB; c++)
 #pragma unroll
@@ -240,23 +249,22 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
     i32x4 bf[S::kBB][L];
 #pragma unroll
     for (int c = 0; c < S::kBB; c++) {
-      const int bcol = wave * S::kWB + c * 16 + r16;  // 0 .. TN-1
+      const int bcol = wq * S::kWB + c * 16 + r16;  // 0 .. TN-1
 #pragma unroll
       for (int l = 0; l < L; l++)
         bf[c][l] = Bs(buf)[((l * (TN / 64) + bcol / 64) * kCPS + kc) * 64 + (bcol & 63)];
     }
-    // A fragments double-buffered in registers: the read of block a+1 is in
-    // flight while the MFMAs of block a issue.
-    i32x4 af[2];
-    af[0] = As(buf)[kc * kTM + r16];
+    const i32x4 *abase = As(buf) + kc * kTM + ob0 * 16 + r16;
 #pragma unroll
-    for (int a = 0; a < kOB; a++) {
-      if (a + 1 < kOB) af[(a + 1) & 1] = As(buf)[kc * kTM + (a + 1) * 16 + r16];
+    for (int a = 0; a < kOBW; a++) {
+      if (a < nob) {
+        const i32x4 af = abase[a * 16];
 #pragma unroll
-      for (int c = 0; c < S::kBB; c++)
+        for (int c = 0; c < S::kBB; c++)
 #pragma unroll
-        for (int l = 0; l < L; l++)
-          acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[a & 1], bf[c][l], acc[a][c][l], 0, 0, 0);
+          for (int l = 0; l < L; l++)
+            acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c][l], acc[a][c][l], 0, 0, 0);
+      }
     }
   };
 
@@ -267,8 +275,8 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
   for (int s0 = 0; s0 < S::kStages - 1; s0++)
     if (s0 < nsteps) issue_stage(s0);
   for (int step = 0; step < nsteps; step++) {
-    // Wait for this wave's loads of `step`: later stages may stay in flight.
-    // (Every wave issues at least kMinLoadsPerWave loads per stage.)
+    // Wait for this wave's loads of `step`: later stages may stay in flight
+    // (every wave issues at least kMinLoadsPerWave loads per stage).
     const int ahead = min(S::kStages - 2, nsteps - 1 - step);
     static_assert(S::kStages == 4, "waits below assume two stages in flight");
     if (ahead >= 2)
@@ -291,24 +299,26 @@ __global__ __launch_bounds__(256, 1) void q8row_gemm_kernel(
   const bool vec = (M & 3) == 0;
 #pragma unroll
   for (int c = 0; c < S::kBB; c++) {
-    const int row = wave * 16 + r16;  // 0..63 within the group
+    const int row = wq * 16 + r16;  // 0..63 within the group
 #pragma unroll
-    for (int a = 0; a < kOB; a++) {
-      float vv[4];
+    for (int a = 0; a < kOBW; a++) {
+      if (a < nob) {
+        float vv[4];
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        if (L == 2)
-          vv[v] = (float)acc[a][c][0][v] * 256.0f + (float)acc[a][c][1][v];
-        else
-          vv[v] = ((float)acc[a][c][0][v] * 65536.0f + (float)acc[a][c][1][v] * 256.0f) +
-                  (float)acc[a][c][L - 1][v];
+        for (int v = 0; v < 4; v++) {
+          if (L == 2)
+            vv[v] = (float)acc[a][c][0][v] * 256.0f + (float)acc[a][c][1][v];
+          else
+            vv[v] = ((float)acc[a][c][0][v] * 65536.0f + (float)acc[a][c][1][v] * 256.0f) +
+                    (float)acc[a][c][L - 1][v];
+        }
+        *reinterpret_cast<float4 *>(ep + row * S::kRowStride + (ob0 + a) * 16 + 4 * kc) =
+            make_float4(vv[0], vv[1], vv[2], vv[3]);
       }
-      *reinterpret_cast<float4 *>(ep + row * S::kRowStride + a * 16 + 4 * kc) =
-          make_float4(vv[0], vv[1], vv[2], vv[3]);
     }
     __syncthreads();
     // 64 rows x 68 float4 per group.
-    for (int f = tid; f < 64 * (kTM / 4); f += 256) {
+    for (int f = tid; f < 64 * (kTM / 4); f += kThreads) {
       const int gr = f / (kTM / 4), col = (f % (kTM / 4)) * 4;
       const int b = bt * TN + (gr / 16) * S::kWB + c * 16 + (gr % 16);
       const int o = o0 + col;
@@ -338,7 +348,7 @@ hipError_t launch_gemm(const void *w, const float *rs, const i32x4 *xl, const i3
   const int n_ot = (M + kTM - 1) / kTM;
   const int n_bt = nbp / TN;
   const int grid = (n_ot + 7) / 8 * 8 * n_bt;
-  q8row_gemm_kernel<L, TN><<<grid, 256, 0, stream>>>(
+  q8row_gemm_kernel<L, TN><<<grid, kThreads, 0, stream>>>(
       reinterpret_cast<const i32x4 *>(w), rs, xl, zero_blk, xexp, need3, y, nb, M, nchunk_w, nchunk,
       nbp / 64, n_ot, n_bt, mode);
   return hipGetLastError();
