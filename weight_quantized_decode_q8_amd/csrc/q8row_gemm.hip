@@ -207,7 +207,29 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
 
   // One stage = wave loads of 1 KiB that go straight from global memory into
   // LDS (lane i's 16 bytes land at base + 16 i); wave w issues wave loads
-  // w, w + 8, ...  Pieces outside the weight image read the zero block.
+  // w, w + 8, ...  Each lane's source address is formed once; a stage moves
+  // every source by 4 chunks (256 pieces).  Rows past the weight image, and
+  // chunks past K in the last stage, read the zero block instead.
+  const i32x4 *a_src[S::kAPerWave];
+  int a_kc[S::kAPerWave];
+#pragma unroll
+  for (int i = 0; i < S::kAPerWave; i++) {
+    const int j = min(wave + 8 * i, S::kAWaveLoads - 1);
+    const int p = 64 * j + lane;
+    const int kc = p / kTM, row = p % kTM;
+    const int o = o0 + row, t = o >> 6;
+    a_kc[i] = kc;
+    a_src[i] = t < m_tiles ? w + ((size_t)t * nchunk_w + kc) * 64 + (o & 63) : nullptr;
+  }
+  const i32x4 *b_src[S::kBPerWave];
+#pragma unroll
+  for (int i = 0; i < S::kBPerWave; i++) {
+    const int j = min(wave + 8 * i, S::kBWaveLoads - 1);
+    const int l = j / ((TN / 64) * kCPS);
+    const int q = j % ((TN / 64) * kCPS);
+    const int bt64 = q / kCPS, kc = q % kCPS;
+    b_src[i] = xl + ((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + kc) * 64 + lane;
+  }
   auto issue_stage = [&](int step) {
     const int buf = step % S::kStages;
     const int c0 = step * kCPS;
@@ -215,24 +237,17 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
     for (int i = 0; i < S::kAPerWave; i++) {
       const int j = wave + 8 * i;
       if (j < S::kAWaveLoads) {
-        const int p = 64 * j + lane;
-        const int kc = p / kTM, row = p % kTM;
-        const int o = o0 + row, t = o >> 6, c = c0 + kc;
-        const i32x4 *src = (t < m_tiles && c < nchunk_w) ? w + ((size_t)t * nchunk_w + c) * 64 + (o & 63)
-                                                        : zero_blk + lane;
+        const i32x4 *src = (a_src[i] != nullptr && c0 + a_kc[i] < nchunk_w)
+                               ? a_src[i] + (size_t)step * (kCPS * 64) : zero_blk + lane;
         __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)(As(buf) + 64 * j), 16, 0, 0);
       }
     }
 #pragma unroll
     for (int i = 0; i < S::kBPerWave; i++) {
       const int j = wave + 8 * i;
-      if (j < S::kBWaveLoads) {
-        const int l = j / ((TN / 64) * kCPS);
-        const int q = j % ((TN / 64) * kCPS);
-        const int bt64 = q / kCPS, kc = q % kCPS;
-        const i32x4 *src = xl + ((size_t)(l * nbt64 + b_tile0 + bt64) * nchunk + c0 + kc) * 64 + lane;
-        __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)(Bs(buf) + 64 * j), 16, 0, 0);
-      }
+      if (j < S::kBWaveLoads)
+        __builtin_amdgcn_global_load_lds((global_void *)(b_src[i] + (size_t)step * (kCPS * 64)),
+                                         (lds_void *)(Bs(buf) + 64 * j), 16, 0, 0);
     }
   };
 
@@ -254,17 +269,29 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
       for (int l = 0; l < L; l++)
         bf[c][l] = Bs(buf)[((l * (TN / 64) + bcol / 64) * kCPS + kc) * 64 + (bcol & 63)];
     }
+    // A fragments in pairs, software-pipelined: the LDS reads of the next
+    // pair are issued before the MFMAs of this one.
     const i32x4 *abase = As(buf) + kc * kTM + ob0 * 16 + r16;
+    i32x4 a0 = abase[0], a1 = abase[16];
 #pragma unroll
-    for (int a = 0; a < kOBW; a++) {
-      if (a < nob) {
-        const i32x4 af = abase[a * 16];
+    for (int a = 0; a < kOBW; a += 2) {
+      i32x4 n0 = a0, n1 = a1;
+      if (a + 2 < kOBW && a + 2 < nob) n0 = abase[(a + 2) * 16];
+      if (a + 3 < kOBW && a + 3 < nob) n1 = abase[(a + 3) * 16];
+#pragma unroll
+      for (int c = 0; c < S::kBB; c++)
+#pragma unroll
+        for (int l = 0; l < L; l++)
+          acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[c][l], acc[a][c][l], 0, 0, 0);
+      if (a + 1 < kOBW && a + 1 < nob) {
 #pragma unroll
         for (int c = 0; c < S::kBB; c++)
 #pragma unroll
           for (int l = 0; l < L; l++)
-            acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c][l], acc[a][c][l], 0, 0, 0);
+            acc[a + 1][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bf[c][l], acc[a + 1][c][l], 0, 0, 0);
       }
+      a0 = n0;
+      a1 = n1;
     }
   };
 
