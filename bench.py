@@ -13,8 +13,10 @@ resident in HBM when timing starts.  The lm_head stream (1.27 GB) evicts the
 256 MB last-level cache every step, so the FFN weights also come from HBM.
 
 Also reported: per-kernel times and roofline fractions, the dominant
-kernel's roofline (HIP events on the launch stream), and the CPU oracle timed
-on this host over the same step (cpu_baseline).
+kernel's roofline (HIP events on the launch stream), the CPU oracle timed
+on this host over the same step (cpu_baseline), and the second half of the
+metric, the batched prefill q8_row GEMM (nb=512 x 17408 x 5120, int8 MFMA
+with exact activation limbs), in algorithmic TFLOP/s (`prefill_gemm`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -31,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP16_DENSE_TFLOPS = 2500.0
+INT8_DENSE_TOPS = 5000.0
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "q8row_gemv_lm_head_248320x5120_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "weight_quantized_decode_q8_amd", "csrc", "q8row_gemv.hip")
@@ -46,6 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel timing table (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -257,6 +262,46 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # ---------------- prefill GEMM: y[b,o] = rs[o] sum_i q[o,i] xs[b,i]
+    gemm = None
+    if not args.no_gemm:
+        del L4
+        torch.cuda.empty_cache()
+        c5 = synth.CONFIGS["C5"]
+        nb5, M5, K5 = c5["nb"], c5["M"], c5["K"]
+        q5, rs5, xs5 = synth.config_inputs("C5")
+        W5 = qg.Q8RowWeight.from_host(q5, rs5, dev)
+        del q5
+        xs5_d = torch.from_numpy(xs5).to(dev)
+        y5 = torch.empty((nb5, M5), dtype=torch.float32, device=dev)
+        ws5 = torch.empty(qg.qgemm_q8row_batched_ws_bytes(nb5, K5), dtype=torch.uint8, device=dev)
+
+        def k_gemm():
+            qg.qgemm_q8row_batched(W5.packed, W5.rs, xs5_d, y5, nb5, M5, K5, ws5, xs_limbs=0)
+
+        n_g = 20
+        g_gemm = capture(k_gemm, 1)
+        for _ in range(3):
+            g_gemm.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n_g):
+            g_gemm.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        g_us = a.elapsed_time(b) * 1e3 / n_g
+        flop = 2 * nb5 * M5 * K5
+        tflops = flop / g_us / 1e6
+        gemm = {"workload": f"batched prefill q8_row GEMM nb={nb5} M={M5} K={K5} (xs limbs: auto)",
+                "us": round(g_us, 2), "TFLOP/s": round(tflops, 1), "unit": "TFLOP/s",
+                "algorithmic_flop": flop,
+                "frac_fp16_dense_peak": round(tflops / FP16_DENSE_TFLOPS, 4),
+                "frac_int8_dense_peak_hw": round(2 * tflops / INT8_DENSE_TOPS, 4),
+                "note": "2 int8 limbs per activation on these N(0,1) rows: hardware int8 ops = 2x algorithmic"}
+        log(f"prefill GEMM: {gemm}")
+
     # ---------------- CPU oracle over the same step, on this host
     cpu = None
     if not args.no_cpu_baseline:
@@ -308,6 +353,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "prefill_gemm": gemm,
     }
     print(json.dumps(out), flush=True)
 

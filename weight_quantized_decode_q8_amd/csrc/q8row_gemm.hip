@@ -278,11 +278,13 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
       i32x4 n0 = a0, n1 = a1;
       if (a + 2 < kOBW && a + 2 < nob) n0 = abase[(a + 2) * 16];
       if (a + 3 < kOBW && a + 3 < nob) n1 = abase[(a + 3) * 16];
+      if (a < nob) {
 #pragma unroll
-      for (int c = 0; c < S::kBB; c++)
+        for (int c = 0; c < S::kBB; c++)
 #pragma unroll
-        for (int l = 0; l < L; l++)
-          acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[c][l], acc[a][c][l], 0, 0, 0);
+          for (int l = 0; l < L; l++)
+            acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[c][l], acc[a][c][l], 0, 0, 0);
+      }
       if (a + 1 < kOBW && a + 1 < nob) {
 #pragma unroll
         for (int c = 0; c < S::kBB; c++)
@@ -295,26 +297,27 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
     }
   };
 
-  // K loop over an LDS ring of kStages buffers: kStages - 1 stages are in
-  // flight ahead of the one being multiplied.
+  // K loop over an LDS ring of 4 stage buffers, two steps per barrier: while
+  // steps s, s+1 are multiplied, the loads of steps s+2, s+3 are in flight
+  // into the two buffers that steps s-2, s-1 used.
   const int nsteps = nchunk / kCPS;
-#pragma unroll
-  for (int s0 = 0; s0 < S::kStages - 1; s0++)
-    if (s0 < nsteps) issue_stage(s0);
-  for (int step = 0; step < nsteps; step++) {
-    // Wait for this wave's loads of `step`: later stages may stay in flight
-    // (every wave issues at least kMinLoadsPerWave loads per stage).
-    const int ahead = min(S::kStages - 2, nsteps - 1 - step);
-    static_assert(S::kStages == 4, "waits below assume two stages in flight");
-    if (ahead >= 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kMinLoadsPerWave));
-    else if (ahead == 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::kMinLoadsPerWave));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    if (step + S::kStages - 1 < nsteps) issue_stage(step + S::kStages - 1);
+  static_assert(S::kStages == 4, "the ring below holds two pairs of stages");
+  if (0 < nsteps) issue_stage(0);
+  if (1 < nsteps) issue_stage(1);
+  for (int step = 0; step < nsteps; step += 2) {
+    // This wave's loads of steps `step` and `step+1` are the oldest ones in
+    // flight (every wave issues at least kMinLoadsPerWave loads per stage).
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // A bare barrier: __syncthreads() would add a workgroup fence around it;
+    // the wait above already covers this wave's loads, and after the barrier
+    // all waves' are in LDS and every wave has finished reading the two
+    // buffers refilled next.  The memory clobber keeps the compiler from
+    // moving LDS accesses across it.
+    asm volatile("s_barrier" ::: "memory");
+    if (step + 2 < nsteps) issue_stage(step + 2);
+    if (step + 3 < nsteps) issue_stage(step + 3);
     compute(step % S::kStages);
+    if (step + 1 < nsteps) compute((step + 1) % S::kStages);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
