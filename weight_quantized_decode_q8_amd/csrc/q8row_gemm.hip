@@ -260,8 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
       for (int l = 0; l < L; l++) acc[a][c][l] = i32x4{0, 0, 0, 0};
 
   const int kc = lane >> 4, r16 = lane & 15;
-  auto compute = [&](int buf) {
-    i32x4 bf[S::kBB][L];
+  auto read_b = [&](int buf, i32x4 (&bf)[S::kBB][L]) {
 #pragma unroll
     for (int c = 0; c < S::kBB; c++) {
       const int bcol = wq * S::kWB + c * 16 + r16;  // 0 .. TN-1
@@ -269,31 +268,49 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
       for (int l = 0; l < L; l++)
         bf[c][l] = Bs(buf)[((l * (TN / 64) + bcol / 64) * kCPS + kc) * 64 + (bcol & 63)];
     }
-    // A fragments in pairs, software-pipelined: the LDS reads of the next
-    // pair are issued before the MFMAs of this one.
-    const i32x4 *abase = As(buf) + kc * kTM + ob0 * 16 + r16;
-    i32x4 a0 = abase[0], a1 = abase[16];
+  };
+  auto read_a = [&](int buf, int a) { return As(buf)[kc * kTM + (ob0 + a) * 16 + r16]; };
+  auto mfma_block = [&](int a, const i32x4 &af, const i32x4 (&bf)[S::kBB][L]) {
+#pragma unroll
+    for (int c = 0; c < S::kBB; c++)
+#pragma unroll
+      for (int l = 0; l < L; l++)
+        acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c][l], acc[a][c][l], 0, 0, 0);
+  };
+  // Two K-steps (stage buffers buf0, buf1) as one software pipeline: the LDS
+  // reads of the next pair of A fragments -- and at the step boundary the next
+  // step's B fragments -- are issued before the MFMAs of the current pair, so
+  // their latency hides behind MFMA work.
+  auto compute2 = [&](int buf0, int buf1, bool has1) {
+    i32x4 bf0[S::kBB][L], bf1[S::kBB][L];
+    read_b(buf0, bf0);
+    i32x4 c0 = read_a(buf0, 0), c1 = read_a(buf0, 1);
 #pragma unroll
     for (int a = 0; a < kOBW; a += 2) {
-      i32x4 n0 = a0, n1 = a1;
-      if (a + 2 < kOBW && a + 2 < nob) n0 = abase[(a + 2) * 16];
-      if (a + 3 < kOBW && a + 3 < nob) n1 = abase[(a + 3) * 16];
-      if (a < nob) {
-#pragma unroll
-        for (int c = 0; c < S::kBB; c++)
-#pragma unroll
-          for (int l = 0; l < L; l++)
-            acc[a][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[c][l], acc[a][c][l], 0, 0, 0);
+      i32x4 n0 = c0, n1 = c1;
+      if (a + 2 < kOBW) {
+        if (a + 2 < nob) n0 = read_a(buf0, a + 2);
+        if (a + 3 < kOBW && a + 3 < nob) n1 = read_a(buf0, a + 3);
+      } else if (has1) {
+        read_b(buf1, bf1);
+        n0 = read_a(buf1, 0);
+        n1 = read_a(buf1, 1);
       }
-      if (a + 1 < kOBW && a + 1 < nob) {
+      if (a < nob) mfma_block(a, c0, bf0);
+      if (a + 1 < kOBW && a + 1 < nob) mfma_block(a + 1, c1, bf0);
+      c0 = n0;
+      c1 = n1;
+    }
+    if (!has1) return;
 #pragma unroll
-        for (int c = 0; c < S::kBB; c++)
-#pragma unroll
-          for (int l = 0; l < L; l++)
-            acc[a + 1][c][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bf[c][l], acc[a + 1][c][l], 0, 0, 0);
-      }
-      a0 = n0;
-      a1 = n1;
+    for (int a = 0; a < kOBW; a += 2) {
+      i32x4 n0 = c0, n1 = c1;
+      if (a + 2 < kOBW && a + 2 < nob) n0 = read_a(buf1, a + 2);
+      if (a + 3 < kOBW && a + 3 < nob) n1 = read_a(buf1, a + 3);
+      if (a < nob) mfma_block(a, c0, bf1);
+      if (a + 1 < kOBW && a + 1 < nob) mfma_block(a + 1, c1, bf1);
+      c0 = n0;
+      c1 = n1;
     }
   };
 
@@ -316,8 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
     asm volatile("s_barrier" ::: "memory");
     if (step + 2 < nsteps) issue_stage(step + 2);
     if (step + 3 < nsteps) issue_stage(step + 3);
-    compute(step % S::kStages);
-    if (step + 1 < nsteps) compute((step + 1) % S::kStages);
+    compute2(step % S::kStages, (step + 1) % S::kStages, step + 1 < nsteps);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
