@@ -41,24 +41,20 @@ constexpr int kCPS = kKS / 16; // 16-byte chunks per stage
 constexpr int kLimbMax = 3;
 constexpr int kR3 = 126 * 65536;  // largest |fixed-point value|, 3 limbs
 
-// ------------------------------------------------------------- prep kernel
-// One workgroup per (padded) row b of xs.  Writes the three limbs in the
-// same tiled form as the weights: limb l, row b, 16-byte chunk c at
-//   ((l * nbt + b / 64) * nchunk + c) * 64 + b % 64        (16-byte units)
-// plus the row's exponent e_b and whether it needs the third limb.
-__global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict__ xs, int nb, int K,
-                                                        int nchunk, int nbt, i32x4 *__restrict__ xl,
-                                                        int *__restrict__ xexp, int *__restrict__ need3,
-                                                        i32x4 *__restrict__ zero_blk) {
+// ------------------------------------------------------------- prep kernels
+// 1) Per row b of xs (one workgroup each, rows past nb included): the
+//    exponent e_b and whether the row needs the third limb.
+__global__ __launch_bounds__(256) void gemm_rowstats_kernel(const float *__restrict__ xs, int nb, int K,
+                                                            int *__restrict__ xexp, int *__restrict__ need3,
+                                                            i32x4 *__restrict__ zero_blk) {
   __shared__ float red_max[4], red_sum[4];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   if (b == 0 && tid < 64) zero_blk[tid] = i32x4{0, 0, 0, 0};
-  const bool live = b < nb;
   const float *row = xs + (size_t)b * K;
 
   float amax = 0.0f, asum = 0.0f;
-  if (live) {
+  if (b < nb) {
     for (int k = tid * 4; k < K; k += 256 * 4) {  // K % 4 == 0, rows 16-byte aligned
       const float4 v = *reinterpret_cast<const float4 *>(row + k);
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
@@ -74,9 +70,9 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict_
     red_sum[tid >> 6] = asum;
   }
   __syncthreads();
+  if (tid != 0) return;
   amax = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
   asum = (red_sum[0] + red_sum[1]) + (red_sum[2] + red_sum[3]);
-
   // Smallest e with amax <= kR3 * 2^e (kR3 * 2^e is exact in f32).
   int e = 0;
   if (amax > 0.0f) {
@@ -84,13 +80,31 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict_
     while (amax > ldexpf((float)kR3, e)) e++;
     while (amax <= ldexpf((float)kR3, e - 1)) e--;
   }
-  if (tid == 0) {
-    xexp[b] = e;
-    const float thresh = 0.9e-5f * asum / sqrtf((float)K);
-    need3[b] = (amax > 0.0f && ldexpf(1.0f, e + 8) > thresh) ? 1 : 0;
-  }
+  xexp[b] = e;
+  const float thresh = 0.9e-5f * asum / sqrtf((float)K);
+  need3[b] = (amax > 0.0f && ldexpf(1.0f, e + 8) > thresh) ? 1 : 0;
+}
 
-  for (int c = tid; c < nchunk; c += 256) {
+// 2) The limbs, in the weights' tiled form: limb l, row b, 16-byte chunk c at
+//      ((l * nbt + b / 64) * nchunk + c) * 64 + b % 64        (16-byte units)
+//    A workgroup covers 64 rows (one tile) x kPrepChunks chunks; the 64
+//    threads of a wave take the 64 rows of one chunk, so every limb store of
+//    a wave is 1 KiB contiguous.
+constexpr int kPrepChunks = 8;
+
+__global__ __launch_bounds__(256) void gemm_limbs_kernel(const float *__restrict__ xs, int nb, int K,
+                                                         int nchunk, int nbt, const int *__restrict__ xexp,
+                                                         i32x4 *__restrict__ xl) {
+  const int tid = threadIdx.x;
+  const int r = tid & 63;
+  const int b = blockIdx.x * 64 + r;
+  const bool live = b < nb;
+  const int e = xexp[b];
+  const float *row = xs + (size_t)b * K;
+#pragma unroll
+  for (int i = 0; i < kPrepChunks / 4; i++) {
+    const int c = blockIdx.y * kPrepChunks + (tid >> 6) + 4 * i;
+    if (c >= nchunk) break;
     float xv[16];
     if (live && c * 16 + 16 <= K) {
 #pragma unroll
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float *__restrict_
     }
 #pragma unroll
     for (int l = 0; l < kLimbMax; l++)
-      xl[((size_t)(l * nbt + b / 64) * nchunk + c) * 64 + (b & 63)] =
+      xl[((size_t)(l * nbt + blockIdx.x) * nchunk + c) * 64 + r] =
           i32x4{lim[l][0], lim[l][1], lim[l][2], lim[l][3]};
   }
 }
@@ -427,7 +441,9 @@ hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, fl
   int *need3 = reinterpret_cast<int *>(base + off_need);
   i32x4 *zero_blk = reinterpret_cast<i32x4 *>(base + off_zero);
 
-  gemm_prep_kernel<<<nbp, 256, 0, stream>>>(xs, nb, K, nchunk, nbp / 64, xl, xexp, need3, zero_blk);
+  gemm_rowstats_kernel<<<nbp, 256, 0, stream>>>(xs, nb, K, xexp, need3, zero_blk);
+  gemm_limbs_kernel<<<dim3(nbp / 64, (nchunk + kPrepChunks - 1) / kPrepChunks), 256, 0, stream>>>(
+      xs, nb, K, nchunk, nbp / 64, xexp, xl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (limbs == 2 || limbs == 0) {
