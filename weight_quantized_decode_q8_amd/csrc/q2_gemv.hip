@@ -20,15 +20,15 @@
 //    16 weights, no shuffles and no lookup tables;
 //  - the activation words and suma are wave-uniform: scalar loads into
 //    SGPRs, used directly as the dot4 operand;
-//  - K is split over the workgroup's 4 waves (LDS combine) and, when the
-//    row tiles alone cannot fill 256 CUs, over blockIdx.y splits whose f32
-//    partials [split][Mp] are summed in fixed order by a second kernel.
+//  - K is split over the workgroup's 8 or 16 waves (LDS combine) and, for
+//    large matrices whose row tiles cannot fill 256 CUs, over blockIdx.y
+//    splits whose f32 partials [split][Mp] are summed in fixed order by a
+//    second kernel.
 #include "qg_internal.h"
 
 namespace qg {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr unsigned kCodeMask = 0x03030303u;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -65,10 +65,10 @@ __device__ inline float half_bits_to_f32(unsigned short h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// grid = (row tiles, splits); block = kWaves wavefronts.
+// grid = (row tiles, splits); block = kWaves wavefronts sharing one tile.
 // UPG = units (of 64 weights) per scale group: 1 for g64, 2 for g128.
 // GPB = groups handled per unrolled step (GPB*UPG code loads in flight).
-template <int UPG, int GPB, bool kDots>
+template <int UPG, int GPB, bool kDots, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(
     const i32x4 *__restrict__ codes, const unsigned short *__restrict__ scales,
     const int8_t *__restrict__ xq, const int *__restrict__ suma,
@@ -158,23 +158,34 @@ __global__ __launch_bounds__(256) void q2_splitk_reduce_kernel(const float *__re
   y[o] = s * act_scale[0];
 }
 
+template <int UPG, int GPB, int W>
+hipError_t launch_main(const i32x4 *c, const unsigned short *s, int M, int K, const int8_t *xq,
+                       const int32_t *suma, const float *act_scale, float *out, int32_t *dots,
+                       int S, hipStream_t stream) {
+  const int tiles = (M + 63) / 64;
+  const dim3 grid(tiles, S);
+  if (dots)
+    q2_gemv_t64_kernel<UPG, GPB, true, W><<<grid, 64 * W, 0, stream>>>(
+        c, s, xq, suma, act_scale, out, dots, M, tiles * 64, K, S);
+  else
+    q2_gemv_t64_kernel<UPG, GPB, false, W><<<grid, 64 * W, 0, stream>>>(
+        c, s, xq, suma, act_scale, out, nullptr, M, tiles * 64, K, S);
+  return hipGetLastError();
+}
+
+// Waves per tile: 8 when the row tiles alone fill the CUs, else 16 so that
+// each of the fewer workgroups keeps more loads in flight.
 template <int UPG, int GPB>
 hipError_t launch_typed(const void *codes, const void *scales, int M, int K, const int8_t *xq,
                         const int32_t *suma, const float *act_scale, float *y, int32_t *dots,
                         float *partials, int S, hipStream_t stream) {
   const int tiles = (M + 63) / 64;
   const int Mp = tiles * 64;
-  const dim3 grid(tiles, S);
   float *out = S == 1 ? y : partials;
   const i32x4 *c = reinterpret_cast<const i32x4 *>(codes);
   const unsigned short *s = reinterpret_cast<const unsigned short *>(scales);
-  if (dots)
-    q2_gemv_t64_kernel<UPG, GPB, true><<<grid, 64 * kWaves, 0, stream>>>(
-        c, s, xq, suma, act_scale, out, dots, M, Mp, K, S);
-  else
-    q2_gemv_t64_kernel<UPG, GPB, false><<<grid, 64 * kWaves, 0, stream>>>(
-        c, s, xq, suma, act_scale, out, nullptr, M, Mp, K, S);
-  hipError_t e = hipGetLastError();
+  hipError_t e = tiles >= 256 ? launch_main<UPG, GPB, 8>(c, s, M, K, xq, suma, act_scale, out, dots, S, stream)
+                              : launch_main<UPG, GPB, 16>(c, s, M, K, xq, suma, act_scale, out, dots, S, stream);
   if (e != hipSuccess || S == 1) return e;
   q2_splitk_reduce_kernel<<<(M + 255) / 256, 256, 0, stream>>>(partials, S, Mp, M, act_scale, y);
   return hipGetLastError();
@@ -183,12 +194,16 @@ hipError_t launch_typed(const void *codes, const void *scales, int M, int K, con
 }  // namespace
 
 int q2_auto_split(int64_t M, int64_t K, int group) {
-  // Enough workgroups that every CU holds several (4 waves each), without
-  // leaving a wave less than one scale group of work.
+  // A second (reduce) launch costs about as much as streaming several MB, so
+  // K is split only for large matrices whose row tiles cannot fill the 256
+  // CUs: then into the fewest power-of-two ranges giving >= 256 workgroups
+  // (and at least one scale group per wave).
   const int64_t tiles = (M + 63) / 64;
   const int64_t ngroups = K / group;
+  const int64_t bytes = M * ngroups * (2 + group / 4);
+  if (tiles >= 256 || bytes < (16LL << 20)) return 1;
   int S = 1;
-  while (S < kMaxSplit && tiles * S < 1024 && ngroups / (2 * S) >= kWaves) S *= 2;
+  while (S < kMaxSplit && tiles * S < 256 && ngroups / (2 * S) >= 16) S *= 2;
   return S;
 }
 

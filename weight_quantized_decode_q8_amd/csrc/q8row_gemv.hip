@@ -19,15 +19,15 @@
 //  - the workgroup's waves split the K chunks of one tile into contiguous
 //    ranges and combine their row sums through LDS (no second launch).
 // Rounding: each lane keeps 16 accumulators (one per byte position), so an
-// accumulator chain has K/16/waves terms, then a 16-way tree and a
-// waves-way sum; at K = 5120 the worst-case bound is about 90 roundings.
+// accumulator chain has K/16/8 terms, then a 16-way tree and an 8-way sum;
+// at K = 5120 the worst-case chain is about 50 roundings.
 #include "qg_internal.h"
 
 namespace qg {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kUnroll = 4;
+constexpr int kWaves = 8;   // 512 threads: 8 waves split the K chunks of one tile
+constexpr int kUnroll = 8;  // 128-bit loads in flight per lane
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
