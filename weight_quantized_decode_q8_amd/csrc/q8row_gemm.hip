@@ -178,14 +178,14 @@ struct GemmShape {
       kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
 };
 
+// One pass of the K loop plus the epilogue for weight block `ot` and the TN
+// xs rows starting at b0, with L limbs.  `lds` is the workgroup's buffer.
 template <int L, int TN>
-__global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
-    const i32x4 *__restrict__ w, const float *__restrict__ rs, const i32x4 *__restrict__ xl,
-    const i32x4 *__restrict__ zero_blk, const int *__restrict__ xexp,
-    const int *__restrict__ need3, float *__restrict__ y, int nb, int M, int nchunk_w, int nchunk,
-    int nbt64, int n_ot, int n_bt, int mode) {
+__device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w, const float *__restrict__ rs,
+                                          const i32x4 *__restrict__ xl, const i32x4 *__restrict__ zero_blk,
+                                          const int *__restrict__ xexp, float *__restrict__ y, int nb, int M,
+                                          int nchunk_w, int nchunk, int nbt64, int ot, int b0) {
   using S = GemmShape<L, TN>;
-  __shared__ __attribute__((aligned(16))) char lds[S::kLdsBytes];
   // Stage buffer `buf` holds the A pieces, then the B pieces.
   auto As = [&](int buf) { return reinterpret_cast<i32x4 *>(lds + buf * S::kStageBytes); };
   auto Bs = [&](int buf) { return As(buf) + S::kAPieces; };
@@ -198,26 +198,9 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
   const int ob0 = wh * kOBW;       // first row block of this wave
   const int nob = wh == 0 ? kOBW : kOB - kOBW;
 
-  // Block order: the n_bt workgroups of one weight block get ids 8 apart, so
-  // the round-robin dispatch over the 8 XCDs puts them on one XCD together.
-  const int id = blockIdx.x;
-  const int per_grp = 8 * n_bt;
-  const int ot = (id / per_grp) * 8 + (id % per_grp) % 8;
-  const int bt = (id % per_grp) / 8;
-  if (ot >= n_ot) return;
-
-  // Auto mode: a 128-row group of xs rows goes to the 3-limb kernel if any
-  // of its rows needs the third limb, else to the 2-limb kernel.
-  if (mode == 1) {
-    const int g0 = (bt * TN) / 128 * 128;
-    const int f = need3[g0 + lane] | need3[g0 + 64 + lane];
-    const bool grp3 = __builtin_amdgcn_ballot_w64(f != 0) != 0;
-    if (grp3 != (L == 3)) return;
-  }
-
   const int o0 = ot * kTM;
   const int m_tiles = (M + 63) / 64;
-  const int b_tile0 = bt * (TN / 64);
+  const int b_tile0 = b0 / 64;
 
   // One stage = wave loads of 1 KiB that go straight from global memory into
   // LDS (lane i's 16 bytes land at base + 16 i); wave w issues wave loads
@@ -380,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
     // 64 rows x 68 float4 per group.
     for (int f = tid; f < 64 * (kTM / 4); f += kThreads) {
       const int gr = f / (kTM / 4), col = (f % (kTM / 4)) * 4;
-      const int b = bt * TN + (gr / 16) * S::kWB + c * 16 + (gr % 16);
+      const int b = b0 + (gr / 16) * S::kWB + c * 16 + (gr % 16);
       const int o = o0 + col;
       if (b >= nb || o >= M) continue;
       const float4 v4 = *reinterpret_cast<const float4 *>(ep + gr * S::kRowStride + col);
@@ -401,17 +384,42 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
   }
 }
 
-template <int L, int TN>
-hipError_t launch_gemm(const void *w, const float *rs, const i32x4 *xl, const i32x4 *zero_blk,
-                       const int *xexp, const int *need3, float *y, int nb, int nbp, int M,
-                       int nchunk_w, int nchunk, int mode, hipStream_t stream) {
-  const int n_ot = (M + kTM - 1) / kTM;
-  const int n_bt = nbp / TN;
-  const int grid = (n_ot + 7) / 8 * 8 * n_bt;
-  q8row_gemm_kernel<L, TN><<<grid, kThreads, 0, stream>>>(
-      reinterpret_cast<const i32x4 *>(w), rs, xl, zero_blk, xexp, need3, y, nb, M, nchunk_w, nchunk,
-      nbp / 64, n_ot, n_bt, mode);
-  return hipGetLastError();
+constexpr int kGemmLds = GemmShape<2, 128>::kLdsBytes > GemmShape<3, 64>::kLdsBytes
+                             ? GemmShape<2, 128>::kLdsBytes
+                             : GemmShape<3, 64>::kLdsBytes;
+
+// One workgroup per (weight block of 272 rows, group of 128 xs rows).  The
+// group is computed with 2 limbs in one pass of 128 rows, or with 3 limbs in
+// two passes of 64 rows.  limbs: 2 or 3 for all groups, 0 = per group from
+// the rows' need3 flags (auto).
+__global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
+    const i32x4 *__restrict__ w, const float *__restrict__ rs, const i32x4 *__restrict__ xl,
+    const i32x4 *__restrict__ zero_blk, const int *__restrict__ xexp,
+    const int *__restrict__ need3, float *__restrict__ y, int nb, int M, int nchunk_w, int nchunk,
+    int nbt64, int n_ot, int n_bt, int limbs) {
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+
+  // Block order: the n_bt workgroups of one weight block get ids 8 apart, so
+  // the round-robin dispatch over the 8 XCDs puts them on one XCD together.
+  const int id = blockIdx.x;
+  const int per_grp = 8 * n_bt;
+  const int ot = (id / per_grp) * 8 + (id % per_grp) % 8;
+  const int bt = (id % per_grp) / 8;
+  if (ot >= n_ot) return;
+  const int g0 = bt * 128;
+
+  bool three = limbs == 3;
+  if (limbs == 0) {
+    const int lane = threadIdx.x & 63;
+    const int f = need3[g0 + lane] | need3[g0 + 64 + lane];
+    three = __builtin_amdgcn_ballot_w64(f != 0) != 0;
+  }
+  if (three) {
+    gemm_pass<3, 64>(lds, w, rs, xl, zero_blk, xexp, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0);
+    gemm_pass<3, 64>(lds, w, rs, xl, zero_blk, xexp, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0 + 64);
+  } else {
+    gemm_pass<2, 128>(lds, w, rs, xl, zero_blk, xexp, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0);
+  }
 }
 
 }  // namespace
@@ -446,14 +454,13 @@ hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, fl
       xs, nb, K, nchunk, nbp / 64, xexp, xl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (limbs == 2 || limbs == 0) {
-    err = launch_gemm<2, 128>(w, rs, xl, zero_blk, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
-                              limbs == 0 ? 1 : 0, stream);
-    if (err != hipSuccess) return err;
-  }
-  if (limbs == 3 || limbs == 0)
-    err = launch_gemm<3, 64>(w, rs, xl, zero_blk, xexp, need3, y, nb, nbp, M, nchunk_w, nchunk,
-                             limbs == 0 ? 1 : 0, stream);
+  const int n_ot = (M + kTM - 1) / kTM;
+  const int n_bt = nbp / 128;
+  const int grid = (n_ot + 7) / 8 * 8 * n_bt;
+  q8row_gemm_kernel<<<grid, kThreads, 0, stream>>>(reinterpret_cast<const i32x4 *>(w), rs, xl, zero_blk, xexp,
+                                                   need3, y, nb, M, nchunk_w, nchunk, nbp / 64, n_ot, n_bt,
+                                                   limbs);
+  err = hipGetLastError();
   return err;
 }
 
