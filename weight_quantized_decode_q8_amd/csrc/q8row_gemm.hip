@@ -23,11 +23,12 @@
 // 2e-5 * sum_i |w_i x_i| at six standard deviations; rows with a large
 // max/mean ratio (activation outliers) get the 24-bit form.
 //
-// gfx950 kernel: v_mfma_i32_16x16x64_i8 (A row and B column = lane % 16, the
-// 16-byte k chunk = lane / 16, D[4 * (lane / 16) + v][lane % 16]), a 256 x 128
-// (2 limbs) or 256 x 64 (3 limbs) output tile per 4-wave workgroup with
-// 256 accumulator registers per lane, operands staged through LDS in two
-// buffers, and a block order that puts the workgroups sharing one weight
+// gfx950 kernels: one prep launch (exponents, limb-count flags and limbs of
+// every xs row), then the product on v_mfma_i32_16x16x64_i8 (A row and B
+// column = lane % 16, the 16-byte k chunk = lane / 16, D[4 * (lane / 16) + v]
+// [lane % 16]): a 272 x 128 output tile per 8-wave workgroup (one tile per
+// CU at the FFN width), operands moved global -> LDS directly through a
+// 4-stage ring, and a block order that puts the workgroups sharing one weight
 // tile on the same XCD (the same L2) at the same time.
 #include "qg_internal.h"
 
@@ -41,24 +42,92 @@ constexpr int kCPS = kKS / 16; // 16-byte chunks per stage
 constexpr int kLimbMax = 3;
 constexpr int kR3 = 126 * 65536;  // largest |fixed-point value|, 3 limbs
 
-// ------------------------------------------------------------- prep kernels
-// 1) Per row b of xs (one workgroup each, rows past nb included): the
-//    exponent e_b and whether the row needs the third limb.
-__global__ __launch_bounds__(256) void gemm_rowstats_kernel(const float *__restrict__ xs, int nb, int K,
-                                                            int *__restrict__ xexp, int *__restrict__ need3,
-                                                            i32x4 *__restrict__ zero_blk) {
-  __shared__ float red_max[4], red_sum[4];
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (b == 0 && tid < 64) zero_blk[tid] = i32x4{0, 0, 0, 0};
-  const float *row = xs + (size_t)b * K;
+// ------------------------------------------------------------- prep kernel
+// One workgroup per row b of xs (rows past nb included, as zeros; the grid
+// is nbp workgroups, nbp a multiple of 128), thread t taking the 16-float
+// chunks t, t + 256, ...  It finds max|x| and sum|x| of the row, hence the
+// exponent e_b (the smallest e with max|x| <= kR3 * 2^e) and whether the row
+// needs the third limb, then writes the row's limbs in the weights' tiled
+// form: limb l, row b, 16-byte chunk c at
+//     ((l * nbt + b / 64) * nchunk + c) * 64 + b % 64        (16-byte units)
+// Rows of up to kPrepHeld chunks per thread stay in registers between the
+// two steps; longer rows are read a second time (from L2).  Chunks past K
+// are written as zeros.
+constexpr int kPrepThreads = 256;
+constexpr int kPrepHeld = 2;
 
+__device__ __forceinline__ void load_chunk(const float *__restrict__ row, int c, int K, bool live, float (&xv)[16]) {
+  if (live && c * 16 + 16 <= K) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float4 v = *reinterpret_cast<const float4 *>(row + c * 16 + 4 * q);
+      xv[4 * q] = v.x, xv[4 * q + 1] = v.y, xv[4 * q + 2] = v.z, xv[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; j++) xv[j] = (live && c * 16 + j < K) ? row[c * 16 + j] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void store_limbs(const float (&xv)[16], int e, i32x4 *__restrict__ dst, size_t limb_stride) {
+  int lim[kLimbMax][4];
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    lim[0][w] = lim[1][w] = lim[2][w] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      int v = (int)rintf(ldexpf(xv[w * 4 + j], -e));  // exact scaling, then nearest
+      const int lo = ((v + 128) & 255) - 128;
+      v = (v - lo) >> 8;
+      const int mi = ((v + 128) & 255) - 128;
+      const int hi = (v - mi) >> 8;
+      lim[0][w] |= (hi & 255) << (8 * j);
+      lim[1][w] |= (mi & 255) << (8 * j);
+      lim[2][w] |= (lo & 255) << (8 * j);
+    }
+  }
+#pragma unroll
+  for (int l = 0; l < kLimbMax; l++) dst[l * limb_stride] = i32x4{lim[l][0], lim[l][1], lim[l][2], lim[l][3]};
+}
+
+__global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__restrict__ xs, int nb, int K,
+                                                                 int nchunk, int nbt, int *__restrict__ xexp,
+                                                                 int *__restrict__ need3, i32x4 *__restrict__ xl,
+                                                                 i32x4 *__restrict__ zero_blk) {
+  __shared__ float red_max[kPrepThreads / 64], red_sum[kPrepThreads / 64];
+  __shared__ int sh_e;
+  const int tid = threadIdx.x;
+  // Consecutive workgroups go to the 8 XCDs in turn; XCD x gets the rows
+  // x * nbp / 8 ... so the 8 rows that share a 128-byte line of limbs are
+  // written through one L2 (no partial lines written back from several).
+  const int b = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  if (blockIdx.x == 0 && tid < 64) zero_blk[tid] = i32x4{0, 0, 0, 0};
+  const bool live = b < nb;
+  const float *row = xs + (size_t)(live ? b : 0) * K;
+  const int nchunk_k = (K + 15) / 16;  // chunks holding any of the row
+  const bool held = nchunk_k <= kPrepHeld * kPrepThreads;
+
+  float xh[kPrepHeld][16];
   float amax = 0.0f, asum = 0.0f;
-  if (b < nb) {
-    for (int k = tid * 4; k < K; k += 256 * 4) {  // K % 4 == 0, rows 16-byte aligned
-      const float4 v = *reinterpret_cast<const float4 *>(row + k);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-      asum += (fabsf(v.x) + fabsf(v.y)) + (fabsf(v.z) + fabsf(v.w));
+  if (held) {
+#pragma unroll
+    for (int h = 0; h < kPrepHeld; h++) load_chunk(row, tid + h * kPrepThreads, K, live, xh[h]);
+#pragma unroll
+    for (int h = 0; h < kPrepHeld; h++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        amax = fmaxf(amax, fabsf(xh[h][j]));
+        asum += fabsf(xh[h][j]);
+      }
+  } else {
+    for (int c = tid; c < nchunk_k; c += kPrepThreads) {
+      float xv[16];
+      load_chunk(row, c, K, live, xv);
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        amax = fmaxf(amax, fabsf(xv[j]));
+        asum += fabsf(xv[j]);
+      }
     }
   }
   for (int off = 32; off > 0; off >>= 1) {
@@ -70,73 +139,41 @@ __global__ __launch_bounds__(256) void gemm_rowstats_kernel(const float *__restr
     red_sum[tid >> 6] = asum;
   }
   __syncthreads();
-  if (tid != 0) return;
-  amax = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
-  asum = (red_sum[0] + red_sum[1]) + (red_sum[2] + red_sum[3]);
-  // Smallest e with amax <= kR3 * 2^e (kR3 * 2^e is exact in f32).
-  int e = 0;
-  if (amax > 0.0f) {
-    e = ilogbf(amax) - 22;
-    while (amax > ldexpf((float)kR3, e)) e++;
-    while (amax <= ldexpf((float)kR3, e - 1)) e--;
+  if (tid == 0) {
+    amax = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+    asum = (red_sum[0] + red_sum[1]) + (red_sum[2] + red_sum[3]);
+    int e = 0;
+    if (amax > 0.0f) {
+      e = ilogbf(amax) - 22;
+      while (amax > ldexpf((float)kR3, e)) e++;
+      while (amax <= ldexpf((float)kR3, e - 1)) e--;
+    }
+    xexp[b] = e;
+    const float thresh = 0.9e-5f * asum / sqrtf((float)K);
+    need3[b] = (amax > 0.0f && ldexpf(1.0f, e + 8) > thresh) ? 1 : 0;
+    sh_e = e;
   }
-  xexp[b] = e;
-  const float thresh = 0.9e-5f * asum / sqrtf((float)K);
-  need3[b] = (amax > 0.0f && ldexpf(1.0f, e + 8) > thresh) ? 1 : 0;
-}
+  __syncthreads();
+  const int e = sh_e;
 
-// 2) The limbs, in the weights' tiled form: limb l, row b, 16-byte chunk c at
-//      ((l * nbt + b / 64) * nchunk + c) * 64 + b % 64        (16-byte units)
-//    A workgroup covers 64 rows (one tile) x kPrepChunks chunks; the 64
-//    threads of a wave take the 64 rows of one chunk, so every limb store of
-//    a wave is 1 KiB contiguous.
-constexpr int kPrepChunks = 8;
-
-__global__ __launch_bounds__(256) void gemm_limbs_kernel(const float *__restrict__ xs, int nb, int K,
-                                                         int nchunk, int nbt, const int *__restrict__ xexp,
-                                                         i32x4 *__restrict__ xl) {
-  const int tid = threadIdx.x;
-  const int r = tid & 63;
-  const int b = blockIdx.x * 64 + r;
-  const bool live = b < nb;
-  const int e = xexp[b];
-  const float *row = xs + (size_t)b * K;
+  const size_t limb_stride = (size_t)nbt * nchunk * 64;
+  i32x4 *dst = xl + (size_t)(b / 64) * nchunk * 64 + (b & 63);
+  if (held) {
 #pragma unroll
-  for (int i = 0; i < kPrepChunks / 4; i++) {
-    const int c = blockIdx.y * kPrepChunks + (tid >> 6) + 4 * i;
-    if (c >= nchunk) break;
-    float xv[16];
-    if (live && c * 16 + 16 <= K) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + c * 16 + 4 * q);
-        xv[4 * q] = v.x, xv[4 * q + 1] = v.y, xv[4 * q + 2] = v.z, xv[4 * q + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; j++) xv[j] = (live && c * 16 + j < K) ? row[c * 16 + j] : 0.0f;
+    for (int h = 0; h < kPrepHeld; h++) {
+      const int c = tid + h * kPrepThreads;
+      if (c < nchunk) store_limbs(xh[h], e, dst + (size_t)c * 64, limb_stride);
     }
-    int lim[kLimbMax][4];
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      lim[0][w] = lim[1][w] = lim[2][w] = 0;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const float x = xv[w * 4 + j];
-        int v = (int)rintf(ldexpf(x, -e));  // exact scaling, then nearest
-        const int lo = ((v + 128) & 255) - 128;
-        v = (v - lo) >> 8;
-        const int mi = ((v + 128) & 255) - 128;
-        const int hi = (v - mi) >> 8;
-        lim[0][w] |= (hi & 255) << (8 * j);
-        lim[1][w] |= (mi & 255) << (8 * j);
-        lim[2][w] |= (lo & 255) << (8 * j);
-      }
+    for (int c = tid + kPrepHeld * kPrepThreads; c < nchunk; c += kPrepThreads) {
+      const float zero[16] = {};
+      store_limbs(zero, e, dst + (size_t)c * 64, limb_stride);
     }
-#pragma unroll
-    for (int l = 0; l < kLimbMax; l++)
-      xl[((size_t)(l * nbt + blockIdx.x) * nchunk + c) * 64 + r] =
-          i32x4{lim[l][0], lim[l][1], lim[l][2], lim[l][3]};
+  } else {
+    for (int c = tid; c < nchunk; c += kPrepThreads) {
+      float xv[16];
+      load_chunk(row, c, K, live, xv);
+      store_limbs(xv, e, dst + (size_t)c * 64, limb_stride);
+    }
   }
 }
 
@@ -150,7 +187,9 @@ __global__ __launch_bounds__(256) void gemm_limbs_kernel(const float *__restrict
 constexpr int kOB = 17;
 constexpr int kOBW = 9;        // row blocks of the first wave half (the second has 8)
 constexpr int kTM = 16 * kOB;  // 272
-constexpr int kThreads = 512;
+constexpr int kWC = 4;         // wave groups along xs rows
+constexpr int kWaves = 2 * kWC;
+constexpr int kThreads = 64 * kWaves;
 
 // s_waitcnt immediate for vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14; expcnt and lgkmcnt left at their maxima, i.e. not waited for).
@@ -161,19 +200,19 @@ typedef const __attribute__((address_space(1))) void global_void;
 
 template <int L, int TN>
 struct GemmShape {
-  static constexpr int kWB = TN / 4;                  // xs rows per wave
+  static constexpr int kWB = TN / kWC;                // xs rows per wave
   static constexpr int kBB = kWB / 16;                // 16-column MFMA blocks per wave
   static constexpr int kAPieces = kTM * kCPS;         // 16-byte pieces of A per stage
   static constexpr int kBPieces = L * TN * kCPS;      // 16-byte pieces of B per stage
   static constexpr int kAWaveLoads = kAPieces / 64;   // 1 KiB wave loads of A (17)
   static constexpr int kBWaveLoads = kBPieces / 64;
-  static constexpr int kAPerWave = (kAWaveLoads + 7) / 8;  // at most, per wave
-  static constexpr int kBPerWave = (kBWaveLoads + 7) / 8;
-  static constexpr int kMinLoadsPerWave = kAWaveLoads / 8 + kBWaveLoads / 8;
+  static constexpr int kAPerWave = (kAWaveLoads + kWaves - 1) / kWaves;  // at most, per wave
+  static constexpr int kBPerWave = (kBWaveLoads + kWaves - 1) / kWaves;
   static constexpr int kStages = 4;                   // LDS ring depth
   static constexpr int kStageBytes = (kAPieces + kBPieces) * 16;
   static constexpr int kRowStride = kTM + 4;          // epilogue row stride (floats)
-  static constexpr int kEpiBytes = 64 * kRowStride * 4;
+  static constexpr int kEpiRows = 16 * kWC;          // xs rows per epilogue group
+  static constexpr int kEpiBytes = kEpiRows * kRowStride * 4;
   static constexpr int kLdsBytes =
       kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
 };
@@ -193,8 +232,8 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wq = wave & 3;         // xs-row quarter
-  const int wh = wave >> 2;        // weight-row half
+  const int wq = wave % kWC;       // xs-row group
+  const int wh = wave / kWC;       // weight-row half
   const int ob0 = wh * kOBW;       // first row block of this wave
   const int nob = wh == 0 ? kOBW : kOB - kOBW;
 
@@ -211,7 +250,7 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
   int a_kc[S::kAPerWave];
 #pragma unroll
   for (int i = 0; i < S::kAPerWave; i++) {
-    const int j = min(wave + 8 * i, S::kAWaveLoads - 1);
+    const int j = min(wave + kWaves * i, S::kAWaveLoads - 1);
     const int p = 64 * j + lane;
     const int kc = p / kTM, row = p % kTM;
     const int o = o0 + row, t = o >> 6;
@@ -221,7 +260,7 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
   const i32x4 *b_src[S::kBPerWave];
 #pragma unroll
   for (int i = 0; i < S::kBPerWave; i++) {
-    const int j = min(wave + 8 * i, S::kBWaveLoads - 1);
+    const int j = min(wave + kWaves * i, S::kBWaveLoads - 1);
     const int l = j / ((TN / 64) * kCPS);
     const int q = j % ((TN / 64) * kCPS);
     const int bt64 = q / kCPS, kc = q % kCPS;
@@ -232,7 +271,7 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
     const int c0 = step * kCPS;
 #pragma unroll
     for (int i = 0; i < S::kAPerWave; i++) {
-      const int j = wave + 8 * i;
+      const int j = wave + kWaves * i;
       if (j < S::kAWaveLoads) {
         const i32x4 *src = (a_src[i] != nullptr && c0 + a_kc[i] < nchunk_w)
                                ? a_src[i] + (size_t)step * (kCPS * 64) : zero_blk + lane;
@@ -241,7 +280,7 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
     }
 #pragma unroll
     for (int i = 0; i < S::kBPerWave; i++) {
-      const int j = wave + 8 * i;
+      const int j = wave + kWaves * i;
       if (j < S::kBWaveLoads)
         __builtin_amdgcn_global_load_lds((global_void *)(b_src[i] + (size_t)step * (kCPS * 64)),
                                          (lds_void *)(Bs(buf) + 64 * j), 16, 0, 0);
@@ -319,8 +358,7 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
   if (0 < nsteps) issue_stage(0);
   if (1 < nsteps) issue_stage(1);
   for (int step = 0; step < nsteps; step += 2) {
-    // This wave's loads of steps `step` and `step+1` are the oldest ones in
-    // flight (every wave issues at least kMinLoadsPerWave loads per stage).
+    // Steps `step` and `step+1` are the oldest loads in flight.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     // A bare barrier: __syncthreads() would add a workgroup fence around it;
     // the wait above already covers this wave's loads, and after the barrier
@@ -342,7 +380,7 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
   const bool vec = (M & 3) == 0;
 #pragma unroll
   for (int c = 0; c < S::kBB; c++) {
-    const int row = wq * 16 + r16;  // 0..63 within the group
+    const int row = wq * 16 + r16;  // within the group of kEpiRows
 #pragma unroll
     for (int a = 0; a < kOBW; a++) {
       if (a < nob) {
@@ -360,8 +398,7 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
       }
     }
     __syncthreads();
-    // 64 rows x 68 float4 per group.
-    for (int f = tid; f < 64 * (kTM / 4); f += kThreads) {
+    for (int f = tid; f < S::kEpiRows * (kTM / 4); f += kThreads) {
       const int gr = f / (kTM / 4), col = (f % (kTM / 4)) * 4;
       const int b = b0 + (gr / 16) * S::kWB + c * 16 + (gr % 16);
       const int o = o0 + col;
@@ -449,9 +486,7 @@ hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, fl
   int *need3 = reinterpret_cast<int *>(base + off_need);
   i32x4 *zero_blk = reinterpret_cast<i32x4 *>(base + off_zero);
 
-  gemm_rowstats_kernel<<<nbp, 256, 0, stream>>>(xs, nb, K, xexp, need3, zero_blk);
-  gemm_limbs_kernel<<<dim3(nbp / 64, (nchunk + kPrepChunks - 1) / kPrepChunks), 256, 0, stream>>>(
-      xs, nb, K, nchunk, nbp / 64, xexp, xl);
+  gemm_prep_kernel<<<nbp, kPrepThreads, 0, stream>>>(xs, nb, K, nchunk, nbp / 64, xexp, need3, xl, zero_blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_ot = (M + kTM - 1) / kTM;
