@@ -63,6 +63,12 @@ class Oracle:
         lib.qo_q2_dots.argtypes = [P, I64, I64, ctypes.c_int, P, P]
         lib.qo_q2_gemv.restype = None
         lib.qo_q2_gemv.argtypes = [P, I64, I64, ctypes.c_int, P, ctypes.c_float, P, I64, P, P]
+        lib.qo_q2_gemv_accum.restype = None
+        lib.qo_q2_gemv_accum.argtypes = [P, I64, I64, ctypes.c_int, P, ctypes.c_float, P, P, I64, P, P]
+        lib.qo_rmsnorm_quant_i8.restype = None
+        lib.qo_rmsnorm_quant_i8.argtypes = [P, P, I64, ctypes.c_float, P, P, P, P]
+        lib.qo_glu_quant_i8.restype = None
+        lib.qo_glu_quant_i8.argtypes = [P, P, I64, ctypes.c_int, P, P, P, P]
         self.lib = lib
 
     def f16_to_f64(self, bits: int) -> float:
@@ -158,6 +164,59 @@ class Oracle:
                             y.ctypes.data, m.ctypes.data)
         return y, m
 
+    def q2_gemv_accum(self, blob, M, K, group, xq, sc, accum, rows=None):
+        """q2_gemv plus a residual: y[o] = proj[o] + accum[o] in fp64 (qxmx page, tmatvec_accum).
+
+        Returns ``(y, mass)``; mass as q2_gemv.
+        """
+        b, bp = _c(blob, np.uint8)
+        xq, xqp = _c(xq, np.int8)
+        a, ap = _c(accum, np.float32)
+        assert a.size == M
+        r, rp, n = _rows(rows)
+        n = M if r is None else n
+        y = np.empty(n, np.float64)
+        m = np.empty(n, np.float64)
+        self.lib.qo_q2_gemv_accum(bp, M, K, group, xqp, ctypes.c_float(float(sc)), ap, rp, n,
+                                  y.ctypes.data, m.ctypes.data)
+        return y, m
+
+    def rmsnorm_quant_i8(self, x, w, eps):
+        """RMSNorm in binary32 then the int8 quantiser (qxmx page, gpu_rmsnorm_quant).
+
+        Returns ``(v float32[K], xq int8[K], act_scale float32, suma int32[K/64])``
+        where v = (x * inv) * w, inv = 1 / sqrt(f32(sum x^2 / K) + eps).
+        """
+        x, xp = _c(x, np.float32)
+        w, wp = _c(w, np.float32)
+        K = x.size
+        assert w.size == K
+        v = np.empty(K, np.float32)
+        xq = np.empty(K, np.int8)
+        sc = np.zeros(1, np.float32)
+        suma = np.empty(K // 64, np.int32)
+        self.lib.qo_rmsnorm_quant_i8(xp, wp, K, ctypes.c_float(float(eps)), v.ctypes.data, xq.ctypes.data,
+                                     sc.ctypes.data, suma.ctypes.data if K // 64 else None)
+        return v, xq, sc[0], suma
+
+    def glu_quant_i8(self, g, u, kind):
+        """Gated product in binary32 then the int8 quantiser (qxmx page,
+        gpu_swiglu_quant / gpu_silu_mul_quant for kind 0, gpu_sigmoid_mul_quant for kind 1).
+
+        Returns ``(t float32[K], xq int8[K], act_scale float32, suma int32[K/64])``.
+        """
+        g, gp = _c(g, np.float32)
+        u, up = _c(u, np.float32)
+        K = g.size
+        assert u.size == K and kind in (0, 1)
+        t = np.empty(K, np.float32)
+        xq = np.empty(K, np.int8)
+        sc = np.zeros(1, np.float32)
+        suma = np.empty(K // 64, np.int32)
+        self.lib.qo_glu_quant_i8(gp, up, K, kind, t.ctypes.data, xq.ctypes.data, sc.ctypes.data,
+                                 suma.ctypes.data if K // 64 else None)
+        return t, xq, sc[0], suma
+
 
 _default = None
 
@@ -198,3 +257,15 @@ def q2_dots(blob, M, K, group, xq):
 
 def q2_gemv(blob, M, K, group, xq, sc, rows=None):
     return default().q2_gemv(blob, M, K, group, xq, sc, rows)
+
+
+def q2_gemv_accum(blob, M, K, group, xq, sc, accum, rows=None):
+    return default().q2_gemv_accum(blob, M, K, group, xq, sc, accum, rows)
+
+
+def rmsnorm_quant_i8(x, w, eps):
+    return default().rmsnorm_quant_i8(x, w, eps)
+
+
+def glu_quant_i8(g, u, kind):
+    return default().glu_quant_i8(g, u, kind)

@@ -26,6 +26,14 @@
  *        group the integer dot of codes with the int8 activations, corrected
  *        by suma to sum (code-1)*xq, scaled by d, summed over groups and
  *        multiplied by act_scale.
+ *  [GA]  qxmx qxmx_gpu.cpp page, tmatvec_accum and the accum argument of
+ *        gemv_dpas8: the projection plus a residual vector.
+ *  [PQ]  qxmx qxmx_gpu.cpp page, gpu_rmsnorm_quant, gpu_swiglu_quant,
+ *        gpu_silu_mul_quant, gpu_sigmoid_mul_quant: the quantiser [AQ]
+ *        applied to a vector formed in binary32 first: x * inv * w with
+ *        inv = 1 / sqrt(mean(x^2) + eps) (the sum of squares in binary64),
+ *        or silu(g) * u = (g / (1 + exp(-g))) * u, or u * sigmoid(g) =
+ *        u * (1 / (1 + exp(-g))).
  *
  * Readings where the pages are silent (each listed in the design notes):
  *  - binary16 is decoded per IEEE 754 (subnormal = m * 2^-24); the page's
@@ -34,6 +42,12 @@
  *  - a block is the 2-byte little-endian d followed by the code bytes.
  *  - the quantiser acts on the given f32 vector (no fused norm).
  *  - the Q2 reference result is built from sc*xq, the quantised activations.
+ *  - the binary32 exponential of the activation producers is the correctly
+ *    rounded one, exp evaluated in binary64 and rounded once (the page calls
+ *    its runtime's single-precision exp; the pages do not fix its accuracy).
+ *  - the norm's epsilon is an argument (its value is not on the pages); the
+ *    binary64 sum of squares runs left to right, sqrt and the divisions are
+ *    IEEE (correctly rounded) binary32 operations.
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared qoracle.c -lm
  */
@@ -204,4 +218,60 @@ void qo_q2_gemv(const uint8_t *blob, int64_t M, int64_t K, int group,
         y[j] = (double)sc * acc;
         if (mass) mass[j] = fabs((double)sc) * am;
     }
+}
+
+/* ---- Q2 GEMV plus residual  [GA] ---------------------------------------- */
+/* y[j] = (qo_q2_gemv result for row rows[j]) + accum[rows[j]], fp64.
+ * mass as qo_q2_gemv (the residual adds no product terms).              */
+void qo_q2_gemv_accum(const uint8_t *blob, int64_t M, int64_t K, int group,
+                      const int8_t *xq, float sc, const float *accum,
+                      const int64_t *rows, int64_t nrows, double *y,
+                      double *mass)
+{
+    int64_t n = rows ? nrows : M;
+    qo_q2_gemv(blob, M, K, group, xq, sc, rows, nrows, y, mass);
+    for (int64_t j = 0; j < n; j++) {
+        int64_t o = rows ? rows[j] : j;
+        y[j] += (double)accum[o];
+    }
+}
+
+/* ---- fused activation producers  [PQ] ----------------------------------- */
+/* RMSNorm then [AQ]: v_i = (x_i * inv) * w_i in binary32, then quantised.
+ * v (K floats, required) receives the normalised vector.                 */
+void qo_rmsnorm_quant_i8(const float *x, const float *w, int64_t K, float eps,
+                         float *v, int8_t *xq, float *act_scale, int32_t *suma)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < K; i++) ss += (double)x[i] * (double)x[i];
+    float ms = (float)(ss / (double)K);
+    float inv = 1.0f / sqrtf(ms + eps);
+    for (int64_t i = 0; i < K; i++) {
+        float xi = x[i] * inv;
+        v[i] = xi * w[i];
+    }
+    qo_act_quant_i8(v, K, xq, act_scale, suma);
+}
+
+/* binary32 exp, correctly rounded: binary64 exp rounded once.            */
+static float exp_f32(float a) { return (float)exp((double)a); }
+
+/* Gated product then [AQ]: kind 0 = silu(g) * u = (g / (1 + e)) * u,
+ * kind 1 = u * sigmoid(g) = u * (1 / (1 + e)), with e = exp(-g), every
+ * step in binary32.  t (K floats, required) receives the product.         */
+void qo_glu_quant_i8(const float *g, const float *u, int64_t K, int kind,
+                     float *t, int8_t *xq, float *act_scale, int32_t *suma)
+{
+    for (int64_t i = 0; i < K; i++) {
+        float e = exp_f32(-g[i]);
+        float den = 1.0f + e;
+        if (kind == 0) {
+            float silu = g[i] / den;
+            t[i] = silu * u[i];
+        } else {
+            float sig = 1.0f / den;
+            t[i] = u[i] * sig;
+        }
+    }
+    qo_act_quant_i8(t, K, xq, act_scale, suma);
 }

@@ -291,4 +291,138 @@ def pin_q2_pow2(orc):
         assert np.array_equal(y, y0 * 2.0 ** k)
 
 
+# ---- Q2 GEMV plus residual ------------------------------------------------
+def pin_q2_accum_hand(orc):
+    """The hand block with y = 126 (codes 2, d = 1, tie activation) plus a residual."""
+    tie = _golden("act_quant_tie.json")
+    case = [c for c in _golden("q2_blocks_hand.json")["cases"] if "dot" in c][0]
+    blob = _hand_block(case)
+    x = np.zeros(64, np.float32)
+    x[: len(tie["x_head"])] = tie["x_head"]
+    xq, sc, _ = orc.act_quant_i8(x)
+    for a, want in [(0.5, 126.5), (-126.0, 0.0), (0.0, 126.0), (-1000.25, -874.25)]:
+        y, _ = orc.q2_gemv_accum(blob, 1, 64, 64, xq, sc, np.array([a], np.float32))
+        assert y[0] == want, (a, y)
+
+
+def pin_q2_accum_zero_projection(orc):
+    """All codes 1: the projection is exactly 0, so the result is the residual itself."""
+    rng = np.random.Generator(np.random.PCG64(22))
+    M, K = 7, 256
+    codes = np.ones((M, K), np.uint8)
+    d_bits = np.abs(rng.normal(0, 0.02, size=(M, K // 128))).astype(np.float16).view(np.uint16)
+    blob = encode_q2(codes, d_bits, 128)
+    xq, sc, _ = orc.act_quant_i8(rng.standard_normal(K).astype(np.float32))
+    acc = rng.standard_normal(M).astype(np.float32)
+    y, _ = orc.q2_gemv_accum(blob, M, K, 128, xq, sc, acc)
+    assert np.array_equal(y, acc.astype(np.float64))
+
+
+def pin_q2_accum_rows_subset(orc):
+    """A row subset returns exactly those rows of the full result, residual included."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    M, K = 9, 192
+    _, _, blob = _q2_case(rng, M, K, 64)
+    xq, sc, _ = orc.act_quant_i8(rng.standard_normal(K).astype(np.float32))
+    acc = (rng.standard_normal(M) * 100).astype(np.float32)
+    y, m = orc.q2_gemv_accum(blob, M, K, 64, xq, sc, acc)
+    rows = [8, 2, 5]
+    ys, ms = orc.q2_gemv_accum(blob, M, K, 64, xq, sc, acc, rows=rows)
+    assert np.array_equal(ys, y[rows]) and np.array_equal(ms, m[rows])
+    y0, m0 = orc.q2_gemv(blob, M, K, 64, xq, sc)
+    assert np.array_equal(m, m0)
+
+
+# ---- RMSNorm + quantiser ----------------------------------------------------
+def pin_rmsnorm_unit_vector(orc):
+    """x = 1 everywhere and eps = 0: mean(x^2) = 1 exactly, inv = 1, so the
+    normalised vector is w itself and the outputs are the quantiser's on w."""
+    rng = np.random.Generator(np.random.PCG64(24))
+    for K in (64, 128, 5120):
+        w = rng.standard_normal(K).astype(np.float32)
+        v, xq, sc, suma = orc.rmsnorm_quant_i8(np.ones(K, np.float32), w, 0.0)
+        xq0, sc0, s0 = orc.act_quant_i8(w)
+        assert np.array_equal(v, w) and np.array_equal(xq, xq0) and sc == sc0 and np.array_equal(suma, s0)
+
+
+def pin_rmsnorm_eps(orc):
+    """x = 1, eps = 3: mean + eps = 4, sqrt = 2, inv = 1/2 exactly, so v = w/2:
+    the same codes as the quantiser on w and half its scale."""
+    rng = np.random.Generator(np.random.PCG64(25))
+    K = 256
+    w = rng.standard_normal(K).astype(np.float32)
+    v, xq, sc, suma = orc.rmsnorm_quant_i8(np.ones(K, np.float32), w, 3.0)
+    xq0, sc0, s0 = orc.act_quant_i8(w)
+    assert np.array_equal(v, w * np.float32(0.5))
+    assert np.array_equal(xq, xq0) and sc == sc0 * np.float32(0.5) and np.array_equal(suma, s0)
+
+
+def pin_rmsnorm_two_level(orc):
+    """x alternating 1, 7 with w = 1 and eps = 0: mean(x^2) = 25, inv = f32(1/5);
+    the 7s carry the maximum (code 127) and the 1s get round(127/7) = 18."""
+    K = 128
+    x = np.tile(np.array([1.0, 7.0], np.float32), K // 2)
+    v, xq, sc, suma = orc.rmsnorm_quant_i8(x, np.ones(K, np.float32), 0.0)
+    inv = np.float32(1.0) / np.float32(5.0)
+    assert v[0] == inv and v[1] == np.float32(np.float32(7.0) * inv)
+    assert np.array_equal(xq, np.tile(np.array([18, 127], np.int8), K // 2))
+    assert list(suma) == [32 * (18 + 127)] * (K // 64)
+
+
+def pin_rmsnorm_pow2(orc):
+    """With eps = 0 the norm is invariant under x -> 2^k x (every step exact)."""
+    rng = np.random.Generator(np.random.PCG64(26))
+    K = 1024
+    x = rng.standard_normal(K).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    ref = orc.rmsnorm_quant_i8(x, w, 0.0)
+    for k in (-9, -1, 2, 13):
+        got = orc.rmsnorm_quant_i8((x * np.float32(2.0 ** k)).astype(np.float32), w, 0.0)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+        assert got[2] == ref[2] and np.array_equal(got[3], ref[3])
+
+
+# ---- gated product + quantiser ----------------------------------------------
+def pin_glu_saturated_gate(orc):
+    """g = 100: exp(-100) is far below half an ulp of 1, so 1 + e = 1 and
+    silu(g) = g, sigmoid(g) = 1 exactly: t = 100 u and t = u."""
+    rng = np.random.Generator(np.random.PCG64(27))
+    K = 320
+    u = rng.standard_normal(K).astype(np.float32)
+    g = np.full(K, 100.0, np.float32)
+    t, xq, sc, suma = orc.glu_quant_i8(g, u, 0)
+    ref = (np.float32(100.0) * u).astype(np.float32)
+    xq0, sc0, s0 = orc.act_quant_i8(ref)
+    assert np.array_equal(t, ref) and np.array_equal(xq, xq0) and sc == sc0 and np.array_equal(suma, s0)
+    t, xq, sc, suma = orc.glu_quant_i8(g, u, 1)
+    xq0, sc0, s0 = orc.act_quant_i8(u)
+    assert np.array_equal(t, u) and np.array_equal(xq, xq0) and sc == sc0 and np.array_equal(suma, s0)
+
+
+def pin_glu_zero_gate(orc):
+    """g = 0: exp(0) = 1, so silu(0) = 0 and sigmoid(0) = 1/2 exactly."""
+    rng = np.random.Generator(np.random.PCG64(28))
+    K = 192
+    u = rng.standard_normal(K).astype(np.float32)
+    g = np.zeros(K, np.float32)
+    t, xq, sc, suma = orc.glu_quant_i8(g, u, 0)
+    assert np.all(t == 0.0) and np.all(xq == 0) and sc == 0.0 and np.all(suma == 0)
+    t, xq, sc, suma = orc.glu_quant_i8(g, u, 1)
+    xq0, sc0, s0 = orc.act_quant_i8(u)
+    assert np.array_equal(t, u * np.float32(0.5))
+    assert np.array_equal(xq, xq0) and sc == sc0 * np.float32(0.5) and np.array_equal(suma, s0)
+
+
+def pin_glu_identities(orc):
+    """sigmoid(g) + sigmoid(-g) = 1 and silu(g) - silu(-g) = g, to a few binary32 ulps."""
+    g = np.linspace(-12.0, 12.0, 256).astype(np.float32)
+    one = np.ones_like(g)
+    sp = orc.glu_quant_i8(g, one, 1)[0].astype(np.float64)
+    sn = orc.glu_quant_i8(-g, one, 1)[0].astype(np.float64)
+    assert np.all(np.abs(sp + sn - 1.0) <= 2.0 ** -22)
+    lp = orc.glu_quant_i8(g, one, 0)[0].astype(np.float64)
+    ln = orc.glu_quant_i8(-g, one, 0)[0].astype(np.float64)
+    assert np.all(np.abs((lp - ln) - g.astype(np.float64)) <= 2.0 ** -20 * (1.0 + np.abs(g)))
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -41,6 +41,19 @@ MUTANTS = {
     "q2 gemv group index": ("const uint8_t *blk = q2_blk(blob, K, group, o, (u * 64) / group);",
                             "const uint8_t *blk = q2_blk(blob, K, group, o, u % (K / group));"),
     "q2 gemv act scale dropped": ("y[j] = (double)sc * acc;", "y[j] = acc;"),
+    "accum dropped": ("y[j] += (double)accum[o];", "y[j] += 0.0;"),
+    "accum sign": ("y[j] += (double)accum[o];", "y[j] -= (double)accum[o];"),
+    "accum row index": ("y[j] += (double)accum[o];", "y[j] += (double)accum[j];"),
+    "rms mean divisor": ("float ms = (float)(ss / (double)K);", "float ms = (float)(ss / (double)(K - 1));"),
+    "rms eps dropped": ("float inv = 1.0f / sqrtf(ms + eps);", "float inv = 1.0f / sqrtf(ms);"),
+    "rms sqrt dropped": ("float inv = 1.0f / sqrtf(ms + eps);", "float inv = 1.0f / (ms + eps);"),
+    "rms weight dropped": ("v[i] = xi * w[i];", "v[i] = xi;"),
+    "rms weight index": ("v[i] = xi * w[i];", "v[i] = xi * w[0];"),
+    "glu exp sign": ("float e = exp_f32(-g[i]);", "float e = exp_f32(g[i]);"),
+    "glu denominator": ("float den = 1.0f + e;", "float den = 1.0f - e;"),
+    "glu silu as sigmoid": ("float silu = g[i] / den;", "float silu = 1.0f / den;"),
+    "glu sigmoid as silu": ("float sig = 1.0f / den;", "float sig = g[i] / den;"),
+    "glu up index": ("t[i] = silu * u[i];", "t[i] = silu * u[0];"),
 }
 
 
