@@ -30,6 +30,10 @@
  *        activation quantisation with per-64 group sums).
  *  [GV]  qxmx qxmx_gpu.cpp page: gemv_dpas8 (int8-activation Q2 GEMV,
  *        split-K partials, the suma correction) and gemv_reduce.
+ *  [GD]  qxmx qxmx_gpu.cpp page: gemv_dpas8_dual (the FFN gate and up
+ *        matrices against one shared quantized activation, bit-exact to two
+ *        separate GEMVs) and tmatvec_accum (the residual add folded into the
+ *        GEMV epilogue, bit-exact to the GEMV followed by the add).
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -185,6 +189,38 @@ qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq,
                         const int32_t *suma, const float *act_scale,
                         float *y, int32_t *dots, void *ws, size_t ws_bytes,
                         int split_k, void *stream);
+
+/* Device: qgemv_q2 with a residual added in the epilogue   [GD]
+ *   y[o] = fl(fl(act_scale * acc[o]) + accum[o])
+ * two binary32 roundings in that order (never one fused multiply-add), so
+ * y equals qgemv_q2 with the same split_k followed by a separate f32 add of
+ * accum, bit for bit.
+ *   accum:     device, f32[M]; may be y itself (in-place residual update),
+ *              otherwise must not overlap y.
+ * Other arguments, workspace and errors as qgemv_q2; QG_EINVAL also for a
+ * null or partly overlapping accum.                                       */
+qg_status qgemv_q2_accum(const qg_q2_weight *w, const int8_t *xq,
+                         const int32_t *suma, const float *act_scale,
+                         const float *accum, float *y, void *ws,
+                         size_t ws_bytes, int split_k, void *stream);
+
+/* Bytes of workspace qgemv_q2_dual needs: twice qgemv_q2_ws_bytes.       */
+size_t qgemv_q2_dual_ws_bytes(int64_t M, int64_t K, int group, int split_k);
+
+/* Device: two Q2 GEMVs of one shape against one quantized activation, in
+ * one launch (plus one reduce launch when split)   [GD]
+ *   w0, w1:    host structs of two weights with equal M, K and group (the
+ *              FFN gate and up projections).
+ *   y0, y1:    device, f32[M] each, written; must not overlap.
+ *   ws:        >= qgemv_q2_dual_ws_bytes(M, K, group, split_k) bytes.
+ * y0 and y1 equal qgemv_q2 on w0 and on w1 with the same split_k (auto
+ * picks the split qgemv_q2 picks for one matrix), bit for bit.
+ * QG_EINVAL: as qgemv_q2, or the weights differ in shape, or the outputs
+ * overlap.                                                                */
+qg_status qgemv_q2_dual(const qg_q2_weight *w0, const qg_q2_weight *w1,
+                        const int8_t *xq, const int32_t *suma,
+                        const float *act_scale, float *y0, float *y1,
+                        void *ws, size_t ws_bytes, int split_k, void *stream);
 
 /* ======================================================================
  * Batched prefill q8_row GEMM  [Q8, q8_matmat / q8_mul_mm]

@@ -40,7 +40,7 @@ def test_library_exports(name):
 
 def test_abi_and_status_strings():
     L = qg.lib()
-    assert L.qg_abi_version() == 1
+    assert L.qg_abi_version() == 2
     assert L.qg_status_string(0) == b"QG_OK"
     assert L.qg_status_string(1) == b"QG_EINVAL"
     assert L.qg_status_string(2) == b"QG_ELAUNCH"
@@ -149,6 +149,30 @@ def test_einval_paths():
     _einval(L.qgemv_q2(ctypes.byref(w), a16, a16, a16, a16, a16, 100, 4, None))       # too small
     _einval(L.qgemv_q2(ctypes.byref(w), P(0x10004), a16, a16, a16, None, 0, 1, None))  # xq misaligned
     _einval(L.qgemv_q2_dots(ctypes.byref(w), a16, a16, a16, a16, None, None, 0, 1, None))
+    # residual epilogue: null accum, accum partly overlapping y
+    _einval(L.qgemv_q2_accum(ctypes.byref(w), a16, a16, a16, None, a16, None, 0, 1, None))
+    _einval(L.qgemv_q2_accum(ctypes.byref(w), a16, a16, a16, P(0x10010), a16, None, 0, 1, None))
+    for b in bad:
+        _einval(L.qgemv_q2_accum(ctypes.byref(b), a16, a16, a16, P(0x40000), a16, None, 0, 1, None))
+    # two matrices in one launch: shape mismatch, overlapping or null outputs,
+    # no second weight, short workspace (twice the one-matrix size)
+    w1 = qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 64, 0)
+    for other in (qg.qg_q2_weight(0x30000, 0x40000, 64, 256, 64, 0),
+                  qg.qg_q2_weight(0x30000, 0x40000, 128, 512, 64, 0),
+                  qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 128, 0)):
+        _einval(L.qgemv_q2_dual(ctypes.byref(w), ctypes.byref(other), a16, a16, a16, a16, P(0x50000),
+                                None, 0, 1, None))
+    for b in bad:
+        _einval(L.qgemv_q2_dual(ctypes.byref(w), ctypes.byref(b), a16, a16, a16, a16, P(0x50000),
+                                None, 0, 1, None))
+    _einval(L.qgemv_q2_dual(ctypes.byref(w), None, a16, a16, a16, a16, P(0x50000), None, 0, 1, None))
+    _einval(L.qgemv_q2_dual(ctypes.byref(w), ctypes.byref(w1), a16, a16, a16, a16, P(0x10100),
+                            None, 0, 1, None))
+    _einval(L.qgemv_q2_dual(ctypes.byref(w), ctypes.byref(w1), a16, a16, a16, a16, None, None, 0, 1, None))
+    one = L.qgemv_q2_ws_bytes(128, 256, 64, 4)
+    assert L.qgemv_q2_dual_ws_bytes(128, 256, 64, 4) == 2 * one > 0
+    _einval(L.qgemv_q2_dual(ctypes.byref(w), ctypes.byref(w1), a16, a16, a16, a16, P(0x50000),
+                            a16, one, 4, None))
     # host repacks
     z = np.zeros(64, np.uint8)
     _einval(L.qg_repack_q8row(None, 4, 4, z.ctypes.data, 64))

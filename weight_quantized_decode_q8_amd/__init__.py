@@ -56,6 +56,10 @@ _SIGS = {
     "qgemv_q2_auto_split": (_I, [_I64, _I64, _I]),
     "qgemv_q2": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qgemv_q2_dots": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P, _SZ, _I, _P]),
+    "qgemv_q2_accum": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P, _SZ, _I, _P]),
+    "qgemv_q2_dual_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
+    "qgemv_q2_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P,
+                           _SZ, _I, _P]),
     "qgemm_q8row_batched_ws_bytes": (_SZ, [_I64, _I64]),
     "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
 }
@@ -250,6 +254,32 @@ def qgemv_q2_dots(w: Q2Weight, xq, suma, act_scale, y, dots, ws=None, split_k=0,
         ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(y, torch.float32, "y"),
         _dev(dots, torch.int32, "dots"), wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
+
+
+def qgemv_q2_accum(w: Q2Weight, xq, suma, act_scale, accum, y, ws=None, split_k=0, stream=None):
+    """y = (act_scale * sum_u d * dot_u) + accum, two f32 roundings; accum may be y itself."""
+    import torch
+    d = w.desc()
+    wsp = _dev(ws, torch.uint8, "ws")
+    _check("qgemv_q2_accum", lib().qgemv_q2_accum(
+        ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(accum, torch.float32, "accum"),
+        _dev(y, torch.float32, "y"), wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
+
+
+def qgemv_q2_dual_ws_bytes(M, K, group, split_k=0) -> int:
+    return lib().qgemv_q2_dual_ws_bytes(M, K, group, split_k)
+
+
+def qgemv_q2_dual(w0: Q2Weight, w1: Q2Weight, xq, suma, act_scale, y0, y1, ws=None, split_k=0, stream=None):
+    """Two Q2 GEMVs of one shape (gate, up) against one quantized activation, one launch."""
+    import torch
+    d0, d1 = w0.desc(), w1.desc()
+    wsp = _dev(ws, torch.uint8, "ws")
+    _check("qgemv_q2_dual", lib().qgemv_q2_dual(
+        ctypes.byref(d0), ctypes.byref(d1), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(y0, torch.float32, "y0"), _dev(y1, torch.float32, "y1"),
+        wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
 
 
 # ------------------------------------------------------ batched q8_row GEMM --

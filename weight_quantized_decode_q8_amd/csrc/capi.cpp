@@ -57,7 +57,7 @@ const char *qg_status_string(qg_status s) {
 
 const char *qg_last_error(void) { return qg::g_msg; }
 
-int qg_abi_version(void) { return 1; }
+int qg_abi_version(void) { return 2; }
 
 qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
                       int64_t K, void *stream) {
@@ -93,35 +93,88 @@ size_t qgemv_q2_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
   return (size_t)S * (size_t)qg::round_up(M, 64) * sizeof(float);
 }
 
-static qg_status q2_common(const char *fn, const qg_q2_weight *w, const int8_t *xq, const int32_t *suma,
-                           const float *act_scale, float *y, int32_t *dots, void *ws, size_t ws_bytes,
-                           int split_k, void *stream) {
+static bool overlap(const float *a, const float *b, int64_t n) { return a < b + n && b < a + n; }
+
+static qg_status q2_common(const char *fn, const qg_q2_weight *w, const qg_q2_weight *w1, const int8_t *xq,
+                           const int32_t *suma, const float *act_scale, const float *accum, float *y,
+                           float *y1, int32_t *dots, void *ws, size_t ws_bytes, int split_k, void *stream) {
   qg_status st = qg::check_q2_weight(w, fn);
   if (st != QG_OK) return st;
+  if (w1) {
+    st = qg::check_q2_weight(w1, fn);
+    if (st != QG_OK) return st;
+    if (w1->M != w->M || w1->K != w->K || w1->group != w->group)
+      return fail(QG_EINVAL, "%s: the two weights differ in shape (%lldx%lld g%d vs %lldx%lld g%d)", fn,
+                  (long long)w->M, (long long)w->K, w->group, (long long)w1->M, (long long)w1->K, w1->group);
+    if (!y1) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (!aligned(y1, 4)) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+    if (overlap(y, y1, w->M)) return fail(QG_EINVAL, "%s: the two outputs overlap", fn);
+  }
   if (!xq || !suma || !act_scale || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (!aligned(xq, 16)) return fail(QG_EINVAL, "%s: xq not 16-byte aligned", fn);
-  if (!aligned(suma, 4) || !aligned(act_scale, 4) || !aligned(y, 4) || (dots && !aligned(dots, 4)))
+  if (!aligned(suma, 4) || !aligned(act_scale, 4) || !aligned(y, 4) || (dots && !aligned(dots, 4)) ||
+      (accum && !aligned(accum, 4)))
     return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  if (accum && accum != y && overlap(accum, y, w->M))
+    return fail(QG_EINVAL, "%s: accum must be y itself or not overlap it", fn);
   if (split_k < 0 || split_k > qg::kMaxSplit) return fail(QG_EINVAL, "%s: split_k=%d outside 0..16", fn, split_k);
   const int S = split_k == 0 ? qg::q2_auto_split(w->M, w->K, w->group) : split_k;
-  const size_t need = qgemv_q2_ws_bytes(w->M, w->K, w->group, S);
+  const size_t need = (w1 ? 2 : 1) * qgemv_q2_ws_bytes(w->M, w->K, w->group, S);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed for split %d", fn, ws ? ws_bytes : (size_t)0, need, S);
   if (need > 0 && !aligned(ws, 4)) return fail(QG_EINVAL, "%s: workspace not 4-byte aligned", fn);
-  return qg::launched(qg::launch_q2_gemv(w->codes, w->scales, (int)w->M, (int)w->K, w->group, xq, suma, act_scale,
-                                         y, dots, static_cast<float *>(ws), S, (hipStream_t)stream),
-                      fn);
+  qg::Q2Call call{};
+  call.codes[0] = w->codes;
+  call.scales[0] = w->scales;
+  call.y[0] = y;
+  if (w1) {
+    call.codes[1] = w1->codes;
+    call.scales[1] = w1->scales;
+    call.y[1] = y1;
+  }
+  call.M = (int)w->M;
+  call.K = (int)w->K;
+  call.group = w->group;
+  call.xq = xq;
+  call.suma = suma;
+  call.act_scale = act_scale;
+  call.accum = accum;
+  call.dots = dots;
+  call.partials = static_cast<float *>(ws);
+  call.split = S;
+  return qg::launched(qg::launch_q2_gemv(call, (hipStream_t)stream), fn);
 }
 
 qg_status qgemv_q2(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
                    float *y, void *ws, size_t ws_bytes, int split_k, void *stream) {
-  return q2_common("qgemv_q2", w, xq, suma, act_scale, y, nullptr, ws, ws_bytes, split_k, stream);
+  return q2_common("qgemv_q2", w, nullptr, xq, suma, act_scale, nullptr, y, nullptr, nullptr, ws, ws_bytes,
+                   split_k, stream);
 }
 
 qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
                         float *y, int32_t *dots, void *ws, size_t ws_bytes, int split_k, void *stream) {
   if (!dots) return fail(QG_EINVAL, "qgemv_q2_dots: null dots");
-  return q2_common("qgemv_q2_dots", w, xq, suma, act_scale, y, dots, ws, ws_bytes, split_k, stream);
+  return q2_common("qgemv_q2_dots", w, nullptr, xq, suma, act_scale, nullptr, y, nullptr, dots, ws, ws_bytes,
+                   split_k, stream);
+}
+
+qg_status qgemv_q2_accum(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
+                         const float *accum, float *y, void *ws, size_t ws_bytes, int split_k, void *stream) {
+  if (!accum) return fail(QG_EINVAL, "qgemv_q2_accum: null accum");
+  return q2_common("qgemv_q2_accum", w, nullptr, xq, suma, act_scale, accum, y, nullptr, nullptr, ws, ws_bytes,
+                   split_k, stream);
+}
+
+size_t qgemv_q2_dual_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
+  return 2 * qgemv_q2_ws_bytes(M, K, group, split_k);
+}
+
+qg_status qgemv_q2_dual(const qg_q2_weight *w0, const qg_q2_weight *w1, const int8_t *xq, const int32_t *suma,
+                        const float *act_scale, float *y0, float *y1, void *ws, size_t ws_bytes, int split_k,
+                        void *stream) {
+  if (!w1) return fail(QG_EINVAL, "qgemv_q2_dual: null weight descriptor");
+  return q2_common("qgemv_q2_dual", w0, w1, xq, suma, act_scale, nullptr, y0, y1, nullptr, ws, ws_bytes, split_k,
+                   stream);
 }
 
 size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K) {

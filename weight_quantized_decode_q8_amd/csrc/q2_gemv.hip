@@ -24,6 +24,16 @@
 //    large matrices whose row tiles cannot fill 256 CUs, over blockIdx.y
 //    splits whose f32 partials [split][Mp] are summed in fixed order by a
 //    second kernel.
+//
+// Two extensions from the same page: the FFN gate and up matrices, which
+// share one quantized activation, in one launch (gemv_dpas8_dual: the row
+// tiles of the second matrix follow those of the first in the grid), and a
+// residual added in the epilogue (the accum argument of gemv_dpas8):
+// y = (acc * act_scale) + accum as two f32 roundings, the order of an
+// unfused GEMV followed by a separate residual add.  Either result equals
+// the unfused calls bit for bit when the split is the same, which the
+// launchers guarantee: waves per tile and the automatic split depend only on
+// one matrix's shape.
 #include "qg_internal.h"
 
 namespace qg {
@@ -65,19 +75,40 @@ __device__ inline float half_bits_to_f32(unsigned short h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// grid = (row tiles, splits); block = kWaves wavefronts sharing one tile.
+// One matrix of a launch: its planes, where its result goes (y when S = 1,
+// else the partials [S][Mp]) and the optional residual (S = 1 only; with
+// splits the reduce kernel adds it).
+struct Q2Job {
+  const i32x4 *codes;
+  const unsigned short *scales;
+  float *out;
+  const float *accum;
+};
+
+// f32 multiply and add, each rounded once (never contracted to an FMA).
+__device__ inline float scale_add(float acc, float sc, const float *accum, int o) {
+  const float y = __fmul_rn(acc, sc);
+  return accum ? __fadd_rn(y, accum[o]) : y;
+}
+
+// grid = (row tiles of job 0 + row tiles of job 1, splits); block = kWaves
+// wavefronts sharing one tile.  A one-matrix launch passes the same job
+// twice with tiles0 = all tiles.
 // UPG = units (of 64 weights) per scale group: 1 for g64, 2 for g128.
 // GPB = groups handled per unrolled step (GPB*UPG code loads in flight).
 template <int UPG, int GPB, bool kDots, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(
-    const i32x4 *__restrict__ codes, const unsigned short *__restrict__ scales,
-    const int8_t *__restrict__ xq, const int *__restrict__ suma,
-    const float *__restrict__ act_scale, float *__restrict__ out, int *__restrict__ dots, int M,
-    int Mp, int K, int S) {
+    Q2Job job0, Q2Job job1, int tiles0, const int8_t *__restrict__ xq, const int *__restrict__ suma,
+    const float *__restrict__ act_scale, int *__restrict__ dots, int M, int Mp, int K, int S) {
   __shared__ float red[kWaves - 1][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = blockIdx.x;
+  const bool second = (int)blockIdx.x >= tiles0;
+  const Q2Job job = second ? job1 : job0;
+  const i32x4 *__restrict__ codes = job.codes;
+  const unsigned short *__restrict__ scales = job.scales;
+  float *__restrict__ out = job.out;
+  const int tile = second ? blockIdx.x - tiles0 : blockIdx.x;
   const int split = blockIdx.y;
   const int nunits = K / 64;
   const int ngroups = nunits / UPG;
@@ -138,56 +169,59 @@ __global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(
 #pragma unroll
     for (int w = 0; w < kWaves - 1; w++) acc += red[w][lane];
     if (S == 1) {
-      if (o < M) out[o] = acc * act_scale[0];
+      if (o < M) out[o] = scale_add(acc, act_scale[0], job.accum, o);
     } else {
       out[(size_t)split * Mp + o] = acc;
     }
   }
 }
 
-// y[o] = act_scale * sum_s part[s][o], the splits added in fixed order
-// (gemv_reduce on the qxmx page).
+// y[o] = act_scale * sum_s part[s][o] (+ accum[o]), the splits added in
+// fixed order (gemv_reduce on the qxmx page).  blockIdx.y picks the matrix
+// of a two-matrix launch, whose partials follow the first's.
 __global__ __launch_bounds__(256) void q2_splitk_reduce_kernel(const float *__restrict__ part, int S,
                                                                int Mp, int M,
                                                                const float *__restrict__ act_scale,
-                                                               float *__restrict__ y) {
+                                                               float *y0, float *y1, const float *accum) {
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= M) return;
+  const float *p = part + (size_t)blockIdx.y * S * Mp;
+  float *y = blockIdx.y ? y1 : y0;
   float s = 0.0f;
-  for (int k = 0; k < S; k++) s += part[(size_t)k * Mp + o];
-  y[o] = s * act_scale[0];
+  for (int k = 0; k < S; k++) s += p[(size_t)k * Mp + o];
+  y[o] = scale_add(s, act_scale[0], accum, o);
 }
 
-template <int UPG, int GPB, int W>
-hipError_t launch_main(const i32x4 *c, const unsigned short *s, int M, int K, const int8_t *xq,
-                       const int32_t *suma, const float *act_scale, float *out, int32_t *dots,
-                       int S, hipStream_t stream) {
-  const int tiles = (M + 63) / 64;
-  const dim3 grid(tiles, S);
-  if (dots)
-    q2_gemv_t64_kernel<UPG, GPB, true, W><<<grid, 64 * W, 0, stream>>>(
-        c, s, xq, suma, act_scale, out, dots, M, tiles * 64, K, S);
-  else
-    q2_gemv_t64_kernel<UPG, GPB, false, W><<<grid, 64 * W, 0, stream>>>(
-        c, s, xq, suma, act_scale, out, nullptr, M, tiles * 64, K, S);
-  return hipGetLastError();
-}
-
-// Waves per tile: 8 when the row tiles alone fill the CUs, else 16 so that
-// each of the fewer workgroups keeps more loads in flight.
+// Waves per tile: 8 when one matrix's row tiles alone fill the CUs, else 16
+// so that each of the fewer workgroups keeps more loads in flight.
 template <int UPG, int GPB>
-hipError_t launch_typed(const void *codes, const void *scales, int M, int K, const int8_t *xq,
-                        const int32_t *suma, const float *act_scale, float *y, int32_t *dots,
-                        float *partials, int S, hipStream_t stream) {
+hipError_t launch_typed(const Q2Call &call, hipStream_t stream) {
+  const int M = call.M, K = call.K, S = call.split;
   const int tiles = (M + 63) / 64;
   const int Mp = tiles * 64;
-  float *out = S == 1 ? y : partials;
-  const i32x4 *c = reinterpret_cast<const i32x4 *>(codes);
-  const unsigned short *s = reinterpret_cast<const unsigned short *>(scales);
-  hipError_t e = tiles >= 256 ? launch_main<UPG, GPB, 8>(c, s, M, K, xq, suma, act_scale, out, dots, S, stream)
-                              : launch_main<UPG, GPB, 16>(c, s, M, K, xq, suma, act_scale, out, dots, S, stream);
+  const int njobs = call.codes[1] ? 2 : 1;
+  Q2Job j[2];
+  for (int n = 0; n < 2; n++) {
+    const int m = n < njobs ? n : 0;
+    j[n].codes = reinterpret_cast<const i32x4 *>(call.codes[m]);
+    j[n].scales = reinterpret_cast<const unsigned short *>(call.scales[m]);
+    j[n].out = S == 1 ? call.y[m] : call.partials + (size_t)m * S * Mp;
+    j[n].accum = S == 1 ? call.accum : nullptr;
+  }
+  const dim3 grid(tiles * njobs, S);
+#define QG_LAUNCH(W, D)                                                                                   \
+  q2_gemv_t64_kernel<UPG, GPB, D, W><<<grid, 64 * W, 0, stream>>>(j[0], j[1], tiles, call.xq, call.suma, \
+                                                                   call.act_scale, call.dots, M, Mp, K, S)
+  if (tiles >= 256) {
+    if (call.dots) QG_LAUNCH(8, true); else QG_LAUNCH(8, false);
+  } else {
+    if (call.dots) QG_LAUNCH(16, true); else QG_LAUNCH(16, false);
+  }
+#undef QG_LAUNCH
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  q2_splitk_reduce_kernel<<<(M + 255) / 256, 256, 0, stream>>>(partials, S, Mp, M, act_scale, y);
+  q2_splitk_reduce_kernel<<<dim3((M + 255) / 256, njobs), 256, 0, stream>>>(
+      call.partials, S, Mp, M, call.act_scale, call.y[0], call.y[1], call.accum);
   return hipGetLastError();
 }
 
@@ -207,15 +241,9 @@ int q2_auto_split(int64_t M, int64_t K, int group) {
   return S;
 }
 
-hipError_t launch_q2_gemv(const void *codes, const void *scales, int M, int K, int group,
-                          const int8_t *xq, const int32_t *suma, const float *act_scale,
-                          float *y, int32_t *dots, float *partials, int split,
-                          hipStream_t stream) {
-  if (group == 64)
-    return launch_typed<1, 4>(codes, scales, M, K, xq, suma, act_scale, y, dots, partials, split,
-                              stream);
-  return launch_typed<2, 2>(codes, scales, M, K, xq, suma, act_scale, y, dots, partials, split,
-                            stream);
+hipError_t launch_q2_gemv(const Q2Call &call, hipStream_t stream) {
+  if (call.group == 64) return launch_typed<1, 4>(call, stream);
+  return launch_typed<2, 2>(call, stream);
 }
 
 }  // namespace qg

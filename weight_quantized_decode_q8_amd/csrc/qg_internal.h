@@ -29,10 +29,25 @@ hipError_t launch_act_quant(const float *x, int K, int8_t *xq, float *act_scale,
 hipError_t launch_q8row_gemv(const void *qpacked, const float *rs, const float *xs,
                              float *y, int M, int K, hipStream_t stream);
 
-hipError_t launch_q2_gemv(const void *codes, const void *scales, int M, int K, int group,
-                          const int8_t *xq, const int32_t *suma, const float *act_scale,
-                          float *y, int32_t *dots, float *partials, int split,
-                          hipStream_t stream);
+// One Q2 GEMV launch over one matrix, or two of one shape sharing the
+// activation (codes[1] non-null).  y[m] receive the results; with split > 1
+// the partials hold [njobs][split][round_up(M, 64)] floats.  accum (one
+// matrix only) is added to the result; dots (one matrix only, test export)
+// receives [M][K/64] int32.
+struct Q2Call {
+  const void *codes[2];
+  const void *scales[2];
+  float *y[2];
+  int M, K, group;
+  const int8_t *xq;
+  const int32_t *suma;
+  const float *act_scale;
+  const float *accum;
+  int32_t *dots;
+  float *partials;
+  int split;
+};
+hipError_t launch_q2_gemv(const Q2Call &call, hipStream_t stream);
 
 int q2_auto_split(int64_t M, int64_t K, int group);
 
