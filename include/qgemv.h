@@ -30,6 +30,10 @@
  *        activation quantisation with per-64 group sums).
  *  [GV]  qxmx qxmx_gpu.cpp page: gemv_dpas8 (int8-activation Q2 GEMV,
  *        split-K partials, the suma correction) and gemv_reduce.
+ *  [PQ]  qxmx qxmx_gpu.cpp page: gpu_rmsnorm_quant, gpu_swiglu_quant,
+ *        gpu_silu_mul_quant, gpu_sigmoid_mul_quant (the activation-side
+ *        producers that form and quantise the next GEMV's input in one
+ *        kernel).
  *  [GD]  qxmx qxmx_gpu.cpp page: gemv_dpas8_dual (the FFN gate and up
  *        matrices against one shared quantized activation, bit-exact to two
  *        separate GEMVs) and tmatvec_accum (the residual add folded into the
@@ -157,6 +161,42 @@ qg_status qg_unpack_q2(const void *codes, size_t codes_bytes,
  * QG_EINVAL: null pointer, K < 64, K % 64 != 0, K > 1 << 24.             */
 qg_status qquant_act_i8(const float *x, int64_t K, int8_t *xq,
                         float *act_scale, int32_t *suma, void *stream);
+
+/* Device: RMSNorm, then the quantiser of qquant_act_i8, in one launch
+ *   [PQ, gpu_rmsnorm_quant]
+ *   x, w:      device, f32[K] each (the vector and the norm weights),
+ *              16-byte aligned, finite.
+ *   eps:       the norm's epsilon, finite and >= 0 (with eps = 0 an all-zero
+ *              x has no defined result).
+ *   Quantised vector v_i = (x_i * inv) * w_i with inv = 1 / sqrt(ms + eps),
+ *   ms = binary32(sum_i x_i^2 / K) (the squares summed in binary64), every
+ *   other step one correctly rounded binary32 operation; xq, act_scale and
+ *   suma are then exactly what qquant_act_i8 writes for v.
+ * QG_EINVAL: null pointer, K < 64, K % 64 != 0, K > 1 << 24, misaligned
+ * input, eps negative or not finite.                                       */
+qg_status qquant_rmsnorm_i8(const float *x, const float *w, int64_t K,
+                            float eps, int8_t *xq, float *act_scale,
+                            int32_t *suma, void *stream);
+
+/* Gate functions of qquant_glu_i8. */
+enum { QG_GLU_SILU = 0, QG_GLU_SIGMOID = 1 };
+
+/* Device: gated product, then the quantiser of qquant_act_i8, in one launch
+ *   [PQ, gpu_swiglu_quant / gpu_silu_mul_quant (SILU),
+ *    gpu_sigmoid_mul_quant (SIGMOID)]
+ *   g, u:      device, f32[K] each (gate and value), 16-byte aligned.
+ *   kind:      QG_GLU_SILU:    t_i = (g_i / (1 + exp(-g_i))) * u_i
+ *              QG_GLU_SIGMOID: t_i = u_i * (1 / (1 + exp(-g_i)))
+ *              every step one binary32 operation; exp is the correctly
+ *              rounded binary32 exponential.
+ *   t:         device, f32[K] receiving the product, or NULL; may be g or u
+ *              itself (in place), otherwise must not overlap them.
+ *   xq, act_scale, suma: exactly what qquant_act_i8 writes for t.
+ * QG_EINVAL: as qquant_rmsnorm_i8, or a bad kind, or t partly overlapping
+ * g or u.                                                                  */
+qg_status qquant_glu_i8(const float *g, const float *u, int64_t K, int kind,
+                        float *t, int8_t *xq, float *act_scale,
+                        int32_t *suma, void *stream);
 
 /* Bytes of split-K workspace qgemv_q2 needs for this shape and split
  * (split_k 0 = the library's choice).                                    */

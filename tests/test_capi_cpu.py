@@ -132,6 +132,22 @@ def test_einval_paths():
     _einval(L.qquant_act_i8(a16, 0, a16, a16, a16, None))
     _einval(L.qquant_act_i8(None, 64, a16, a16, a16, None))
     _einval(L.qquant_act_i8(P(0x10008), 64, a16, a16, a16, None))
+    # fused producers
+    F = ctypes.c_float
+    _einval(L.qquant_rmsnorm_i8(None, a16, 64, F(1e-6), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8(a16, a16, 100, F(1e-6), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8(a16, P(0x10008), 64, F(1e-6), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8(a16, a16, 64, F(-1.0), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8(a16, a16, 64, F(float("nan")), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8(a16, a16, 64, F(float("inf")), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8(a16, a16, 64, F(1e-6), None, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, a16, 64, 2, None, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, a16, 64, -1, None, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, None, 64, 0, None, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, a16, 32, 0, None, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(P(0x10004), a16, 64, 1, None, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(P(0x20000), P(0x30000), 64, 0, P(0x20010), a16, a16, a16, None))  # t inside g
+    _einval(L.qquant_glu_i8(P(0x20000), P(0x30000), 64, 0, P(0x2FFF0), a16, a16, a16, None))  # t over u
     # Q2 GEMV
     w = qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 64, 0)
     bad = [qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 96, 0),

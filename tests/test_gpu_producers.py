@@ -1,0 +1,131 @@
+"""The fused activation producers through the C-ABI (qquant_rmsnorm_i8,
+qquant_glu_i8) against the oracle.
+
+Everything they write is decided in binary32 on both sides, so the check is
+bit-exact: the gated product t, the int8 codes, act_scale and the group sums.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import gpu_available
+from test_gpu_parity import dev, host, qg
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a HIP device")]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _outs(K):
+    torch = _torch()
+    return (torch.empty(K, dtype=torch.int8, device="cuda"),
+            torch.empty(1, dtype=torch.float32, device="cuda"),
+            torch.empty(K // 64, dtype=torch.int32, device="cuda"))
+
+
+def gpu_rmsnorm(x, w, eps):
+    xq, sc, suma = _outs(x.size)
+    qg().qquant_rmsnorm_i8(dev(x), dev(w), eps, xq, sc, suma)
+    return host(xq), host(sc)[0], host(suma)
+
+
+def gpu_glu(g, u, kind, t_mode="separate"):
+    """t_mode: 'separate' (own buffer), 'none', 'in_u' or 'in_g' (in place)."""
+    torch = _torch()
+    K = g.size
+    xq, sc, suma = _outs(K)
+    gd, ud = dev(g), dev(u)
+    t = {"separate": torch.empty(K, dtype=torch.float32, device="cuda"), "none": None,
+         "in_u": ud, "in_g": gd}[t_mode]
+    qg().qquant_glu_i8(gd, ud, kind, t, xq, sc, suma)
+    return (None if t is None else host(t)), host(xq), host(sc)[0], host(suma)
+
+
+def same_bits(a, b):
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
+def assert_quant_equal(got, ref, what):
+    xq, sc, suma = got
+    rxq, rsc, rsuma = ref
+    assert np.array_equal(xq, rxq), f"{what}: {int((xq != rxq).sum())} codes differ"
+    assert same_bits(sc, rsc), f"{what}: act_scale {sc!r} vs {rsc!r}"
+    assert np.array_equal(suma, rsuma), f"{what}: suma differs"
+
+
+# ----------------------------------------------------------------- RMSNorm --
+@pytest.mark.parametrize("K,scale,eps,seed", [(64, 1.0, 1e-6, 1), (192, 1e-3, 1e-5, 2), (4096, 1.0, 1e-6, 3),
+                                              (5120, 1.0, 1e-6, 4), (5120, 40.0, 0.0, 5), (17408, 1.0, 1e-5, 6),
+                                              (65536, 0.25, 1e-6, 7)])
+def test_rmsnorm_quant_bit_exact(K, scale, eps, seed):
+    rng = synth.rng_for(4000 + seed)
+    x = (rng.standard_normal(K) * scale).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    _, rxq, rsc, rsuma = oracle.rmsnorm_quant_i8(x, w, eps)
+    assert_quant_equal(gpu_rmsnorm(x, w, eps), (rxq, rsc, rsuma), f"rmsnorm K={K}")
+
+
+def test_rmsnorm_closed_forms():
+    rng = synth.rng_for(4010)
+    K = 1024
+    w = rng.standard_normal(K).astype(np.float32)
+    ref = oracle.act_quant_i8(w)
+    # unit x, eps 0: the quantiser of w itself
+    assert_quant_equal(gpu_rmsnorm(np.ones(K, np.float32), w, 0.0), ref, "unit x")
+    # unit x, eps 3: inv = 1/2 exactly, same codes, half the scale
+    xq, sc, suma = gpu_rmsnorm(np.ones(K, np.float32), w, 3.0)
+    assert np.array_equal(xq, ref[0]) and sc == ref[1] * np.float32(0.5) and np.array_equal(suma, ref[2])
+    # two-level x (1, 7): codes 18 and 127
+    x = np.tile(np.array([1.0, 7.0], np.float32), K // 2)
+    xq, _, _ = gpu_rmsnorm(x, np.ones(K, np.float32), 0.0)
+    assert np.array_equal(xq, np.tile(np.array([18, 127], np.int8), K // 2))
+
+
+def test_rmsnorm_zero_vector_with_eps():
+    xq, sc, suma = gpu_rmsnorm(np.zeros(256, np.float32), np.ones(256, np.float32), 1e-6)
+    assert sc == 0.0 and np.all(xq == 0) and np.all(suma == 0)
+
+
+# ----------------------------------------------------------- gated product --
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("K,seed", [(64, 1), (320, 2), (5120, 3), (17408, 4), (65536, 5)])
+def test_glu_quant_bit_exact(kind, K, seed):
+    rng = synth.rng_for(4100 + seed)
+    g = (rng.standard_normal(K) * 2.5).astype(np.float32)
+    u = rng.standard_normal(K).astype(np.float32)
+    rt, rxq, rsc, rsuma = oracle.glu_quant_i8(g, u, kind)
+    t, xq, sc, suma = gpu_glu(g, u, kind)
+    assert same_bits(t, rt), f"t: {int((t.view(np.uint32) != rt.view(np.uint32)).sum())} differ"
+    assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu kind={kind} K={K}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_glu_extreme_gates(kind):
+    """Gates where exp(-g) underflows to a subnormal or 0, overflows to inf, is 1."""
+    K = 256
+    rng = synth.rng_for(4120 + kind)
+    g = rng.choice(np.array([0.0, -0.0, 100.0, -100.0, 87.5, -87.5, 88.8, -88.8, 103.9, -104.0, 150.0,
+                             -150.0, 1e-7, -1e-7, 20.0, -20.0], np.float32), size=K).astype(np.float32)
+    u = rng.standard_normal(K).astype(np.float32)
+    rt, rxq, rsc, rsuma = oracle.glu_quant_i8(g, u, kind)
+    t, xq, sc, suma = gpu_glu(g, u, kind)
+    assert same_bits(t, rt)
+    assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu extremes kind={kind}")
+
+
+@pytest.mark.parametrize("mode", ["none", "in_u", "in_g"])
+def test_glu_output_modes(mode):
+    rng = synth.rng_for(4130)
+    K = 4096
+    g = (rng.standard_normal(K) * 2.0).astype(np.float32)
+    u = rng.standard_normal(K).astype(np.float32)
+    rt, rxq, rsc, rsuma = oracle.glu_quant_i8(g, u, 0)
+    t, xq, sc, suma = gpu_glu(g, u, 0, mode)
+    if t is not None:
+        assert same_bits(t, rt)
+    assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu t={mode}")

@@ -52,6 +52,8 @@ _SIGS = {
     "qg_repack_q2": (_I, [_P, _SZ, _I64, _I64, _I, _P, _SZ, _P, _SZ]),
     "qg_unpack_q2": (_I, [_P, _SZ, _P, _SZ, _I64, _I64, _I, _P, _SZ]),
     "qquant_act_i8": (_I, [_P, _I64, _P, _P, _P, _P]),
+    "qquant_rmsnorm_i8": (_I, [_P, _P, _I64, ctypes.c_float, _P, _P, _P, _P]),
+    "qquant_glu_i8": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _P]),
     "qgemv_q2_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
     "qgemv_q2_auto_split": (_I, [_I64, _I64, _I]),
     "qgemv_q2": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _SZ, _I, _P]),
@@ -201,6 +203,27 @@ def qquant_act_i8(x, xq, act_scale, suma, stream=None):
     import torch
     _check("qquant_act_i8", lib().qquant_act_i8(
         _dev(x, torch.float32, "x"), x.numel(), _dev(xq, torch.int8, "xq"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
+
+
+QG_GLU_SILU, QG_GLU_SIGMOID = 0, 1
+
+
+def qquant_rmsnorm_i8(x, w, eps, xq, act_scale, suma, stream=None):
+    """RMSNorm of x with weights w, then the int8 quantiser (one launch)."""
+    import torch
+    _check("qquant_rmsnorm_i8", lib().qquant_rmsnorm_i8(
+        _dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), x.numel(), float(eps),
+        _dev(xq, torch.int8, "xq"), _dev(act_scale, torch.float32, "act_scale"),
+        _dev(suma, torch.int32, "suma"), _stream(stream)))
+
+
+def qquant_glu_i8(g, u, kind, t, xq, act_scale, suma, stream=None):
+    """t = silu(g) * u (kind 0) or u * sigmoid(g) (kind 1), then the int8 quantiser; t may be None."""
+    import torch
+    _check("qquant_glu_i8", lib().qquant_glu_i8(
+        _dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), g.numel(), int(kind),
+        _dev(t, torch.float32, "t"), _dev(xq, torch.int8, "xq"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
 
 

@@ -81,6 +81,40 @@ qg_status qquant_act_i8(const float *x, int64_t K, int8_t *xq, float *act_scale,
   return qg::launched(qg::launch_act_quant(x, (int)K, xq, act_scale, suma, (hipStream_t)stream), fn);
 }
 
+static qg_status check_quant_outputs(const char *fn, int64_t K, const int8_t *xq, const float *act_scale,
+                                     const int32_t *suma) {
+  if (!xq || !act_scale || !suma) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (K < 64 || K % 64 != 0 || K > (1 << 24)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
+  if (!aligned(xq, 4) || !aligned(act_scale, 4) || !aligned(suma, 4)) return fail(QG_EINVAL, "%s: misaligned output", fn);
+  return QG_OK;
+}
+
+qg_status qquant_rmsnorm_i8(const float *x, const float *w, int64_t K, float eps, int8_t *xq, float *act_scale,
+                            int32_t *suma, void *stream) {
+  const char *fn = "qquant_rmsnorm_i8";
+  qg_status st = check_quant_outputs(fn, K, xq, act_scale, suma);
+  if (st != QG_OK) return st;
+  if (!x || !w) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(w, 16)) return fail(QG_EINVAL, "%s: x and w must be 16-byte aligned", fn);
+  if (!(eps >= 0.0f) || eps > 3.4e38f) return fail(QG_EINVAL, "%s: eps must be finite and >= 0", fn);
+  return qg::launched(qg::launch_rmsnorm_quant(x, w, (int)K, eps, xq, act_scale, suma, (hipStream_t)stream), fn);
+}
+
+qg_status qquant_glu_i8(const float *g, const float *u, int64_t K, int kind, float *t, int8_t *xq,
+                        float *act_scale, int32_t *suma, void *stream) {
+  const char *fn = "qquant_glu_i8";
+  qg_status st = check_quant_outputs(fn, K, xq, act_scale, suma);
+  if (st != QG_OK) return st;
+  if (!g || !u) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
+  if (!aligned(g, 16) || !aligned(u, 16) || (t && !aligned(t, 16)))
+    return fail(QG_EINVAL, "%s: g, u and t must be 16-byte aligned", fn);
+  auto part_overlap = [K](const float *a, const float *b) { return a != b && a < b + K && b < a + K; };
+  if (t && (part_overlap(t, g) || part_overlap(t, u)))
+    return fail(QG_EINVAL, "%s: t must be g, u or a separate buffer", fn);
+  return qg::launched(qg::launch_glu_quant(g, u, (int)K, kind, t, xq, act_scale, suma, (hipStream_t)stream), fn);
+}
+
 int qgemv_q2_auto_split(int64_t M, int64_t K, int group) {
   if (M < 1 || (group != 64 && group != 128) || K < group || K % group) return 1;
   return qg::q2_auto_split(M, K, group);

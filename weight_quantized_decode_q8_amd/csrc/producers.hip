@@ -1,0 +1,130 @@
+// producers.hip -- fused activation producers: the vector the next Q2 GEMV
+// consumes is formed and quantised in one launch.
+//
+// What is computed (qxmx qxmx_gpu.cpp page, gpu_rmsnorm_quant,
+// gpu_swiglu_quant, gpu_silu_mul_quant, gpu_sigmoid_mul_quant), every
+// element step one IEEE binary32 operation, correctly rounded:
+//   rmsnorm:  ms  = f32(sum_i x_i^2 / K), the sum of the (exact) binary64
+//                   squares in binary64;
+//             inv = 1 / sqrt(ms + eps);   v_i = (x_i * inv) * w_i
+//   silu:     e = exp(-g_i);  t_i = (g_i / (1 + e)) * u_i
+//   sigmoid:  e = exp(-g_i);  t_i = u_i * (1 / (1 + e))
+// then the int8 rule of quant_rule.h on v or t.  exp is the correctly
+// rounded binary32 exponential, evaluated in binary64 and rounded once (the
+// page calls its runtime's single-precision exp, whose accuracy the pages do
+// not fix; a correctly rounded one makes the result independent of the
+// math library).  The binary64 sum of squares is reduced as a tree, whose
+// rounding to binary32 equals a left-to-right sum's unless the two binary64
+// sums fall on opposite sides of a binary32 rounding boundary.
+//
+// One workgroup of 1024 threads per vector, as the quantiser: the passes
+// re-read x, w or g, u from L2 (a few tens of KiB) instead of holding them,
+// so any K the quantiser takes works.
+#include "qg_internal.h"
+#include "quant_rule.h"
+
+namespace qg {
+namespace {
+
+__device__ inline float4 mul4(float4 a, float4 b) {
+  return make_float4(__fmul_rn(a.x, b.x), __fmul_rn(a.y, b.y), __fmul_rn(a.z, b.z), __fmul_rn(a.w, b.w));
+}
+
+__device__ inline float4 scale4(float4 a, float s) {
+  return make_float4(__fmul_rn(a.x, s), __fmul_rn(a.y, s), __fmul_rn(a.z, s), __fmul_rn(a.w, s));
+}
+
+// Correctly rounded binary32 square root: the binary64 root (correctly
+// rounded) rounded once more to binary32, which for sqrt gives the correctly
+// rounded binary32 result (53 >= 2 * 24 + 2).  The single-precision
+// hardware root is not correctly rounded.
+__device__ inline float sqrt_rn(float a) { return (float)sqrt((double)a); }
+
+__global__ __launch_bounds__(kQuantThreads) void rmsnorm_quant_kernel(
+    const float4 *__restrict__ x4, const float4 *__restrict__ w4, int n4, float eps,
+    int *__restrict__ xq4, float *__restrict__ act_scale, int *__restrict__ suma) {
+  __shared__ double red_ss[kQuantThreads / 64];
+  __shared__ float red_max[kQuantThreads / 64];
+  const int tid = threadIdx.x;
+
+  double ss = 0.0;
+  for (int i = tid; i < n4; i += kQuantThreads) {
+    const float4 v = x4[i];
+    ss += ((double)v.x * (double)v.x + (double)v.y * (double)v.y) +
+          ((double)v.z * (double)v.z + (double)v.w * (double)v.w);
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63) == 0) red_ss[tid >> 6] = ss;
+  __syncthreads();
+  ss = 0.0;
+#pragma unroll
+  for (int w = 0; w < kQuantThreads / 64; w++) ss += red_ss[w];
+  const float ms = (float)(ss / (double)(4 * n4));
+  const float inv = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
+
+  float m = 0.0f;
+  for (int i = tid; i < n4; i += kQuantThreads) m = fmaxf(m, abs_max4(mul4(scale4(x4[i], inv), w4[i])));
+  const float qinv = scale_and_inverse(block_max(m, red_max), act_scale);
+  for (int i = tid; i < n4; i += kQuantThreads) quant_quad(i, mul4(scale4(x4[i], inv), w4[i]), qinv, xq4, suma);
+}
+
+// exp(-g) rounded once to binary32.
+__device__ inline float exp_neg(float g) { return (float)exp(-(double)g); }
+
+template <int KIND>
+__device__ inline float glu1(float g, float u) {
+  const float den = __fadd_rn(1.0f, exp_neg(g));
+  if (KIND == 0) return __fmul_rn(__fdiv_rn(g, den), u);
+  return __fmul_rn(u, __fdiv_rn(1.0f, den));
+}
+
+template <int KIND>
+__device__ inline float4 glu4(float4 g, float4 u) {
+  return make_float4(glu1<KIND>(g.x, u.x), glu1<KIND>(g.y, u.y), glu1<KIND>(g.z, u.z), glu1<KIND>(g.w, u.w));
+}
+
+// t4 may be null (nothing stored, the quantising pass recomputes t), or may
+// be g4 or u4 itself: every quad is read and then written by one thread, and
+// the quantising pass reads the stored t back.
+template <int KIND>
+__global__ __launch_bounds__(kQuantThreads) void glu_quant_kernel(
+    const float4 *g4, const float4 *u4, float4 *t4, int n4, int *__restrict__ xq4,
+    float *__restrict__ act_scale, int *__restrict__ suma) {
+  __shared__ float red_max[kQuantThreads / 64];
+  const int tid = threadIdx.x;
+  float m = 0.0f;
+  for (int i = tid; i < n4; i += kQuantThreads) {
+    const float4 t = glu4<KIND>(g4[i], u4[i]);
+    if (t4) t4[i] = t;
+    m = fmaxf(m, abs_max4(t));
+  }
+  const float qinv = scale_and_inverse(block_max(m, red_max), act_scale);
+  for (int i = tid; i < n4; i += kQuantThreads)
+    quant_quad(i, t4 ? t4[i] : glu4<KIND>(g4[i], u4[i]), qinv, xq4, suma);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_quant(const float *x, const float *w, int K, float eps, int8_t *xq,
+                                float *act_scale, int32_t *suma, hipStream_t stream) {
+  rmsnorm_quant_kernel<<<1, kQuantThreads, 0, stream>>>(
+      reinterpret_cast<const float4 *>(x), reinterpret_cast<const float4 *>(w), K / 4, eps,
+      reinterpret_cast<int *>(xq), act_scale, reinterpret_cast<int *>(suma));
+  return hipGetLastError();
+}
+
+hipError_t launch_glu_quant(const float *g, const float *u, int K, int kind, float *t, int8_t *xq,
+                            float *act_scale, int32_t *suma, hipStream_t stream) {
+  const float4 *g4 = reinterpret_cast<const float4 *>(g);
+  const float4 *u4 = reinterpret_cast<const float4 *>(u);
+  float4 *t4 = reinterpret_cast<float4 *>(t);
+  int *q4 = reinterpret_cast<int *>(xq);
+  int *s = reinterpret_cast<int *>(suma);
+  if (kind == 0)
+    glu_quant_kernel<0><<<1, kQuantThreads, 0, stream>>>(g4, u4, t4, K / 4, q4, act_scale, s);
+  else
+    glu_quant_kernel<1><<<1, kQuantThreads, 0, stream>>>(g4, u4, t4, K / 4, q4, act_scale, s);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -26,6 +26,13 @@ qg_status fail(qg_status s, const char *fmt, ...);
 hipError_t launch_act_quant(const float *x, int K, int8_t *xq, float *act_scale,
                             int32_t *suma, hipStream_t stream);
 
+// Fused producers: RMSNorm (x, w, eps) or a gated product (kind 0 silu(g)*u,
+// kind 1 u*sigmoid(g); t optional) followed by the quantiser.
+hipError_t launch_rmsnorm_quant(const float *x, const float *w, int K, float eps, int8_t *xq,
+                                float *act_scale, int32_t *suma, hipStream_t stream);
+hipError_t launch_glu_quant(const float *g, const float *u, int K, int kind, float *t, int8_t *xq,
+                            float *act_scale, int32_t *suma, hipStream_t stream);
+
 hipError_t launch_q8row_gemv(const void *qpacked, const float *rs, const float *xs,
                              float *y, int M, int K, hipStream_t stream);
 
