@@ -16,7 +16,10 @@ Also reported: per-kernel times and roofline fractions, the dominant
 kernel's roofline (HIP events on the launch stream), the CPU oracle timed
 on this host over the same step (cpu_baseline), and the second half of the
 metric, the batched prefill q8_row GEMM (nb=512 x 17408 x 5120, int8 MFMA
-with exact activation limbs), in algorithmic TFLOP/s (`prefill_gemm`).
+with exact activation limbs), in algorithmic TFLOP/s (`prefill_gemm`), and
+the FFN block in its fused form (RMSNorm+quant, gate|up in one launch,
+SiLU-gate+quant, down with the residual in its epilogue) next to the
+unfused launches (`fused_ffn`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -255,6 +258,58 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
                 "avg_launch_us": round(dom_us, 2), "algorithmic_bytes_per_launch": lm_bytes}
 
+    # ---------------- fused FFN block: the same three matrices with the fused
+    # producers, gate and up in one launch and the residual in the down
+    # projection's epilogue (4 launches instead of the step's 5 FFN launches)
+    fused = None
+    if not args.no_breakdown:
+        rng = np.random.Generator(np.random.PCG64(20260 + 900))
+        h_d = torch.from_numpy(rng.standard_normal(Kgu, dtype=np.float32)).to(dev)
+        nw_d = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(Kgu)).astype(np.float32)).to(dev)
+        h_out = torch.empty(Kgu, dtype=torch.float32, device=dev)
+        Mgu = W["C3_gate"].M
+        ws_gu = torch.zeros(max(1, qg.qgemv_q2_dual_ws_bytes(Mgu, Kgu, 128, 0)), dtype=torch.uint8, device=dev)
+        g_buf = torch.empty(Mgu, dtype=torch.float32, device=dev)
+        u_buf = torch.empty(Mgu, dtype=torch.float32, device=dev)
+
+        def ffn_fused():
+            qg.qquant_rmsnorm_i8(h_d, nw_d, 1e-6, xq_gu, sc_gu, su_gu)
+            qg.qgemv_q2_dual(W["C3_gate"], W["C3_up"], xq_gu, su_gu, sc_gu, g_buf, u_buf, ws_gu)
+            qg.qquant_glu_i8(g_buf, u_buf, qg.QG_GLU_SILU, None, xq_dn, sc_dn, su_dn)
+            qg.qgemv_q2_accum(W["C3_down"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["C3_down"])
+
+        def step_fused():
+            ffn_fused()
+            k_lm_head()
+
+        step_fused()
+        torch.cuda.synchronize()
+        ref_h = h_out.clone()
+        g_f = capture(step_fused, 1)
+        for _ in range(3):
+            g_f.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(h_out, ref_h), "graph replay of the fused FFN differs from eager"
+        for _ in range(args.warmup):
+            g_f.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            g_f.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us_fs = a.elapsed_time(b) * 1e3 / args.steps
+        fused = {"workload": "decode step with the FFN block fused: RMSNorm+quant -> gate|up dual Q2 GEMV "
+                             "-> SiLU-gate+quant -> down Q2 GEMV + residual, then the q8_row lm_head",
+                 "us_per_step": round(us_fs, 2), "GB/s": round(step_bytes / us_fs / 1e3, 1),
+                 "frac_hbm_peak": round(step_bytes / us_fs / 1e3 / HBM_PEAK_GBS, 4),
+                 "launches": 5, "unfused_us_per_step": round(ms_per_step * 1e3, 2), "unfused_launches": 6,
+                 "step_weight_bytes": step_bytes,
+                 "note": "timed like the main step (graph replays, the lm_head evicting the last-level cache)"}
+        log(f"fused FFN: {fused}")
+
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -354,6 +409,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill_gemm": gemm,
+        "fused_ffn": fused,
     }
     print(json.dumps(out), flush=True)
 
