@@ -19,7 +19,8 @@ metric, the batched prefill q8_row GEMM (nb=512 x 17408 x 5120, int8 MFMA
 with exact activation limbs), in algorithmic TFLOP/s (`prefill_gemm`), and
 the FFN block in its fused form (RMSNorm+quant, gate|up in one launch,
 SiLU-gate+quant, down with the residual in its epilogue) next to the
-unfused launches (`fused_ffn`).
+unfused launches (`fused_ffn`), and each Q2 GEMV's streaming rate from HBM
+over rotated weight copies launched back to back (`q2_sustained`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -275,7 +276,7 @@ def main():
         def ffn_fused():
             qg.qquant_rmsnorm_i8(h_d, nw_d, 1e-6, xq_gu, sc_gu, su_gu)
             qg.qgemv_q2_dual(W["C3_gate"], W["C3_up"], xq_gu, su_gu, sc_gu, g_buf, u_buf, ws_gu)
-            qg.qquant_glu_i8(g_buf, u_buf, qg.QG_GLU_SILU, None, xq_dn, sc_dn, su_dn)
+            qg.qquant_glu_i8(g_buf, u_buf, qg.QG_GLU_SILU, g_buf, xq_dn, sc_dn, su_dn)
             qg.qgemv_q2_accum(W["C3_down"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["C3_down"])
 
         def step_fused():
@@ -309,6 +310,63 @@ def main():
                  "step_weight_bytes": step_bytes,
                  "note": "timed like the main step (graph replays, the lm_head evicting the last-level cache)"}
         log(f"fused FFN: {fused}")
+
+    # ---------------- Q2 GEMV streaming rate from HBM: copies of one matrix
+    # (>= 512 MB, twice the last-level cache) launched back to back in one
+    # graph, each launch reading weights no earlier launch left in cache
+    sustained = None
+    if not args.no_breakdown:
+        sustained = {}
+        xs_by_k = {Kgu: (xq_gu, su_gu, sc_gu), Kdn: (xq_dn, su_dn, sc_dn)}
+        c2 = synth.CONFIGS["C2"]
+        b2, x2 = synth.config_inputs("C2")
+        W2 = qg.Q2Weight.from_blocks(b2, c2["M"], c2["K"], c2["group"], dev)
+        xq2 = torch.empty(c2["K"], dtype=torch.int8, device=dev)
+        sc2 = torch.empty(1, dtype=torch.float32, device=dev)
+        su2 = torch.empty(c2["K"] // 64, dtype=torch.int32, device=dev)
+        qg.qquant_act_i8(torch.from_numpy(x2).to(dev), xq2, sc2, su2)
+        xs_by_k[c2["K"]] = (xq2, su2, sc2)
+        for label, W0, mode in [("C2 Q2 g64 4096x4096", W2, "single"),
+                                ("C2 Q2 g64 4096x4096, 16 per launch", W2, "batch"),
+                                ("C3 gate Q2 g128 17408x5120", W["C3_gate"], "single"),
+                                ("C3 gate|up dual Q2 g128 2x17408x5120", W["C3_gate"], "dual"),
+                                ("C3 gate Q2 g128 17408x5120, 16 per launch", W["C3_gate"], "batch"),
+                                ("C3 down Q2 g128 5120x17408", W["C3_down"], "single"),
+                                ("C3 down Q2 g128 5120x17408, 16 per launch", W["C3_down"], "batch")]:
+            dual = mode == "dual"
+            nb_w = W0.M * (W0.K // W0.group) * (2 + W0.group // 4)
+            ncopy = max(2, -(-(512 << 20) // nb_w))
+            ncopy += ncopy % 2
+            copies = [W0] + [qg.Q2Weight(W0.codes.clone(), W0.scales.clone(), W0.M, W0.K, W0.group)
+                             for _ in range(ncopy - 1)]
+            xq_c, su_c, sc_c = xs_by_k[W0.K]
+            outs = [torch.empty(W0.M, dtype=torch.float32, device=dev) for _ in range(ncopy)]
+            nws = (qg.qgemv_q2_dual_ws_bytes if dual else qg.qgemv_q2_ws_bytes)(W0.M, W0.K, W0.group, 0)
+            ws_c = torch.zeros(max(1, nws), dtype=torch.uint8, device=dev)
+
+            def rotate():
+                if dual:
+                    for i in range(0, ncopy, 2):
+                        qg.qgemv_q2_dual(copies[i], copies[i + 1], xq_c, su_c, sc_c, outs[i], outs[i + 1], ws_c)
+                elif mode == "batch":
+                    for i in range(0, ncopy, qg.QG_Q2_BATCH_MAX):
+                        qg.qgemv_q2_batch([(copies[k], xq_c, su_c, sc_c, outs[k])
+                                           for k in range(i, min(ncopy, i + qg.QG_Q2_BATCH_MAX))])
+                else:
+                    for i in range(ncopy):
+                        qg.qgemv_q2(copies[i], xq_c, su_c, sc_c, outs[i], ws_c)
+
+            us = kernel_us(rotate, 1) / ncopy
+            split = 1 if mode == "batch" else qg.qgemv_q2_auto_split(W0.M, W0.K, W0.group)
+            launches = {"dual": ncopy // 2, "batch": -(-ncopy // qg.QG_Q2_BATCH_MAX)}.get(mode, ncopy)
+            sustained[label] = {"us_per_matrix": round(us, 2), "GB/s": round(nb_w / us / 1e3, 1),
+                                "frac_hbm_peak": round(nb_w / us / 1e3 / HBM_PEAK_GBS, 4),
+                                "copies": ncopy, "weight_bytes": nb_w, "split_k": split,
+                                "launches": launches}
+            log(f"  sustained {label}: {sustained[label]}")
+            del copies, outs
+        del W2
+        torch.cuda.empty_cache()
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -410,6 +468,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill_gemm": gemm,
         "fused_ffn": fused,
+        "q2_sustained": sustained,
     }
     print(json.dumps(out), flush=True)
 

@@ -181,7 +181,8 @@ qg_status qquant_rmsnorm_i8(const float *x, const float *w, int64_t K,
 /* Gate functions of qquant_glu_i8. */
 enum { QG_GLU_SILU = 0, QG_GLU_SIGMOID = 1 };
 
-/* Device: gated product, then the quantiser of qquant_act_i8, in one launch
+/* Device: gated product, then the quantiser of qquant_act_i8 (two
+ * launches: the product over the whole GPU, then the quantiser)
  *   [PQ, gpu_swiglu_quant / gpu_silu_mul_quant (SILU),
  *    gpu_sigmoid_mul_quant (SIGMOID)]
  *   g, u:      device, f32[K] each (gate and value), 16-byte aligned.
@@ -189,11 +190,13 @@ enum { QG_GLU_SILU = 0, QG_GLU_SIGMOID = 1 };
  *              QG_GLU_SIGMOID: t_i = u_i * (1 / (1 + exp(-g_i)))
  *              every step one binary32 operation; exp is the correctly
  *              rounded binary32 exponential.
- *   t:         device, f32[K] receiving the product, or NULL; may be g or u
- *              itself (in place), otherwise must not overlap them.
- *   xq, act_scale, suma: exactly what qquant_act_i8 writes for t.
- * QG_EINVAL: as qquant_rmsnorm_i8, or a bad kind, or t partly overlapping
- * g or u.                                                                  */
+ *   t:         device, f32[K] receiving the product, 16-byte aligned; may
+ *              be g or u itself (in place), otherwise must not overlap them.
+ *   xq, act_scale, suma: exactly what qquant_act_i8 writes for t (suma
+ *              also serves as scratch between the two launches).
+ *   The outputs must not overlap g, u or t.
+ * QG_EINVAL: as qquant_rmsnorm_i8, or a bad kind, null t, or t partly
+ * overlapping g or u.                                                      */
 qg_status qquant_glu_i8(const float *g, const float *u, int64_t K, int kind,
                         float *t, int8_t *xq, float *act_scale,
                         int32_t *suma, void *stream);
@@ -261,6 +264,38 @@ qg_status qgemv_q2_dual(const qg_q2_weight *w0, const qg_q2_weight *w1,
                         const int8_t *xq, const int32_t *suma,
                         const float *act_scale, float *y0, float *y1,
                         void *ws, size_t ws_bytes, int split_k, void *stream);
+
+/* One GEMV of a qgemv_q2_batch launch. */
+typedef struct {
+    qg_q2_weight w;          /* the matrix (host struct of device planes)  */
+    const int8_t *xq;        /* device, int8[w.K]: its quantised input     */
+    const int32_t *suma;     /* device, int32[w.K/64]                      */
+    const float *act_scale;  /* device, f32[1]                             */
+    const float *accum;      /* device, f32[w.M] residual, or NULL; may be
+                                y itself                                   */
+    float *y;                /* device, f32[w.M], written                  */
+} qg_q2_job;
+
+/* Most GEMVs one qgemv_q2_batch call takes. */
+#define QG_Q2_BATCH_MAX 16
+
+/* Device: up to QG_Q2_BATCH_MAX independent Q2 GEMVs in one launch (each
+ * launch has a fixed cost of a few microseconds, as much as streaming tens
+ * of MB, so small GEMVs of one decode step -- several projections, or the
+ * experts of a layer -- are better issued together)   [GV, GD]
+ *   jobs:      host array of njobs descriptors; each job may have its own
+ *              shape and activation (all with the same group size) and an
+ *              optional residual, added as in qgemv_q2_accum.
+ * No K split and no workspace.  Each y equals qgemv_q2 (or qgemv_q2_accum)
+ * of that job with split_k = 1 bit for bit when the job's row tiles
+ * (ceil(M/64)) and the launch's total row tiles are on the same side of
+ * 256 (the rule that picks 8 or 16 waves per tile); otherwise only the f32
+ * summation order differs, within the same bound.
+ * QG_EINVAL: null table, njobs outside 1..QG_Q2_BATCH_MAX, a bad weight
+ * struct, mixed group sizes, a null or misaligned pointer, a residual
+ * partly overlapping its y, or an output overlapping another job's output
+ * or residual.                                                             */
+qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream);
 
 /* ======================================================================
  * Batched prefill q8_row GEMM  [Q8, q8_matmat / q8_mul_mm]

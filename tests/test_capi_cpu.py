@@ -141,11 +141,13 @@ def test_einval_paths():
     _einval(L.qquant_rmsnorm_i8(a16, a16, 64, F(float("nan")), a16, a16, a16, None))
     _einval(L.qquant_rmsnorm_i8(a16, a16, 64, F(float("inf")), a16, a16, a16, None))
     _einval(L.qquant_rmsnorm_i8(a16, a16, 64, F(1e-6), None, a16, a16, None))
-    _einval(L.qquant_glu_i8(a16, a16, 64, 2, None, a16, a16, a16, None))
-    _einval(L.qquant_glu_i8(a16, a16, 64, -1, None, a16, a16, a16, None))
-    _einval(L.qquant_glu_i8(a16, None, 64, 0, None, a16, a16, a16, None))
-    _einval(L.qquant_glu_i8(a16, a16, 32, 0, None, a16, a16, a16, None))
-    _einval(L.qquant_glu_i8(P(0x10004), a16, 64, 1, None, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, a16, 64, 2, a16, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, a16, 64, -1, a16, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, None, 64, 0, a16, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, a16, 64, 0, None, a16, a16, a16, None))     # t is required
+    _einval(L.qquant_glu_i8(a16, a16, 32, 0, a16, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(P(0x10004), a16, 64, 1, a16, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8(a16, a16, 64, 1, P(0x10008), a16, a16, a16, None))  # t misaligned
     _einval(L.qquant_glu_i8(P(0x20000), P(0x30000), 64, 0, P(0x20010), a16, a16, a16, None))  # t inside g
     _einval(L.qquant_glu_i8(P(0x20000), P(0x30000), 64, 0, P(0x2FFF0), a16, a16, a16, None))  # t over u
     # Q2 GEMV
@@ -189,6 +191,26 @@ def test_einval_paths():
     assert L.qgemv_q2_dual_ws_bytes(128, 256, 64, 4) == 2 * one > 0
     _einval(L.qgemv_q2_dual(ctypes.byref(w), ctypes.byref(w1), a16, a16, a16, a16, P(0x50000),
                             a16, one, 4, None))
+    # batched launch: table, count, group mix, pointers, overlaps
+    def job(w_, y=0x50000, accum=None, xq=0x10000):
+        return qg.qg_q2_job(w_, xq, 0x10000, 0x10000, accum, y)
+
+    def batch(*jobs):
+        arr = (qg.qg_q2_job * len(jobs))(*jobs)
+        return L.qgemv_q2_batch(arr, len(jobs), None)
+
+    w128 = qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 128, 0)
+    _einval(L.qgemv_q2_batch(None, 1, None))
+    _einval(L.qgemv_q2_batch((qg.qg_q2_job * 1)(job(w)), 0, None))
+    _einval(L.qgemv_q2_batch((qg.qg_q2_job * 17)(*[job(w, y=0x50000 + 0x1000 * i) for i in range(17)]), 17, None))
+    _einval(batch(job(w), job(w128, y=0x60000)))                      # mixed group sizes
+    for b in bad:
+        _einval(batch(job(w), job(b, y=0x60000)))
+    _einval(batch(job(w, xq=0x10004)))                                # xq misaligned
+    _einval(batch(job(w, y=0)))                                       # null y
+    _einval(batch(job(w, y=0x50000, accum=0x50010)))                  # accum partly over y
+    _einval(batch(job(w, y=0x50000), job(w1, y=0x50100)))             # outputs overlap
+    _einval(batch(job(w, y=0x50000), job(w1, y=0x60000, accum=0x50000)))  # output over a residual
     # host repacks
     z = np.zeros(64, np.uint8)
     _einval(L.qg_repack_q8row(None, 4, 4, z.ctypes.data, 64))

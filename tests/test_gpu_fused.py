@@ -1,11 +1,13 @@
-"""The FFN extensions of the Q2 GEMV, through the C-ABI: gate and up in one
-launch against a shared quantized activation (qgemv_q2_dual), and the
-residual added in the epilogue (qgemv_q2_accum).
+"""The extensions of the Q2 GEMV, through the C-ABI: gate and up in one
+launch against a shared quantized activation (qgemv_q2_dual), the residual
+added in the epilogue (qgemv_q2_accum), and up to 16 independent GEMVs in
+one launch (qgemv_q2_batch).
 
-Both must equal the unfused calls bit for bit (the qxmx page claims exactly
-that for gemv_dpas8_dual and tmatvec_accum), and both are checked against the
-fp64 oracle: |y - y_ref| <= 2e-5 * sum_i |w_i x_i| per output, plus, for the
-residual, one binary32 rounding of the final add (2^-24 |y_ref|).
+The first two must equal the unfused calls bit for bit (the qxmx page claims
+exactly that for gemv_dpas8_dual and tmatvec_accum), the batch must where it
+uses the same waves per tile; all are checked against the fp64 oracle:
+|y - y_ref| <= 2e-5 * sum_i |w_i x_i| per output, plus, for the residual, one
+binary32 rounding of the final add (2^-24 |y_ref|).
 """
 import numpy as np
 import pytest
@@ -165,3 +167,67 @@ def test_accum_zero_projection_returns_residual():
     for split in (1, 4):
         y = gpu_accum(W, xq, sc, suma, accum, split)
         assert np.array_equal(bits(y), bits(accum + np.float32(0.0)))
+
+
+# ------------------------------------------------------- batched launch --
+def _batch_case(specs, group, seed):
+    """specs: list of (M, K, with_accum).  Returns per-job host data and device jobs."""
+    m = qg()
+    torch = _torch()
+    host_jobs, dev_jobs = [], []
+    acts = {}
+    for n, (M, K, with_acc) in enumerate(specs):
+        blob, _ = synth.q2_inputs(M, K, group, seed=seed + 17 * n)
+        if K not in acts:
+            x = synth.activation(K, seed + 1000 + K)
+            acts[K] = (x, gpu_act_quant(x))
+        x, (xq_h, sc_h, _, (xq, sc, suma)) = acts[K]
+        W = m.Q2Weight.from_blocks(blob, M, K, group)
+        y = torch.empty(M, dtype=torch.float32, device="cuda")
+        accum = (synth.rng_for(seed + 31 * n).standard_normal(M) * 2).astype(np.float32) if with_acc else None
+        job = (W, xq, suma, sc, y) + ((dev(accum),) if with_acc else ())
+        dev_jobs.append(job)
+        host_jobs.append(dict(blob=blob, M=M, K=K, W=W, xq=xq, sc=sc, suma=suma, xq_h=xq_h, sc_h=sc_h,
+                              accum=accum, y=y))
+    return host_jobs, dev_jobs
+
+
+def _check_batch(specs, group, seed, exact):
+    hj, dj = _batch_case(specs, group, seed)
+    qg().qgemv_q2_batch(dj)
+    for n, j in enumerate(hj):
+        y = host(j["y"])
+        if j["accum"] is None:
+            single = gpu_single(j["W"], j["xq"], j["sc"], j["suma"], 1)
+            yref, mass = oracle.q2_gemv(j["blob"], j["M"], j["K"], group, j["xq_h"], j["sc_h"])
+        else:
+            single = gpu_accum(j["W"], j["xq"], j["sc"], j["suma"], j["accum"], 1)
+            yref, mass = oracle.q2_gemv_accum(j["blob"], j["M"], j["K"], group, j["xq_h"], j["sc_h"], j["accum"])
+            mass = mass + U32 / REL * np.abs(yref)
+        if exact:
+            assert np.array_equal(bits(y), bits(single)), f"job {n}: differs from the single call"
+        within(y, yref, mass, what=f"batch job {n} {j['M']}x{j['K']} g{group}")
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_batch_small_jobs_equal_single_calls(group):
+    # every job and the launch below 256 row tiles: 16 waves per tile everywhere
+    specs = [(64, 256, False), (130, 1024, True), (1, 128, False), (1000, 512, True), (257, 2048, False)]
+    _check_batch(specs, group, 5000 + group, exact=True)
+
+
+def test_batch_sixteen_jobs_shared_activation():
+    specs = [(100 + 37 * n, 1024, n % 3 == 0) for n in range(16)]
+    _check_batch(specs, 128, 5200, exact=sum((M + 63) // 64 for M, _, _ in specs) < 256)
+
+
+def test_batch_large_jobs_equal_single_calls():
+    # every job and the launch at 256 row tiles or more: 8 waves per tile everywhere
+    specs = [(16384, 1024, False), (17408, 640, True)]
+    _check_batch(specs, 128, 5300, exact=True)
+
+
+def test_batch_mixed_sizes_within_bound():
+    # small jobs in a launch of >= 256 tiles: only the summation order changes
+    specs = [(16384, 512, False), (200, 1024, True), (64, 2048, False)]
+    _check_batch(specs, 64, 5400, exact=False)

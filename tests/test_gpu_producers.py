@@ -35,15 +35,14 @@ def gpu_rmsnorm(x, w, eps):
 
 
 def gpu_glu(g, u, kind, t_mode="separate"):
-    """t_mode: 'separate' (own buffer), 'none', 'in_u' or 'in_g' (in place)."""
+    """t_mode: 'separate' (own buffer), 'in_u' or 'in_g' (in place)."""
     torch = _torch()
     K = g.size
     xq, sc, suma = _outs(K)
     gd, ud = dev(g), dev(u)
-    t = {"separate": torch.empty(K, dtype=torch.float32, device="cuda"), "none": None,
-         "in_u": ud, "in_g": gd}[t_mode]
+    t = {"separate": torch.empty(K, dtype=torch.float32, device="cuda"), "in_u": ud, "in_g": gd}[t_mode]
     qg().qquant_glu_i8(gd, ud, kind, t, xq, sc, suma)
-    return (None if t is None else host(t)), host(xq), host(sc)[0], host(suma)
+    return host(t), host(xq), host(sc)[0], host(suma)
 
 
 def same_bits(a, b):
@@ -118,7 +117,7 @@ def test_glu_extreme_gates(kind):
     assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu extremes kind={kind}")
 
 
-@pytest.mark.parametrize("mode", ["none", "in_u", "in_g"])
+@pytest.mark.parametrize("mode", ["in_u", "in_g"])
 def test_glu_output_modes(mode):
     rng = synth.rng_for(4130)
     K = 4096
@@ -126,6 +125,5 @@ def test_glu_output_modes(mode):
     u = rng.standard_normal(K).astype(np.float32)
     rt, rxq, rsc, rsuma = oracle.glu_quant_i8(g, u, 0)
     t, xq, sc, suma = gpu_glu(g, u, 0, mode)
-    if t is not None:
-        assert same_bits(t, rt)
+    assert same_bits(t, rt)
     assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu t={mode}")

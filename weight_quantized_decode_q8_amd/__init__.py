@@ -37,6 +37,13 @@ class qg_q2_weight(ctypes.Structure):
                 ("group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class qg_q2_job(ctypes.Structure):
+    _fields_ = [("w", qg_q2_weight), ("xq", ctypes.c_void_p), ("suma", ctypes.c_void_p),
+                ("act_scale", ctypes.c_void_p), ("accum", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+QG_Q2_BATCH_MAX = 16
+
 _P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
 _SIGS = {
     "qg_status_string": (ctypes.c_char_p, [_I]),
@@ -62,6 +69,7 @@ _SIGS = {
     "qgemv_q2_dual_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
     "qgemv_q2_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P,
                            _SZ, _I, _P]),
+    "qgemv_q2_batch": (_I, [ctypes.POINTER(qg_q2_job), _I, _P]),
     "qgemm_q8row_batched_ws_bytes": (_SZ, [_I64, _I64]),
     "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
 }
@@ -219,7 +227,7 @@ def qquant_rmsnorm_i8(x, w, eps, xq, act_scale, suma, stream=None):
 
 
 def qquant_glu_i8(g, u, kind, t, xq, act_scale, suma, stream=None):
-    """t = silu(g) * u (kind 0) or u * sigmoid(g) (kind 1), then the int8 quantiser; t may be None."""
+    """t = silu(g) * u (kind 0) or u * sigmoid(g) (kind 1), then the int8 quantiser; t may be g or u."""
     import torch
     _check("qquant_glu_i8", lib().qquant_glu_i8(
         _dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), g.numel(), int(kind),
@@ -303,6 +311,20 @@ def qgemv_q2_dual(w0: Q2Weight, w1: Q2Weight, xq, suma, act_scale, y0, y1, ws=No
         ctypes.byref(d0), ctypes.byref(d1), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(y0, torch.float32, "y0"), _dev(y1, torch.float32, "y1"),
         wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
+
+
+def qgemv_q2_batch(jobs, stream=None):
+    """Independent Q2 GEMVs in one launch.  jobs: sequence of
+    (Q2Weight, xq, suma, act_scale, y) or (Q2Weight, xq, suma, act_scale, y, accum)."""
+    import torch
+    arr = (qg_q2_job * max(1, len(jobs)))()
+    for n, job in enumerate(jobs):
+        w, xq, suma, sc, y = job[:5]
+        accum = job[5] if len(job) > 5 else None
+        arr[n] = qg_q2_job(w.desc(), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+                           _dev(sc, torch.float32, "act_scale"), _dev(accum, torch.float32, "accum"),
+                           _dev(y, torch.float32, "y"))
+    _check("qgemv_q2_batch", lib().qgemv_q2_batch(arr, len(jobs), _stream(stream)))
 
 
 # ------------------------------------------------------ batched q8_row GEMM --

@@ -105,12 +105,12 @@ qg_status qquant_glu_i8(const float *g, const float *u, int64_t K, int kind, flo
   const char *fn = "qquant_glu_i8";
   qg_status st = check_quant_outputs(fn, K, xq, act_scale, suma);
   if (st != QG_OK) return st;
-  if (!g || !u) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!g || !u || !t) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
-  if (!aligned(g, 16) || !aligned(u, 16) || (t && !aligned(t, 16)))
+  if (!aligned(g, 16) || !aligned(u, 16) || !aligned(t, 16))
     return fail(QG_EINVAL, "%s: g, u and t must be 16-byte aligned", fn);
   auto part_overlap = [K](const float *a, const float *b) { return a != b && a < b + K && b < a + K; };
-  if (t && (part_overlap(t, g) || part_overlap(t, u)))
+  if (part_overlap(t, g) || part_overlap(t, u))
     return fail(QG_EINVAL, "%s: t must be g, u or a separate buffer", fn);
   return qg::launched(qg::launch_glu_quant(g, u, (int)K, kind, t, xq, act_scale, suma, (hipStream_t)stream), fn);
 }
@@ -209,6 +209,45 @@ qg_status qgemv_q2_dual(const qg_q2_weight *w0, const qg_q2_weight *w1, const in
   if (!w1) return fail(QG_EINVAL, "qgemv_q2_dual: null weight descriptor");
   return q2_common("qgemv_q2_dual", w0, w1, xq, suma, act_scale, nullptr, y0, y1, nullptr, ws, ws_bytes, split_k,
                    stream);
+}
+
+qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream) {
+  const char *fn = "qgemv_q2_batch";
+  if (!jobs) return fail(QG_EINVAL, "%s: null job table", fn);
+  if (njobs < 1 || njobs > QG_Q2_BATCH_MAX) return fail(QG_EINVAL, "%s: njobs=%d outside 1..%d", fn, njobs, QG_Q2_BATCH_MAX);
+  qg::Q2BatchCall c[qg::kMaxQ2Jobs];
+  int64_t tiles = 0;
+  for (int n = 0; n < njobs; n++) {
+    const qg_q2_job &j = jobs[n];
+    qg_status st = qg::check_q2_weight(&j.w, fn);
+    if (st != QG_OK) return st;
+    if (j.w.group != jobs[0].w.group) return fail(QG_EINVAL, "%s: job %d has group %d, job 0 has %d", fn, n, j.w.group, jobs[0].w.group);
+    if (!j.xq || !j.suma || !j.act_scale || !j.y) return fail(QG_EINVAL, "%s: job %d: null pointer", fn, n);
+    if (!aligned(j.xq, 16)) return fail(QG_EINVAL, "%s: job %d: xq not 16-byte aligned", fn, n);
+    if (!aligned(j.suma, 4) || !aligned(j.act_scale, 4) || !aligned(j.y, 4) || (j.accum && !aligned(j.accum, 4)))
+      return fail(QG_EINVAL, "%s: job %d: misaligned pointer", fn, n);
+    if (j.accum && j.accum != j.y && overlap(j.accum, j.y, j.w.M))
+      return fail(QG_EINVAL, "%s: job %d: accum must be y itself or not overlap it", fn, n);
+    for (int m = 0; m < n; m++) {
+      const qg_q2_job &o = jobs[m];
+      const bool yy = j.y < o.y + o.w.M && o.y < j.y + j.w.M;
+      const bool ya = o.accum && j.y < o.accum + o.w.M && o.accum < j.y + j.w.M;
+      const bool ay = j.accum && o.y < j.accum + j.w.M && j.accum < o.y + o.w.M;
+      if (yy || ya || ay) return fail(QG_EINVAL, "%s: jobs %d and %d: an output overlaps the other's output or residual", fn, m, n);
+    }
+    tiles += (j.w.M + 63) / 64;
+    c[n].codes = j.w.codes;
+    c[n].scales = j.w.scales;
+    c[n].xq = j.xq;
+    c[n].suma = j.suma;
+    c[n].act_scale = j.act_scale;
+    c[n].accum = j.accum;
+    c[n].y = j.y;
+    c[n].M = (int)j.w.M;
+    c[n].K = (int)j.w.K;
+  }
+  if (tiles > (1LL << 30)) return fail(QG_EINVAL, "%s: too many row tiles", fn);
+  return qg::launched(qg::launch_q2_batch(c, njobs, jobs[0].w.group, (hipStream_t)stream), fn);
 }
 
 size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K) {

@@ -17,9 +17,12 @@
 // rounding to binary32 equals a left-to-right sum's unless the two binary64
 // sums fall on opposite sides of a binary32 rounding boundary.
 //
-// One workgroup of 1024 threads per vector, as the quantiser: the passes
-// re-read x, w or g, u from L2 (a few tens of KiB) instead of holding them,
-// so any K the quantiser takes works.
+// RMSNorm + quantiser is one workgroup of 1024 threads per vector, as the
+// quantiser: its passes re-read x and w from L2 (a few tens of KiB) instead
+// of holding them, so any K the quantiser takes works.  The gated product
+// spends about a hundred binary64 operations per element on exp, too much
+// for one CU at K = 17408, so it is two launches: the product over the
+// whole GPU (with per-workgroup maxima), then one workgroup quantising t.
 #include "qg_internal.h"
 #include "quant_rule.h"
 
@@ -83,24 +86,46 @@ __device__ inline float4 glu4(float4 g, float4 u) {
   return make_float4(glu1<KIND>(g.x, u.x), glu1<KIND>(g.y, u.y), glu1<KIND>(g.z, u.z), glu1<KIND>(g.w, u.w));
 }
 
-// t4 may be null (nothing stored, the quantising pass recomputes t), or may
-// be g4 or u4 itself: every quad is read and then written by one thread, and
-// the quantising pass reads the stored t back.
+// Gated product, step 1 of 2, over the whole GPU: quad i of t (one per
+// thread) and, per workgroup, the largest |t| of its quads, stored as float
+// bits in part[blockIdx.x] (the caller's suma buffer, which has room: at most
+// K/1024 workgroups against K/64 entries).  t may be g or u itself: every
+// quad is read and then written by one thread.
+constexpr int kGluThreads = 256;
+
 template <int KIND>
-__global__ __launch_bounds__(kQuantThreads) void glu_quant_kernel(
-    const float4 *g4, const float4 *u4, float4 *t4, int n4, int *__restrict__ xq4,
-    float *__restrict__ act_scale, int *__restrict__ suma) {
-  __shared__ float red_max[kQuantThreads / 64];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kGluThreads) void glu_kernel(const float4 *g4, const float4 *u4, float4 *t4, int n4,
+                                                          int *__restrict__ part) {
+  __shared__ float red[kGluThreads / 64];
+  const int i = blockIdx.x * kGluThreads + threadIdx.x;
   float m = 0.0f;
-  for (int i = tid; i < n4; i += kQuantThreads) {
+  if (i < n4) {
     const float4 t = glu4<KIND>(g4[i], u4[i]);
-    if (t4) t4[i] = t;
-    m = fmaxf(m, abs_max4(t));
+    t4[i] = t;
+    m = abs_max4(t);
   }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kGluThreads / 64; w++) r = fmaxf(r, red[w]);
+    part[blockIdx.x] = __float_as_int(r);
+  }
+}
+
+// Step 2 of 2, one workgroup: max|t| from the nparts partial maxima (all
+// read before any group sum overwrites them), then the quantiser over t.
+__global__ __launch_bounds__(kQuantThreads) void quant_from_parts_kernel(const float4 *__restrict__ t4, int n4,
+                                                                         int nparts, int *__restrict__ xq4,
+                                                                         float *__restrict__ act_scale,
+                                                                         int *__restrict__ suma) {
+  __shared__ float red_max[kQuantThreads / 64];
+  float m = 0.0f;
+  for (int j = threadIdx.x; j < nparts; j += kQuantThreads) m = fmaxf(m, __int_as_float(suma[j]));
   const float qinv = scale_and_inverse(block_max(m, red_max), act_scale);
-  for (int i = tid; i < n4; i += kQuantThreads)
-    quant_quad(i, t4 ? t4[i] : glu4<KIND>(g4[i], u4[i]), qinv, xq4, suma);
+  for (int i = threadIdx.x; i < n4; i += kQuantThreads) quant_quad(i, t4[i], qinv, xq4, suma);
 }
 
 }  // namespace
@@ -118,12 +143,17 @@ hipError_t launch_glu_quant(const float *g, const float *u, int K, int kind, flo
   const float4 *g4 = reinterpret_cast<const float4 *>(g);
   const float4 *u4 = reinterpret_cast<const float4 *>(u);
   float4 *t4 = reinterpret_cast<float4 *>(t);
-  int *q4 = reinterpret_cast<int *>(xq);
   int *s = reinterpret_cast<int *>(suma);
+  const int n4 = K / 4;
+  const int nparts = (n4 + kGluThreads - 1) / kGluThreads;
   if (kind == 0)
-    glu_quant_kernel<0><<<1, kQuantThreads, 0, stream>>>(g4, u4, t4, K / 4, q4, act_scale, s);
+    glu_kernel<0><<<nparts, kGluThreads, 0, stream>>>(g4, u4, t4, n4, s);
   else
-    glu_quant_kernel<1><<<1, kQuantThreads, 0, stream>>>(g4, u4, t4, K / 4, q4, act_scale, s);
+    glu_kernel<1><<<nparts, kGluThreads, 0, stream>>>(g4, u4, t4, n4, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  quant_from_parts_kernel<<<1, kQuantThreads, 0, stream>>>(t4, n4, nparts, reinterpret_cast<int *>(xq), act_scale,
+                                                           s);
   return hipGetLastError();
 }
 

@@ -25,13 +25,15 @@
 //    splits whose f32 partials [split][Mp] are summed in fixed order by a
 //    second kernel.
 //
-// Two extensions from the same page: the FFN gate and up matrices, which
-// share one quantized activation, in one launch (gemv_dpas8_dual: the row
-// tiles of the second matrix follow those of the first in the grid), and a
-// residual added in the epilogue (the accum argument of gemv_dpas8):
-// y = (acc * act_scale) + accum as two f32 roundings, the order of an
-// unfused GEMV followed by a separate residual add.  Either result equals
-// the unfused calls bit for bit when the split is the same, which the
+// Every launch runs a table of matrices (one Q2Job each), whose row tiles
+// follow one another in the grid.  That serves three extensions: the FFN
+// gate and up matrices against one shared quantized activation in one
+// launch (gemv_dpas8_dual on the same page), a residual added in the
+// epilogue (the accum argument of gemv_dpas8): y = (acc * act_scale) + accum
+// as two f32 roundings, the order of an unfused GEMV followed by a separate
+// residual add, and up to 16 independent GEMVs in one launch (launch batching
+// against the fixed cost of each launch).  The gate/up and residual forms
+// equal the unfused calls bit for bit when the split is the same, which the
 // launchers guarantee: waves per tile and the automatic split depend only on
 // one matrix's shape.
 #include "qg_internal.h"
@@ -75,15 +77,44 @@ __device__ inline float half_bits_to_f32(unsigned short h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// One matrix of a launch: its planes, where its result goes (y when S = 1,
-// else the partials [S][Mp]) and the optional residual (S = 1 only; with
-// splits the reduce kernel adds it).
+// One matrix of a launch: its planes and activation, where its result goes
+// (y when S = 1, else the partials [S][Mp]) and the optional residual (S = 1
+// only; with splits the reduce kernel adds it).
 struct Q2Job {
   const i32x4 *codes;
   const unsigned short *scales;
+  const int8_t *xq;
+  const int *suma;
+  const float *act_scale;
   float *out;
   const float *accum;
+  int M, K;
 };
+
+// The matrices of one launch, passed by value in the kernel arguments: job
+// j owns the row tiles [tile_end[j-1], tile_end[j]) of the grid.
+struct Q2Batch {
+  Q2Job job[kMaxQ2Jobs];
+  int tile_end[kMaxQ2Jobs];
+  int njobs;
+};
+
+// This workgroup's job, selected with constant indices only, so the table
+// is read from the kernel-argument segment (scalar loads, no private copy).
+__device__ inline void pick_job(const Q2Batch &b, int block, Q2Job &job, int &tile) {
+  int j = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxQ2Jobs - 1; i++) j += (i + 1 < b.njobs && block >= b.tile_end[i]) ? 1 : 0;
+  job = b.job[0];
+  int first = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxQ2Jobs; i++)
+    if (i == j) {
+      job = b.job[i];
+      first = b.tile_end[i - 1];
+    }
+  tile = block - first;
+}
 
 // f32 multiply and add, each rounded once (never contracted to an FMA).
 __device__ inline float scale_add(float acc, float sc, const float *accum, int o) {
@@ -91,24 +122,23 @@ __device__ inline float scale_add(float acc, float sc, const float *accum, int o
   return accum ? __fadd_rn(y, accum[o]) : y;
 }
 
-// grid = (row tiles of job 0 + row tiles of job 1, splits); block = kWaves
-// wavefronts sharing one tile.  A one-matrix launch passes the same job
-// twice with tiles0 = all tiles.
-// UPG = units (of 64 weights) per scale group: 1 for g64, 2 for g128.
-// GPB = groups handled per unrolled step (GPB*UPG code loads in flight).
+// grid = (row tiles of all jobs, splits); block = kWaves wavefronts sharing
+// one tile.  UPG = units (of 64 weights) per scale group: 1 for g64, 2 for
+// g128.  GPB = groups handled per unrolled step (GPB*UPG code loads in
+// flight).  dots (kDots, one-job launches only) receives [M][K/64] int32.
 template <int UPG, int GPB, bool kDots, int kWaves>
-__global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(
-    Q2Job job0, Q2Job job1, int tiles0, const int8_t *__restrict__ xq, const int *__restrict__ suma,
-    const float *__restrict__ act_scale, int *__restrict__ dots, int M, int Mp, int K, int S) {
+__global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(Q2Batch batch, int *__restrict__ dots, int S) {
   __shared__ float red[kWaves - 1][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool second = (int)blockIdx.x >= tiles0;
-  const Q2Job job = second ? job1 : job0;
+  Q2Job job;
+  int tile;
+  pick_job(batch, blockIdx.x, job, tile);
   const i32x4 *__restrict__ codes = job.codes;
   const unsigned short *__restrict__ scales = job.scales;
   float *__restrict__ out = job.out;
-  const int tile = second ? blockIdx.x - tiles0 : blockIdx.x;
+  const int M = job.M, K = job.K;
+  const int Mp = (M + 63) / 64 * 64;
   const int split = blockIdx.y;
   const int nunits = K / 64;
   const int ngroups = nunits / UPG;
@@ -123,8 +153,8 @@ __global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(
 
   const i32x4 *cp = codes + (size_t)tile * nunits * 64 + lane;
   const unsigned short *sp = scales + (size_t)tile * ngroups * 64 + lane;
-  const uniform_i32x4 *xw = (const uniform_i32x4 *)xq;
-  const uniform_i32 *sa = (const uniform_i32 *)suma;
+  const uniform_i32x4 *xw = (const uniform_i32x4 *)job.xq;
+  const uniform_i32 *sa = (const uniform_i32 *)job.suma;
   const int o = tile * 64 + lane;
 
   float acc = 0.0f;
@@ -169,7 +199,7 @@ __global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(
 #pragma unroll
     for (int w = 0; w < kWaves - 1; w++) acc += red[w][lane];
     if (S == 1) {
-      if (o < M) out[o] = scale_add(acc, act_scale[0], job.accum, o);
+      if (o < M) out[o] = scale_add(acc, job.act_scale[0], job.accum, o);
     } else {
       out[(size_t)split * Mp + o] = acc;
     }
@@ -177,73 +207,112 @@ __global__ __launch_bounds__(64 * kWaves) void q2_gemv_t64_kernel(
 }
 
 // y[o] = act_scale * sum_s part[s][o] (+ accum[o]), the splits added in
-// fixed order (gemv_reduce on the qxmx page).  blockIdx.y picks the matrix
-// of a two-matrix launch, whose partials follow the first's.
-__global__ __launch_bounds__(256) void q2_splitk_reduce_kernel(const float *__restrict__ part, int S,
-                                                               int Mp, int M,
-                                                               const float *__restrict__ act_scale,
-                                                               float *y0, float *y1, const float *accum) {
+// fixed order (gemv_reduce on the qxmx page).  blockIdx.y picks job 0 or 1
+// (one matrix, or the gate/up pair); job j's partials are job.out[s*Mp+o].
+__global__ __launch_bounds__(256) void q2_splitk_reduce_kernel(Q2Batch batch, float *y0, float *y1,
+                                                               const float *accum, int S) {
+  const bool second = blockIdx.y != 0;
+  const Q2Job job = second ? batch.job[1] : batch.job[0];
+  const int M = job.M, Mp = (M + 63) / 64 * 64;
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= M) return;
-  const float *p = part + (size_t)blockIdx.y * S * Mp;
-  float *y = blockIdx.y ? y1 : y0;
+  float *y = second ? y1 : y0;
   float s = 0.0f;
-  for (int k = 0; k < S; k++) s += p[(size_t)k * Mp + o];
-  y[o] = scale_add(s, act_scale[0], accum, o);
+  for (int k = 0; k < S; k++) s += job.out[(size_t)k * Mp + o];
+  y[o] = scale_add(s, job.act_scale[0], accum, o);
 }
 
-// Waves per tile: 8 when one matrix's row tiles alone fill the CUs, else 16
-// so that each of the fewer workgroups keeps more loads in flight.
 template <int UPG, int GPB>
-hipError_t launch_typed(const Q2Call &call, hipStream_t stream) {
-  const int M = call.M, K = call.K, S = call.split;
-  const int tiles = (M + 63) / 64;
-  const int Mp = tiles * 64;
-  const int njobs = call.codes[1] ? 2 : 1;
-  Q2Job j[2];
-  for (int n = 0; n < 2; n++) {
-    const int m = n < njobs ? n : 0;
-    j[n].codes = reinterpret_cast<const i32x4 *>(call.codes[m]);
-    j[n].scales = reinterpret_cast<const unsigned short *>(call.scales[m]);
-    j[n].out = S == 1 ? call.y[m] : call.partials + (size_t)m * S * Mp;
-    j[n].accum = S == 1 ? call.accum : nullptr;
-  }
-  const dim3 grid(tiles * njobs, S);
-#define QG_LAUNCH(W, D)                                                                                   \
-  q2_gemv_t64_kernel<UPG, GPB, D, W><<<grid, 64 * W, 0, stream>>>(j[0], j[1], tiles, call.xq, call.suma, \
-                                                                   call.act_scale, call.dots, M, Mp, K, S)
-  if (tiles >= 256) {
-    if (call.dots) QG_LAUNCH(8, true); else QG_LAUNCH(8, false);
+hipError_t launch_typed(const Q2Batch &b, int waves, int S, int *dots, float *y0, float *y1, const float *accum,
+                        hipStream_t stream) {
+  const dim3 grid(b.tile_end[b.njobs - 1], S);
+#define QG_LAUNCH(W, D) q2_gemv_t64_kernel<UPG, GPB, D, W><<<grid, 64 * W, 0, stream>>>(b, dots, S)
+  if (waves == 8) {
+    if (dots) QG_LAUNCH(8, true); else QG_LAUNCH(8, false);
   } else {
-    if (call.dots) QG_LAUNCH(16, true); else QG_LAUNCH(16, false);
+    if (dots) QG_LAUNCH(16, true); else QG_LAUNCH(16, false);
   }
 #undef QG_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  q2_splitk_reduce_kernel<<<dim3((M + 255) / 256, njobs), 256, 0, stream>>>(
-      call.partials, S, Mp, M, call.act_scale, call.y[0], call.y[1], call.accum);
+  const int M = b.job[0].M;
+  q2_splitk_reduce_kernel<<<dim3((M + 255) / 256, b.njobs), 256, 0, stream>>>(b, y0, y1, accum, S);
   return hipGetLastError();
+}
+
+hipError_t launch_batch(const Q2Batch &b, int group, int waves, int S, int *dots, float *y0, float *y1,
+                        const float *accum, hipStream_t stream) {
+  if (group == 64) return launch_typed<1, 4>(b, waves, S, dots, y0, y1, accum, stream);
+  return launch_typed<2, 2>(b, waves, S, dots, y0, y1, accum, stream);
 }
 
 }  // namespace
 
 int q2_auto_split(int64_t M, int64_t K, int group) {
   // A second (reduce) launch costs about as much as streaming several MB, so
-  // K is split only for large matrices whose row tiles cannot fill the 256
-  // CUs: then into the fewest power-of-two ranges giving >= 256 workgroups
-  // (and at least one scale group per wave).
+  // K is split only for large matrices whose row tiles cannot half-fill the
+  // 256 CUs: then into the fewest power-of-two ranges giving >= 128
+  // workgroups of 16 waves (and at least 16 scale groups per range).
+  // Measured on HBM-cold 5120 x 17408 g128 weights: S = 2 streams at 2.45
+  // TB/s, S = 1 at 2.10, S = 4 at 2.14, S = 8 at 2.01.
   const int64_t tiles = (M + 63) / 64;
   const int64_t ngroups = K / group;
   const int64_t bytes = M * ngroups * (2 + group / 4);
-  if (tiles >= 256 || bytes < (16LL << 20)) return 1;
+  if (tiles >= 128 || bytes < (16LL << 20)) return 1;
   int S = 1;
-  while (S < kMaxSplit && tiles * S < 256 && ngroups / (2 * S) >= 16) S *= 2;
+  while (S < kMaxSplit && tiles * S < 128 && ngroups / (2 * S) >= 16) S *= 2;
   return S;
 }
 
+// One matrix or the gate/up pair.  Waves per tile: 8 when one matrix's row
+// tiles alone fill the CUs, else 16 so that each of the fewer workgroups
+// keeps more loads in flight.
 hipError_t launch_q2_gemv(const Q2Call &call, hipStream_t stream) {
-  if (call.group == 64) return launch_typed<1, 4>(call, stream);
-  return launch_typed<2, 2>(call, stream);
+  const int M = call.M, S = call.split;
+  const int tiles = (M + 63) / 64;
+  const int Mp = tiles * 64;
+  const int njobs = call.codes[1] ? 2 : 1;
+  Q2Batch b{};
+  b.njobs = njobs;
+  for (int n = 0; n < njobs; n++) {
+    Q2Job &j = b.job[n];
+    j.codes = reinterpret_cast<const i32x4 *>(call.codes[n]);
+    j.scales = reinterpret_cast<const unsigned short *>(call.scales[n]);
+    j.xq = call.xq;
+    j.suma = call.suma;
+    j.act_scale = call.act_scale;
+    j.out = S == 1 ? call.y[n] : call.partials + (size_t)n * S * Mp;
+    j.accum = S == 1 ? call.accum : nullptr;
+    j.M = M;
+    j.K = call.K;
+    b.tile_end[n] = tiles * (n + 1);
+  }
+  return launch_batch(b, call.group, tiles >= 256 ? 8 : 16, S, call.dots, call.y[0], call.y[1], call.accum,
+                      stream);
+}
+
+// Independent GEMVs of one group size in one launch, no split; 8 waves per
+// tile when the launch's row tiles fill the CUs, else 16.
+hipError_t launch_q2_batch(const Q2BatchCall *jobs, int njobs, int group, hipStream_t stream) {
+  Q2Batch b{};
+  b.njobs = njobs;
+  int tiles = 0;
+  for (int n = 0; n < njobs; n++) {
+    const Q2BatchCall &c = jobs[n];
+    Q2Job &j = b.job[n];
+    j.codes = reinterpret_cast<const i32x4 *>(c.codes);
+    j.scales = reinterpret_cast<const unsigned short *>(c.scales);
+    j.xq = c.xq;
+    j.suma = c.suma;
+    j.act_scale = c.act_scale;
+    j.out = c.y;
+    j.accum = c.accum;
+    j.M = c.M;
+    j.K = c.K;
+    tiles += (c.M + 63) / 64;
+    b.tile_end[n] = tiles;
+  }
+  return launch_batch(b, group, tiles >= 256 ? 8 : 16, 1, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 }  // namespace qg

@@ -56,6 +56,18 @@ struct Q2Call {
 };
 hipError_t launch_q2_gemv(const Q2Call &call, hipStream_t stream);
 
+// Several independent Q2 GEMVs of one group size in one launch (no split).
+constexpr int kMaxQ2Jobs = QG_Q2_BATCH_MAX;
+struct Q2BatchCall {
+  const void *codes, *scales;
+  const int8_t *xq;
+  const int32_t *suma;
+  const float *act_scale, *accum;
+  float *y;
+  int M, K;
+};
+hipError_t launch_q2_batch(const Q2BatchCall *jobs, int njobs, int group, hipStream_t stream);
+
 int q2_auto_split(int64_t M, int64_t K, int group);
 
 // Batched q8_row GEMM: workspace layout (limbs, exponents, flags) and launch.
