@@ -261,7 +261,7 @@ def main():
 
     # ---------------- fused FFN block: the same three matrices with the fused
     # producers, gate and up in one launch and the residual in the down
-    # projection's epilogue (4 launches instead of the step's 5 FFN launches)
+    # projection's epilogue
     fused = None
     if not args.no_breakdown:
         rng = np.random.Generator(np.random.PCG64(20260 + 900))
@@ -306,7 +306,7 @@ def main():
                              "-> SiLU-gate+quant -> down Q2 GEMV + residual, then the q8_row lm_head",
                  "us_per_step": round(us_fs, 2), "GB/s": round(step_bytes / us_fs / 1e3, 1),
                  "frac_hbm_peak": round(step_bytes / us_fs / 1e3 / HBM_PEAK_GBS, 4),
-                 "launches": 5, "unfused_us_per_step": round(ms_per_step * 1e3, 2), "unfused_launches": 6,
+                 "launches": 7, "unfused_us_per_step": round(ms_per_step * 1e3, 2), "unfused_launches": 7,
                  "step_weight_bytes": step_bytes,
                  "note": "timed like the main step (graph replays, the lm_head evicting the last-level cache)"}
         log(f"fused FFN: {fused}")

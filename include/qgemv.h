@@ -34,6 +34,10 @@
  *        gpu_silu_mul_quant, gpu_sigmoid_mul_quant (the activation-side
  *        producers that form and quantise the next GEMV's input in one
  *        kernel).
+ *  [LB]  cortiq-engine 0.5.43 gpu_wgpu.rs page: matvec_pair (two jobs laid
+ *        end to end in one row space of one dispatch); cortiq-engine 0.3.7
+ *        gpu_metal.rs page: matvec_batch (several independent matvecs in one
+ *        command buffer).
  *  [GD]  qxmx qxmx_gpu.cpp page: gemv_dpas8_dual (the FFN gate and up
  *        matrices against one shared quantized activation, bit-exact to two
  *        separate GEMVs) and tmatvec_accum (the residual add folded into the
@@ -282,7 +286,7 @@ typedef struct {
 /* Device: up to QG_Q2_BATCH_MAX independent Q2 GEMVs in one launch (each
  * launch has a fixed cost of a few microseconds, as much as streaming tens
  * of MB, so small GEMVs of one decode step -- several projections, or the
- * experts of a layer -- are better issued together)   [GV, GD]
+ * experts of a layer -- are better issued together)   [LB, GV, GD]
  *   jobs:      host array of njobs descriptors; each job may have its own
  *              shape and activation (all with the same group size) and an
  *              optional residual, added as in qgemv_q2_accum.

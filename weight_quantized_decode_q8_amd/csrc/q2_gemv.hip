@@ -31,8 +31,11 @@
 // launch (gemv_dpas8_dual on the same page), a residual added in the
 // epilogue (the accum argument of gemv_dpas8): y = (acc * act_scale) + accum
 // as two f32 roundings, the order of an unfused GEMV followed by a separate
-// residual add, and up to 16 independent GEMVs in one launch (launch batching
-// against the fixed cost of each launch).  The gate/up and residual forms
+// residual add, and up to 16 independent GEMVs in one launch against the
+// fixed cost of each launch (matvec_pair on the cortiq-engine 0.5.43
+// gpu_wgpu.rs page lays two jobs end to end in one row space the same way;
+// matvec_batch on the 0.3.7 gpu_metal.rs page groups several per command
+// buffer).  The gate/up and residual forms
 // equal the unfused calls bit for bit when the split is the same, which the
 // launchers guarantee: waves per tile and the automatic split depend only on
 // one matrix's shape.
