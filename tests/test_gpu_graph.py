@@ -68,3 +68,63 @@ def test_graph_replays_match_eager():
                               (xq, sc, suma, y2, y8, yb), ref):
             assert torch.equal(t, r), f"replay {rep}: {name} differs from the eager result"
     assert np.isfinite(yb.cpu().numpy()).all()
+
+
+def test_graph_replays_fused_forms():
+    """The fused FFN forms and a batched launch, captured and replayed."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+
+    dev = "cuda"
+    D, F = 1024, 2048
+    rng = np.random.Generator(np.random.PCG64(41))
+    h = torch.from_numpy(rng.standard_normal(D).astype(np.float32)).to(dev)
+    nw = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)).to(dev)
+    Wg = qg.Q2Weight.from_blocks(synth.q2_inputs(F, D, 128, seed=42)[0], F, D, 128)
+    Wu = qg.Q2Weight.from_blocks(synth.q2_inputs(F, D, 128, seed=43)[0], F, D, 128)
+    Wd = qg.Q2Weight.from_blocks(synth.q2_inputs(D, F, 128, seed=44)[0], D, F, 128)
+    Wx = [qg.Q2Weight.from_blocks(synth.q2_inputs(300 + 64 * n, D, 128, seed=45 + n)[0], 300 + 64 * n, D, 128)
+          for n in range(3)]
+    xq1 = torch.empty(D, dtype=torch.int8, device=dev)
+    sc1 = torch.empty(1, device=dev)
+    su1 = torch.empty(D // 64, dtype=torch.int32, device=dev)
+    g = torch.empty(F, device=dev)
+    u = torch.empty(F, device=dev)
+    t = torch.empty(F, device=dev)
+    xq2 = torch.empty(F, dtype=torch.int8, device=dev)
+    sc2 = torch.empty(1, device=dev)
+    su2 = torch.empty(F // 64, dtype=torch.int32, device=dev)
+    hout = torch.empty(D, device=dev)
+    ys = [torch.empty(W.M, device=dev) for W in Wx]
+    ws_gu = torch.empty(max(1, qg.qgemv_q2_dual_ws_bytes(F, D, 128, 2)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, qg.qgemv_q2_ws_bytes(D, F, 128, 2)), dtype=torch.uint8, device=dev)
+
+    def path():
+        qg.qquant_rmsnorm_i8(h, nw, 1e-6, xq1, sc1, su1)
+        qg.qgemv_q2_dual(Wg, Wu, xq1, su1, sc1, g, u, ws_gu, split_k=2)
+        qg.qquant_glu_i8(g, u, qg.QG_GLU_SILU, t, xq2, sc2, su2)
+        qg.qgemv_q2_accum(Wd, xq2, su2, sc2, h, hout, ws_d, split_k=2)
+        qg.qgemv_q2_batch([(W, xq1, su1, sc1, y) + ((h[:W.M],) if W.M <= D and n == 0 else ())
+                           for n, (W, y) in enumerate(zip(Wx, ys))])
+
+    outs = (xq1, sc1, su1, g, u, t, xq2, sc2, su2, hout, *ys)
+    path()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        path()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, r), f"replay {rep}: output {n} differs from the eager result"
