@@ -65,6 +65,8 @@ class Oracle:
         lib.qo_q2_gemv.argtypes = [P, I64, I64, ctypes.c_int, P, ctypes.c_float, P, I64, P, P]
         lib.qo_q2_gemv_accum.restype = None
         lib.qo_q2_gemv_accum.argtypes = [P, I64, I64, ctypes.c_int, P, ctypes.c_float, P, P, I64, P, P]
+        lib.qo_q2_gemm.restype = None
+        lib.qo_q2_gemm.argtypes = [P, I64, I64, ctypes.c_int, P, P, I64, P, P, P, I64, P, P]
         lib.qo_rmsnorm_quant_i8.restype = None
         lib.qo_rmsnorm_quant_i8.argtypes = [P, P, I64, ctypes.c_float, P, P, P, P]
         lib.qo_glu_quant_i8.restype = None
@@ -181,6 +183,36 @@ class Oracle:
                                   y.ctypes.data, m.ctypes.data)
         return y, m
 
+    def q2_gemm(self, blob, M, K, group, xq, sc, accum=None, entries=None):
+        """Batched Q2: y[b,o] = sc[b] * sum_u d(o,u) * dot(b,o,u) (+ accum[b,o]) in fp64
+        (qxmx page, ffn_forward_b with gemm_gpu_v4).
+
+        xq is int8 [nb][K] (row b quantised with scale sc[b]); ``entries=None``
+        gives the full ``[nb][M]`` output, else ``(bs, os)`` index arrays.
+        Returns (y, mass).
+        """
+        b, bp = _c(blob, np.uint8)
+        xq, xqp = _c(xq, np.int8)
+        sc, scp = _c(sc, np.float32)
+        nb = sc.size
+        assert xq.shape == (nb, K)
+        ap = None
+        if accum is not None:
+            accum, ap = _c(accum, np.float32)
+            assert accum.shape == (nb, M)
+        if entries is None:
+            y = np.empty((nb, M), np.float64)
+            m = np.empty((nb, M), np.float64)
+            self.lib.qo_q2_gemm(bp, M, K, group, xqp, scp, nb, ap, None, None, 0, y.ctypes.data, m.ctypes.data)
+            return y, m
+        bs, bsp = _c(entries[0], np.int64)
+        os_, osp = _c(entries[1], np.int64)
+        n = len(bs)
+        y = np.empty(n, np.float64)
+        m = np.empty(n, np.float64)
+        self.lib.qo_q2_gemm(bp, M, K, group, xqp, scp, nb, ap, bsp, osp, n, y.ctypes.data, m.ctypes.data)
+        return y, m
+
     def rmsnorm_quant_i8(self, x, w, eps):
         """RMSNorm in binary32 then the int8 quantiser (qxmx page, gpu_rmsnorm_quant).
 
@@ -269,3 +301,7 @@ def rmsnorm_quant_i8(x, w, eps):
 
 def glu_quant_i8(g, u, kind):
     return default().glu_quant_i8(g, u, kind)
+
+
+def q2_gemm(blob, M, K, group, xq, sc, accum=None, entries=None):
+    return default().q2_gemm(blob, M, K, group, xq, sc, accum, entries)

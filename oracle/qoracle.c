@@ -28,6 +28,10 @@
  *        multiplied by act_scale.
  *  [GA]  qxmx qxmx_gpu.cpp page, tmatvec_accum and the accum argument of
  *        gemv_dpas8: the projection plus a residual vector.
+ *  [QG]  qxmx qxmx_gpu.cpp page, ffn_forward_b with gemm_gpu_v4 /
+ *        gemm_gpu_v4_dual: the batched (prefill) Q2 product over tokens b,
+ *        each token's activation quantised with its own act_scale[b] and
+ *        group sums, the output token-major y[b][o], an optional residual.
  *  [PQ]  qxmx qxmx_gpu.cpp page, gpu_rmsnorm_quant, gpu_swiglu_quant,
  *        gpu_silu_mul_quant, gpu_sigmoid_mul_quant: the quantiser [AQ]
  *        applied to a vector formed in binary32 first: x * inv * w with
@@ -274,4 +278,25 @@ void qo_glu_quant_i8(const float *g, const float *u, int64_t K, int kind,
         }
     }
     qo_act_quant_i8(t, K, xq, act_scale, suma);
+}
+
+/* ---- batched Q2: y[b,o] = sc[b] * sum_u d(o,u) * dots[b][o][u]  [QG] ---- */
+/* xq [nb][K] (row b quantised with scale sc[b]); accum [nb][M] or NULL.
+ * bs/os == NULL: the full [nb][M] output; else the n listed (b, o) entries.
+ * mass[.] = sum_i |d (code-1)| * |sc[b] xq[b,i]|.                          */
+void qo_q2_gemm(const uint8_t *blob, int64_t M, int64_t K, int group,
+                const int8_t *xq, const float *sc, int64_t nb,
+                const float *accum, const int64_t *bs, const int64_t *os,
+                int64_t n, double *y, double *mass)
+{
+    int64_t total = bs ? n : nb * M;
+    for (int64_t j = 0; j < total; j++) {
+        int64_t b = bs ? bs[j] : j / M;
+        int64_t o = bs ? os[j] : j % M;
+        double yj, mj;
+        qo_q2_gemv(blob, M, K, group, xq + b * K, sc[b], &o, 1, &yj, &mj);
+        if (accum) yj += (double)accum[b * M + o];
+        y[j] = yj;
+        if (mass) mass[j] = mj;
+    }
 }

@@ -333,6 +333,56 @@ def pin_q2_accum_rows_subset(orc):
     assert np.array_equal(m, m0)
 
 
+# ---- batched Q2 ---------------------------------------------------------------
+def _q2_rows_case(orc, rng, nb, M, K, group):
+    _, _, blob = _q2_case(rng, M, K, group)
+    X = (rng.standard_normal((nb, K)) * rng.uniform(0.1, 10.0, size=(nb, 1))).astype(np.float32)
+    q = [orc.act_quant_i8(X[b]) for b in range(nb)]
+    xq = np.stack([t[0] for t in q])
+    sc = np.array([t[1] for t in q], np.float32)
+    return blob, xq, sc
+
+
+def pin_q2_gemm_rows_are_gemvs(orc):
+    """One token of the batched product is the GEMV of that token's activation."""
+    rng = np.random.Generator(np.random.PCG64(29))
+    nb, M, K = 5, 7, 384
+    blob, xq, sc = _q2_rows_case(orc, rng, nb, M, K, 128)
+    y, m = orc.q2_gemm(blob, M, K, 128, xq, sc)
+    for b in range(nb):
+        yb, mb = orc.q2_gemv(blob, M, K, 128, xq[b], sc[b])
+        assert np.array_equal(y[b], yb) and np.array_equal(m[b], mb)
+
+
+def pin_q2_gemm_vs_dense(orc):
+    """Dense dequantised weights times sc[b] * xq[b] by numpy's fp64 matmul."""
+    rng = np.random.Generator(np.random.PCG64(30))
+    for group, nb, M, K in [(64, 4, 6, 256), (128, 3, 5, 512)]:
+        blob, xq, sc = _q2_rows_case(orc, rng, nb, M, K, group)
+        w = orc.q2_dequant(blob, M, K, group)
+        ref = (xq.astype(np.float64) * sc.astype(np.float64)[:, None]) @ w.T
+        y, _ = orc.q2_gemm(blob, M, K, group, xq, sc)
+        _close(y, ref, rel=1e-12, abs_=1e-12)
+
+
+def pin_q2_gemm_entries_and_residual(orc):
+    """Listed entries equal the full output; a residual adds per (b, o)."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    nb, M, K = 4, 9, 192
+    blob, xq, sc = _q2_rows_case(orc, rng, nb, M, K, 64)
+    y, m = orc.q2_gemm(blob, M, K, 64, xq, sc)
+    bs = np.array([3, 0, 2, 1, 3])
+    os_ = np.array([8, 4, 0, 7, 1])
+    ye, me = orc.q2_gemm(blob, M, K, 64, xq, sc, entries=(bs, os_))
+    assert np.array_equal(ye, y[bs, os_]) and np.array_equal(me, m[bs, os_])
+    acc = np.round(rng.standard_normal((nb, M)) * 8).astype(np.float32)  # integers: the sums are exact
+    ya, _ = orc.q2_gemm(blob, M, K, 64, xq, sc, accum=acc)
+    codes_one = encode_q2(np.ones((M, K), np.uint8), np.full((M, K // 64), 0x3C00, np.uint16), 64)
+    y0, _ = orc.q2_gemm(codes_one, M, K, 64, xq, sc, accum=acc)
+    assert np.array_equal(y0, acc.astype(np.float64))
+    _close(ya, y + acc.astype(np.float64), rel=1e-15, abs_=1e-12)
+
+
 # ---- RMSNorm + quantiser ----------------------------------------------------
 def pin_rmsnorm_unit_vector(orc):
     """x = 1 everywhere and eps = 0: mean(x^2) = 1 exactly, inv = 1, so the

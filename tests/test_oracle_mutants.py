@@ -54,6 +54,11 @@ MUTANTS = {
     "glu silu as sigmoid": ("float silu = g[i] / den;", "float silu = 1.0f / den;"),
     "glu sigmoid as silu": ("float sig = 1.0f / den;", "float sig = g[i] / den;"),
     "glu up index": ("t[i] = silu * u[i];", "t[i] = silu * u[0];"),
+    "q2 gemm token row ignored": ("qo_q2_gemv(blob, M, K, group, xq + b * K, sc[b], &o, 1, &yj, &mj);",
+                                  "qo_q2_gemv(blob, M, K, group, xq, sc[b], &o, 1, &yj, &mj);"),
+    "q2 gemm scale of token 0": ("qo_q2_gemv(blob, M, K, group, xq + b * K, sc[b], &o, 1, &yj, &mj);",
+                                 "qo_q2_gemv(blob, M, K, group, xq + b * K, sc[0], &o, 1, &yj, &mj);"),
+    "q2 gemm residual index": ("if (accum) yj += (double)accum[b * M + o];", "if (accum) yj += (double)accum[o * nb + b];"),
 }
 
 
