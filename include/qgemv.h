@@ -30,6 +30,10 @@
  *        activation quantisation with per-64 group sums).
  *  [GV]  qxmx qxmx_gpu.cpp page: gemv_dpas8 (int8-activation Q2 GEMV,
  *        split-K partials, the suma correction) and gemv_reduce.
+ *  [QG]  qxmx qxmx_gpu.cpp page: ffn_forward_b (the batched FFN: the
+ *        token rows quantised by the batched producers, gemm_gpu_v4 /
+ *        gemm_gpu_v4_dual writing token-major outputs, the residual folded
+ *        into the down projection).
  *  [PQ]  qxmx qxmx_gpu.cpp page: gpu_rmsnorm_quant, gpu_swiglu_quant,
  *        gpu_silu_mul_quant, gpu_sigmoid_mul_quant (the activation-side
  *        producers that form and quantise the next GEMV's input in one
@@ -166,6 +170,16 @@ qg_status qg_unpack_q2(const void *codes, size_t codes_bytes,
 qg_status qquant_act_i8(const float *x, int64_t K, int8_t *xq,
                         float *act_scale, int32_t *suma, void *stream);
 
+/* Device: qquant_act_i8 on each row of a [nb][K] batch (the prefill form,
+ * one act_scale per token row)   [AQ, gpu_rmsnorm_quant with n_tok]
+ *   x:         device, f32[nb][K] row-major, 16-byte aligned, finite.
+ *   xq:        device, int8[nb][K]; act_scale: f32[nb]; suma: int32[nb][K/64].
+ *   Row b of each output is exactly what qquant_act_i8 writes for row b.
+ * QG_EINVAL: as qquant_act_i8, or nb < 1.                                 */
+qg_status qquant_act_i8_rows(const float *x, int64_t nb, int64_t K,
+                             int8_t *xq, float *act_scale, int32_t *suma,
+                             void *stream);
+
 /* Device: RMSNorm, then the quantiser of qquant_act_i8, in one launch
  *   [PQ, gpu_rmsnorm_quant]
  *   x, w:      device, f32[K] each (the vector and the norm weights),
@@ -300,6 +314,26 @@ typedef struct {
  * partly overlapping its y, or an output overlapping another job's output
  * or residual.                                                             */
 qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream);
+
+/* Device: the batched (prefill) Q2 product over nb token rows, on int8
+ * MFMA   [QG, ffn_forward_b with gemm_gpu_v4]
+ *   y[b, o] = act_scale[b] * sum_g d(o, g) * sum_{i in g} (code - 1) * xq[b, i]
+ *             (+ accum[b, o])
+ *   w:         host struct of the device planes (scales 8-byte aligned).
+ *   xq, suma, act_scale: device, as written by qquant_act_i8_rows:
+ *              int8[nb][K], int32[nb][K/64], f32[nb].
+ *   accum:     device, f32[nb][M] residual, or NULL; may be y itself,
+ *              otherwise must not overlap it.
+ *   y:         device, f32[nb][M] (token-major), 16-byte aligned, written.
+ * The per-group int32 dots are exact; each output accumulates d * dot over
+ * the groups in f32, then act_scale[b] and the residual are applied with one
+ * binary32 rounding each.  No workspace.
+ * QG_EINVAL: null pointer, bad weight struct, nb < 1, misaligned pointer,
+ * accum partly overlapping y.                                              */
+qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq,
+                           const int32_t *suma, const float *act_scale,
+                           const float *accum, float *y, int64_t nb,
+                           void *stream);
 
 /* ======================================================================
  * Batched prefill q8_row GEMM  [Q8, q8_matmat / q8_mul_mm]

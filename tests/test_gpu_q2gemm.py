@@ -1,0 +1,111 @@
+"""The batched (prefill) Q2 product and the row-batched quantiser, through
+the C-ABI, against the oracle: per-row quantisation bit for bit, the product
+within |y - y_ref| <= 2e-5 * sum_i |w_i x_i| per output (plus one binary32
+rounding, 2^-24 |y_ref|, when a residual is added)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import gpu_available
+from test_gpu_parity import REL, dev, host, qg, within
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a HIP device")]
+
+U32 = 2.0 ** -24
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def gpu_quant_rows(X):
+    torch = _torch()
+    nb, K = X.shape
+    xq = torch.empty((nb, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty(nb, dtype=torch.float32, device="cuda")
+    suma = torch.empty((nb, K // 64), dtype=torch.int32, device="cuda")
+    qg().qquant_act_i8_rows(dev(X), xq, sc, suma)
+    return xq, sc, suma
+
+
+def token_rows(nb, K, seed):
+    rng = synth.rng_for(seed)
+    # rows of different magnitudes, as tokens of a prefill batch
+    return (rng.standard_normal((nb, K)) * rng.uniform(0.05, 20.0, size=(nb, 1))).astype(np.float32)
+
+
+@pytest.mark.parametrize("nb,K", [(1, 64), (3, 192), (130, 1024), (512, 5120)])
+def test_quant_rows_bit_exact(nb, K):
+    X = token_rows(nb, K, 6000 + nb)
+    xq, sc, suma = (host(t) for t in gpu_quant_rows(X))
+    for b in range(nb):
+        rq, rsc, rsu = oracle.act_quant_i8(X[b])
+        assert np.array_equal(xq[b], rq), f"row {b}: codes differ"
+        assert np.float32(sc[b]).view(np.uint32) == np.float32(rsc).view(np.uint32), f"row {b}: scale"
+        assert np.array_equal(suma[b], rsu), f"row {b}: suma"
+
+
+def run_gemm(blob, M, K, group, X, accum=None, in_place=False):
+    torch = _torch()
+    m = qg()
+    W = m.Q2Weight.from_blocks(blob, M, K, group)
+    xq, sc, suma = gpu_quant_rows(X)
+    nb = X.shape[0]
+    if in_place:
+        y = dev(accum)
+        m.qgemm_q2_batched(W, xq, suma, sc, y, accum=y)
+    else:
+        y = torch.empty((nb, M), dtype=torch.float32, device="cuda")
+        m.qgemm_q2_batched(W, xq, suma, sc, y, accum=None if accum is None else dev(accum))
+    return host(y), host(xq), host(sc)
+
+
+@pytest.mark.parametrize("nb,M,K,group", [(1, 64, 64, 64), (5, 100, 256, 128), (128, 272, 1024, 64),
+                                          (129, 545, 640, 128), (200, 300, 2048, 64), (256, 1088, 512, 128)])
+def test_q2_gemm_small_all_outputs(nb, M, K, group):
+    blob, _ = synth.q2_inputs(M, K, group, seed=6100 + M + K)
+    X = token_rows(nb, K, 6200 + nb)
+    y, xq, sc = run_gemm(blob, M, K, group, X)
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc)
+    within(y.reshape(-1), yref.reshape(-1), mass.reshape(-1), what=f"q2 gemm nb={nb} {M}x{K} g{group}")
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_q2_gemm_residual(in_place):
+    nb, M, K, group = 96, 700, 1536, 128
+    blob, _ = synth.q2_inputs(M, K, group, seed=6300)
+    X = token_rows(nb, K, 6301)
+    acc = (synth.rng_for(6302).standard_normal((nb, M)) * 3).astype(np.float32)
+    y, xq, sc = run_gemm(blob, M, K, group, X, accum=acc, in_place=in_place)
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, accum=acc)
+    within(y.reshape(-1), yref.reshape(-1), (mass + U32 / REL * np.abs(yref)).reshape(-1), what="q2 gemm + residual")
+
+
+def test_q2_gemm_c3_gate_prefill_sampled():
+    """The 17408 x 5120 g128 gate matrix over 512 prefill tokens, sampled entries."""
+    c = synth.CONFIGS["C3_gate"]
+    M, K, group = c["M"], c["K"], c["group"]
+    blob, _ = synth.config_inputs("C3_gate")
+    nb = 512
+    X = token_rows(nb, K, 6400)
+    y, xq, sc = run_gemm(blob, M, K, group, X)
+    assert np.all(np.isfinite(y))
+    rng = synth.rng_for(6401)
+    bs = np.concatenate([rng.integers(0, nb, 3000), np.full(64, nb - 1), np.zeros(64, np.int64)])
+    os_ = np.concatenate([rng.integers(0, M, 3000), np.arange(M - 64, M), np.arange(64)])
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, entries=(bs, os_))
+    within(y[bs, os_], yref, mass, what="C3 gate prefill")
+
+
+def test_q2_gemm_token_rows_match_gemv_bound():
+    """Each token row of the product also matches the GEMV oracle of that token."""
+    nb, M, K, group = 7, 130, 512, 64
+    blob, _ = synth.q2_inputs(M, K, group, seed=6500)
+    X = token_rows(nb, K, 6501)
+    y, xq, sc = run_gemm(blob, M, K, group, X)
+    for b in range(nb):
+        yr, mr = oracle.q2_gemv(blob, M, K, group, xq[b], sc[b])
+        within(y[b], yr, mr, what=f"token {b}")

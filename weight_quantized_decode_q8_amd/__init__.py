@@ -59,6 +59,7 @@ _SIGS = {
     "qg_repack_q2": (_I, [_P, _SZ, _I64, _I64, _I, _P, _SZ, _P, _SZ]),
     "qg_unpack_q2": (_I, [_P, _SZ, _P, _SZ, _I64, _I64, _I, _P, _SZ]),
     "qquant_act_i8": (_I, [_P, _I64, _P, _P, _P, _P]),
+    "qquant_act_i8_rows": (_I, [_P, _I64, _I64, _P, _P, _P, _P]),
     "qquant_rmsnorm_i8": (_I, [_P, _P, _I64, ctypes.c_float, _P, _P, _P, _P]),
     "qquant_glu_i8": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _P]),
     "qgemv_q2_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
@@ -70,6 +71,7 @@ _SIGS = {
     "qgemv_q2_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P,
                            _SZ, _I, _P]),
     "qgemv_q2_batch": (_I, [ctypes.POINTER(qg_q2_job), _I, _P]),
+    "qgemm_q2_batched": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _I64, _P]),
     "qgemm_q8row_batched_ws_bytes": (_SZ, [_I64, _I64]),
     "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
 }
@@ -214,6 +216,15 @@ def qquant_act_i8(x, xq, act_scale, suma, stream=None):
         _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
 
 
+def qquant_act_i8_rows(x, xq, act_scale, suma, stream=None):
+    """Row-wise int8 quantisation of x (f32 [nb][K]): xq [nb][K], act_scale [nb], suma [nb][K/64]."""
+    import torch
+    nb, K = x.shape
+    _check("qquant_act_i8_rows", lib().qquant_act_i8_rows(
+        _dev(x, torch.float32, "x"), nb, K, _dev(xq, torch.int8, "xq"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
+
+
 QG_GLU_SILU, QG_GLU_SIGMOID = 0, 1
 
 
@@ -325,6 +336,17 @@ def qgemv_q2_batch(jobs, stream=None):
                            _dev(sc, torch.float32, "act_scale"), _dev(accum, torch.float32, "accum"),
                            _dev(y, torch.float32, "y"))
     _check("qgemv_q2_batch", lib().qgemv_q2_batch(arr, len(jobs), _stream(stream)))
+
+
+def qgemm_q2_batched(w: Q2Weight, xq, suma, act_scale, y, accum=None, stream=None):
+    """Batched Q2: y[b,o] = act_scale[b] * sum_g d * dot(b,o,g) (+ accum), y [nb][M]."""
+    import torch
+    d = w.desc()
+    nb = act_scale.numel()
+    _check("qgemm_q2_batched", lib().qgemm_q2_batched(
+        ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(accum, torch.float32, "accum"),
+        _dev(y, torch.float32, "y"), nb, _stream(stream)))
 
 
 # ------------------------------------------------------ batched q8_row GEMM --

@@ -11,17 +11,26 @@
 // One workgroup of 1024 threads per vector: the vector is at most a few
 // tens of KiB (the pages' widths are 5120 and 17408), so a single pass over
 // L2-resident data is all it needs; the launch, not bandwidth, is its cost.
+// A batch of token rows (the prefill form, gpu_rmsnorm_quant's n_tok on the
+// same page) is one workgroup per row, each row with its own act_scale.
 #include "qg_internal.h"
 #include "quant_rule.h"
 
 namespace qg {
 namespace {
 
+// One workgroup per vector: row blockIdx.x of a [rows][K] batch, each row
+// with its own act_scale and group sums (rows = 1 for a single vector).
 __global__ __launch_bounds__(kQuantThreads) void act_quant_i8_kernel(
     const float4 *__restrict__ x4, int n4, int *__restrict__ xq4,
     float *__restrict__ act_scale, int *__restrict__ suma) {
   __shared__ float red[kQuantThreads / 64];
   const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;
+  x4 += row * n4;
+  xq4 += row * n4;
+  suma += row * (n4 / 16);
+  act_scale += row;
 
   // Pass 1: exact max |x| (order-independent).
   float m = 0.0f;
@@ -34,9 +43,9 @@ __global__ __launch_bounds__(kQuantThreads) void act_quant_i8_kernel(
 
 }  // namespace
 
-hipError_t launch_act_quant(const float *x, int K, int8_t *xq, float *act_scale,
+hipError_t launch_act_quant(const float *x, int rows, int K, int8_t *xq, float *act_scale,
                             int32_t *suma, hipStream_t stream) {
-  act_quant_i8_kernel<<<1, kQuantThreads, 0, stream>>>(
+  act_quant_i8_kernel<<<rows, kQuantThreads, 0, stream>>>(
       reinterpret_cast<const float4 *>(x), K / 4, reinterpret_cast<int *>(xq), act_scale,
       reinterpret_cast<int *>(suma));
   return hipGetLastError();

@@ -78,7 +78,19 @@ qg_status qquant_act_i8(const float *x, int64_t K, int8_t *xq, float *act_scale,
   if (K < 64 || K % 64 != 0 || K > (1 << 24)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
   if (!aligned(x, 16)) return fail(QG_EINVAL, "%s: x not 16-byte aligned", fn);
   if (!aligned(xq, 4) || !aligned(act_scale, 4) || !aligned(suma, 4)) return fail(QG_EINVAL, "%s: misaligned output", fn);
-  return qg::launched(qg::launch_act_quant(x, (int)K, xq, act_scale, suma, (hipStream_t)stream), fn);
+  return qg::launched(qg::launch_act_quant(x, 1, (int)K, xq, act_scale, suma, (hipStream_t)stream), fn);
+}
+
+qg_status qquant_act_i8_rows(const float *x, int64_t nb, int64_t K, int8_t *xq, float *act_scale, int32_t *suma,
+                             void *stream) {
+  const char *fn = "qquant_act_i8_rows";
+  if (!x || !xq || !act_scale || !suma) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (nb < 1 || nb > (1 << 24)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
+  if (K < 64 || K % 64 != 0 || K > (1 << 24)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
+  if (nb * K > (1LL << 40)) return fail(QG_EINVAL, "%s: problem too large", fn);
+  if (!aligned(x, 16)) return fail(QG_EINVAL, "%s: x not 16-byte aligned", fn);
+  if (!aligned(xq, 4) || !aligned(act_scale, 4) || !aligned(suma, 4)) return fail(QG_EINVAL, "%s: misaligned output", fn);
+  return qg::launched(qg::launch_act_quant(x, (int)nb, (int)K, xq, act_scale, suma, (hipStream_t)stream), fn);
 }
 
 static qg_status check_quant_outputs(const char *fn, int64_t K, const int8_t *xq, const float *act_scale,
@@ -248,6 +260,25 @@ qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream) {
   }
   if (tiles > (1LL << 30)) return fail(QG_EINVAL, "%s: too many row tiles", fn);
   return qg::launched(qg::launch_q2_batch(c, njobs, jobs[0].w.group, (hipStream_t)stream), fn);
+}
+
+qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
+                           const float *accum, float *y, int64_t nb, void *stream) {
+  const char *fn = "qgemm_q2_batched";
+  qg_status st = qg::check_q2_weight(w, fn);
+  if (st != QG_OK) return st;
+  if (!xq || !suma || !act_scale || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (nb < 1 || nb > (1 << 24)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
+  if (nb * w->M > (1LL << 40) || nb * w->K > (1LL << 40)) return fail(QG_EINVAL, "%s: problem too large", fn);
+  if (!aligned(w->scales, 8)) return fail(QG_EINVAL, "%s: scales plane not 8-byte aligned", fn);
+  if (!aligned(xq, 16) || !aligned(y, 16)) return fail(QG_EINVAL, "%s: xq and y must be 16-byte aligned", fn);
+  if (!aligned(suma, 4) || !aligned(act_scale, 4) || (accum && !aligned(accum, 4)))
+    return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  if (accum && accum != y && overlap(accum, y, nb * w->M))
+    return fail(QG_EINVAL, "%s: accum must be y itself or not overlap it", fn);
+  return qg::launched(qg::launch_q2_gemm(w->codes, w->scales, (int)w->M, (int)w->K, w->group, xq, suma, act_scale,
+                                         accum, y, (int)nb, (hipStream_t)stream),
+                      fn);
 }
 
 size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K) {

@@ -23,7 +23,7 @@ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 qg_status fail(qg_status s, const char *fmt, ...);
 
 // Launchers.  Arguments are validated by the C-ABI layer before any call.
-hipError_t launch_act_quant(const float *x, int K, int8_t *xq, float *act_scale,
+hipError_t launch_act_quant(const float *x, int rows, int K, int8_t *xq, float *act_scale,
                             int32_t *suma, hipStream_t stream);
 
 // Fused producers: RMSNorm (x, w, eps) or a gated product (kind 0 silu(g)*u,
@@ -69,6 +69,11 @@ struct Q2BatchCall {
 hipError_t launch_q2_batch(const Q2BatchCall *jobs, int njobs, int group, hipStream_t stream);
 
 int q2_auto_split(int64_t M, int64_t K, int group);
+
+// Batched Q2 product over nb token rows (int8 MFMA), y [nb][M] token-major.
+hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, int group, const int8_t *xq,
+                          const int32_t *suma, const float *act_scale, const float *accum, float *y, int nb,
+                          hipStream_t stream);
 
 // Batched q8_row GEMM: workspace layout (limbs, exponents, flags) and launch.
 size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need, size_t *off_zero);
