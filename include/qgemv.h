@@ -325,15 +325,23 @@ qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream);
  *   accum:     device, f32[nb][M] residual, or NULL; may be y itself,
  *              otherwise must not overlap it.
  *   y:         device, f32[nb][M] (token-major), 16-byte aligned, written.
+ *   ws:        device workspace of >= qgemm_q2_batched_ws_bytes(M, K,
+ *              group, nb) bytes, 16-byte aligned (may be NULL when that is
+ *              0): f32 partial sums [S][nb][M] of a K split, used when the
+ *              row and token tiles alone cannot fill the GPU; contents on
+ *              entry are ignored.
  * The per-group int32 dots are exact; each output accumulates d * dot over
- * the groups in f32, then act_scale[b] and the residual are applied with one
- * binary32 rounding each.  No workspace.
+ * the groups in f32 (split partials added in fixed order), then act_scale[b]
+ * and the residual are applied with one binary32 rounding each.
  * QG_EINVAL: null pointer, bad weight struct, nb < 1, misaligned pointer,
- * accum partly overlapping y.                                              */
+ * accum partly overlapping y, workspace too small.                         */
 qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq,
                            const int32_t *suma, const float *act_scale,
                            const float *accum, float *y, int64_t nb,
-                           void *stream);
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace qgemm_q2_batched needs for this shape (0: none). */
+size_t qgemm_q2_batched_ws_bytes(int64_t M, int64_t K, int group, int64_t nb);
 
 /* ======================================================================
  * Batched prefill q8_row GEMM  [Q8, q8_matmat / q8_mul_mm]

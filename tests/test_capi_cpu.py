@@ -217,14 +217,20 @@ def test_einval_paths():
     _einval(L.qquant_act_i8_rows(None, 4, 64, a16, a16, a16, None))
     _einval(L.qquant_act_i8_rows(P(0x10004), 4, 64, a16, a16, a16, None))
     w8 = qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 64, 0)
-    _einval(L.qgemm_q2_batched(ctypes.byref(w8), a16, a16, a16, None, a16, 0, None))          # nb < 1
-    _einval(L.qgemm_q2_batched(ctypes.byref(w8), None, a16, a16, None, a16, 4, None))
-    _einval(L.qgemm_q2_batched(ctypes.byref(w8), a16, a16, a16, None, P(0x10004), 4, None))   # y misaligned
-    _einval(L.qgemm_q2_batched(ctypes.byref(w8), a16, a16, a16, P(0x10010), a16, 4, None))    # accum over y
+    _einval(L.qgemm_q2_batched(ctypes.byref(w8), a16, a16, a16, None, a16, 0, None, 0, None))          # nb < 1
+    _einval(L.qgemm_q2_batched(ctypes.byref(w8), None, a16, a16, None, a16, 4, None, 0, None))
+    _einval(L.qgemm_q2_batched(ctypes.byref(w8), a16, a16, a16, None, P(0x10004), 4, None, 0, None))   # y misaligned
+    _einval(L.qgemm_q2_batched(ctypes.byref(w8), a16, a16, a16, P(0x10010), a16, 4, None, 0, None))    # accum over y
     ws2 = qg.qg_q2_weight(0x10000, 0x20002, 128, 256, 64, 0)                                  # scales not 8-aligned
-    _einval(L.qgemm_q2_batched(ctypes.byref(ws2), a16, a16, a16, None, a16, 4, None))
+    _einval(L.qgemm_q2_batched(ctypes.byref(ws2), a16, a16, a16, None, a16, 4, None, 0, None))
     for b in bad:
-        _einval(L.qgemm_q2_batched(ctypes.byref(b), a16, a16, a16, None, a16, 4, None))
+        _einval(L.qgemm_q2_batched(ctypes.byref(b), a16, a16, a16, None, a16, 4, None, 0, None))
+    wdown = qg.qg_q2_weight(0x10000, 0x20000, 5120, 17408, 128, 0)                            # splits K
+    need = L.qgemm_q2_batched_ws_bytes(5120, 17408, 128, 512)
+    assert need == 3 * 512 * 5120 * 4, need
+    assert L.qgemm_q2_batched_ws_bytes(17408, 5120, 128, 512) == 0
+    _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, None, 0, None))
+    _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, a16, need - 16, None))
     # host repacks
     z = np.zeros(64, np.uint8)
     _einval(L.qg_repack_q8row(None, 4, 4, z.ctypes.data, 64))

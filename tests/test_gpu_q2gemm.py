@@ -54,12 +54,14 @@ def run_gemm(blob, M, K, group, X, accum=None, in_place=False):
     W = m.Q2Weight.from_blocks(blob, M, K, group)
     xq, sc, suma = gpu_quant_rows(X)
     nb = X.shape[0]
+    nws = m.qgemm_q2_batched_ws_bytes(M, K, group, nb)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
     if in_place:
         y = dev(accum)
-        m.qgemm_q2_batched(W, xq, suma, sc, y, accum=y)
+        m.qgemm_q2_batched(W, xq, suma, sc, y, accum=y, ws=ws)
     else:
         y = torch.empty((nb, M), dtype=torch.float32, device="cuda")
-        m.qgemm_q2_batched(W, xq, suma, sc, y, accum=None if accum is None else dev(accum))
+        m.qgemm_q2_batched(W, xq, suma, sc, y, accum=None if accum is None else dev(accum), ws=ws)
     return host(y), host(xq), host(sc)
 
 
@@ -98,6 +100,33 @@ def test_q2_gemm_c3_gate_prefill_sampled():
     os_ = np.concatenate([rng.integers(0, M, 3000), np.arange(M - 64, M), np.arange(64)])
     yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, entries=(bs, os_))
     within(y[bs, os_], yref, mass, what="C3 gate prefill")
+
+
+def test_q2_gemm_c3_down_prefill_split_sampled():
+    """The 5120 x 17408 g128 down matrix over 512 tokens: its tiles take a K split."""
+    c = synth.CONFIGS["C3_down"]
+    M, K, group = c["M"], c["K"], c["group"]
+    assert qg().qgemm_q2_batched_ws_bytes(M, K, group, 512) > 0
+    blob, _ = synth.config_inputs("C3_down")
+    X = token_rows(512, K, 6450)
+    acc = synth.rng_for(6451).standard_normal((512, M)).astype(np.float32)
+    y, xq, sc = run_gemm(blob, M, K, group, X, accum=acc)
+    rng = synth.rng_for(6452)
+    bs = np.concatenate([rng.integers(0, 512, 1500), np.full(32, 511)])
+    os_ = np.concatenate([rng.integers(0, M, 1500), np.arange(M - 32, M)])
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, accum=acc, entries=(bs, os_))
+    within(y[bs, os_], yref, mass + U32 / REL * np.abs(yref), what="C3 down prefill + residual")
+
+
+@pytest.mark.parametrize("nb,M,K,group", [(40, 300, 1024, 64), (7, 64, 256, 128)])
+def test_q2_gemm_split_small_shapes(nb, M, K, group):
+    """Few tiles: K is split (several splits, short last split)."""
+    assert qg().qgemm_q2_batched_ws_bytes(M, K, group, nb) > 0
+    blob, _ = synth.q2_inputs(M, K, group, seed=6460 + M)
+    X = token_rows(nb, K, 6470 + nb)
+    y, xq, sc = run_gemm(blob, M, K, group, X)
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc)
+    within(y.reshape(-1), yref.reshape(-1), mass.reshape(-1), what=f"split nb={nb} {M}x{K}")
 
 
 def test_q2_gemm_token_rows_match_gemv_bound():

@@ -71,7 +71,8 @@ _SIGS = {
     "qgemv_q2_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P,
                            _SZ, _I, _P]),
     "qgemv_q2_batch": (_I, [ctypes.POINTER(qg_q2_job), _I, _P]),
-    "qgemm_q2_batched": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _I64, _P]),
+    "qgemm_q2_batched": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "qgemm_q2_batched_ws_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "qgemm_q8row_batched_ws_bytes": (_SZ, [_I64, _I64]),
     "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
 }
@@ -338,15 +339,20 @@ def qgemv_q2_batch(jobs, stream=None):
     _check("qgemv_q2_batch", lib().qgemv_q2_batch(arr, len(jobs), _stream(stream)))
 
 
-def qgemm_q2_batched(w: Q2Weight, xq, suma, act_scale, y, accum=None, stream=None):
-    """Batched Q2: y[b,o] = act_scale[b] * sum_g d * dot(b,o,g) (+ accum), y [nb][M]."""
+def qgemm_q2_batched_ws_bytes(M, K, group, nb) -> int:
+    return lib().qgemm_q2_batched_ws_bytes(M, K, group, nb)
+
+
+def qgemm_q2_batched(w: Q2Weight, xq, suma, act_scale, y, accum=None, ws=None, stream=None):
+    """Batched Q2: y[b,o] = act_scale[b] * sum_g d * dot(b,o,g) (+ accum), y [nb][M]; ws a uint8 tensor or None."""
     import torch
     d = w.desc()
     nb = act_scale.numel()
     _check("qgemm_q2_batched", lib().qgemm_q2_batched(
         ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(accum, torch.float32, "accum"),
-        _dev(y, torch.float32, "y"), nb, _stream(stream)))
+        _dev(y, torch.float32, "y"), nb, _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(),
+        _stream(stream)))
 
 
 # ------------------------------------------------------ batched q8_row GEMM --

@@ -262,8 +262,14 @@ qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream) {
   return qg::launched(qg::launch_q2_batch(c, njobs, jobs[0].w.group, (hipStream_t)stream), fn);
 }
 
+size_t qgemm_q2_batched_ws_bytes(int64_t M, int64_t K, int group, int64_t nb) {
+  if (M < 1 || nb < 1 || (group != 64 && group != 128) || K < group || K % group) return 0;
+  const int S = qg::q2_gemm_split(M, K, group, nb);
+  return S > 1 ? (size_t)S * (size_t)nb * (size_t)M * sizeof(float) : 0;
+}
+
 qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
-                           const float *accum, float *y, int64_t nb, void *stream) {
+                           const float *accum, float *y, int64_t nb, void *ws, size_t ws_bytes, void *stream) {
   const char *fn = "qgemm_q2_batched";
   qg_status st = qg::check_q2_weight(w, fn);
   if (st != QG_OK) return st;
@@ -276,8 +282,12 @@ qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq, const int32_
     return fail(QG_EINVAL, "%s: misaligned pointer", fn);
   if (accum && accum != y && overlap(accum, y, nb * w->M))
     return fail(QG_EINVAL, "%s: accum must be y itself or not overlap it", fn);
+  const size_t need = qgemm_q2_batched_ws_bytes(w->M, w->K, w->group, nb);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws ? ws_bytes : (size_t)0, need);
+  if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
   return qg::launched(qg::launch_q2_gemm(w->codes, w->scales, (int)w->M, (int)w->K, w->group, xq, suma, act_scale,
-                                         accum, y, (int)nb, (hipStream_t)stream),
+                                         accum, y, (int)nb, static_cast<float *>(ws), (hipStream_t)stream),
                       fn);
 }
 

@@ -30,6 +30,9 @@
 //    the token pieces are stored with an XOR swizzle so the 128-bit fragment
 //    reads hit distinct LDS banks; workgroups sharing a weight tile are
 //    dispatched to one XCD.
+//  - shapes whose tiles cannot fill the CUs (the 5120-row down projection:
+//    76 tiles) split K over blockIdx.y into f32 partials [S][nb][M], added
+//    in fixed order by a second kernel.
 #include "qg_internal.h"
 
 namespace qg {
@@ -68,7 +71,7 @@ template <int UPG>
 __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
     const i32x4 *__restrict__ codes, const unsigned short *__restrict__ scales, const int8_t *__restrict__ xq,
     const int *__restrict__ suma, const float *__restrict__ act_scale, const float *accum, float *y, int nb, int M,
-    int K, int n_ot, int n_bt) {
+    int K, int n_ot, int n_bt, float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
 
   // Block order: the n_bt workgroups of one weight tile get ids 8 apart, so
@@ -89,6 +92,12 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   const int m_tiles = (M + 63) / 64;
   const int nunits = K / 64;
   const int ngroups = nunits / UPG;
+  // K split over blockIdx.y (gridDim.y splits of contiguous scale groups):
+  // this workgroup's units are [u_lo, u_hi).
+  const int S = gridDim.y, split = blockIdx.y;
+  const int gps = (ngroups + S - 1) / S;
+  const int u_lo = min(ngroups, split * gps) * UPG;
+  const int u_hi = min(ngroups, split * gps + gps) * UPG;
   const int kc = lane >> 4, r16 = lane & 15;
 
   // Load sources, formed once; a unit step moves each by 64 (codes, in
@@ -213,13 +222,13 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   // K loop over the ring, two units per barrier: while units u, u+1 are
   // multiplied, the loads of u+2, u+3 are in flight into the buffers that
   // u-2, u-1 used.
-  if (0 < nunits) issue_stage(0);
-  if (1 < nunits) issue_stage(1);
-  for (int u = 0; u < nunits; u += 2) {
+  if (u_lo < u_hi) issue_stage(u_lo);
+  if (u_lo + 1 < u_hi) issue_stage(u_lo + 1);
+  for (int u = u_lo; u < u_hi; u += 2) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     asm volatile("s_barrier" ::: "memory");  // every wave's loads of u, u+1 are in LDS
-    if (u + 2 < nunits) issue_stage(u + 2);
-    if (u + 3 < nunits) issue_stage(u + 3);
+    if (u + 2 < u_hi) issue_stage(u + 2);
+    if (u + 3 < u_hi) issue_stage(u + 3);
     const int b0u = u % kStages, b1u = (u + 1) % kStages;
     i32x4 nc[kBB];
     if (UPG == 2) {  // one g128 group: units u, u+1 (K is a multiple of 128)
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
       group_start(b0u, b0u, nc);
       compute_unit(b0u, true, nc);
       close_group(b0u);
-      if (u + 1 < nunits) {
+      if (u + 1 < u_hi) {
         group_start(b1u, b1u, nc);
         compute_unit(b1u, true, nc);
         close_group(b1u);
@@ -240,8 +249,31 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // Epilogue: y[b, o] = act_scale[b] * acc (+ accum[b, o]), two roundings.
+  // Epilogue: y[b, o] = act_scale[b] * acc (+ accum[b, o]), two roundings;
+  // with a K split, the f32 partial sums go to part[split][b][o] instead.
   const bool vec = (M & 3) == 0;
+  if (S > 1) {
+#pragma unroll
+    for (int c = 0; c < kBB; c++) {
+      const int b = b0 + wq * (kTN / kWC) + c * 16 + r16;
+      if (b >= nb) continue;
+#pragma unroll
+      for (int a = 0; a < kOBW; a++) {
+        if (a >= nob) continue;
+        const int o = o0 + (ob0 + a) * 16 + 4 * kc;
+        if (o >= M) continue;
+        float *dst = part + ((size_t)split * nb + b) * M + o;
+        if (vec && o + 3 < M) {
+          *reinterpret_cast<float4 *>(dst) = make_float4(facc[a][c][0], facc[a][c][1], facc[a][c][2], facc[a][c][3]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; v++)
+            if (o + v < M) dst[v] = facc[a][c][v];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < kBB; c++) {
     const int b = b0 + wq * (kTN / kWC) + c * 16 + r16;
@@ -270,21 +302,52 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   }
 }
 
+
+// y[b, o] = act_scale[b] * sum_s part[s][b][o] (+ accum[b, o]), the splits
+// added in fixed order.
+__global__ __launch_bounds__(256) void q2_gemm_reduce_kernel(const float *__restrict__ part, int S, size_t n, int M,
+                                                            const float *__restrict__ act_scale, const float *accum,
+                                                            float *y) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int k = 0; k < S; k++) s += part[(size_t)k * n + i];
+  float r = __fmul_rn(s, act_scale[i / M]);
+  if (accum) r = __fadd_rn(r, accum[i]);
+  y[i] = r;
+}
+
 }  // namespace
+
+// K splits: enough to give about one workgroup per CU when the (row tile,
+// token tile) pairs alone cannot (at least one scale group per split).
+int q2_gemm_split(int64_t M, int64_t K, int group, int64_t nb) {
+  const int64_t tiles = (M + kTM - 1) / kTM * ((nb + kTN - 1) / kTN);
+  const int64_t ngroups = K / group;
+  int64_t S = 256 / tiles;
+  if (S > ngroups) S = ngroups;
+  if (S > 16) S = 16;
+  return S < 1 ? 1 : (int)S;
+}
 
 hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, int group, const int8_t *xq,
                           const int32_t *suma, const float *act_scale, const float *accum, float *y, int nb,
-                          hipStream_t stream) {
+                          float *part, hipStream_t stream) {
   const int n_ot = (M + kTM - 1) / kTM;
   const int n_bt = (nb + kTN - 1) / kTN;
-  const int grid = (n_ot + 7) / 8 * 8 * n_bt;
+  const int S = q2_gemm_split(M, K, group, nb);
+  const dim3 grid((n_ot + 7) / 8 * 8 * n_bt, S);
   const i32x4 *c = reinterpret_cast<const i32x4 *>(codes);
   const unsigned short *s = reinterpret_cast<const unsigned short *>(scales);
   const int *sa = reinterpret_cast<const int *>(suma);
   if (group == 64)
-    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt);
+    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, part);
   else
-    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt);
+    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const size_t n = (size_t)nb * M;
+  q2_gemm_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, S, n, M, act_scale, accum, y);
   return hipGetLastError();
 }
 
