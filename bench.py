@@ -19,8 +19,9 @@ metric, the batched prefill q8_row GEMM (nb=512 x 17408 x 5120, int8 MFMA
 with exact activation limbs), in algorithmic TFLOP/s (`prefill_gemm`), and
 the FFN block in its fused form (RMSNorm+quant, gate|up in one launch,
 SiLU-gate+quant, down with the residual in its epilogue) next to the
-unfused launches (`fused_ffn`), and each Q2 GEMV's streaming rate from HBM
-over rotated weight copies launched back to back (`q2_sustained`).
+unfused launches (`fused_ffn`), each Q2 GEMV's streaming rate from HBM
+over rotated weight copies launched back to back (`q2_sustained`), and the
+batched prefill Q2 product over 512 token rows (`prefill_q2_gemm`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -415,6 +416,43 @@ def main():
                 "note": "2 int8 limbs per activation on these N(0,1) rows: hardware int8 ops = 2x algorithmic"}
         log(f"prefill GEMM: {gemm}")
 
+    # ---------------- prefill Q2 product: 512 token rows through the FFN gate
+    # matrix (17408 x 5120 g128): row-batched quantiser, then int8 MFMA
+    q2gemm = None
+    if not args.no_gemm:
+        cg = synth.CONFIGS["C3_gate"]
+        Mg, Kg, Gg = cg["M"], cg["K"], cg["group"]
+        nbq = 512
+        Wq = W["C3_gate"]
+        Xq = torch.from_numpy(synth.rng_for(20260 + 950).standard_normal((nbq, Kg), dtype=np.float32)).to(dev)
+        xq_r = torch.empty((nbq, Kg), dtype=torch.int8, device=dev)
+        sc_r = torch.empty(nbq, dtype=torch.float32, device=dev)
+        su_r = torch.empty((nbq, Kg // 64), dtype=torch.int32, device=dev)
+        y_r = torch.empty((nbq, Mg), dtype=torch.float32, device=dev)
+        nws_r = qg.qgemm_q2_batched_ws_bytes(Mg, Kg, Gg, nbq)
+        ws_r = torch.empty(nws_r, dtype=torch.uint8, device=dev) if nws_r else None
+
+        def k_quant_rows():
+            qg.qquant_act_i8_rows(Xq, xq_r, sc_r, su_r)
+
+        def k_q2gemm():
+            qg.qgemm_q2_batched(Wq, xq_r, su_r, sc_r, y_r, ws=ws_r)
+
+        k_quant_rows()
+        us_g = kernel_us(k_q2gemm, 10)
+        us_q = kernel_us(k_quant_rows, 10)
+        flop = 2 * nbq * Mg * Kg
+        tops = flop / us_g / 1e6
+        q2gemm = {"workload": f"batched prefill Q2 g128 product nb={nbq} M={Mg} K={Kg} (int8 activations per token)",
+                  "us": round(us_g, 2), "TOP/s": round(tops, 1), "unit": "TOP/s", "algorithmic_ops": flop,
+                  "frac_int8_dense_peak": round(tops / INT8_DENSE_TOPS, 4),
+                  "frac_fp16_dense_peak": round(tops / FP16_DENSE_TFLOPS, 4),
+                  "quant_rows_us": round(us_q, 2),
+                  "note": "one int8 MFMA per 64-wide unit; per-group scaling in f32 on the vector ALUs"}
+        log(f"prefill Q2 product: {q2gemm}")
+        del Xq, xq_r, y_r
+        torch.cuda.empty_cache()
+
     # ---------------- CPU oracle over the same step, on this host
     cpu = None
     if not args.no_cpu_baseline:
@@ -467,6 +505,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill_gemm": gemm,
+        "prefill_q2_gemm": q2gemm,
         "fused_ffn": fused,
         "q2_sustained": sustained,
     }
