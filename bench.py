@@ -450,7 +450,40 @@ def main():
                   "quant_rows_us": round(us_q, 2),
                   "note": "one int8 MFMA per 64-wide unit; per-group scaling in f32 on the vector ALUs"}
         log(f"prefill Q2 product: {q2gemm}")
-        del Xq, xq_r, y_r
+
+        # the whole prefill FFN block over the same 512 tokens: RMSNorm+quant
+        # rows -> gate, up products -> SiLU gate+quant rows -> down product
+        # with the residual (as the qxmx page's ffn_forward_b)
+        Wd = W["C3_down"]
+        Fd = Wd.K
+        H = torch.from_numpy(synth.rng_for(20260 + 951).standard_normal((nbq, Kg), dtype=np.float32)).to(dev)
+        Hout = torch.empty_like(H)
+        nw = torch.from_numpy((1.0 + 0.1 * synth.rng_for(20260 + 952).standard_normal(Kg)).astype(np.float32)).to(dev)
+        G = torch.empty((nbq, Fd), dtype=torch.float32, device=dev)
+        U = torch.empty((nbq, Fd), dtype=torch.float32, device=dev)
+        xq_f = torch.empty((nbq, Fd), dtype=torch.int8, device=dev)
+        sc_f = torch.empty(nbq, dtype=torch.float32, device=dev)
+        su_f = torch.empty((nbq, Fd // 64), dtype=torch.int32, device=dev)
+        nws_d = qg.qgemm_q2_batched_ws_bytes(Wd.M, Wd.K, Wd.group, nbq)
+        ws_d = torch.empty(nws_d, dtype=torch.uint8, device=dev) if nws_d else None
+
+        def ffn_prefill():
+            qg.qquant_rmsnorm_i8_rows(H, nw, 1e-6, xq_r, sc_r, su_r)
+            qg.qgemm_q2_batched(W["C3_gate"], xq_r, su_r, sc_r, G, ws=ws_r)
+            qg.qgemm_q2_batched(W["C3_up"], xq_r, su_r, sc_r, U, ws=ws_r)
+            qg.qquant_glu_i8_rows(G, U, qg.QG_GLU_SILU, G, xq_f, sc_f, su_f)
+            qg.qgemm_q2_batched(Wd, xq_f, su_f, sc_f, Hout, accum=H, ws=ws_d)
+
+        ffn_prefill()
+        us_ffn = kernel_us(ffn_prefill, 5)
+        ops3 = 3 * flop
+        q2gemm["ffn_block"] = {
+            "workload": f"prefill FFN block, {nbq} tokens: RMSNorm+quant rows -> gate, up -> SiLU gate+quant rows "
+                        f"-> down + residual (Q2 g128 17408x5120 / 5120x17408)",
+            "us": round(us_ffn, 2), "TOP/s": round(ops3 / us_ffn / 1e6, 1),
+            "frac_int8_dense_peak": round(ops3 / us_ffn / 1e6 / INT8_DENSE_TOPS, 4)}
+        log(f"prefill FFN block: {q2gemm['ffn_block']}")
+        del Xq, xq_r, y_r, H, Hout, G, U, xq_f
         torch.cuda.empty_cache()
 
     # ---------------- CPU oracle over the same step, on this host

@@ -196,6 +196,16 @@ qg_status qquant_rmsnorm_i8(const float *x, const float *w, int64_t K,
                             float eps, int8_t *xq, float *act_scale,
                             int32_t *suma, void *stream);
 
+/* Device: qquant_rmsnorm_i8 on each row of a [nb][K] batch (the prefill
+ * form, gpu_rmsnorm_quant with n_tok): x f32[nb][K]; w f32[K], shared by
+ * all rows; xq int8[nb][K], act_scale f32[nb], suma int32[nb][K/64].  Row b
+ * of each output is exactly what qquant_rmsnorm_i8 writes for row b.
+ * QG_EINVAL: as qquant_rmsnorm_i8, or nb < 1.                              */
+qg_status qquant_rmsnorm_i8_rows(const float *x, const float *w, int64_t nb,
+                                 int64_t K, float eps, int8_t *xq,
+                                 float *act_scale, int32_t *suma,
+                                 void *stream);
+
 /* Gate functions of qquant_glu_i8. */
 enum { QG_GLU_SILU = 0, QG_GLU_SIGMOID = 1 };
 
@@ -218,6 +228,15 @@ enum { QG_GLU_SILU = 0, QG_GLU_SIGMOID = 1 };
 qg_status qquant_glu_i8(const float *g, const float *u, int64_t K, int kind,
                         float *t, int8_t *xq, float *act_scale,
                         int32_t *suma, void *stream);
+
+/* Device: qquant_glu_i8 on each row of a [nb][K] batch (the prefill form,
+ * gpu_swiglu_quant / gpu_silu_mul_quant / gpu_sigmoid_mul_quant with
+ * n_tok): g, u, t f32[nb][K]; xq int8[nb][K], act_scale f32[nb], suma
+ * int32[nb][K/64].  Row b of each output is exactly what qquant_glu_i8
+ * writes for row b.  QG_EINVAL: as qquant_glu_i8, or nb < 1.              */
+qg_status qquant_glu_i8_rows(const float *g, const float *u, int64_t nb,
+                             int64_t K, int kind, float *t, int8_t *xq,
+                             float *act_scale, int32_t *suma, void *stream);
 
 /* Bytes of split-K workspace qgemv_q2 needs for this shape and split
  * (split_k 0 = the library's choice).                                    */

@@ -150,6 +150,12 @@ def test_einval_paths():
     _einval(L.qquant_glu_i8(a16, a16, 64, 1, P(0x10008), a16, a16, a16, None))  # t misaligned
     _einval(L.qquant_glu_i8(P(0x20000), P(0x30000), 64, 0, P(0x20010), a16, a16, a16, None))  # t inside g
     _einval(L.qquant_glu_i8(P(0x20000), P(0x30000), 64, 0, P(0x2FFF0), a16, a16, a16, None))  # t over u
+    _einval(L.qquant_rmsnorm_i8_rows(a16, a16, 0, 64, F(1e-6), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8_rows(a16, a16, 4, 96, F(1e-6), a16, a16, a16, None))
+    _einval(L.qquant_rmsnorm_i8_rows(a16, a16, 4, 64, F(-2.0), a16, a16, a16, None))
+    _einval(L.qquant_glu_i8_rows(a16, a16, 0, 64, 0, a16, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8_rows(a16, a16, 4, 64, 5, a16, a16, a16, a16, None))
+    _einval(L.qquant_glu_i8_rows(P(0x20000), P(0x30000), 4, 64, 0, P(0x20100), a16, a16, a16, None))  # t in g
     # Q2 GEMV
     w = qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 64, 0)
     bad = [qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 96, 0),

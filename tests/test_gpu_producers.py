@@ -127,3 +127,39 @@ def test_glu_output_modes(mode):
     t, xq, sc, suma = gpu_glu(g, u, 0, mode)
     assert same_bits(t, rt)
     assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu t={mode}")
+
+
+# ---------------------------------------------------- batches of token rows --
+@pytest.mark.parametrize("nb,K", [(1, 64), (5, 320), (64, 5120), (33, 17408)])
+def test_rmsnorm_quant_rows_bit_exact(nb, K):
+    torch = _torch()
+    rng = synth.rng_for(4200 + nb)
+    X = (rng.standard_normal((nb, K)) * rng.uniform(0.01, 30.0, size=(nb, 1))).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    xq = torch.empty((nb, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty(nb, dtype=torch.float32, device="cuda")
+    suma = torch.empty((nb, K // 64), dtype=torch.int32, device="cuda")
+    qg().qquant_rmsnorm_i8_rows(dev(X), dev(w), 1e-6, xq, sc, suma)
+    xq, sc, suma = host(xq), host(sc), host(suma)
+    for b in range(nb):
+        _, rxq, rsc, rsu = oracle.rmsnorm_quant_i8(X[b], w, 1e-6)
+        assert_quant_equal((xq[b], sc[b], suma[b]), (rxq, rsc, rsu), f"rmsnorm row {b}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("nb,K", [(1, 64), (7, 1088), (48, 17408)])
+def test_glu_quant_rows_bit_exact(kind, nb, K):
+    torch = _torch()
+    rng = synth.rng_for(4300 + nb + kind)
+    G = (rng.standard_normal((nb, K)) * 2.5).astype(np.float32)
+    U = rng.standard_normal((nb, K)).astype(np.float32)
+    t = torch.empty((nb, K), dtype=torch.float32, device="cuda")
+    xq = torch.empty((nb, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty(nb, dtype=torch.float32, device="cuda")
+    suma = torch.empty((nb, K // 64), dtype=torch.int32, device="cuda")
+    qg().qquant_glu_i8_rows(dev(G), dev(U), kind, t, xq, sc, suma)
+    t, xq, sc, suma = host(t), host(xq), host(sc), host(suma)
+    for b in range(nb):
+        rt, rxq, rsc, rsu = oracle.glu_quant_i8(G[b], U[b], kind)
+        assert same_bits(t[b], rt), f"row {b}: t differs"
+        assert_quant_equal((xq[b], sc[b], suma[b]), (rxq, rsc, rsu), f"glu row {b}")

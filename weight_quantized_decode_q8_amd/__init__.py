@@ -62,6 +62,8 @@ _SIGS = {
     "qquant_act_i8_rows": (_I, [_P, _I64, _I64, _P, _P, _P, _P]),
     "qquant_rmsnorm_i8": (_I, [_P, _P, _I64, ctypes.c_float, _P, _P, _P, _P]),
     "qquant_glu_i8": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _P]),
+    "qquant_rmsnorm_i8_rows": (_I, [_P, _P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P]),
+    "qquant_glu_i8_rows": (_I, [_P, _P, _I64, _I64, _I, _P, _P, _P, _P, _P]),
     "qgemv_q2_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
     "qgemv_q2_auto_split": (_I, [_I64, _I64, _I]),
     "qgemv_q2": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _SZ, _I, _P]),
@@ -243,6 +245,26 @@ def qquant_glu_i8(g, u, kind, t, xq, act_scale, suma, stream=None):
     import torch
     _check("qquant_glu_i8", lib().qquant_glu_i8(
         _dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), g.numel(), int(kind),
+        _dev(t, torch.float32, "t"), _dev(xq, torch.int8, "xq"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
+
+
+def qquant_rmsnorm_i8_rows(x, w, eps, xq, act_scale, suma, stream=None):
+    """RMSNorm (shared weights w [K]) then the int8 quantiser on each row of x [nb][K]."""
+    import torch
+    nb, K = x.shape
+    _check("qquant_rmsnorm_i8_rows", lib().qquant_rmsnorm_i8_rows(
+        _dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), nb, K, float(eps),
+        _dev(xq, torch.int8, "xq"), _dev(act_scale, torch.float32, "act_scale"),
+        _dev(suma, torch.int32, "suma"), _stream(stream)))
+
+
+def qquant_glu_i8_rows(g, u, kind, t, xq, act_scale, suma, stream=None):
+    """The gated product and the int8 quantiser on each row of g, u [nb][K]."""
+    import torch
+    nb, K = g.shape
+    _check("qquant_glu_i8_rows", lib().qquant_glu_i8_rows(
+        _dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), nb, K, int(kind),
         _dev(t, torch.float32, "t"), _dev(xq, torch.int8, "xq"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
 

@@ -101,30 +101,52 @@ static qg_status check_quant_outputs(const char *fn, int64_t K, const int8_t *xq
   return QG_OK;
 }
 
-qg_status qquant_rmsnorm_i8(const float *x, const float *w, int64_t K, float eps, int8_t *xq, float *act_scale,
-                            int32_t *suma, void *stream) {
-  const char *fn = "qquant_rmsnorm_i8";
+static qg_status rmsnorm_common(const char *fn, const float *x, const float *w, int64_t nb, int64_t K, float eps,
+                                int8_t *xq, float *act_scale, int32_t *suma, void *stream) {
   qg_status st = check_quant_outputs(fn, K, xq, act_scale, suma);
   if (st != QG_OK) return st;
   if (!x || !w) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (nb < 1 || nb > (1 << 24) || nb * K > (1LL << 40)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
   if (!aligned(x, 16) || !aligned(w, 16)) return fail(QG_EINVAL, "%s: x and w must be 16-byte aligned", fn);
   if (!(eps >= 0.0f) || eps > 3.4e38f) return fail(QG_EINVAL, "%s: eps must be finite and >= 0", fn);
-  return qg::launched(qg::launch_rmsnorm_quant(x, w, (int)K, eps, xq, act_scale, suma, (hipStream_t)stream), fn);
+  return qg::launched(qg::launch_rmsnorm_quant(x, w, (int)nb, (int)K, eps, xq, act_scale, suma, (hipStream_t)stream),
+                      fn);
+}
+
+qg_status qquant_rmsnorm_i8(const float *x, const float *w, int64_t K, float eps, int8_t *xq, float *act_scale,
+                            int32_t *suma, void *stream) {
+  return rmsnorm_common("qquant_rmsnorm_i8", x, w, 1, K, eps, xq, act_scale, suma, stream);
+}
+
+qg_status qquant_rmsnorm_i8_rows(const float *x, const float *w, int64_t nb, int64_t K, float eps, int8_t *xq,
+                                 float *act_scale, int32_t *suma, void *stream) {
+  return rmsnorm_common("qquant_rmsnorm_i8_rows", x, w, nb, K, eps, xq, act_scale, suma, stream);
+}
+
+static qg_status glu_common(const char *fn, const float *g, const float *u, int64_t nb, int64_t K, int kind, float *t,
+                            int8_t *xq, float *act_scale, int32_t *suma, void *stream) {
+  qg_status st = check_quant_outputs(fn, K, xq, act_scale, suma);
+  if (st != QG_OK) return st;
+  if (!g || !u || !t) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (nb < 1 || nb > (1 << 24) || nb * K > (1LL << 40)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
+  if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
+  if (!aligned(g, 16) || !aligned(u, 16) || !aligned(t, 16))
+    return fail(QG_EINVAL, "%s: g, u and t must be 16-byte aligned", fn);
+  const int64_t n = nb * K;
+  auto part_overlap = [n](const float *a, const float *b) { return a != b && a < b + n && b < a + n; };
+  if (part_overlap(t, g) || part_overlap(t, u)) return fail(QG_EINVAL, "%s: t must be g, u or a separate buffer", fn);
+  return qg::launched(
+      qg::launch_glu_quant(g, u, (int)nb, (int)K, kind, t, xq, act_scale, suma, (hipStream_t)stream), fn);
 }
 
 qg_status qquant_glu_i8(const float *g, const float *u, int64_t K, int kind, float *t, int8_t *xq,
                         float *act_scale, int32_t *suma, void *stream) {
-  const char *fn = "qquant_glu_i8";
-  qg_status st = check_quant_outputs(fn, K, xq, act_scale, suma);
-  if (st != QG_OK) return st;
-  if (!g || !u || !t) return fail(QG_EINVAL, "%s: null pointer", fn);
-  if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
-  if (!aligned(g, 16) || !aligned(u, 16) || !aligned(t, 16))
-    return fail(QG_EINVAL, "%s: g, u and t must be 16-byte aligned", fn);
-  auto part_overlap = [K](const float *a, const float *b) { return a != b && a < b + K && b < a + K; };
-  if (part_overlap(t, g) || part_overlap(t, u))
-    return fail(QG_EINVAL, "%s: t must be g, u or a separate buffer", fn);
-  return qg::launched(qg::launch_glu_quant(g, u, (int)K, kind, t, xq, act_scale, suma, (hipStream_t)stream), fn);
+  return glu_common("qquant_glu_i8", g, u, 1, K, kind, t, xq, act_scale, suma, stream);
+}
+
+qg_status qquant_glu_i8_rows(const float *g, const float *u, int64_t nb, int64_t K, int kind, float *t, int8_t *xq,
+                             float *act_scale, int32_t *suma, void *stream) {
+  return glu_common("qquant_glu_i8_rows", g, u, nb, K, kind, t, xq, act_scale, suma, stream);
 }
 
 int qgemv_q2_auto_split(int64_t M, int64_t K, int group) {

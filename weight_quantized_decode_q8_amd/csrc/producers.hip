@@ -17,6 +17,8 @@
 // rounding to binary32 equals a left-to-right sum's unless the two binary64
 // sums fall on opposite sides of a binary32 rounding boundary.
 //
+// Batches of token rows (the prefill form: the page's n_tok) run one
+// workgroup per row for the norm and the quantising step.
 // RMSNorm + quantiser is one workgroup of 1024 threads per vector, as the
 // quantiser: its passes re-read x and w from L2 (a few tens of KiB) instead
 // of holding them, so any K the quantiser takes works.  The gated product
@@ -49,6 +51,11 @@ __global__ __launch_bounds__(kQuantThreads) void rmsnorm_quant_kernel(
   __shared__ double red_ss[kQuantThreads / 64];
   __shared__ float red_max[kQuantThreads / 64];
   const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;  // one workgroup per token row; w is shared
+  x4 += row * n4;
+  xq4 += row * n4;
+  suma += row * (n4 / 16);
+  act_scale += row;
 
   double ss = 0.0;
   for (int i = tid; i < n4; i += kQuantThreads) {
@@ -88,7 +95,7 @@ __device__ inline float4 glu4(float4 g, float4 u) {
 
 // Gated product, step 1 of 2, over the whole GPU: quad i of t (one per
 // thread) and, per workgroup, the largest |t| of its quads, stored as float
-// bits in part[blockIdx.x] (the caller's suma buffer, which has room: at most
+// bits in part[blockIdx.x] of the token row's suma (which has room: at most
 // K/1024 workgroups against K/64 entries).  t may be g or u itself: every
 // quad is read and then written by one thread.
 constexpr int kGluThreads = 256;
@@ -97,6 +104,11 @@ template <int KIND>
 __global__ __launch_bounds__(kGluThreads) void glu_kernel(const float4 *g4, const float4 *u4, float4 *t4, int n4,
                                                           int *__restrict__ part) {
   __shared__ float red[kGluThreads / 64];
+  const size_t row = blockIdx.y;  // token row; its partial maxima go to its own suma row
+  g4 += row * n4;
+  u4 += row * n4;
+  t4 += row * n4;
+  part += row * (n4 / 16);
   const int i = blockIdx.x * kGluThreads + threadIdx.x;
   float m = 0.0f;
   if (i < n4) {
@@ -115,13 +127,19 @@ __global__ __launch_bounds__(kGluThreads) void glu_kernel(const float4 *g4, cons
   }
 }
 
-// Step 2 of 2, one workgroup: max|t| from the nparts partial maxima (all
-// read before any group sum overwrites them), then the quantiser over t.
+// Step 2 of 2, one workgroup per token row: max|t| from the row's nparts
+// partial maxima (all read before any group sum overwrites them), then the
+// quantiser over t.
 __global__ __launch_bounds__(kQuantThreads) void quant_from_parts_kernel(const float4 *__restrict__ t4, int n4,
                                                                          int nparts, int *__restrict__ xq4,
                                                                          float *__restrict__ act_scale,
                                                                          int *__restrict__ suma) {
   __shared__ float red_max[kQuantThreads / 64];
+  const size_t row = blockIdx.x;  // one workgroup per token row
+  t4 += row * n4;
+  xq4 += row * n4;
+  suma += row * (n4 / 16);
+  act_scale += row;
   float m = 0.0f;
   for (int j = threadIdx.x; j < nparts; j += kQuantThreads) m = fmaxf(m, __int_as_float(suma[j]));
   const float qinv = scale_and_inverse(block_max(m, red_max), act_scale);
@@ -130,15 +148,15 @@ __global__ __launch_bounds__(kQuantThreads) void quant_from_parts_kernel(const f
 
 }  // namespace
 
-hipError_t launch_rmsnorm_quant(const float *x, const float *w, int K, float eps, int8_t *xq,
+hipError_t launch_rmsnorm_quant(const float *x, const float *w, int rows, int K, float eps, int8_t *xq,
                                 float *act_scale, int32_t *suma, hipStream_t stream) {
-  rmsnorm_quant_kernel<<<1, kQuantThreads, 0, stream>>>(
+  rmsnorm_quant_kernel<<<rows, kQuantThreads, 0, stream>>>(
       reinterpret_cast<const float4 *>(x), reinterpret_cast<const float4 *>(w), K / 4, eps,
       reinterpret_cast<int *>(xq), act_scale, reinterpret_cast<int *>(suma));
   return hipGetLastError();
 }
 
-hipError_t launch_glu_quant(const float *g, const float *u, int K, int kind, float *t, int8_t *xq,
+hipError_t launch_glu_quant(const float *g, const float *u, int rows, int K, int kind, float *t, int8_t *xq,
                             float *act_scale, int32_t *suma, hipStream_t stream) {
   const float4 *g4 = reinterpret_cast<const float4 *>(g);
   const float4 *u4 = reinterpret_cast<const float4 *>(u);
@@ -146,14 +164,15 @@ hipError_t launch_glu_quant(const float *g, const float *u, int K, int kind, flo
   int *s = reinterpret_cast<int *>(suma);
   const int n4 = K / 4;
   const int nparts = (n4 + kGluThreads - 1) / kGluThreads;
+  const dim3 grid(nparts, rows);
   if (kind == 0)
-    glu_kernel<0><<<nparts, kGluThreads, 0, stream>>>(g4, u4, t4, n4, s);
+    glu_kernel<0><<<grid, kGluThreads, 0, stream>>>(g4, u4, t4, n4, s);
   else
-    glu_kernel<1><<<nparts, kGluThreads, 0, stream>>>(g4, u4, t4, n4, s);
+    glu_kernel<1><<<grid, kGluThreads, 0, stream>>>(g4, u4, t4, n4, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  quant_from_parts_kernel<<<1, kQuantThreads, 0, stream>>>(t4, n4, nparts, reinterpret_cast<int *>(xq), act_scale,
-                                                           s);
+  quant_from_parts_kernel<<<rows, kQuantThreads, 0, stream>>>(t4, n4, nparts, reinterpret_cast<int *>(xq), act_scale,
+                                                              s);
   return hipGetLastError();
 }
 

@@ -28,9 +28,10 @@ hipError_t launch_act_quant(const float *x, int rows, int K, int8_t *xq, float *
 
 // Fused producers: RMSNorm (x, w, eps) or a gated product (kind 0 silu(g)*u,
 // kind 1 u*sigmoid(g); t optional) followed by the quantiser.
-hipError_t launch_rmsnorm_quant(const float *x, const float *w, int K, float eps, int8_t *xq,
+// rows >= 1 token rows of K values each ([rows][K] row-major; w shared).
+hipError_t launch_rmsnorm_quant(const float *x, const float *w, int rows, int K, float eps, int8_t *xq,
                                 float *act_scale, int32_t *suma, hipStream_t stream);
-hipError_t launch_glu_quant(const float *g, const float *u, int K, int kind, float *t, int8_t *xq,
+hipError_t launch_glu_quant(const float *g, const float *u, int rows, int K, int kind, float *t, int8_t *xq,
                             float *act_scale, int32_t *suma, hipStream_t stream);
 
 hipError_t launch_q8row_gemv(const void *qpacked, const float *rs, const float *xs,
