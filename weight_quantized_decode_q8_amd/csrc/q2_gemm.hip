@@ -31,8 +31,8 @@
 //    reads hit distinct LDS banks; workgroups sharing a weight tile are
 //    dispatched to one XCD.
 //  - shapes whose tiles cannot fill the CUs (the 5120-row down projection:
-//    76 tiles) split K over blockIdx.y into f32 partials [S][nb][M], added
-//    in fixed order by a second kernel.
+//    76 tiles) split K into f32 partials [S][nb][M], added in fixed order by
+//    a second kernel; (row tile, split) pairs are spread evenly over XCDs.
 #include "qg_internal.h"
 
 namespace qg {
@@ -71,16 +71,19 @@ template <int UPG>
 __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
     const i32x4 *__restrict__ codes, const unsigned short *__restrict__ scales, const int8_t *__restrict__ xq,
     const int *__restrict__ suma, const float *__restrict__ act_scale, const float *accum, float *y, int nb, int M,
-    int K, int n_ot, int n_bt, float *__restrict__ part) {
+    int K, int n_ot, int n_bt, int n_split, float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
 
-  // Block order: the n_bt workgroups of one weight tile get ids 8 apart, so
-  // the round-robin dispatch over the 8 XCDs puts them on one XCD together.
+  // Block order: a weight tile is a (row tile, K split) pair; its n_bt
+  // workgroups get ids 8 apart, so the round-robin dispatch over the 8 XCDs
+  // puts them on one XCD together, and the pairs spread evenly over XCDs.
+  const int S = n_split;
   const int id = blockIdx.x;
   const int per_grp = 8 * n_bt;
-  const int ot = (id / per_grp) * 8 + (id % per_grp) % 8;
+  const int pair = (id / per_grp) * 8 + (id % per_grp) % 8;
   const int bt = (id % per_grp) / 8;
-  if (ot >= n_ot) return;
+  if (pair >= n_ot * S) return;
+  const int ot = pair / S, split = pair % S;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,9 +95,8 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   const int m_tiles = (M + 63) / 64;
   const int nunits = K / 64;
   const int ngroups = nunits / UPG;
-  // K split over blockIdx.y (gridDim.y splits of contiguous scale groups):
-  // this workgroup's units are [u_lo, u_hi).
-  const int S = gridDim.y, split = blockIdx.y;
+  // K split into S ranges of contiguous scale groups: this workgroup's
+  // units are [u_lo, u_hi).
   const int gps = (ngroups + S - 1) / S;
   const int u_lo = min(ngroups, split * gps) * UPG;
   const int u_hi = min(ngroups, split * gps + gps) * UPG;
@@ -336,14 +338,14 @@ hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, i
   const int n_ot = (M + kTM - 1) / kTM;
   const int n_bt = (nb + kTN - 1) / kTN;
   const int S = q2_gemm_split(M, K, group, nb);
-  const dim3 grid((n_ot + 7) / 8 * 8 * n_bt, S);
+  const int grid = (n_ot * S + 7) / 8 * 8 * n_bt;
   const i32x4 *c = reinterpret_cast<const i32x4 *>(codes);
   const unsigned short *s = reinterpret_cast<const unsigned short *>(scales);
   const int *sa = reinterpret_cast<const int *>(suma);
   if (group == 64)
-    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, part);
+    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, S, part);
   else
-    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, part);
+    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, S, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const size_t n = (size_t)nb * M;
