@@ -128,3 +128,56 @@ def test_graph_replays_fused_forms():
         torch.cuda.synchronize()
         for n, (o, r) in enumerate(zip(outs, ref)):
             assert torch.equal(o, r), f"replay {rep}: output {n} differs from the eager result"
+
+
+def test_graph_replays_prefill_forms():
+    """Row-batched producers and the batched Q2 product (with a K split), captured and replayed."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+
+    dev = "cuda"
+    nb, D, F = 40, 1024, 2048
+    rng = np.random.Generator(np.random.PCG64(51))
+    H = torch.from_numpy(rng.standard_normal((nb, D)).astype(np.float32)).to(dev)
+    nw = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)).to(dev)
+    Wg = qg.Q2Weight.from_blocks(synth.q2_inputs(F, D, 64, seed=52)[0], F, D, 64)
+    Wd = qg.Q2Weight.from_blocks(synth.q2_inputs(D, F, 64, seed=53)[0], D, F, 64)
+    xq1 = torch.empty((nb, D), dtype=torch.int8, device=dev)
+    sc1 = torch.empty(nb, device=dev)
+    su1 = torch.empty((nb, D // 64), dtype=torch.int32, device=dev)
+    G = torch.empty((nb, F), device=dev)
+    xq2 = torch.empty((nb, F), dtype=torch.int8, device=dev)
+    sc2 = torch.empty(nb, device=dev)
+    su2 = torch.empty((nb, F // 64), dtype=torch.int32, device=dev)
+    Hout = torch.empty((nb, D), device=dev)
+    ws1 = torch.empty(max(1, qg.qgemm_q2_batched_ws_bytes(F, D, 64, nb)), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(max(1, qg.qgemm_q2_batched_ws_bytes(D, F, 64, nb)), dtype=torch.uint8, device=dev)
+    assert qg.qgemm_q2_batched_ws_bytes(D, F, 64, nb) > 0
+
+    def path():
+        qg.qquant_rmsnorm_i8_rows(H, nw, 1e-6, xq1, sc1, su1)
+        qg.qgemm_q2_batched(Wg, xq1, su1, sc1, G, ws=ws1)
+        qg.qquant_glu_i8_rows(G, G, qg.QG_GLU_SIGMOID, G, xq2, sc2, su2)
+        qg.qgemm_q2_batched(Wd, xq2, su2, sc2, Hout, accum=H, ws=ws2)
+
+    outs = (xq1, sc1, su1, G, xq2, sc2, su2, Hout)
+    path()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        path()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, r), f"replay {rep}: output {n} differs from the eager result"
