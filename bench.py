@@ -226,19 +226,42 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / (reps * n)
 
+    # the two small workloads: the 256 x 512 q8_row GEMV and the 4096 x 4096
+    # g64 Q2 GEMV (with its quantiser), each back to back in a graph
+    small = []
+    if not args.no_breakdown:
+        q1, rs1, xs1 = synth.config_inputs("C1")
+        W1 = qg.Q8RowWeight.from_host(q1, rs1, dev)
+        xs1_d = torch.from_numpy(xs1).to(dev)
+        y1 = torch.empty(q1.shape[0], dtype=torch.float32, device=dev)
+        c2 = synth.CONFIGS["C2"]
+        b2s, x2s = synth.config_inputs("C2")
+        W2s = qg.Q2Weight.from_blocks(b2s, c2["M"], c2["K"], c2["group"], dev)
+        x2s_d = torch.from_numpy(x2s).to(dev)
+        xq2s = torch.empty(c2["K"], dtype=torch.int8, device=dev)
+        sc2s = torch.empty(1, dtype=torch.float32, device=dev)
+        su2s = torch.empty(c2["K"] // 64, dtype=torch.int32, device=dev)
+        y2s = torch.empty(c2["M"], dtype=torch.float32, device=dev)
+        qg.qquant_act_i8(x2s_d, xq2s, sc2s, su2s)
+        small = [("q8row_256x512", lambda: W1.gemv(xs1_d, y1), q1.shape[0] * (q1.shape[1] + 4), 50),
+                 ("q2_4096x4096_g64", lambda: qg.qgemv_q2(W2s, xq2s, su2s, sc2s, y2s), 4096 * 64 * 18, 50),
+                 ("act_quant_K4096", lambda: qg.qquant_act_i8(x2s_d, xq2s, sc2s, su2s), None, 50)]
+
     kernels = {}
-    for name, fn, nbytes, n in [] if args.no_breakdown else [("act_quant_K5120", k_quant_gu, None, 50),
+    for name, fn, nbytes, n in small + ([] if args.no_breakdown else [("act_quant_K5120", k_quant_gu, None, 50),
                                 ("q2_gate_17408x5120_g128", k_gate, q2_bytes["C3_gate"], 20),
                                 ("q2_up_17408x5120_g128", k_up, q2_bytes["C3_up"], 20),
                                 ("act_quant_K17408", k_quant_dn, None, 50),
                                 ("q2_down_5120x17408_g128", k_down, q2_bytes["C3_down"], 20),
-                                ("q8row_lm_head_248320x5120", k_lm_head, lm_bytes, 10)]:
+                                ("q8row_lm_head_248320x5120", k_lm_head, lm_bytes, 10)]):
         us = kernel_us(fn, n)
         ent = {"us": round(us, 3)}
         if nbytes:
             gbs = nbytes / us / 1e3
             ent.update({"weight_bytes": nbytes, "GB/s": round(gbs, 1),
                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        if nbytes and nbytes < (64 << 20):
+            ent["note"] = "back-to-back calls: weights cache-resident, launch-bound"
         kernels[name] = ent
         log(f"  {name}: {ent}")
 
