@@ -71,6 +71,8 @@ class Oracle:
         lib.qo_rmsnorm_quant_i8.argtypes = [P, P, I64, ctypes.c_float, P, P, P, P]
         lib.qo_glu_quant_i8.restype = None
         lib.qo_glu_quant_i8.argtypes = [P, P, I64, ctypes.c_int, P, P, P, P]
+        lib.qo_silu_mul_pre.restype = None
+        lib.qo_silu_mul_pre.argtypes = [P, P, P, I64, I64, P]
         self.lib = lib
 
     def f16_to_f64(self, bits: int) -> float:
@@ -249,6 +251,26 @@ class Oracle:
                                  suma.ctypes.data if K // 64 else None)
         return t, xq, sc[0], suma
 
+    def silu_mul_pre(self, g, u, col=None):
+        """act = silu(g) * u * col in binary32 (cortiq pages, silu_mul_pre): the
+        down projection's prescaled input.  g, u [n] or [rows][n]; col [n] or
+        None (no column field).  Returns float32 of g's shape.
+        """
+        g = np.asarray(g, np.float32)
+        shape = g.shape
+        n = shape[-1] if g.ndim else 1
+        rows = g.size // n if n else 0
+        g, gp = _c(g, np.float32)
+        u, up = _c(u, np.float32)
+        assert u.shape == shape
+        cp = None
+        if col is not None:
+            col, cp = _c(col, np.float32)
+            assert col.shape == (n,)
+        act = np.empty(shape, np.float32)
+        self.lib.qo_silu_mul_pre(gp, up, cp, rows, n, act.ctypes.data)
+        return act
+
 
 _default = None
 
@@ -301,6 +323,10 @@ def rmsnorm_quant_i8(x, w, eps):
 
 def glu_quant_i8(g, u, kind):
     return default().glu_quant_i8(g, u, kind)
+
+
+def silu_mul_pre(g, u, col=None):
+    return default().silu_mul_pre(g, u, col)
 
 
 def q2_gemm(blob, M, K, group, xq, sc, accum=None, entries=None):

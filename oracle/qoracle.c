@@ -54,6 +54,12 @@
  *    IEEE (correctly rounded) binary32 operations.
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared qoracle.c -lm
+ *  [SP]  cortiq-engine 0.5.43 gpu_wgpu.rs page, silu_mul_pre shader of the
+ *        MoE block, and cortiq-engine 0.3.7 gpu_metal.rs page, silu_mul_pre
+ *        kernel (has_col): the down projection's prescaled input
+ *        act = silu(g) * u * col in binary32, with col the q8_2f column
+ *        field (left out when a tensor has none); the Metal page's
+ *        q8_mul_mm_silu forms silu(g) * u inside the batched product.
  */
 #include <math.h>
 #include <stdint.h>
@@ -278,6 +284,26 @@ void qo_glu_quant_i8(const float *g, const float *u, int64_t K, int kind,
         }
     }
     qo_act_quant_i8(t, K, xq, act_scale, suma);
+}
+
+/* [SP] act[r][i] = silu(g[r][i]) * u[r][i] * col[i] over rows x n values
+ * (row-major; col shared by the rows, NULL = no column field): e = exp(-g),
+ * s = g / (1 + e), then s * u, then times col[i], every step in binary32. */
+void qo_silu_mul_pre(const float *g, const float *u, const float *col,
+                     int64_t rows, int64_t n, float *act)
+{
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t i = 0; i < n; i++) {
+            int64_t k = r * n + i;
+            float e = exp_f32(-g[k]);
+            float den = 1.0f + e;
+            float s = g[k] / den;
+            float v = s * u[k];
+            if (col)
+                v = v * col[i];
+            act[k] = v;
+        }
+    }
 }
 
 /* ---- batched Q2: y[b,o] = sc[b] * sum_u d(o,u) * dots[b][o][u]  [QG] ---- */

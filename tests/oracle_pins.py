@@ -475,4 +475,73 @@ def pin_glu_identities(orc):
     assert np.all(np.abs((lp - ln) - g.astype(np.float64)) <= 2.0 ** -20 * (1.0 + np.abs(g)))
 
 
+
+# ---- silu * mul * column prescale -------------------------------------------
+def pin_silu_pre_values(orc):
+    """Closed forms: silu(0) = 0; sigmoid(ln 3) = 3/4, so silu(ln 3) = 0.75 ln 3
+    (to a few ulps: exp(-ln 3) = 1/3 is rounded); for g = 30, exp(-30) is below
+    half an ulp of 1, so silu(30) = 30 exactly; for g = -100, exp(100)
+    overflows binary32 and silu(-100) = -0."""
+    g = np.array([0.0, np.log(3.0), 30.0, -100.0], np.float32)
+    act = orc.silu_mul_pre(g, np.ones(4, np.float32))
+    assert act[0] == 0.0 and act[2] == 30.0 and act[3] == 0.0
+    assert abs(float(act[1]) - 0.75 * float(g[1])) <= 2.0 ** -21 * float(g[1])
+
+
+def pin_silu_pre_vs_fp64(orc):
+    """Against the definition x u c / (1 + exp(-x)) in fp64: five binary32
+    roundings, so within 2^-21 relative."""
+    rng = np.random.Generator(np.random.PCG64(61))
+    n = 1000
+    g = (3.0 * rng.standard_normal(n)).astype(np.float32)
+    u = rng.standard_normal(n).astype(np.float32)
+    c = rng.uniform(0.5, 2.0, n).astype(np.float32)
+    act = orc.silu_mul_pre(g, u, c).astype(np.float64)
+    gd, ud, cd = g.astype(np.float64), u.astype(np.float64), c.astype(np.float64)
+    ref = gd * ud * cd / (1.0 + np.exp(-gd))
+    assert np.all(np.abs(act - ref) <= 2.0 ** -21 * np.abs(ref))
+
+
+def pin_silu_pre_odd_identity(orc):
+    """silu(g) - silu(-g) = g (since sigmoid(g) + sigmoid(-g) = 1), to a few ulps."""
+    g = np.linspace(-12.0, 12.0, 256).astype(np.float32)
+    one = np.ones_like(g)
+    lp = orc.silu_mul_pre(g, one).astype(np.float64)
+    ln = orc.silu_mul_pre(-g, one).astype(np.float64)
+    assert np.all(np.abs((lp - ln) - g.astype(np.float64)) <= 2.0 ** -20 * (1.0 + np.abs(g)))
+
+
+def pin_silu_pre_scaling(orc):
+    """Powers of two in u and col pass through every rounding exactly; no column
+    field is the same as a column of ones."""
+    rng = np.random.Generator(np.random.PCG64(62))
+    n = 300
+    g = (2.0 * rng.standard_normal(n)).astype(np.float32)
+    u = rng.standard_normal(n).astype(np.float32)
+    c = rng.uniform(0.25, 4.0, n).astype(np.float32)
+    ref = orc.silu_mul_pre(g, u, c)
+    assert np.array_equal(orc.silu_mul_pre(g, u), orc.silu_mul_pre(g, u, np.ones(n, np.float32)))
+    assert np.array_equal(orc.silu_mul_pre(g, u * np.float32(8.0), c), ref * np.float32(8.0))
+    assert np.array_equal(orc.silu_mul_pre(g, u, c * np.float32(0.25)), ref * np.float32(0.25))
+    assert np.array_equal(orc.silu_mul_pre(g, u, np.full(n, 2.0, np.float32)),
+                          orc.silu_mul_pre(g, u) * np.float32(2.0))
+
+
+def pin_silu_pre_rows(orc):
+    """Rows share the column field: every element of a [rows][n] call equals the
+    one-element call on (g[r, i], u[r, i], col[i]), and a row without a column
+    equals the gated product of the quantising producer."""
+    rng = np.random.Generator(np.random.PCG64(63))
+    rows, n = 3, 37
+    g = (2.0 * rng.standard_normal((rows, n))).astype(np.float32)
+    u = rng.standard_normal((rows, n)).astype(np.float32)
+    c = rng.uniform(0.5, 2.0, n).astype(np.float32)
+    act = orc.silu_mul_pre(g, u, c)
+    for r in range(rows):
+        for i in range(n):
+            one = orc.silu_mul_pre(g[r, i:i + 1], u[r, i:i + 1], c[i:i + 1])
+            assert act[r, i] == one[0], (r, i)
+        t = orc.glu_quant_i8(np.pad(g[r], (0, 64 - n)), np.pad(u[r], (0, 64 - n)), 0)[0][:n]
+        assert np.array_equal(orc.silu_mul_pre(g[r], u[r]), t)
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

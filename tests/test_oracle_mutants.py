@@ -50,10 +50,16 @@ MUTANTS = {
     "rms weight dropped": ("v[i] = xi * w[i];", "v[i] = xi;"),
     "rms weight index": ("v[i] = xi * w[i];", "v[i] = xi * w[0];"),
     "glu exp sign": ("float e = exp_f32(-g[i]);", "float e = exp_f32(g[i]);"),
-    "glu denominator": ("float den = 1.0f + e;", "float den = 1.0f - e;"),
+    "glu denominator": ("float den = 1.0f + e;\n        if (kind == 0) {", "float den = 1.0f - e;\n        if (kind == 0) {"),
+    "silu_pre denominator": ("float den = 1.0f + e;\n            float s = g[k] / den;", "float den = 1.0f - e;\n            float s = g[k] / den;"),
     "glu silu as sigmoid": ("float silu = g[i] / den;", "float silu = 1.0f / den;"),
     "glu sigmoid as silu": ("float sig = 1.0f / den;", "float sig = g[i] / den;"),
     "glu up index": ("t[i] = silu * u[i];", "t[i] = silu * u[0];"),
+    "silu_pre exp sign": ("float e = exp_f32(-g[k]);", "float e = exp_f32(g[k]);"),
+    "silu_pre product for quotient": ("float s = g[k] / den;", "float s = g[k] * den;"),
+    "silu_pre column dropped": ("                v = v * col[i];", "                v = v;"),
+    "silu_pre column by row": ("                v = v * col[i];", "                v = v * col[r];"),
+    "silu_pre up from row 0": ("float v = s * u[k];", "float v = s * u[i];"),
     "q2 gemm token row ignored": ("qo_q2_gemv(blob, M, K, group, xq + b * K, sc[b], &o, 1, &yj, &mj);",
                                   "qo_q2_gemv(blob, M, K, group, xq, sc[b], &o, 1, &yj, &mj);"),
     "q2 gemm scale of token 0": ("qo_q2_gemv(blob, M, K, group, xq + b * K, sc[b], &o, 1, &yj, &mj);",
