@@ -271,6 +271,10 @@ def main():
         small = [("q8row_256x512", lambda: W1.gemv(xs1_d, y1), q1.shape[0] * (q1.shape[1] + 4), 50),
                  ("q2_4096x4096_g64", lambda: qg.qgemv_q2(W2s, xq2s, su2s, sc2s, y2s), 4096 * 64 * 18, 50),
                  ("act_quant_K4096", lambda: qg.qquant_act_i8(x2s_d, xq2s, sc2s, su2s), None, 50)]
+        # the column prescale act = silu(g) u col at the down projection's K
+        gp, up_, cp = (torch.from_numpy(a).to(dev) for a in synth.gate_inputs(1, 17408, seed=20260 + 960))
+        actp = torch.empty_like(gp)
+        small.append(("silu_mul_pre_K17408", lambda: qg.qact_silu_mul_pre(gp, up_, cp, actp), None, 50))
 
     kernels = {}
     for name, fn, nbytes, n in small + ([] if args.no_breakdown else [("act_quant_K5120", k_quant_gu, None, 50),
@@ -451,6 +455,29 @@ def main():
                 "frac_fp16_dense_peak": round(tflops / FP16_DENSE_TFLOPS, 4),
                 "frac_int8_dense_peak_hw": round(2 * tflops / INT8_DENSE_TOPS, 4),
                 "note": "2 int8 limbs per activation on these N(0,1) rows: hardware int8 ops = 2x algorithmic"}
+        # The same product fed by the column prescale of the q8_row FFN: act =
+        # silu(g) u col formed inside the product's prep, against the prescale
+        # launch followed by the product.
+        g5, u5, c5c = (torch.from_numpy(a).to(dev) for a in synth.gate_inputs(nb5, K5, seed=20260 + 961))
+        act5 = torch.empty_like(g5)
+
+        def k_gemm_silu():
+            qg.qgemm_q8row_batched_silu(W5.packed, W5.rs, g5, u5, c5c, y5, nb5, M5, K5, ws5, xs_limbs=0)
+
+        def k_two_step():
+            qg.qact_silu_mul_pre(g5, u5, c5c, act5)
+            qg.qgemm_q8row_batched(W5.packed, W5.rs, act5, y5, nb5, M5, K5, ws5, xs_limbs=0)
+
+        us_f, _ = steady_us(k_gemm_silu, 1, reps=20)
+        us_t, _ = steady_us(k_two_step, 1, reps=20)
+        gemm["silu_fused"] = {"workload": f"the same product of act = silu(g) u col (g, u [{nb5}][{K5}])",
+                              "us": round(us_f, 2), "TFLOP/s": round(flop / us_f / 1e6, 1),
+                              "two_step_us": round(us_t, 2),
+                              "note": "auto limbs pick the 24-bit (3-limb) form for most of these rows: a gated "
+                                      "product's max/mean ratio per row is about 26 (N(0,1): about 5), beyond "
+                                      "what 16-bit activations keep inside the bound"}
+        del g5, u5, c5c, act5
+
         # Context, not this library's path: the vendor GEMMs on the same shape,
         # timed the same way -- hipBLASLt int8 with the same hardware int8 work
         # (17408 x 5120 by 5120 x 1024, i.e. two limbs of 512 rows) and torch's

@@ -46,6 +46,12 @@
  *        matrices against one shared quantized activation, bit-exact to two
  *        separate GEMVs) and tmatvec_accum (the residual add folded into the
  *        GEMV epilogue, bit-exact to the GEMV followed by the add).
+ *  [SP]  cortiq-engine 0.5.43 gpu_wgpu.rs page: silu_mul_pre (the MoE
+ *        block's element-wise pass forming the down projection's input
+ *        silu(g) * u, times the q8_2f column field when the tensor has one);
+ *        cortiq-engine 0.3.7 gpu_metal.rs page: silu_mul_pre (has_col) and
+ *        q8_mul_mm_silu (the batched down product with silu(g) * u formed in
+ *        its activation load).
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -394,6 +400,45 @@ qg_status qgemm_q8row_batched(const void *qpacked, const float *rs,
                               const float *xs, float *y, int64_t nb,
                               int64_t M, int64_t K, int xs_limbs, void *ws,
                               size_t ws_bytes, void *stream);
+
+/* ======================================================================
+ * Column prescale of the q8_row down projection's input  [SP]
+ *
+ *   act[r][i] = silu(g[r][i]) * u[r][i] * col[i]
+ *
+ * in IEEE binary32, one correctly rounded operation per step: e = exp(-g)
+ * (the binary64 exponential rounded once), s = g / (1 + e), then s * u,
+ * then times col[i].  col == NULL means the tensor has no column field
+ * (the product is left unscaled).  The result is the prescaled xs that
+ * qgemv_q8row / qgemm_q8row_batched expect.
+ * Arguments:
+ *   g, u: device f32[rows][n] row-major;  col: device f32[n] or NULL, shared
+ *   by every row;  act: device f32[rows][n], written; it may be g or u
+ *   itself, otherwise it must not overlap g, u or col.
+ *   rows >= 1, n >= 1 (any n; n % 4 == 0 with 16-byte aligned pointers takes
+ *   128-bit accesses).
+ * QG_EINVAL: null g/u/act, bad shape, pointers not 4-byte aligned, act
+ * partly overlapping g or u, or overlapping col.                          */
+qg_status qact_silu_mul_pre(const float *g, const float *u, const float *col,
+                            float *act, int64_t rows, int64_t n, void *stream);
+
+/* Batched q8_row product of the prescaled down-projection input  [Q8, SP]
+ *
+ *   y[b, o] = rs[o] * sum_i q[o, i] * act[b, i],
+ *   act[b, i] = silu(g[b, i]) * u[b, i] * col[i]
+ *
+ * act is formed inside the product's activation prep (never written to
+ * memory) by exactly the rule of qact_silu_mul_pre, so y is bit-identical to
+ * qact_silu_mul_pre followed by qgemm_q8row_batched with the same xs_limbs.
+ * Arguments as qgemm_q8row_batched, with g, u: device f32[nb][K] row-major
+ * and col: device f32[K] or NULL, all 16-byte aligned; the workspace is
+ * qgemm_q8row_batched_ws_bytes(nb, K) bytes.
+ * QG_EINVAL: as qgemm_q8row_batched, or null g/u, or g/u/col misaligned.  */
+qg_status qgemm_q8row_batched_silu(const void *qpacked, const float *rs,
+                                   const float *g, const float *u,
+                                   const float *col, float *y, int64_t nb,
+                                   int64_t M, int64_t K, int xs_limbs,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

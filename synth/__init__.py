@@ -70,6 +70,17 @@ def q8gemm_inputs(nb: int, M: int, K: int, rs_range=(0.001, 0.01), seed: int = 0
     return q, rs, xs
 
 
+def gate_inputs(rows: int, n: int, seed: int = 0, col: bool = True):
+    """Inputs of the column prescale: gate g = 2 N(0,1) (reaching the saturated
+    ends of silu), up u N(0,1), both [rows][n], and a column field col U[0.5, 2)
+    of n values (None when col is False)."""
+    r = rng_for(seed)
+    g = (2.0 * r.standard_normal((rows, n))).astype(np.float32)
+    u = r.standard_normal((rows, n), dtype=np.float32)
+    c = r.uniform(0.5, 2.0, n).astype(np.float32) if col else None
+    return g, u, c
+
+
 def q2_scales_f16(g: np.random.Generator, M: int, ngroups: int, sigma: float = 0.02):
     """f16 group scales |N(0, sigma)|, rounded to nearest-even binary16; raw bit patterns."""
     d = np.abs(g.normal(0.0, sigma, size=(M, ngroups))).astype(np.float16)

@@ -40,7 +40,7 @@ def test_library_exports(name):
 
 def test_abi_and_status_strings():
     L = qg.lib()
-    assert L.qg_abi_version() == 2
+    assert L.qg_abi_version() == 3
     assert L.qg_status_string(0) == b"QG_OK"
     assert L.qg_status_string(1) == b"QG_EINVAL"
     assert L.qg_status_string(2) == b"QG_ELAUNCH"
@@ -237,6 +237,20 @@ def test_einval_paths():
     assert L.qgemm_q2_batched_ws_bytes(17408, 5120, 128, 512) == 0
     _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, None, 0, None))
     _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, a16, need - 16, None))
+    # column prescale and the batched q8_row product of it
+    _einval(L.qact_silu_mul_pre(None, a16, None, a16, 1, 64, None))
+    _einval(L.qact_silu_mul_pre(a16, a16, None, a16, 0, 64, None))                     # rows < 1
+    _einval(L.qact_silu_mul_pre(a16, a16, None, a16, 4, 0, None))                      # n < 1
+    _einval(L.qact_silu_mul_pre(P(0x10002), a16, None, P(0x40000), 4, 64, None))      # g misaligned
+    _einval(L.qact_silu_mul_pre(P(0x20000), P(0x30000), None, P(0x20100), 4, 64, None))  # act partly over g
+    _einval(L.qact_silu_mul_pre(P(0x20000), P(0x30000), P(0x40040), P(0x40000), 4, 64, None))  # col inside act
+    gws = L.qgemm_q8row_batched_ws_bytes(256, 512)
+    _einval(L.qgemm_q8row_batched_silu(a16, a16, None, a16, None, a16, 256, 64, 512, 0, P(0x100000), gws, None))
+    _einval(L.qgemm_q8row_batched_silu(a16, a16, a16, P(0x20004), None, a16, 256, 64, 512, 0, P(0x100000), gws, None))
+    _einval(L.qgemm_q8row_batched_silu(a16, a16, a16, a16, P(0x20008), a16, 256, 64, 512, 0, P(0x100000), gws, None))
+    _einval(L.qgemm_q8row_batched_silu(a16, a16, a16, a16, None, a16, 256, 64, 512, 4, P(0x100000), gws, None))
+    _einval(L.qgemm_q8row_batched_silu(a16, a16, a16, a16, None, a16, 256, 64, 510, 0, P(0x100000), gws, None))
+    _einval(L.qgemm_q8row_batched_silu(a16, a16, a16, a16, None, a16, 256, 64, 512, 0, P(0x100000), gws - 1, None))
     # host repacks
     z = np.zeros(64, np.uint8)
     _einval(L.qg_repack_q8row(None, 4, 4, z.ctypes.data, 64))

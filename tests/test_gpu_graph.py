@@ -39,15 +39,24 @@ def test_graph_replays_match_eager():
     yb = torch.empty((256, 600), dtype=torch.float32, device=dev)
     wsb = torch.empty(qg.qgemm_q8row_batched_ws_bytes(256, 2048), dtype=torch.uint8, device=dev)
 
+    # column prescale and the batched product that forms it (second workspace)
+    gg, uu, cc = (torch.from_numpy(a).to(dev) for a in synth.gate_inputs(256, 2048, seed=34))
+    act = torch.empty((256, 2048), dtype=torch.float32, device=dev)
+    ys = torch.empty((256, 600), dtype=torch.float32, device=dev)
+    wss = torch.empty(qg.qgemm_q8row_batched_ws_bytes(256, 2048), dtype=torch.uint8, device=dev)
+
     def path():
         qg.qquant_act_i8(x_d, xq, sc, suma)
         qg.qgemv_q2(W2, xq, suma, sc, y2, ws2, split_k=4)
         W8.gemv(xs_d, y8)
         qg.qgemm_q8row_batched(Wb.packed, Wb.rs, xsb_d, yb, 256, 600, 2048, wsb, xs_limbs=0)
+        qg.qact_silu_mul_pre(gg, uu, cc, act)
+        qg.qgemm_q8row_batched_silu(Wb.packed, Wb.rs, gg, uu, cc, ys, 256, 600, 2048, wss, xs_limbs=0)
 
     path()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (xq, sc, suma, y2, y8, yb)]
+    outs = (xq, sc, suma, y2, y8, yb, act, ys)
+    ref = [t.clone() for t in outs]
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -59,13 +68,13 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(g):
         path()
     for rep in range(4):
-        for t in (xq, sc, suma, y2, y8, yb):   # eager work between replays
+        for t in outs:   # eager work between replays
             t.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, t, r in zip(("xq", "act_scale", "suma", "y_q2", "y_q8", "y_gemm"),
-                              (xq, sc, suma, y2, y8, yb), ref):
+        for name, t, r in zip(("xq", "act_scale", "suma", "y_q2", "y_q8", "y_gemm", "act", "y_gemm_silu"),
+                              outs, ref):
             assert torch.equal(t, r), f"replay {rep}: {name} differs from the eager result"
     assert np.isfinite(yb.cpu().numpy()).all()
 

@@ -77,6 +77,8 @@ _SIGS = {
     "qgemm_q2_batched_ws_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "qgemm_q8row_batched_ws_bytes": (_SZ, [_I64, _I64]),
     "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "qgemm_q8row_batched_silu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "qact_silu_mul_pre": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
 }
 
 _lib = None
@@ -269,6 +271,17 @@ def qquant_glu_i8_rows(g, u, kind, t, xq, act_scale, suma, stream=None):
         _dev(act_scale, torch.float32, "act_scale"), _dev(suma, torch.int32, "suma"), _stream(stream)))
 
 
+def qact_silu_mul_pre(g, u, col, act, stream=None):
+    """act = silu(g) * u * col (col None: no column field); g, u, act [n] or
+    [rows][n], col [n]; act may be g or u."""
+    import torch
+    n = g.shape[-1]
+    rows = g.numel() // n
+    _check("qact_silu_mul_pre", lib().qact_silu_mul_pre(
+        _dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), _dev(col, torch.float32, "col"),
+        _dev(act, torch.float32, "act"), rows, n, _stream(stream)))
+
+
 def qgemv_q2_ws_bytes(M, K, group, split_k=0) -> int:
     return lib().qgemv_q2_ws_bytes(M, K, group, split_k)
 
@@ -388,4 +401,16 @@ def qgemm_q8row_batched(qpacked, rs, xs, y, nb: int, M: int, K: int, ws, xs_limb
     _check("qgemm_q8row_batched", lib().qgemm_q8row_batched(
         _dev(qpacked, torch.uint8, "qpacked"), _dev(rs, torch.float32, "rs"),
         _dev(xs, torch.float32, "xs"), _dev(y, torch.float32, "y"), nb, M, K, xs_limbs,
+        _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def qgemm_q8row_batched_silu(qpacked, rs, g, u, col, y, nb: int, M: int, K: int, ws, xs_limbs: int = 0,
+                             stream=None):
+    """y[b,o] = rs[o] * sum_i q[o,i] act[b,i] with act = silu(g) * u * col formed in the
+    product's prep (g, u [nb][K]; col [K] or None); ws as for qgemm_q8row_batched."""
+    import torch
+    _check("qgemm_q8row_batched_silu", lib().qgemm_q8row_batched_silu(
+        _dev(qpacked, torch.uint8, "qpacked"), _dev(rs, torch.float32, "rs"),
+        _dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), _dev(col, torch.float32, "col"),
+        _dev(y, torch.float32, "y"), nb, M, K, xs_limbs,
         _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)))

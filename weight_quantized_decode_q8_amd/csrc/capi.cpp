@@ -57,7 +57,7 @@ const char *qg_status_string(qg_status s) {
 
 const char *qg_last_error(void) { return qg::g_msg; }
 
-int qg_abi_version(void) { return 2; }
+int qg_abi_version(void) { return 3; }
 
 qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
                       int64_t K, void *stream) {
@@ -319,24 +319,61 @@ size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K) {
   return qg::gemm_ws_layout(nb, K, &a, &b, &c);
 }
 
-qg_status qgemm_q8row_batched(const void *qpacked, const float *rs, const float *xs, float *y,
-                              int64_t nb, int64_t M, int64_t K, int xs_limbs, void *ws,
-                              size_t ws_bytes, void *stream) {
-  const char *fn = "qgemm_q8row_batched";
-  if (!qpacked || !rs || !xs || !y || !ws) return fail(QG_EINVAL, "%s: null pointer", fn);
+static qg_status gemm_common(const char *fn, const void *qpacked, const float *rs, const qg::GemmAct &act, float *y,
+                             int64_t nb, int64_t M, int64_t K, int xs_limbs, void *ws, size_t ws_bytes,
+                             void *stream) {
+  if (!qpacked || !rs || !y || !ws) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (nb < 1 || nb > (1 << 24)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
   if (M < 1 || M > (1LL << 31) - 256) return fail(QG_EINVAL, "%s: bad M=%lld", fn, (long long)M);
   if (K < 4 || K % 4 != 0 || K > (1 << 24)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 4", fn, (long long)K);
   if (nb * M > (1LL << 40) || qg::round_up(nb, 128) * qg::round_up(K, 64) * 3 > (1LL << 40))
     return fail(QG_EINVAL, "%s: problem too large", fn);
   if (xs_limbs != 0 && xs_limbs != 2 && xs_limbs != 3) return fail(QG_EINVAL, "%s: xs_limbs=%d must be 0, 2 or 3", fn, xs_limbs);
-  if (!aligned(qpacked, 16) || !aligned(xs, 16) || !aligned(ws, 256))
-    return fail(QG_EINVAL, "%s: qpacked and xs must be 16-byte aligned, ws 256-byte aligned", fn);
+  if (!aligned(qpacked, 16) || !aligned(ws, 256))
+    return fail(QG_EINVAL, "%s: qpacked must be 16-byte aligned, ws 256-byte aligned", fn);
   if (!aligned(rs, 4) || !aligned(y, 4)) return fail(QG_EINVAL, "%s: rs/y not 4-byte aligned", fn);
   const size_t need = qgemm_q8row_batched_ws_bytes(nb, K);
   if (ws_bytes < need) return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
-  return qg::launched(qg::launch_q8row_gemm(qpacked, rs, xs, y, (int)nb, (int)M, (int)K, xs_limbs, ws,
+  return qg::launched(qg::launch_q8row_gemm(qpacked, rs, act, y, (int)nb, (int)M, (int)K, xs_limbs, ws,
                                             (hipStream_t)stream), fn);
+}
+
+qg_status qgemm_q8row_batched(const void *qpacked, const float *rs, const float *xs, float *y,
+                              int64_t nb, int64_t M, int64_t K, int xs_limbs, void *ws,
+                              size_t ws_bytes, void *stream) {
+  const char *fn = "qgemm_q8row_batched";
+  if (!xs) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!aligned(xs, 16)) return fail(QG_EINVAL, "%s: xs must be 16-byte aligned", fn);
+  return gemm_common(fn, qpacked, rs, qg::GemmAct{xs, nullptr, nullptr, nullptr}, y, nb, M, K, xs_limbs, ws, ws_bytes,
+                     stream);
+}
+
+qg_status qgemm_q8row_batched_silu(const void *qpacked, const float *rs, const float *g, const float *u,
+                                   const float *col, float *y, int64_t nb, int64_t M, int64_t K, int xs_limbs,
+                                   void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "qgemm_q8row_batched_silu";
+  if (!g || !u) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!aligned(g, 16) || !aligned(u, 16) || (col && !aligned(col, 16)))
+    return fail(QG_EINVAL, "%s: g, u and col must be 16-byte aligned", fn);
+  return gemm_common(fn, qpacked, rs, qg::GemmAct{nullptr, g, u, col}, y, nb, M, K, xs_limbs, ws, ws_bytes, stream);
+}
+
+static bool spans_overlap(const float *a, int64_t na, const float *b, int64_t nb) { return a < b + nb && b < a + na; }
+
+qg_status qact_silu_mul_pre(const float *g, const float *u, const float *col, float *act, int64_t rows, int64_t n,
+                            void *stream) {
+  const char *fn = "qact_silu_mul_pre";
+  if (!g || !u || !act) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (rows < 1 || n < 1 || n > (1 << 30) || rows > (1LL << 40) / n)
+    return fail(QG_EINVAL, "%s: bad shape rows=%lld n=%lld", fn, (long long)rows, (long long)n);
+  if (!aligned(g, 4) || !aligned(u, 4) || !aligned(act, 4) || (col && !aligned(col, 4)))
+    return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  const int64_t total = rows * n;
+  if ((act != g && spans_overlap(act, total, g, total)) || (act != u && spans_overlap(act, total, u, total)))
+    return fail(QG_EINVAL, "%s: act must be g, u or a separate buffer", fn);
+  if (col && spans_overlap(act, total, col, n)) return fail(QG_EINVAL, "%s: act overlaps col", fn);
+  const bool vec = n % 4 == 0 && aligned(g, 16) && aligned(u, 16) && aligned(act, 16) && (!col || aligned(col, 16));
+  return qg::launched(qg::launch_silu_mul_pre(g, u, col, act, rows, (int)n, vec, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

@@ -17,6 +17,10 @@
 // rounding to binary32 equals a left-to-right sum's unless the two binary64
 // sums fall on opposite sides of a binary32 rounding boundary.
 //
+// The column prescale (cortiq pages, silu_mul_pre) forms the q8_row down
+// projection's f32 input act = silu(g) * u * col without quantising it:
+// one element-wise launch over [rows][n] values, col shared by the rows.
+//
 // Batches of token rows (the prefill form: the page's n_tok) run one
 // workgroup per row for the norm and the quantising step.
 // RMSNorm + quantiser is one workgroup of 1024 threads per vector, as the
@@ -26,6 +30,7 @@
 // for one CU at K = 17408, so it is two launches: the product over the
 // whole GPU (with per-workgroup maxima), then one workgroup quantising t.
 #include "qg_internal.h"
+#include "gate_rule.h"
 #include "quant_rule.h"
 
 namespace qg {
@@ -76,16 +81,6 @@ __global__ __launch_bounds__(kQuantThreads) void rmsnorm_quant_kernel(
   for (int i = tid; i < n4; i += kQuantThreads) m = fmaxf(m, abs_max4(mul4(scale4(x4[i], inv), w4[i])));
   const float qinv = scale_and_inverse(block_max(m, red_max), act_scale);
   for (int i = tid; i < n4; i += kQuantThreads) quant_quad(i, mul4(scale4(x4[i], inv), w4[i]), qinv, xq4, suma);
-}
-
-// exp(-g) rounded once to binary32.
-__device__ inline float exp_neg(float g) { return (float)exp(-(double)g); }
-
-template <int KIND>
-__device__ inline float glu1(float g, float u) {
-  const float den = __fadd_rn(1.0f, exp_neg(g));
-  if (KIND == 0) return __fmul_rn(__fdiv_rn(g, den), u);
-  return __fmul_rn(u, __fdiv_rn(1.0f, den));
 }
 
 template <int KIND>
@@ -146,7 +141,51 @@ __global__ __launch_bounds__(kQuantThreads) void quant_from_parts_kernel(const f
   for (int i = threadIdx.x; i < n4; i += kQuantThreads) quant_quad(i, t4[i], qinv, xq4, suma);
 }
 
+// Column prescale: act[r][i] = silu(g[r][i]) * u[r][i] * col[i] (col null:
+// 1).  Workgroup `blk` of the grid-stride loop takes chunk blk % nck of row
+// blk / nck, 256 consecutive elements (VEC: quads) of that row; act may be g
+// or u itself (each element is read and written by one thread).
+constexpr int kPreThreads = 256;
+
+template <bool VEC>
+__global__ __launch_bounds__(kPreThreads) void silu_mul_pre_kernel(const float *g, const float *u,
+                                                                   const float *__restrict__ col, float *act,
+                                                                   int64_t rows, int n, int nck) {
+  const int64_t nblk = rows * nck;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int64_t r = blk / nck;
+    const int i = (int)(blk % nck) * kPreThreads + threadIdx.x;  // element (quad) index in the row
+    if (VEC) {
+      const int n4 = n / 4;
+      if (i >= n4) continue;
+      const size_t k = (size_t)r * n4 + i;
+      const float4 gv = reinterpret_cast<const float4 *>(g)[k];
+      const float4 uv = reinterpret_cast<const float4 *>(u)[k];
+      const float4 cv = col ? reinterpret_cast<const float4 *>(col)[i] : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+      reinterpret_cast<float4 *>(act)[k] = make_float4(silu_pre1(gv.x, uv.x, cv.x), silu_pre1(gv.y, uv.y, cv.y),
+                                                       silu_pre1(gv.z, uv.z, cv.z), silu_pre1(gv.w, uv.w, cv.w));
+    } else {
+      if (i >= n) continue;
+      const size_t k = (size_t)r * n + i;
+      act[k] = silu_pre1(g[k], u[k], col ? col[i] : 1.0f);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_silu_mul_pre(const float *g, const float *u, const float *col, float *act, int64_t rows, int n,
+                               bool vec, hipStream_t stream) {
+  const int per = vec ? n / 4 : n;
+  const int nck = (per + kPreThreads - 1) / kPreThreads;
+  const int64_t nblk = rows * nck;
+  const int grid = (int)(nblk < 65536 ? nblk : 65536);
+  if (vec)
+    silu_mul_pre_kernel<true><<<grid, kPreThreads, 0, stream>>>(g, u, col, act, rows, n, nck);
+  else
+    silu_mul_pre_kernel<false><<<grid, kPreThreads, 0, stream>>>(g, u, col, act, rows, n, nck);
+  return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm_quant(const float *x, const float *w, int rows, int K, float eps, int8_t *xq,
                                 float *act_scale, int32_t *suma, hipStream_t stream) {

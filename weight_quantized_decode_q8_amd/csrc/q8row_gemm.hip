@@ -4,6 +4,10 @@
 // q8_mul_mm; cortiq-engine 0.3.7 gpu_metal.rs page, q8_matmat / q8_mul_mm):
 //     y[b, o] = rs[o] * sum_i q[o, i] * xs[b, i]
 // with xs [nb][K] and y [nb][M] row-major and the weights in the T64 image.
+// The silu form takes g, u [nb][K] and a column field col [K] instead of xs
+// and forms xs = silu(g) * u * col in the prep kernel by the rule of
+// gate_rule.h (cortiq pages, silu_mul_pre; the Metal page's q8_mul_mm_silu
+// forms silu(g) * u in its activation load the same way).
 //
 // Precision scheme (differs from the Metal page, whose fast kernel rounds
 // w*rs and xs to half): the weights stay exact int8 and the f32 activations
@@ -30,6 +34,7 @@
 // CU at the FFN width), operands moved global -> LDS directly through a
 // 4-stage ring, and a block order that puts the workgroups sharing one weight
 // tile on the same XCD (the same L2) at the same time.
+#include "gate_rule.h"
 #include "qg_internal.h"
 
 namespace qg {
@@ -56,16 +61,40 @@ constexpr int kR3 = 126 * 65536;  // largest |fixed-point value|, 3 limbs
 constexpr int kPrepThreads = 256;
 constexpr int kPrepHeld = 2;
 
-__device__ __forceinline__ void load_chunk(const float *__restrict__ row, int c, int K, bool live, float (&xv)[16]) {
+// The activation row a prep workgroup reads: xs row b, or (kSilu) the rows
+// b of g and u with the shared column field col (null: none), from which
+// act = silu(g) * u * col is formed by the rule of gate_rule.h.
+struct PrepRow {
+  const float *x;    // xs row, or g row
+  const float *u;    // u row (kSilu)
+  const float *col;  // column field or null (kSilu)
+};
+
+template <bool kSilu>
+__device__ __forceinline__ float act1(const PrepRow &r, int i) {
+  if (!kSilu) return r.x[i];
+  return silu_pre1(r.x[i], r.u[i], r.col ? r.col[i] : 1.0f);
+}
+
+template <bool kSilu>
+__device__ __forceinline__ void load_chunk(const PrepRow &r, int c, int K, bool live, float (&xv)[16]) {
   if (live && c * 16 + 16 <= K) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const float4 v = *reinterpret_cast<const float4 *>(row + c * 16 + 4 * q);
-      xv[4 * q] = v.x, xv[4 * q + 1] = v.y, xv[4 * q + 2] = v.z, xv[4 * q + 3] = v.w;
+      const int i = c * 16 + 4 * q;
+      const float4 v = *reinterpret_cast<const float4 *>(r.x + i);
+      if (kSilu) {
+        const float4 uv = *reinterpret_cast<const float4 *>(r.u + i);
+        const float4 cv = r.col ? *reinterpret_cast<const float4 *>(r.col + i) : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        xv[4 * q] = silu_pre1(v.x, uv.x, cv.x), xv[4 * q + 1] = silu_pre1(v.y, uv.y, cv.y);
+        xv[4 * q + 2] = silu_pre1(v.z, uv.z, cv.z), xv[4 * q + 3] = silu_pre1(v.w, uv.w, cv.w);
+      } else {
+        xv[4 * q] = v.x, xv[4 * q + 1] = v.y, xv[4 * q + 2] = v.z, xv[4 * q + 3] = v.w;
+      }
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; j++) xv[j] = (live && c * 16 + j < K) ? row[c * 16 + j] : 0.0f;
+    for (int j = 0; j < 16; j++) xv[j] = (live && c * 16 + j < K) ? act1<kSilu>(r, c * 16 + j) : 0.0f;
   }
 }
 
@@ -90,7 +119,10 @@ __device__ __forceinline__ void store_limbs(const float (&xv)[16], int e, i32x4 
   for (int l = 0; l < kLimbMax; l++) dst[l * limb_stride] = i32x4{lim[l][0], lim[l][1], lim[l][2], lim[l][3]};
 }
 
-__global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__restrict__ xs, int nb, int K,
+template <bool kSilu>
+__global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__restrict__ xs,
+                                                                 const float *__restrict__ u,
+                                                                 const float *__restrict__ col, int nb, int K,
                                                                  int nchunk, int nbt, int *__restrict__ xexp,
                                                                  int *__restrict__ need3, i32x4 *__restrict__ xl,
                                                                  i32x4 *__restrict__ zero_blk) {
@@ -103,7 +135,8 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
   const int b = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   if (blockIdx.x == 0 && tid < 64) zero_blk[tid] = i32x4{0, 0, 0, 0};
   const bool live = b < nb;
-  const float *row = xs + (size_t)(live ? b : 0) * K;
+  const size_t roff = (size_t)(live ? b : 0) * K;
+  const PrepRow row{xs + roff, kSilu ? u + roff : nullptr, col};
   const int nchunk_k = (K + 15) / 16;  // chunks holding any of the row
   const bool held = nchunk_k <= kPrepHeld * kPrepThreads;
 
@@ -111,7 +144,7 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
   float amax = 0.0f, asum = 0.0f;
   if (held) {
 #pragma unroll
-    for (int h = 0; h < kPrepHeld; h++) load_chunk(row, tid + h * kPrepThreads, K, live, xh[h]);
+    for (int h = 0; h < kPrepHeld; h++) load_chunk<kSilu>(row, tid + h * kPrepThreads, K, live, xh[h]);
 #pragma unroll
     for (int h = 0; h < kPrepHeld; h++)
 #pragma unroll
@@ -122,7 +155,7 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
   } else {
     for (int c = tid; c < nchunk_k; c += kPrepThreads) {
       float xv[16];
-      load_chunk(row, c, K, live, xv);
+      load_chunk<kSilu>(row, c, K, live, xv);
 #pragma unroll
       for (int j = 0; j < 16; j++) {
         amax = fmaxf(amax, fabsf(xv[j]));
@@ -171,7 +204,7 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
   } else {
     for (int c = tid; c < nchunk; c += kPrepThreads) {
       float xv[16];
-      load_chunk(row, c, K, live, xv);
+      load_chunk<kSilu>(row, c, K, live, xv);
       store_limbs(xv, e, dst + (size_t)c * 64, limb_stride);
     }
   }
@@ -473,7 +506,7 @@ size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need, 
   return *off_zero + 1024;
 }
 
-hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, float *y, int nb,
+hipError_t launch_q8row_gemm(const void *w, const float *rs, const GemmAct &act, float *y, int nb,
                              int M, int K, int limbs, void *ws, hipStream_t stream) {
   size_t off_exp, off_need, off_zero;
   gemm_ws_layout(nb, K, &off_exp, &off_need, &off_zero);
@@ -486,7 +519,12 @@ hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, fl
   int *need3 = reinterpret_cast<int *>(base + off_need);
   i32x4 *zero_blk = reinterpret_cast<i32x4 *>(base + off_zero);
 
-  gemm_prep_kernel<<<nbp, kPrepThreads, 0, stream>>>(xs, nb, K, nchunk, nbp / 64, xexp, need3, xl, zero_blk);
+  if (act.g)
+    gemm_prep_kernel<true><<<nbp, kPrepThreads, 0, stream>>>(act.g, act.u, act.col, nb, K, nchunk, nbp / 64, xexp,
+                                                             need3, xl, zero_blk);
+  else
+    gemm_prep_kernel<false><<<nbp, kPrepThreads, 0, stream>>>(act.xs, nullptr, nullptr, nb, K, nchunk, nbp / 64,
+                                                              xexp, need3, xl, zero_blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_ot = (M + kTM - 1) / kTM;

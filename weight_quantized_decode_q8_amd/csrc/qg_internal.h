@@ -34,6 +34,11 @@ hipError_t launch_rmsnorm_quant(const float *x, const float *w, int rows, int K,
 hipError_t launch_glu_quant(const float *g, const float *u, int rows, int K, int kind, float *t, int8_t *xq,
                             float *act_scale, int32_t *suma, hipStream_t stream);
 
+// Column prescale act = silu(g) * u * col over rows x n values (col null: no
+// column field); vec: n % 4 == 0 and every pointer 16-byte aligned.
+hipError_t launch_silu_mul_pre(const float *g, const float *u, const float *col, float *act, int64_t rows, int n,
+                               bool vec, hipStream_t stream);
+
 hipError_t launch_q8row_gemv(const void *qpacked, const float *rs, const float *xs,
                              float *y, int M, int K, hipStream_t stream);
 
@@ -80,7 +85,13 @@ hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, i
 
 // Batched q8_row GEMM: workspace layout (limbs, exponents, flags) and launch.
 size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need, size_t *off_zero);
-hipError_t launch_q8row_gemm(const void *w, const float *rs, const float *xs, float *y, int nb,
+// The activation rows of the batched q8_row product: xs itself, or (g non-
+// null) act = silu(g) * u * col formed in the prep kernel (col null: none).
+struct GemmAct {
+  const float *xs;
+  const float *g, *u, *col;
+};
+hipError_t launch_q8row_gemm(const void *w, const float *rs, const GemmAct &act, float *y, int nb,
                              int M, int K, int limbs, void *ws, hipStream_t stream);
 
 }  // namespace qg
