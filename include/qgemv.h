@@ -368,6 +368,30 @@ qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq,
 /* Bytes of workspace qgemm_q2_batched needs for this shape (0: none). */
 size_t qgemm_q2_batched_ws_bytes(int64_t M, int64_t K, int group, int64_t nb);
 
+/* Gate|up pair of the batched Q2 product  [QG, gemm_gpu_v4_dual]
+ *
+ *   y0[b, o] = act_scale[b] * sum_g d0(o, g) * sum_{i in g} (code0(o, i) - 1) * xq[b, i]
+ *   y1[b, o] = the same with the second matrix
+ *
+ * One launch over two matrices of the same M, K and group against the same
+ * token rows (the FFN's gate and up projections).  Each output is computed
+ * exactly as qgemm_q2_batched computes it (same tiles, same K split), so
+ * y0 and y1 are bit-identical to two qgemm_q2_batched calls without a
+ * residual.
+ * Arguments as qgemm_q2_batched, with w0, w1 the two matrices and y0, y1:
+ * device f32[nb][M] each (16-byte aligned, not overlapping); ws holds
+ * qgemm_q2_batched_dual_ws_bytes(M, K, group, nb) bytes (0: none needed).
+ * QG_EINVAL: as qgemm_q2_batched, or the matrices differ in M, K or group,
+ * or the outputs overlap.                                                 */
+qg_status qgemm_q2_batched_dual(const qg_q2_weight *w0, const qg_q2_weight *w1,
+                                const int8_t *xq, const int32_t *suma,
+                                const float *act_scale, float *y0, float *y1,
+                                int64_t nb, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* Bytes of workspace qgemm_q2_batched_dual needs (twice the one-matrix need). */
+size_t qgemm_q2_batched_dual_ws_bytes(int64_t M, int64_t K, int group, int64_t nb);
+
 /* ======================================================================
  * Batched prefill q8_row GEMM  [Q8, q8_matmat / q8_mul_mm]
  *

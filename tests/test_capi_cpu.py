@@ -40,7 +40,7 @@ def test_library_exports(name):
 
 def test_abi_and_status_strings():
     L = qg.lib()
-    assert L.qg_abi_version() == 3
+    assert L.qg_abi_version() == 4
     assert L.qg_status_string(0) == b"QG_OK"
     assert L.qg_status_string(1) == b"QG_EINVAL"
     assert L.qg_status_string(2) == b"QG_ELAUNCH"
@@ -237,6 +237,19 @@ def test_einval_paths():
     assert L.qgemm_q2_batched_ws_bytes(17408, 5120, 128, 512) == 0
     _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, None, 0, None))
     _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, a16, need - 16, None))
+    # gate|up pair of the batched Q2 product
+    w8b = qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 64, 0)
+    w8c = qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 128, 0)                                 # other group
+    _einval(L.qgemm_q2_batched_dual(ctypes.byref(w8), ctypes.byref(w8c), a16, a16, a16, P(0x50000), P(0x60000), 4, None, 0, None))
+    _einval(L.qgemm_q2_batched_dual(ctypes.byref(w8), ctypes.byref(w8b), a16, a16, a16, P(0x50000), None, 4, None, 0, None))
+    _einval(L.qgemm_q2_batched_dual(ctypes.byref(w8), ctypes.byref(w8b), a16, a16, a16, P(0x50000), P(0x50100), 4, None, 0, None))  # overlap
+    _einval(L.qgemm_q2_batched_dual(ctypes.byref(w8), ctypes.byref(w8b), a16, a16, a16, P(0x50000), P(0x60004), 4, None, 0, None))  # misaligned
+    _einval(L.qgemm_q2_batched_dual(ctypes.byref(w8), ctypes.byref(w8b), a16, a16, a16, P(0x50000), P(0x60000), 0, None, 0, None))  # nb < 1
+    assert L.qgemm_q2_batched_dual_ws_bytes(5120, 17408, 128, 512) == 2 * L.qgemm_q2_batched_ws_bytes(5120, 17408, 128, 512)
+    wd0 = qg.qg_q2_weight(0x10000, 0x20000, 5120, 17408, 128, 0)
+    wd1 = qg.qg_q2_weight(0x30000, 0x40000, 5120, 17408, 128, 0)
+    _einval(L.qgemm_q2_batched_dual(ctypes.byref(wd0), ctypes.byref(wd1), a16, a16, a16, P(0x1000000), P(0x9000000), 512,
+                                    a16, L.qgemm_q2_batched_ws_bytes(5120, 17408, 128, 512), None))     # ws holds one matrix only
     # column prescale and the batched q8_row product of it
     _einval(L.qact_silu_mul_pre(None, a16, None, a16, 1, 64, None))
     _einval(L.qact_silu_mul_pre(a16, a16, None, a16, 0, 64, None))                     # rows < 1

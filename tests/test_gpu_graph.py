@@ -163,13 +163,19 @@ def test_graph_replays_prefill_forms():
     ws2 = torch.empty(max(1, qg.qgemm_q2_batched_ws_bytes(D, F, 64, nb)), dtype=torch.uint8, device=dev)
     assert qg.qgemm_q2_batched_ws_bytes(D, F, 64, nb) > 0
 
+    Wu = qg.Q2Weight.from_blocks(synth.q2_inputs(F, D, 64, seed=54)[0], F, D, 64)
+    U = torch.empty((nb, F), device=dev)
+    G2 = torch.empty((nb, F), device=dev)
+    ws3 = torch.empty(max(1, qg.qgemm_q2_batched_dual_ws_bytes(F, D, 64, nb)), dtype=torch.uint8, device=dev)
+
     def path():
         qg.qquant_rmsnorm_i8_rows(H, nw, 1e-6, xq1, sc1, su1)
         qg.qgemm_q2_batched(Wg, xq1, su1, sc1, G, ws=ws1)
+        qg.qgemm_q2_batched_dual(Wg, Wu, xq1, su1, sc1, G2, U, ws=ws3)
         qg.qquant_glu_i8_rows(G, G, qg.QG_GLU_SIGMOID, G, xq2, sc2, su2)
         qg.qgemm_q2_batched(Wd, xq2, su2, sc2, Hout, accum=H, ws=ws2)
 
-    outs = (xq1, sc1, su1, G, xq2, sc2, su2, Hout)
+    outs = (xq1, sc1, su1, G, xq2, sc2, su2, Hout, G2, U)
     path()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]

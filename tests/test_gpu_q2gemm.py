@@ -138,3 +138,37 @@ def test_q2_gemm_token_rows_match_gemv_bound():
     for b in range(nb):
         yr, mr = oracle.q2_gemv(blob, M, K, group, xq[b], sc[b])
         within(y[b], yr, mr, what=f"token {b}")
+
+
+@pytest.mark.parametrize("nb,M,K,group", [(40, 300, 1024, 128), (130, 600, 2048, 64), (512, 17408, 5120, 128)])
+def test_q2_gemm_dual_equals_two_calls(nb, M, K, group):
+    """The gate|up pair launch (the page's gemm_gpu_v4_dual) gives both outputs
+    bit for bit as two one-matrix launches, with and without a K split; the
+    small shapes are also held to the oracle's bound."""
+    torch = _torch()
+    m = qg()
+    b0, _ = synth.q2_inputs(M, K, group, seed=7000 + M)
+    b1, _ = synth.q2_inputs(M, K, group, seed=7001 + M)
+    W0 = m.Q2Weight.from_blocks(b0, M, K, group)
+    W1 = m.Q2Weight.from_blocks(b1, M, K, group)
+    X = token_rows(nb, K, 7002 + nb)
+    xq, sc, suma = gpu_quant_rows(X)
+    n1 = m.qgemm_q2_batched_ws_bytes(M, K, group, nb)
+    n2 = m.qgemm_q2_batched_dual_ws_bytes(M, K, group, nb)
+    assert n2 == 2 * n1
+    ws1 = torch.empty(n1, dtype=torch.uint8, device="cuda") if n1 else None
+    ws2 = torch.empty(n2, dtype=torch.uint8, device="cuda") if n2 else None
+    y0 = torch.full((nb, M), float("nan"), device="cuda")
+    y1 = torch.full((nb, M), float("nan"), device="cuda")
+    m.qgemm_q2_batched_dual(W0, W1, xq, suma, sc, y0, y1, ws=ws2)
+    r0 = torch.full((nb, M), float("nan"), device="cuda")
+    r1 = torch.full((nb, M), float("nan"), device="cuda")
+    m.qgemm_q2_batched(W0, xq, suma, sc, r0, ws=ws1)
+    m.qgemm_q2_batched(W1, xq, suma, sc, r1, ws=ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, r0) and torch.equal(y1, r1), f"pair launch differs ({nb}x{M}x{K} g{group})"
+    if nb * M <= 200000:
+        xq_h, sc_h = host(xq), host(sc)
+        for blob, out in ((b0, y0), (b1, y1)):
+            yref, mass = oracle.q2_gemm(blob, M, K, group, xq_h, sc_h)
+            within(host(out).reshape(-1), yref.reshape(-1), mass.reshape(-1), what=f"pair {nb}x{M}x{K} g{group}")

@@ -75,6 +75,9 @@ _SIGS = {
     "qgemv_q2_batch": (_I, [ctypes.POINTER(qg_q2_job), _I, _P]),
     "qgemm_q2_batched": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "qgemm_q2_batched_ws_bytes": (_SZ, [_I64, _I64, _I, _I64]),
+    "qgemm_q2_batched_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P,
+                                   _I64, _P, _SZ, _P]),
+    "qgemm_q2_batched_dual_ws_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "qgemm_q8row_batched_ws_bytes": (_SZ, [_I64, _I64]),
     "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "qgemm_q8row_batched_silu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
@@ -388,6 +391,22 @@ def qgemm_q2_batched(w: Q2Weight, xq, suma, act_scale, y, accum=None, ws=None, s
         _dev(act_scale, torch.float32, "act_scale"), _dev(accum, torch.float32, "accum"),
         _dev(y, torch.float32, "y"), nb, _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(),
         _stream(stream)))
+
+
+def qgemm_q2_batched_dual_ws_bytes(M, K, group, nb) -> int:
+    return lib().qgemm_q2_batched_dual_ws_bytes(M, K, group, nb)
+
+
+def qgemm_q2_batched_dual(w0: Q2Weight, w1: Q2Weight, xq, suma, act_scale, y0, y1, ws=None, stream=None):
+    """Gate|up pair of the batched Q2 product in one launch: y0, y1 [nb][M] from w0, w1
+    (same shape) against the same token rows; bit-identical to two qgemm_q2_batched calls."""
+    import torch
+    d0, d1 = w0.desc(), w1.desc()
+    nb = act_scale.numel()
+    _check("qgemm_q2_batched_dual", lib().qgemm_q2_batched_dual(
+        ctypes.byref(d0), ctypes.byref(d1), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(y0, torch.float32, "y0"), _dev(y1, torch.float32, "y1"),
+        nb, _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 # ------------------------------------------------------ batched q8_row GEMM --

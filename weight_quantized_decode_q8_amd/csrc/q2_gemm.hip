@@ -30,6 +30,10 @@
 //    the token pieces are stored with an XOR swizzle so the 128-bit fragment
 //    reads hit distinct LDS banks; workgroups sharing a weight tile are
 //    dispatched to one XCD.
+//  - a pair launch (the page's gemm_gpu_v4_dual: gate and up against the same
+//    token rows) runs both matrices' workgroups in one grid, blockIdx.y
+//    choosing the matrix; every output is computed exactly as in a
+//    one-matrix launch (same tiles, same K split);
 //  - shapes whose tiles cannot fill the CUs (the 5120-row down projection:
 //    76 tiles) split K into f32 partials [S][nb][M], added in fixed order by
 //    a second kernel; (row tile, split) pairs are spread evenly over XCDs.
@@ -67,12 +71,27 @@ __device__ inline int b_slot(int t, int k) { return t * 4 + (k ^ ((t >> 2) & 3))
 
 __device__ inline float half_bits_to_f32(unsigned short h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// The two weight matrices of a pair launch (gate and up against one set of
+// token rows); a one-matrix launch uses entry 0 only.
+struct Q2Pair {
+  const i32x4 *codes[2];
+  const unsigned short *scales[2];
+  float *y[2];
+};
+
 template <int UPG>
 __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
-    const i32x4 *__restrict__ codes, const unsigned short *__restrict__ scales, const int8_t *__restrict__ xq,
-    const int *__restrict__ suma, const float *__restrict__ act_scale, const float *accum, float *y, int nb, int M,
-    int K, int n_ot, int n_bt, int n_split, float *__restrict__ part) {
+    Q2Pair pair_args, const int8_t *__restrict__ xq, const int *__restrict__ suma,
+    const float *__restrict__ act_scale, const float *accum, int nb, int M, int K, int n_ot, int n_bt, int n_split,
+    float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
+  // Matrix of this workgroup (blockIdx.y); its partials follow the first
+  // matrix's [S][nb][M] block.
+  const int job = blockIdx.y;
+  const i32x4 *__restrict__ codes = job ? pair_args.codes[1] : pair_args.codes[0];
+  const unsigned short *__restrict__ scales = job ? pair_args.scales[1] : pair_args.scales[0];
+  float *y = job ? pair_args.y[1] : pair_args.y[0];
+  part += (size_t)job * n_split * nb * M;
 
   // Block order: a weight tile is a (row tile, K split) pair; its n_bt
   // workgroups get ids 8 apart, so the round-robin dispatch over the 8 XCDs
@@ -307,9 +326,13 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
 
 // y[b, o] = act_scale[b] * sum_s part[s][b][o] (+ accum[b, o]), the splits
 // added in fixed order.
+// blockIdx.y selects the matrix of a pair launch: its partials start at
+// part + y * S * n and its output is y0 or y1.
 __global__ __launch_bounds__(256) void q2_gemm_reduce_kernel(const float *__restrict__ part, int S, size_t n, int M,
                                                             const float *__restrict__ act_scale, const float *accum,
-                                                            float *y) {
+                                                            float *y0, float *y1) {
+  float *y = blockIdx.y ? y1 : y0;
+  part += (size_t)blockIdx.y * S * n;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.0f;
@@ -334,22 +357,29 @@ int q2_gemm_split(int64_t M, int64_t K, int group, int64_t nb) {
 
 hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, int group, const int8_t *xq,
                           const int32_t *suma, const float *act_scale, const float *accum, float *y, int nb,
-                          float *part, hipStream_t stream) {
+                          float *part, hipStream_t stream, const void *codes1, const void *scales1, float *y1) {
   const int n_ot = (M + kTM - 1) / kTM;
   const int n_bt = (nb + kTN - 1) / kTN;
   const int S = q2_gemm_split(M, K, group, nb);
-  const int grid = (n_ot * S + 7) / 8 * 8 * n_bt;
-  const i32x4 *c = reinterpret_cast<const i32x4 *>(codes);
-  const unsigned short *s = reinterpret_cast<const unsigned short *>(scales);
+  const int njobs = codes1 ? 2 : 1;
+  const dim3 grid((n_ot * S + 7) / 8 * 8 * n_bt, njobs);
+  Q2Pair pa{};
+  pa.codes[0] = reinterpret_cast<const i32x4 *>(codes);
+  pa.scales[0] = reinterpret_cast<const unsigned short *>(scales);
+  pa.y[0] = y;
+  pa.codes[1] = codes1 ? reinterpret_cast<const i32x4 *>(codes1) : pa.codes[0];
+  pa.scales[1] = scales1 ? reinterpret_cast<const unsigned short *>(scales1) : pa.scales[0];
+  pa.y[1] = y1 ? y1 : y;
   const int *sa = reinterpret_cast<const int *>(suma);
   if (group == 64)
-    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, S, part);
+    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(pa, xq, sa, act_scale, accum, nb, M, K, n_ot, n_bt, S, part);
   else
-    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(c, s, xq, sa, act_scale, accum, y, nb, M, K, n_ot, n_bt, S, part);
+    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(pa, xq, sa, act_scale, accum, nb, M, K, n_ot, n_bt, S, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const size_t n = (size_t)nb * M;
-  q2_gemm_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, S, n, M, act_scale, accum, y);
+  const dim3 rgrid((unsigned)((n + 255) / 256), njobs);
+  q2_gemm_reduce_kernel<<<rgrid, 256, 0, stream>>>(part, S, n, M, act_scale, accum, pa.y[0], pa.y[1]);
   return hipGetLastError();
 }
 

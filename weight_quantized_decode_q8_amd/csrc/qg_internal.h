@@ -79,9 +79,12 @@ int q2_auto_split(int64_t M, int64_t K, int group);
 // Batched Q2 product over nb token rows (int8 MFMA), y [nb][M] token-major.
 // part: [S][nb][M] f32 partials when q2_gemm_split(...) = S > 1, else unused.
 int q2_gemm_split(int64_t M, int64_t K, int group, int64_t nb);
+// codes1 non-null: a pair launch, the second matrix (same M, K, group) into
+// y1 with its partials after the first's ([2][S][nb][M]); accum then null.
 hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, int group, const int8_t *xq,
                           const int32_t *suma, const float *act_scale, const float *accum, float *y, int nb,
-                          float *part, hipStream_t stream);
+                          float *part, hipStream_t stream, const void *codes1 = nullptr,
+                          const void *scales1 = nullptr, float *y1 = nullptr);
 
 // Batched q8_row GEMM: workspace layout (limbs, exponents, flags) and launch.
 size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need, size_t *off_zero);
