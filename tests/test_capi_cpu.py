@@ -275,3 +275,13 @@ def test_einval_paths():
 def test_binding_raises_on_error():
     with pytest.raises(qg.QGError):
         qg.repack_q2(np.zeros(10, np.uint8), 1, 64, 64)
+
+
+def test_c_client_builds_against_the_header(tmp_path):
+    """A plain C program (no Python, no framework) compiles with -Wall -Werror
+    against include/qgemv.h and links against libqgemv.so and the HIP runtime."""
+    import sys
+    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi"))
+    import build_client
+    out = build_client.build(str(tmp_path / "qgemv_c_client"))
+    assert os.path.exists(out)
