@@ -263,7 +263,7 @@ int qgemv_q2_auto_split(int64_t M, int64_t K, int group);
  *   split_k:   0 = auto, else 1..16 contiguous ranges of 64-wide units.
  * The int32 unit dots are exact; y is accumulated in f32 from d * dot.
  * QG_EINVAL: null pointer, bad weight struct, split_k out of range,
- * workspace too small.                                                    */
+ * workspace too small or overlapping y (or a residual).                   */
 qg_status qgemv_q2(const qg_q2_weight *w, const int8_t *xq,
                    const int32_t *suma, const float *act_scale, float *y,
                    void *ws, size_t ws_bytes, int split_k, void *stream);
@@ -359,7 +359,7 @@ qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream);
  * the groups in f32 (split partials added in fixed order), then act_scale[b]
  * and the residual are applied with one binary32 rounding each.
  * QG_EINVAL: null pointer, bad weight struct, nb < 1, misaligned pointer,
- * accum partly overlapping y, workspace too small.                         */
+ * accum partly overlapping y, workspace too small or overlapping y/accum. */
 qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq,
                            const int32_t *suma, const float *act_scale,
                            const float *accum, float *y, int64_t nb,
@@ -382,7 +382,7 @@ size_t qgemm_q2_batched_ws_bytes(int64_t M, int64_t K, int group, int64_t nb);
  * device f32[nb][M] each (16-byte aligned, not overlapping); ws holds
  * qgemm_q2_batched_dual_ws_bytes(M, K, group, nb) bytes (0: none needed).
  * QG_EINVAL: as qgemm_q2_batched, or the matrices differ in M, K or group,
- * or the outputs overlap.                                                 */
+ * or the outputs overlap (each other or the workspace).                   */
 qg_status qgemm_q2_batched_dual(const qg_q2_weight *w0, const qg_q2_weight *w1,
                                 const int8_t *xq, const int32_t *suma,
                                 const float *act_scale, float *y0, float *y1,
@@ -417,7 +417,7 @@ size_t qgemm_q2_batched_dual_ws_bytes(int64_t M, int64_t K, int group, int64_t n
  *       (nb, K) bytes; holds the limbs and per-row exponents; contents on
  *       entry are ignored.
  * QG_EINVAL: null pointer, nb < 1, M < 1, K < 4 or K % 4 != 0, xs_limbs
- * not 0/2/3, misalignment, workspace too small.                          */
+ * not 0/2/3, misalignment, workspace too small or overlapping y or xs.   */
 size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K);
 
 qg_status qgemm_q8row_batched(const void *qpacked, const float *rs,

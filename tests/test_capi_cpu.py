@@ -250,6 +250,15 @@ def test_einval_paths():
     wd1 = qg.qg_q2_weight(0x30000, 0x40000, 5120, 17408, 128, 0)
     _einval(L.qgemm_q2_batched_dual(ctypes.byref(wd0), ctypes.byref(wd1), a16, a16, a16, P(0x1000000), P(0x9000000), 512,
                                     a16, L.qgemm_q2_batched_ws_bytes(5120, 17408, 128, 512), None))     # ws holds one matrix only
+    # a workspace overlapping an output or an input
+    w2s = qg.qg_q2_weight(0x10000, 0x20000, 5120, 17408, 128, 0)
+    nws = L.qgemv_q2_ws_bytes(5120, 17408, 128, 4)
+    _einval(L.qgemv_q2(ctypes.byref(w2s), a16, a16, a16, P(0x200000), P(0x200000 + 4 * 5120 - 16), nws, 4, None))
+    nwb = L.qgemm_q2_batched_ws_bytes(5120, 17408, 128, 512)
+    _einval(L.qgemm_q2_batched(ctypes.byref(w2s), a16, a16, a16, None, P(0x1000000), 512, P(0x1000000 + 4096), nwb, None))
+    gws2 = L.qgemm_q8row_batched_ws_bytes(256, 512)
+    _einval(L.qgemm_q8row_batched(a16, a16, P(0x800000), P(0x400000), 256, 64, 512, 0, P(0x800000 - 256), gws2, None))
+    _einval(L.qgemm_q8row_batched(a16, a16, P(0x800000), P(0x400000), 256, 64, 512, 0, P(0x400000), gws2, None))
     # column prescale and the batched q8_row product of it
     _einval(L.qact_silu_mul_pre(None, a16, None, a16, 1, 64, None))
     _einval(L.qact_silu_mul_pre(a16, a16, None, a16, 0, 64, None))                     # rows < 1

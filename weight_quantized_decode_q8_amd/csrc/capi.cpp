@@ -163,6 +163,13 @@ size_t qgemv_q2_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
 
 static bool overlap(const float *a, const float *b, int64_t n) { return a < b + n && b < a + n; }
 
+// Byte ranges [a, a + na) and [b, b + nb) share a byte (null b: never).
+static bool bytes_overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 static qg_status q2_common(const char *fn, const qg_q2_weight *w, const qg_q2_weight *w1, const int8_t *xq,
                            const int32_t *suma, const float *act_scale, const float *accum, float *y,
                            float *y1, int32_t *dots, void *ws, size_t ws_bytes, int split_k, void *stream) {
@@ -191,6 +198,10 @@ static qg_status q2_common(const char *fn, const qg_q2_weight *w, const qg_q2_we
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed for split %d", fn, ws ? ws_bytes : (size_t)0, need, S);
   if (need > 0 && !aligned(ws, 4)) return fail(QG_EINVAL, "%s: workspace not 4-byte aligned", fn);
+  const size_t ybytes = (size_t)w->M * sizeof(float);
+  if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, y1, ybytes) ||
+                   bytes_overlap(ws, need, accum, ybytes)))
+    return fail(QG_EINVAL, "%s: workspace overlaps an output or the residual", fn);
   qg::Q2Call call{};
   call.codes[0] = w->codes;
   call.scales[0] = w->scales;
@@ -308,6 +319,9 @@ qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq, const int32_
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws ? ws_bytes : (size_t)0, need);
   if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
+  const size_t ybytes = (size_t)nb * w->M * sizeof(float);
+  if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, accum, ybytes)))
+    return fail(QG_EINVAL, "%s: workspace overlaps the output or the residual", fn);
   return qg::launched(qg::launch_q2_gemm(w->codes, w->scales, (int)w->M, (int)w->K, w->group, xq, suma, act_scale,
                                          accum, y, (int)nb, static_cast<float *>(ws), (hipStream_t)stream),
                       fn);
@@ -339,6 +353,9 @@ qg_status qgemm_q2_batched_dual(const qg_q2_weight *w0, const qg_q2_weight *w1, 
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws ? ws_bytes : (size_t)0, need);
   if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
+  const size_t ybytes = (size_t)nb * w0->M * sizeof(float);
+  if (need > 0 && (bytes_overlap(ws, need, y0, ybytes) || bytes_overlap(ws, need, y1, ybytes)))
+    return fail(QG_EINVAL, "%s: workspace overlaps an output", fn);
   return qg::launched(qg::launch_q2_gemm(w0->codes, w0->scales, (int)w0->M, (int)w0->K, w0->group, xq, suma,
                                          act_scale, nullptr, y0, (int)nb, static_cast<float *>(ws),
                                          (hipStream_t)stream, w1->codes, w1->scales, y1),
@@ -366,6 +383,11 @@ static qg_status gemm_common(const char *fn, const void *qpacked, const float *r
   if (!aligned(rs, 4) || !aligned(y, 4)) return fail(QG_EINVAL, "%s: rs/y not 4-byte aligned", fn);
   const size_t need = qgemm_q8row_batched_ws_bytes(nb, K);
   if (ws_bytes < need) return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  const size_t abytes = (size_t)nb * K * sizeof(float);
+  if (bytes_overlap(ws, need, y, (size_t)nb * M * sizeof(float)) || bytes_overlap(ws, need, act.xs, abytes) ||
+      bytes_overlap(ws, need, act.g, abytes) || bytes_overlap(ws, need, act.u, abytes) ||
+      bytes_overlap(ws, need, act.col, (size_t)K * sizeof(float)))
+    return fail(QG_EINVAL, "%s: workspace overlaps the output or an activation input", fn);
   return qg::launched(qg::launch_q8row_gemm(qpacked, rs, act, y, (int)nb, (int)M, (int)K, xs_limbs, ws,
                                             (hipStream_t)stream), fn);
 }
