@@ -416,7 +416,9 @@ size_t qgemm_q2_batched_dual_ws_bytes(int64_t M, int64_t K, int group, int64_t n
  *   ws: device workspace, 256-byte aligned, >= qgemm_q8row_batched_ws_bytes
  *       (nb, K) bytes; holds the limbs and per-row exponents; contents on
  *       entry are ignored.
- * QG_EINVAL: null pointer, nb < 1, M < 1, K < 4 or K % 4 != 0, xs_limbs
+ * K is at most 131068: each limb's exact int32 sum over K, at most
+ * 128 * 128 * K in magnitude, then stays below 2^31.
+ * QG_EINVAL: null pointer, nb < 1, M < 1, K < 4, K % 4 != 0, K > 131068, xs_limbs
  * not 0/2/3, misalignment, workspace too small or overlapping y or xs.   */
 size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K);
 

@@ -250,6 +250,9 @@ def test_einval_paths():
     wd1 = qg.qg_q2_weight(0x30000, 0x40000, 5120, 17408, 128, 0)
     _einval(L.qgemm_q2_batched_dual(ctypes.byref(wd0), ctypes.byref(wd1), a16, a16, a16, P(0x1000000), P(0x9000000), 512,
                                     a16, L.qgemm_q2_batched_ws_bytes(5120, 17408, 128, 512), None))     # ws holds one matrix only
+    # the batched q8_row product's K limit (int32 limb sums)
+    assert L.qgemm_q8row_batched_ws_bytes(4, 131068) > 0 and L.qgemm_q8row_batched_ws_bytes(4, 131072) == 0
+    _einval(L.qgemm_q8row_batched(a16, a16, a16, a16, 4, 64, 131072, 0, P(0x100000), 1 << 30, None))
     # a workspace overlapping an output or an input
     w2s = qg.qg_q2_weight(0x10000, 0x20000, 5120, 17408, 128, 0)
     nws = L.qgemv_q2_ws_bytes(5120, 17408, 128, 4)

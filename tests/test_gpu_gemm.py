@@ -134,3 +134,22 @@ def test_gemm_workspace_too_small_is_rejected():
     ws = torch.empty(256, dtype=torch.uint8, device="cuda")
     with pytest.raises(m.QGError):
         m.qgemm_q8row_batched(W.packed, W.rs, x, y, 4, 64, 64, ws)
+
+
+def test_gemm_largest_k_extreme_values():
+    """K = 131068, the largest the entry point takes: every weight -128 (or
+    127) against activation rows whose limbs reach the limb range's ends, so
+    each limb's int32 sum comes close to 2^31 without wrapping."""
+    nb, M, K = 4, 64, 131068
+    r = synth.rng_for(97)
+    q = r.integers(-127, 128, (M, K), dtype=np.int8)
+    q[0, :] = -128
+    q[1, :] = 127
+    rs = r.uniform(0.001, 0.01, M).astype(np.float32)
+    xs = r.standard_normal((nb, K)).astype(np.float32)
+    xs[0, :] = -3.0                                   # a constant row: top limb -126 everywhere
+    xs[1, :] = np.where(np.arange(K) % 2 == 0, 3.0, -3.0 + 2.0 ** -14).astype(np.float32)
+    for limbs in (0, 3):
+        y = gpu_gemm(q, rs, xs, limbs)
+        yref, mass = oracle.q8row_gemm(q, rs, xs)
+        within(y, yref, mass, f"largest K, limbs={limbs}")

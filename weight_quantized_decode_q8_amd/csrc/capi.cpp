@@ -363,7 +363,7 @@ qg_status qgemm_q2_batched_dual(const qg_q2_weight *w0, const qg_q2_weight *w1, 
 }
 
 size_t qgemm_q8row_batched_ws_bytes(int64_t nb, int64_t K) {
-  if (nb < 1 || K < 4 || K % 4 != 0) return 0;
+  if (nb < 1 || K < 4 || K % 4 != 0 || K > qg::kGemmMaxK) return 0;
   size_t a, b, c;
   return qg::gemm_ws_layout(nb, K, &a, &b, &c);
 }
@@ -374,7 +374,9 @@ static qg_status gemm_common(const char *fn, const void *qpacked, const float *r
   if (!qpacked || !rs || !y || !ws) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (nb < 1 || nb > (1 << 24)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
   if (M < 1 || M > (1LL << 31) - 256) return fail(QG_EINVAL, "%s: bad M=%lld", fn, (long long)M);
-  if (K < 4 || K % 4 != 0 || K > (1 << 24)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 4", fn, (long long)K);
+  if (K < 4 || K % 4 != 0) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 4", fn, (long long)K);
+  // Each limb's int32 sum over K is at most 128 * 128 * K in magnitude.
+  if (K > qg::kGemmMaxK) return fail(QG_EINVAL, "%s: K=%lld above %d (int32 limb sums)", fn, (long long)K, qg::kGemmMaxK);
   if (nb * M > (1LL << 40) || qg::round_up(nb, 128) * qg::round_up(K, 64) * 3 > (1LL << 40))
     return fail(QG_EINVAL, "%s: problem too large", fn);
   if (xs_limbs != 0 && xs_limbs != 2 && xs_limbs != 3) return fail(QG_EINVAL, "%s: xs_limbs=%d must be 0, 2 or 3", fn, xs_limbs);

@@ -86,6 +86,10 @@ hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, i
                           float *part, hipStream_t stream, const void *codes1 = nullptr,
                           const void *scales1 = nullptr, float *y1 = nullptr);
 
+// Batched q8_row GEMM: largest K (a multiple of 4) whose int32 limb sums
+// cannot overflow, |sum_i q_i * limb_i| <= 128 * 128 * K < 2^31.
+constexpr int kGemmMaxK = 131068;
+
 // Batched q8_row GEMM: workspace layout (limbs, exponents, flags) and launch.
 size_t gemm_ws_layout(int64_t nb, int64_t K, size_t *off_exp, size_t *off_need, size_t *off_zero);
 // The activation rows of the batched q8_row product: xs itself, or (g non-
