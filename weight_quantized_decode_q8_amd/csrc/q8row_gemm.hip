@@ -59,7 +59,10 @@ constexpr int kR3 = 126 * 65536;  // largest |fixed-point value|, 3 limbs
 // two steps; longer rows are read a second time (from L2).  Chunks past K
 // are written as zeros.
 constexpr int kPrepThreads = 256;
-constexpr int kPrepHeld = 2;
+// Chunks per thread held in registers: 2 for rows up to 8192 values, 5 up
+// to 20480 (measured: 5 is 14 % faster at K = 17408 and 25 % slower at
+// K = 5120, where its idle unrolled slots cost more than the second read saves).
+constexpr int kPrepHeldShort = 2, kPrepHeldLong = 5;
 
 // The activation row a prep workgroup reads: xs row b, or (kSilu) the rows
 // b of g and u with the shared column field col (null: none), from which
@@ -119,7 +122,7 @@ __device__ __forceinline__ void store_limbs(const float (&xv)[16], int e, i32x4 
   for (int l = 0; l < kLimbMax; l++) dst[l * limb_stride] = i32x4{lim[l][0], lim[l][1], lim[l][2], lim[l][3]};
 }
 
-template <bool kSilu>
+template <bool kSilu, int kPrepHeld>
 __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__restrict__ xs,
                                                                  const float *__restrict__ u,
                                                                  const float *__restrict__ col, int nb, int K,
@@ -521,12 +524,17 @@ hipError_t launch_q8row_gemm(const void *w, const float *rs, const GemmAct &act,
   int *need3 = reinterpret_cast<int *>(base + off_need);
   i32x4 *zero_blk = reinterpret_cast<i32x4 *>(base + off_zero);
 
-  if (act.g)
-    gemm_prep_kernel<true><<<nbp, kPrepThreads, 0, stream>>>(act.g, act.u, act.col, nb, K, nchunk, nbp / 64, xexp,
-                                                             need3, xl, zero_blk);
-  else
-    gemm_prep_kernel<false><<<nbp, kPrepThreads, 0, stream>>>(act.xs, nullptr, nullptr, nb, K, nchunk, nbp / 64,
-                                                              xexp, need3, xl, zero_blk);
+  const bool long_rows = (K + 15) / 16 > kPrepHeldShort * kPrepThreads;
+#define QG_PREP(S, H, X, U, C) \
+  gemm_prep_kernel<S, H><<<nbp, kPrepThreads, 0, stream>>>(X, U, C, nb, K, nchunk, nbp / 64, xexp, need3, xl, zero_blk)
+  if (act.g) {
+    if (long_rows) QG_PREP(true, kPrepHeldLong, act.g, act.u, act.col);
+    else QG_PREP(true, kPrepHeldShort, act.g, act.u, act.col);
+  } else {
+    if (long_rows) QG_PREP(false, kPrepHeldLong, act.xs, nullptr, nullptr);
+    else QG_PREP(false, kPrepHeldShort, act.xs, nullptr, nullptr);
+  }
+#undef QG_PREP
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_ot = (M + kTM - 1) / kTM;
