@@ -1,0 +1,106 @@
+"""A seeded sweep over random valid shapes for every product: rows not a
+multiple of 64, K tails, both group sizes, every split factor, token counts
+around the 128-row tiles, each limb mode; every output against the oracle
+(integer outputs bit for bit, f32 within |y - y_ref| <= 2e-5 sum_i |w_i x_i|)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a HIP device")]
+
+REL = 2e-5
+N_CASES = 24
+
+
+def _within(y, yref, mass, what):
+    err = np.abs(np.asarray(y, np.float64) - yref)
+    bad = ~(err <= REL * mass)
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs outside the bound"
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_sweep_q8row_gemv(case):
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(30000 + case)
+    M = int(r.integers(1, 700))
+    K = 4 * int(r.integers(1, 1500))
+    q, rs, xs = synth.q8row_inputs(M, K, rng=r)
+    W = qg.Q8RowWeight.from_host(q, rs)
+    y = torch.empty(M, device="cuda")
+    W.gemv(torch.from_numpy(xs).cuda(), y)
+    yref, mass = oracle.q8row_gemv(q, rs, xs)
+    _within(y.cpu().numpy(), yref, mass, f"q8row M={M} K={K}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_sweep_q2_gemv(case):
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(31000 + case)
+    group = int(r.choice([64, 128]))
+    M = int(r.integers(1, 900))
+    K = group * int(r.integers(1, 40))
+    split = int(r.integers(0, 17))
+    blob, x = synth.q2_inputs(M, K, group, seed=31500 + case)
+    W = qg.Q2Weight.from_blocks(blob, M, K, group)
+    xq = torch.empty(K, dtype=torch.int8, device="cuda")
+    sc = torch.empty(1, device="cuda")
+    su = torch.empty(K // 64, dtype=torch.int32, device="cuda")
+    qg.qquant_act_i8(torch.from_numpy(x).cuda(), xq, sc, su)
+    ws = torch.empty(max(1, qg.qgemv_q2_ws_bytes(M, K, group, split)), dtype=torch.uint8, device="cuda")
+    y = torch.empty(M, device="cuda")
+    dots = torch.empty((M, K // 64), dtype=torch.int32, device="cuda")
+    qg.qgemv_q2_dots(W, xq, su, sc, y, dots, ws, split_k=split)
+    rq, rsc, rsu = oracle.act_quant_i8(x)
+    assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(su.cpu().numpy(), rsu)
+    assert np.array_equal(dots.cpu().numpy(), oracle.q2_dots(blob, M, K, group, rq))
+    yref, mass = oracle.q2_gemv(blob, M, K, group, rq, rsc)
+    _within(y.cpu().numpy(), yref, mass, f"q2 M={M} K={K} g{group} split {split}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_sweep_q2_product(case):
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(32000 + case)
+    group = int(r.choice([64, 128]))
+    nb = int(r.integers(1, 300))
+    M = int(r.integers(1, 700))
+    K = group * int(r.integers(1, 24))
+    blob, _ = synth.q2_inputs(M, K, group, seed=32500 + case)
+    W = qg.Q2Weight.from_blocks(blob, M, K, group)
+    X = (r.standard_normal((nb, K)) * r.uniform(0.1, 10.0, (nb, 1))).astype(np.float32)
+    xq = torch.empty((nb, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty(nb, device="cuda")
+    su = torch.empty((nb, K // 64), dtype=torch.int32, device="cuda")
+    qg.qquant_act_i8_rows(torch.from_numpy(X).cuda(), xq, sc, su)
+    n = qg.qgemm_q2_batched_ws_bytes(M, K, group, nb)
+    y = torch.empty((nb, M), device="cuda")
+    qg.qgemm_q2_batched(W, xq, su, sc, y, ws=torch.empty(n, dtype=torch.uint8, device="cuda") if n else None)
+    xq_h, sc_h = xq.cpu().numpy(), sc.cpu().numpy()
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq_h, sc_h)
+    _within(y.cpu().numpy(), yref, mass, f"q2 product nb={nb} M={M} K={K} g{group}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_sweep_q8row_gemm(case):
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(33000 + case)
+    nb = int(r.integers(1, 300))
+    M = int(r.integers(1, 600))
+    K = 4 * int(r.integers(1, 600))
+    limbs = int(r.choice([0, 3]))
+    q, rs, _ = synth.q8row_inputs(M, K, rng=r)
+    xs = (r.standard_normal((nb, K)) * r.uniform(0.01, 100.0, (nb, 1))).astype(np.float32)
+    W = qg.Q8RowWeight.from_host(q, rs)
+    y = torch.empty((nb, M), device="cuda")
+    ws = torch.empty(qg.qgemm_q8row_batched_ws_bytes(nb, K), dtype=torch.uint8, device="cuda")
+    qg.qgemm_q8row_batched(W.packed, W.rs, torch.from_numpy(xs).cuda(), y, nb, M, K, ws, xs_limbs=limbs)
+    yref, mass = oracle.q8row_gemm(q, rs, xs)
+    _within(y.cpu().numpy(), yref, mass, f"gemm nb={nb} M={M} K={K} limbs={limbs}")
