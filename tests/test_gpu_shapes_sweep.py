@@ -104,3 +104,69 @@ def test_sweep_q8row_gemm(case):
     qg.qgemm_q8row_batched(W.packed, W.rs, torch.from_numpy(xs).cuda(), y, nb, M, K, ws, xs_limbs=limbs)
     yref, mass = oracle.q8row_gemm(q, rs, xs)
     _within(y.cpu().numpy(), yref, mass, f"gemm nb={nb} M={M} K={K} limbs={limbs}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_sweep_producers(case):
+    """RMSNorm + quantiser and the gated products + quantiser over random row
+    counts, lengths and scales: every code, scale and group sum bit for bit."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(34000 + case)
+    nb = int(r.integers(1, 40))
+    K = 64 * int(r.integers(1, 300))
+    kind = int(r.integers(0, 2))
+    eps = float(r.choice([0.0, 1e-6, 1e-5]))
+    X = (r.standard_normal((nb, K)) * r.uniform(0.01, 30.0, (nb, 1))).astype(np.float32)
+    G = (2.5 * r.standard_normal((nb, K))).astype(np.float32)
+    w = (1.0 + 0.1 * r.standard_normal(K)).astype(np.float32)
+    xq = torch.empty((nb, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty(nb, device="cuda")
+    su = torch.empty((nb, K // 64), dtype=torch.int32, device="cuda")
+    qg.qquant_rmsnorm_i8_rows(torch.from_numpy(X).cuda(), torch.from_numpy(w).cuda(), eps, xq, sc, su)
+    xq_h, sc_h, su_h = xq.cpu().numpy(), sc.cpu().numpy(), su.cpu().numpy()
+    for b in range(nb):
+        _, rq, rsc, rsu = oracle.rmsnorm_quant_i8(X[b], w, eps)
+        assert np.array_equal(xq_h[b], rq) and sc_h[b] == rsc and np.array_equal(su_h[b], rsu), f"rmsnorm row {b}"
+    t = torch.empty((nb, K), device="cuda")
+    qg.qquant_glu_i8_rows(torch.from_numpy(G).cuda(), torch.from_numpy(X).cuda(), kind, t, xq, sc, su)
+    t_h, xq_h, sc_h, su_h = t.cpu().numpy(), xq.cpu().numpy(), sc.cpu().numpy(), su.cpu().numpy()
+    for b in range(nb):
+        rt, rq, rsc, rsu = oracle.glu_quant_i8(G[b], X[b], kind)
+        assert np.array_equal(t_h[b].view(np.uint32), rt.view(np.uint32)), f"gated product row {b}"
+        assert np.array_equal(xq_h[b], rq) and sc_h[b] == rsc and np.array_equal(su_h[b], rsu), f"glu row {b}"
+
+
+@pytest.mark.parametrize("case", range(N_CASES // 2))
+def test_sweep_q2_batch_jobs(case):
+    """Random job tables for the batched GEMV launch: own shapes, activations
+    and residuals, one group size per launch."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(35000 + case)
+    group = int(r.choice([64, 128]))
+    njobs = int(r.integers(1, 17))
+    jobs, refs = [], []
+    for j in range(njobs):
+        M = int(r.integers(1, 500))
+        K = group * int(r.integers(1, 20))
+        blob, x = synth.q2_inputs(M, K, group, seed=35500 + 100 * case + j)
+        W = qg.Q2Weight.from_blocks(blob, M, K, group)
+        xq = torch.empty(K, dtype=torch.int8, device="cuda")
+        sc = torch.empty(1, device="cuda")
+        su = torch.empty(K // 64, dtype=torch.int32, device="cuda")
+        qg.qquant_act_i8(torch.from_numpy(x).cuda(), xq, sc, su)
+        y = torch.empty(M, device="cuda")
+        acc = r.standard_normal(M).astype(np.float32) if r.random() < 0.5 else None
+        jobs.append((W, xq, su, sc, y) + ((torch.from_numpy(acc).cuda(),) if acc is not None else ()))
+        refs.append((blob, M, K, x, acc, y))
+    qg.qgemv_q2_batch(jobs)
+    for blob, M, K, x, acc, y in refs:
+        rq, rsc, _ = oracle.act_quant_i8(x)
+        if acc is None:
+            yref, mass = oracle.q2_gemv(blob, M, K, group, rq, rsc)
+            _within(y.cpu().numpy(), yref, mass, f"batch job {M}x{K}")
+        else:
+            yref, mass = oracle.q2_gemv_accum(blob, M, K, group, rq, rsc, acc)
+            err = np.abs(y.cpu().numpy().astype(np.float64) - yref)
+            assert np.all(err <= REL * mass + 2.0 ** -24 * np.abs(yref)), f"batch job with residual {M}x{K}"
