@@ -52,6 +52,9 @@
  *        cortiq-engine 0.3.7 gpu_metal.rs page: silu_mul_pre (has_col) and
  *        q8_mul_mm_silu (the batched down product with silu(g) * u formed in
  *        its activation load).
+ *  [GU]  cortiq-engine 0.5.43 gpu_wgpu.rs page: moe_gate_up (one workgroup
+ *        computes both the gate and the up row dot of a row and writes
+ *        act = silu(g) * u).
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -307,6 +310,32 @@ qg_status qgemv_q2_dual(const qg_q2_weight *w0, const qg_q2_weight *w1,
                         const int8_t *xq, const int32_t *suma,
                         const float *act_scale, float *y0, float *y1,
                         void *ws, size_t ws_bytes, int split_k, void *stream);
+
+/* Gate|up GEMV with the gated product and its quantiser  [GD, GU, PQ]
+ *
+ *   g = qgemv_q2(w_gate, xq),  u = qgemv_q2(w_up, xq)          (one launch)
+ *   t = silu(g) * u (kind QG_GLU_SILU) or u * sigmoid(g) (QG_GLU_SIGMOID)
+ *   xq_out, act_scale_out, suma_out = the int8 quantiser of t
+ *
+ * The FFN's gate and up projections and the next projection's input in two
+ * launches instead of three: each workgroup computes the gate and the up dot
+ * of the same 64 rows (as the page's moe_gate_up does per row) and forms t
+ * in its epilogue; a second launch quantises t.  t, xq_out, act_scale_out
+ * and suma_out are bit-identical to qgemv_q2_dual with split_k = 1 followed
+ * by qquant_glu_i8 on its two outputs (g and u are not written).
+ * Arguments: w_gate, w_up: same M, K and group, M % 64 == 0; xq, suma,
+ * act_scale: the quantised input as for qgemv_q2; t: device f32[M] (16-byte
+ * aligned), written; xq_out int8[M], act_scale_out f32[1], suma_out
+ * int32[M/64]: device, written.  No workspace (suma_out holds the per-tile
+ * maxima between the two launches).
+ * QG_EINVAL: as qgemv_q2_dual, or a bad kind, M % 64 != 0, misalignment,
+ * or outputs overlapping each other or the inputs.                        */
+qg_status qgemv_q2_gate_up_glu(const qg_q2_weight *w_gate,
+                               const qg_q2_weight *w_up, const int8_t *xq,
+                               const int32_t *suma, const float *act_scale,
+                               int kind, float *t, int8_t *xq_out,
+                               float *act_scale_out, int32_t *suma_out,
+                               void *stream);
 
 /* One GEMV of a qgemv_q2_batch launch. */
 typedef struct {

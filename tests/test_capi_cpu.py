@@ -40,7 +40,7 @@ def test_library_exports(name):
 
 def test_abi_and_status_strings():
     L = qg.lib()
-    assert L.qg_abi_version() == 4
+    assert L.qg_abi_version() == 5
     assert L.qg_status_string(0) == b"QG_OK"
     assert L.qg_status_string(1) == b"QG_EINVAL"
     assert L.qg_status_string(2) == b"QG_ELAUNCH"
@@ -237,6 +237,18 @@ def test_einval_paths():
     assert L.qgemm_q2_batched_ws_bytes(17408, 5120, 128, 512) == 0
     _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, None, 0, None))
     _einval(L.qgemm_q2_batched(ctypes.byref(wdown), a16, a16, a16, None, a16, 512, a16, need - 16, None))
+    # gate|up GEMV with the gated product and its quantiser
+    wg = qg.qg_q2_weight(0x10000, 0x20000, 128, 256, 64, 0)
+    wu = qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 64, 0)
+    wu100 = qg.qg_q2_weight(0x30000, 0x40000, 100, 256, 64, 0)
+    wg100 = qg.qg_q2_weight(0x10000, 0x20000, 100, 256, 64, 0)
+    ok = (a16, a16, a16)
+    _einval(L.qgemv_q2_gate_up_glu(ctypes.byref(wg100), ctypes.byref(wu100), *ok, 0, P(0x50000), P(0x60000), P(0x61000), P(0x62000), None))  # M % 64
+    _einval(L.qgemv_q2_gate_up_glu(ctypes.byref(wg), ctypes.byref(wu100), *ok, 0, P(0x50000), P(0x60000), P(0x61000), P(0x62000), None))   # shapes differ
+    _einval(L.qgemv_q2_gate_up_glu(ctypes.byref(wg), ctypes.byref(wu), *ok, 7, P(0x50000), P(0x60000), P(0x61000), P(0x62000), None))      # kind
+    _einval(L.qgemv_q2_gate_up_glu(ctypes.byref(wg), ctypes.byref(wu), *ok, 0, P(0x50008), P(0x60000), P(0x61000), P(0x62000), None))      # t misaligned
+    _einval(L.qgemv_q2_gate_up_glu(ctypes.byref(wg), ctypes.byref(wu), *ok, 0, P(0x50000), P(0x50100), P(0x61000), P(0x62000), None))      # xq_out in t
+    _einval(L.qgemv_q2_gate_up_glu(ctypes.byref(wg), ctypes.byref(wu), *ok, 0, None, P(0x60000), P(0x61000), P(0x62000), None))
     # gate|up pair of the batched Q2 product
     w8b = qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 64, 0)
     w8c = qg.qg_q2_weight(0x30000, 0x40000, 128, 256, 128, 0)                                 # other group

@@ -231,3 +231,36 @@ def test_batch_mixed_sizes_within_bound():
     # small jobs in a launch of >= 256 tiles: only the summation order changes
     specs = [(16384, 512, False), (200, 1024, True), (64, 2048, False)]
     _check_batch(specs, 64, 5400, exact=False)
+
+
+@pytest.mark.parametrize("M,K,group,kind", [(17408, 5120, 128, 0), (17408, 5120, 128, 1), (2048, 1024, 64, 0),
+                                            (64, 640, 64, 1), (4096, 4096, 128, 0)])
+def test_gate_up_glu_equals_dual_then_glu(M, K, group, kind):
+    """The gate|up GEMV with the gated product in its epilogue and the
+    quantiser after it (cortiq moe_gate_up) gives t, xq, act_scale and suma
+    bit for bit as qgemv_q2_dual (split 1) followed by qquant_glu_i8."""
+    import torch
+    m = qg()
+    bg, x = synth.q2_inputs(M, K, group, seed=9100 + M)
+    bu, _ = synth.q2_inputs(M, K, group, seed=9101 + M)
+    Wg, Wu = m.Q2Weight.from_blocks(bg, M, K, group), m.Q2Weight.from_blocks(bu, M, K, group)
+    xq = torch.empty(K, dtype=torch.int8, device="cuda")
+    sc = torch.empty(1, device="cuda")
+    su = torch.empty(K // 64, dtype=torch.int32, device="cuda")
+    m.qquant_act_i8(dev(x), xq, sc, su)
+    t = torch.full((M,), float("nan"), device="cuda")
+    xq2 = torch.empty(M, dtype=torch.int8, device="cuda")
+    sc2 = torch.empty(1, device="cuda")
+    su2 = torch.empty(M // 64, dtype=torch.int32, device="cuda")
+    m.qgemv_q2_gate_up_glu(Wg, Wu, xq, su, sc, kind, t, xq2, sc2, su2)
+    g = torch.empty(M, device="cuda")
+    u = torch.empty(M, device="cuda")
+    m.qgemv_q2_dual(Wg, Wu, xq, su, sc, g, u, None, split_k=1)
+    t_r = torch.empty(M, device="cuda")
+    xq_r = torch.empty(M, dtype=torch.int8, device="cuda")
+    sc_r = torch.empty(1, device="cuda")
+    su_r = torch.empty(M // 64, dtype=torch.int32, device="cuda")
+    m.qquant_glu_i8(g, u, kind, t_r, xq_r, sc_r, su_r)
+    torch.cuda.synchronize()
+    assert torch.equal(t.view(torch.int32), t_r.view(torch.int32)), "t differs"
+    assert torch.equal(xq2, xq_r) and torch.equal(sc2.view(torch.int32), sc_r.view(torch.int32)) and torch.equal(su2, su_r)

@@ -108,15 +108,21 @@ def test_graph_replays_fused_forms():
     ws_gu = torch.empty(max(1, qg.qgemv_q2_dual_ws_bytes(F, D, 128, 2)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(1, qg.qgemv_q2_ws_bytes(D, F, 128, 2)), dtype=torch.uint8, device=dev)
 
+    t2 = torch.empty(F, device=dev)
+    xq3 = torch.empty(F, dtype=torch.int8, device=dev)
+    sc3 = torch.empty(1, device=dev)
+    su3 = torch.empty(F // 64, dtype=torch.int32, device=dev)
+
     def path():
         qg.qquant_rmsnorm_i8(h, nw, 1e-6, xq1, sc1, su1)
+        qg.qgemv_q2_gate_up_glu(Wg, Wu, xq1, su1, sc1, qg.QG_GLU_SILU, t2, xq3, sc3, su3)
         qg.qgemv_q2_dual(Wg, Wu, xq1, su1, sc1, g, u, ws_gu, split_k=2)
         qg.qquant_glu_i8(g, u, qg.QG_GLU_SILU, t, xq2, sc2, su2)
         qg.qgemv_q2_accum(Wd, xq2, su2, sc2, h, hout, ws_d, split_k=2)
         qg.qgemv_q2_batch([(W, xq1, su1, sc1, y) + ((h[:W.M],) if W.M <= D and n == 0 else ())
                            for n, (W, y) in enumerate(zip(Wx, ys))])
 
-    outs = (xq1, sc1, su1, g, u, t, xq2, sc2, su2, hout, *ys)
+    outs = (xq1, sc1, su1, g, u, t, xq2, sc2, su2, hout, t2, xq3, sc3, su3, *ys)
     path()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]

@@ -73,6 +73,8 @@ _SIGS = {
     "qgemv_q2_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P,
                            _SZ, _I, _P]),
     "qgemv_q2_batch": (_I, [ctypes.POINTER(qg_q2_job), _I, _P]),
+    "qgemv_q2_gate_up_glu": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _I, _P, _P,
+                                  _P, _P, _P]),
     "qgemm_q2_batched": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "qgemm_q2_batched_ws_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "qgemm_q2_batched_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P,
@@ -361,6 +363,19 @@ def qgemv_q2_dual(w0: Q2Weight, w1: Q2Weight, xq, suma, act_scale, y0, y1, ws=No
         ctypes.byref(d0), ctypes.byref(d1), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(y0, torch.float32, "y0"), _dev(y1, torch.float32, "y1"),
         wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
+
+
+def qgemv_q2_gate_up_glu(w_gate: Q2Weight, w_up: Q2Weight, xq, suma, act_scale, kind, t, xq_out, act_scale_out,
+                         suma_out, stream=None):
+    """Gate|up GEMV with t = silu(g)*u (kind 0) or u*sigmoid(g) (kind 1) formed in its epilogue,
+    then the int8 quantiser of t: two launches, bit-identical to qgemv_q2_dual + qquant_glu_i8."""
+    import torch
+    dg, du = w_gate.desc(), w_up.desc()
+    _check("qgemv_q2_gate_up_glu", lib().qgemv_q2_gate_up_glu(
+        ctypes.byref(dg), ctypes.byref(du), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), int(kind), _dev(t, torch.float32, "t"),
+        _dev(xq_out, torch.int8, "xq_out"), _dev(act_scale_out, torch.float32, "act_scale_out"),
+        _dev(suma_out, torch.int32, "suma_out"), _stream(stream)))
 
 
 def qgemv_q2_batch(jobs, stream=None):

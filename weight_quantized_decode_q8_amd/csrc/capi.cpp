@@ -57,7 +57,7 @@ const char *qg_status_string(qg_status s) {
 
 const char *qg_last_error(void) { return qg::g_msg; }
 
-int qg_abi_version(void) { return 4; }
+int qg_abi_version(void) { return 5; }
 
 qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
                       int64_t K, void *stream) {
@@ -254,6 +254,46 @@ qg_status qgemv_q2_dual(const qg_q2_weight *w0, const qg_q2_weight *w1, const in
   if (!w1) return fail(QG_EINVAL, "qgemv_q2_dual: null weight descriptor");
   return q2_common("qgemv_q2_dual", w0, w1, xq, suma, act_scale, nullptr, y0, y1, nullptr, ws, ws_bytes, split_k,
                    stream);
+}
+
+qg_status qgemv_q2_gate_up_glu(const qg_q2_weight *w_gate, const qg_q2_weight *w_up, const int8_t *xq,
+                               const int32_t *suma, const float *act_scale, int kind, float *t, int8_t *xq_out,
+                               float *act_scale_out, int32_t *suma_out, void *stream) {
+  const char *fn = "qgemv_q2_gate_up_glu";
+  qg_status st = qg::check_q2_weight(w_gate, fn);
+  if (st != QG_OK) return st;
+  st = qg::check_q2_weight(w_up, fn);
+  if (st != QG_OK) return st;
+  if (w_up->M != w_gate->M || w_up->K != w_gate->K || w_up->group != w_gate->group)
+    return fail(QG_EINVAL, "%s: the two weights differ in shape or group", fn);
+  if (!xq || !suma || !act_scale || !t || !xq_out || !act_scale_out || !suma_out)
+    return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
+  const int64_t M = w_gate->M;
+  if (M % 64 != 0 || M > (1 << 24)) return fail(QG_EINVAL, "%s: M=%lld must be a multiple of 64 (the gated vector is quantised)", fn, (long long)M);
+  if (!aligned(xq, 16) || !aligned(t, 16)) return fail(QG_EINVAL, "%s: xq and t must be 16-byte aligned", fn);
+  if (!aligned(suma, 4) || !aligned(act_scale, 4) || !aligned(xq_out, 4) || !aligned(act_scale_out, 4) ||
+      !aligned(suma_out, 4))
+    return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  const size_t tb = (size_t)M * sizeof(float);
+  if (bytes_overlap(t, tb, xq_out, (size_t)M) || bytes_overlap(t, tb, suma_out, (size_t)(M / 64) * 4) ||
+      bytes_overlap(t, tb, act_scale_out, 4) || bytes_overlap(xq_out, (size_t)M, suma_out, (size_t)(M / 64) * 4) ||
+      bytes_overlap(t, tb, xq, (size_t)w_gate->K) || bytes_overlap(suma_out, (size_t)(M / 64) * 4, suma, (size_t)(w_gate->K / 64) * 4))
+    return fail(QG_EINVAL, "%s: an output overlaps another output or an input", fn);
+  qg::Q2Call call{};
+  call.codes[0] = w_gate->codes;
+  call.scales[0] = w_gate->scales;
+  call.codes[1] = w_up->codes;
+  call.scales[1] = w_up->scales;
+  call.M = (int)M;
+  call.K = (int)w_gate->K;
+  call.group = w_gate->group;
+  call.xq = xq;
+  call.suma = suma;
+  call.act_scale = act_scale;
+  call.split = 1;
+  return qg::launched(qg::launch_q2_gate_up_glu(call, kind, t, xq_out, act_scale_out, suma_out, (hipStream_t)stream),
+                      fn);
 }
 
 qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream) {

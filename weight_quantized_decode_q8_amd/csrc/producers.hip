@@ -187,6 +187,14 @@ hipError_t launch_silu_mul_pre(const float *g, const float *u, const float *col,
   return hipGetLastError();
 }
 
+hipError_t launch_quant_from_parts(const float *t, int rows, int K, int nparts, int8_t *xq, float *act_scale,
+                                   int32_t *suma, hipStream_t stream) {
+  quant_from_parts_kernel<<<rows, kQuantThreads, 0, stream>>>(reinterpret_cast<const float4 *>(t), K / 4, nparts,
+                                                              reinterpret_cast<int *>(xq), act_scale,
+                                                              reinterpret_cast<int *>(suma));
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm_quant(const float *x, const float *w, int rows, int K, float eps, int8_t *xq,
                                 float *act_scale, int32_t *suma, hipStream_t stream) {
   rmsnorm_quant_kernel<<<rows, kQuantThreads, 0, stream>>>(

@@ -39,6 +39,7 @@
 // equal the unfused calls bit for bit when the split is the same, which the
 // launchers guarantee: waves per tile and the automatic split depend only on
 // one matrix's shape.
+#include "gate_rule.h"
 #include "qg_internal.h"
 
 namespace qg {
@@ -225,6 +226,179 @@ __global__ __launch_bounds__(256) void q2_splitk_reduce_kernel(Q2Batch batch, fl
   y[o] = scale_add(s, job.act_scale[0], accum, o);
 }
 
+// Gate and up rows of one tile in one workgroup, then the gated product
+// (cortiq-engine 0.5.43 gpu_wgpu.rs page, moe_gate_up: one workgroup does
+// both row dots of a row and writes silu(g) * u).  Each matrix's dot is
+// accumulated exactly as q2_gemv_t64_kernel accumulates it (same groups per
+// wave, same order, same wave combine), g and u are each rounded once as
+// fl(acc * act_scale), and t = glu(g, u) follows the producers' rule, so t
+// equals the dual GEMV followed by the gated product bit for bit.  Lane 0
+// of wave 0 then stores the tile's largest |t| as float bits in part[tile]
+// for the quantiser's second step (quant_from_parts_kernel).
+template <int UPG, int GPB, int kWaves, int KIND>
+__global__ __launch_bounds__(64 * kWaves) void q2_gate_up_glu_kernel(Q2Job gate, Q2Job up, float *__restrict__ t,
+                                                                     int *__restrict__ part) {
+  __shared__ float red[2][kWaves - 1][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = blockIdx.x;
+  const int M = gate.M, K = gate.K;
+  const int nunits = K / 64;
+  const int ngroups = nunits / UPG;
+  const int per = (ngroups + kWaves - 1) / kWaves;
+  const int g0 = min(ngroups, wave * per);
+  const int g1 = min(ngroups, g0 + per);
+  const i32x4 *cg = gate.codes + (size_t)tile * nunits * 64 + lane;
+  const i32x4 *cu = up.codes + (size_t)tile * nunits * 64 + lane;
+  const unsigned short *sg = gate.scales + (size_t)tile * ngroups * 64 + lane;
+  const unsigned short *su = up.scales + (size_t)tile * ngroups * 64 + lane;
+  const uniform_i32x4 *xw = (const uniform_i32x4 *)gate.xq;
+  const uniform_i32 *sa = (const uniform_i32 *)gate.suma;
+  const int o = tile * 64 + lane;
+
+  float ag = 0.0f, au = 0.0f;
+  int g = g0;
+  for (; g + GPB <= g1; g += GPB) {
+    i32x4 c0[GPB * UPG], c1[GPB * UPG];
+    unsigned short d0[GPB], d1[GPB];
+#pragma unroll
+    for (int v = 0; v < GPB * UPG; v++) {
+      c0[v] = __builtin_nontemporal_load(cg + (size_t)(g * UPG + v) * 64);
+      c1[v] = __builtin_nontemporal_load(cu + (size_t)(g * UPG + v) * 64);
+    }
+#pragma unroll
+    for (int j = 0; j < GPB; j++) {
+      d0[j] = __builtin_nontemporal_load(sg + (size_t)(g + j) * 64);
+      d1[j] = __builtin_nontemporal_load(su + (size_t)(g + j) * 64);
+    }
+#pragma unroll
+    for (int j = 0; j < GPB; j++) {
+      int p0 = 0, p1 = 0;
+#pragma unroll
+      for (int v = 0; v < UPG; v++) {
+        const int u = (g + j) * UPG + v;
+        p0 += unit_dot(c0[j * UPG + v], xw + (size_t)u * 4, sa[u]);
+        p1 += unit_dot(c1[j * UPG + v], xw + (size_t)u * 4, sa[u]);
+      }
+      ag = fmaf(half_bits_to_f32(d0[j]), (float)p0, ag);
+      au = fmaf(half_bits_to_f32(d1[j]), (float)p1, au);
+    }
+  }
+  for (; g < g1; g++) {
+    int p0 = 0, p1 = 0;
+#pragma unroll
+    for (int v = 0; v < UPG; v++) {
+      const int u = g * UPG + v;
+      p0 += unit_dot(__builtin_nontemporal_load(cg + (size_t)u * 64), xw + (size_t)u * 4, sa[u]);
+      p1 += unit_dot(__builtin_nontemporal_load(cu + (size_t)u * 64), xw + (size_t)u * 4, sa[u]);
+    }
+    ag = fmaf(half_bits_to_f32(__builtin_nontemporal_load(sg + (size_t)g * 64)), (float)p0, ag);
+    au = fmaf(half_bits_to_f32(__builtin_nontemporal_load(su + (size_t)g * 64)), (float)p1, au);
+  }
+
+  if (wave > 0) {
+    red[0][wave - 1][lane] = ag;
+    red[1][wave - 1][lane] = au;
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < kWaves - 1; w++) {
+      ag += red[0][w][lane];
+      au += red[1][w][lane];
+    }
+    const float sc = gate.act_scale[0];
+    float m = 0.0f;
+    if (o < M) {
+      const float tv = glu1<KIND>(__fmul_rn(ag, sc), __fmul_rn(au, sc));
+      t[o] = tv;
+      m = fabsf(tv);
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) part[tile] = __float_as_int(m);
+  }
+}
+
+// The same with the two matrices on the two halves of a 2W-wave workgroup:
+// waves 0..W-1 accumulate the gate tile and waves W..2W-1 the up tile, each
+// half exactly as a W-wave q2_gemv_t64_kernel workgroup does (same groups per
+// wave, same combine order), so the loads in flight match the dual GEMV's.
+template <int UPG, int GPB, int W, int KIND>
+__global__ __launch_bounds__(128 * W) void q2_gate_up_glu_halves_kernel(Q2Job gate, Q2Job up,
+                                                                        float *__restrict__ t,
+                                                                        int *__restrict__ part) {
+  __shared__ float red[2][W - 1][64];
+  __shared__ float fin[64];
+  const int lane = threadIdx.x & 63;
+  const int wave2 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mat = wave2 / W;        // 0 gate, 1 up
+  const int wave = wave2 % W;       // wave within the matrix's half
+  const Q2Job &job = mat ? up : gate;
+  const int tile = blockIdx.x;
+  const int M = gate.M, K = gate.K;
+  const int nunits = K / 64;
+  const int ngroups = nunits / UPG;
+  const int per = (ngroups + W - 1) / W;
+  const int g0 = min(ngroups, wave * per);
+  const int g1 = min(ngroups, g0 + per);
+  const i32x4 *cp = (mat ? up.codes : gate.codes) + (size_t)tile * nunits * 64 + lane;
+  const unsigned short *sp = (mat ? up.scales : gate.scales) + (size_t)tile * ngroups * 64 + lane;
+  const uniform_i32x4 *xw = (const uniform_i32x4 *)job.xq;
+  const uniform_i32 *sa = (const uniform_i32 *)job.suma;
+  const int o = tile * 64 + lane;
+
+  float acc = 0.0f;
+  int g = g0;
+  for (; g + GPB <= g1; g += GPB) {
+    i32x4 c[GPB * UPG];
+    unsigned short dh[GPB];
+#pragma unroll
+    for (int v = 0; v < GPB * UPG; v++) c[v] = __builtin_nontemporal_load(cp + (size_t)(g * UPG + v) * 64);
+#pragma unroll
+    for (int j = 0; j < GPB; j++) dh[j] = __builtin_nontemporal_load(sp + (size_t)(g + j) * 64);
+#pragma unroll
+    for (int j = 0; j < GPB; j++) {
+      int p = 0;
+#pragma unroll
+      for (int v = 0; v < UPG; v++) {
+        const int u = (g + j) * UPG + v;
+        p += unit_dot(c[j * UPG + v], xw + (size_t)u * 4, sa[u]);
+      }
+      acc = fmaf(half_bits_to_f32(dh[j]), (float)p, acc);
+    }
+  }
+  for (; g < g1; g++) {
+    const unsigned short dh = __builtin_nontemporal_load(sp + (size_t)g * 64);
+    int p = 0;
+#pragma unroll
+    for (int v = 0; v < UPG; v++) {
+      const int u = g * UPG + v;
+      p += unit_dot(__builtin_nontemporal_load(cp + (size_t)u * 64), xw + (size_t)u * 4, sa[u]);
+    }
+    acc = fmaf(half_bits_to_f32(dh), (float)p, acc);
+  }
+
+  if (wave > 0) red[mat][wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < W - 1; w++) acc += red[mat][w][lane];
+    if (mat == 1) fin[lane] = acc;
+  }
+  __syncthreads();
+  if (wave2 == 0) {
+    const float sc = gate.act_scale[0];
+    float m = 0.0f;
+    if (o < M) {
+      const float tv = glu1<KIND>(__fmul_rn(acc, sc), __fmul_rn(fin[lane], sc));
+      t[o] = tv;
+      m = fabsf(tv);
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) part[tile] = __float_as_int(m);
+  }
+}
+
 template <int UPG, int GPB>
 hipError_t launch_typed(const Q2Batch &b, int waves, int S, int *dots, float *y0, float *y1, const float *accum,
                         hipStream_t stream) {
@@ -318,4 +492,44 @@ hipError_t launch_q2_batch(const Q2BatchCall *jobs, int njobs, int group, hipStr
   return launch_batch(b, group, tiles >= 256 ? 8 : 16, 1, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
+
+// The gate|up GEMV with the gated product in its epilogue (one launch), then
+// the quantiser's second step over t (one workgroup).  Same waves per tile
+// as the dual GEMV of this shape, and no K split.
+hipError_t launch_q2_gate_up_glu(const Q2Call &call, int kind, float *t, int8_t *xq_out, float *act_scale_out,
+                                 int32_t *suma_out, hipStream_t stream) {
+  Q2Job gate{}, up{};
+  gate.codes = reinterpret_cast<const i32x4 *>(call.codes[0]);
+  gate.scales = reinterpret_cast<const unsigned short *>(call.scales[0]);
+  up.codes = reinterpret_cast<const i32x4 *>(call.codes[1]);
+  up.scales = reinterpret_cast<const unsigned short *>(call.scales[1]);
+  gate.xq = up.xq = call.xq;
+  gate.suma = up.suma = call.suma;
+  gate.act_scale = up.act_scale = call.act_scale;
+  gate.M = up.M = call.M;
+  gate.K = up.K = call.K;
+  const int tiles = (call.M + 63) / 64;
+  const bool w8 = tiles >= 256;
+  int *part = reinterpret_cast<int *>(suma_out);
+#define QG_GLU(UPG, GPB, W, KD) \
+  q2_gate_up_glu_kernel<UPG, GPB, W, KD><<<tiles, 64 * W, 0, stream>>>(gate, up, t, part)
+#define QG_GLU_H(UPG, GPB, KD) \
+  q2_gate_up_glu_halves_kernel<UPG, GPB, 8, KD><<<tiles, 128 * 8, 0, stream>>>(gate, up, t, part)
+  // 8 waves per matrix (the dual GEMV's choice at >= 256 tiles): the two
+  // matrices on the halves of a 16-wave workgroup; 16 waves per matrix
+  // (fewer tiles): both matrices on the same 16 waves, one after the other
+  // in each group step.
+  if (call.group == 64) {
+    if (w8) { if (kind == 0) QG_GLU_H(1, 4, 0); else QG_GLU_H(1, 4, 1); }
+    else { if (kind == 0) QG_GLU(1, 4, 16, 0); else QG_GLU(1, 4, 16, 1); }
+  } else {
+    if (w8) { if (kind == 0) QG_GLU_H(2, 2, 0); else QG_GLU_H(2, 2, 1); }
+    else { if (kind == 0) QG_GLU(2, 2, 16, 0); else QG_GLU(2, 2, 16, 1); }
+  }
+#undef QG_GLU
+#undef QG_GLU_H
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_quant_from_parts(t, 1, call.M, tiles, xq_out, act_scale_out, suma_out, stream);
+}
 }  // namespace qg

@@ -76,6 +76,17 @@ hipError_t launch_q2_batch(const Q2BatchCall *jobs, int njobs, int group, hipStr
 
 int q2_auto_split(int64_t M, int64_t K, int group);
 
+// Gate|up Q2 GEMV (call.codes[0], [1]; no split) with t = glu(g, u) (kind 0
+// silu, 1 sigmoid) in its epilogue, each tile's max|t| in suma_out[tile],
+// then the quantiser's second step over t into xq_out, act_scale_out and
+// suma_out.  M % 64 == 0.
+hipError_t launch_q2_gate_up_glu(const Q2Call &call, int kind, float *t, int8_t *xq_out, float *act_scale_out,
+                                 int32_t *suma_out, hipStream_t stream);
+// The quantiser's second step: rows of t [rows][K] whose max|t| is spread
+// over nparts partial maxima (float bits) at the start of each row's suma.
+hipError_t launch_quant_from_parts(const float *t, int rows, int K, int nparts, int8_t *xq, float *act_scale,
+                                   int32_t *suma, hipStream_t stream);
+
 // Batched Q2 product over nb token rows (int8 MFMA), y [nb][M] token-major.
 // part: [S][nb][M] f32 partials when q2_gemm_split(...) = S > 1, else unused.
 int q2_gemm_split(int64_t M, int64_t K, int group, int64_t nb);
