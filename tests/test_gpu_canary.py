@@ -84,7 +84,7 @@ def test_canary_q8row_gemv(M, K):
     check(y)
 
 
-@pytest.mark.parametrize("M,K,group,split", [(100, 1024, 128, 3), (65, 640, 64, 0), (300, 4096, 64, 16)])
+@pytest.mark.parametrize("M,K,group,split", [(100, 1024, 128, 3), (65, 640, 64, 0), (300, 4096, 64, 16), (17408, 640, 64, 0), (128, 1024, 128, 1)])
 def test_canary_q2_gemvs(M, K, group, split):
     import torch
     import weight_quantized_decode_q8_amd as qg
@@ -110,6 +110,11 @@ def test_canary_q2_gemvs(M, K, group, split):
     check(y, ws)
     qg.qgemv_q2_dual(W, W1, xq, su, sc, y.t, y1.t, ws2.t if n1 else None, split_k=split)
     check(y, y1, ws2)
+    if M % 64 == 0:
+        t, xq2 = Guarded(M, torch.float32), Guarded(M, torch.int8)
+        sc2, su2 = Guarded(1, torch.float32), Guarded(M // 64, torch.int32)
+        qg.qgemv_q2_gate_up_glu(W, W1, xq, su, sc, qg.QG_GLU_SILU, t.t, xq2.t, sc2.t, su2.t)
+        check(t, xq2, sc2, su2)
     ys = [Guarded(M, torch.float32) for _ in range(3)]
     qg.qgemv_q2_batch([(W, xq, su, sc, ys[0].t), (W1, xq, su, sc, ys[1].t), (W, xq, su, sc, ys[2].t, res)])
     check(*ys)
