@@ -106,15 +106,15 @@ def main():
     # ---------------- inputs (seeded, synthetic; shapes of the pages' model)
     t0 = time.time()
     host = {}
-    for name in ("C3_gate", "C3_up", "C3_down"):
+    for name in ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120", "q2_g128_down_5120x17408"):
         host[name] = synth.config_inputs(name)
-    q4, rs4, xs4 = synth.config_inputs("C4")
-    x_dn = host["C3_down"][1]
-    x_gu = host["C3_gate"][1]
+    q4, rs4, xs4 = synth.config_inputs("q8row_lm_head_248320x5120")
+    x_dn = host["q2_g128_down_5120x17408"][1]
+    x_gu = host["q2_g128_gate_17408x5120"][1]
     log(f"inputs generated in {time.time() - t0:.1f}s")
 
     W = {}
-    for name in ("C3_gate", "C3_up", "C3_down"):
+    for name in ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120", "q2_g128_down_5120x17408"):
         c = synth.CONFIGS[name]
         W[name] = qg.Q2Weight.from_blocks(host[name][0], c["M"], c["K"], c["group"], dev)
     L4 = qg.Q8RowWeight.from_host(q4, rs4, dev)
@@ -142,20 +142,20 @@ def main():
         qg.qquant_act_i8(xdn_d, xq_dn, sc_dn, su_dn)
 
     def k_gate():
-        qg.qgemv_q2(W["C3_gate"], xq_gu, su_gu, sc_gu, y["C3_gate"], ws["C3_gate"])
+        qg.qgemv_q2(W["q2_g128_gate_17408x5120"], xq_gu, su_gu, sc_gu, y["q2_g128_gate_17408x5120"], ws["q2_g128_gate_17408x5120"])
 
     def k_up():
-        qg.qgemv_q2(W["C3_up"], xq_gu, su_gu, sc_gu, y["C3_up"], ws["C3_up"])
+        qg.qgemv_q2(W["q2_g128_up_17408x5120"], xq_gu, su_gu, sc_gu, y["q2_g128_up_17408x5120"], ws["q2_g128_up_17408x5120"])
 
-    Mgu_ = W["C3_gate"].M
-    ws_pair = torch.zeros(max(1, qg.qgemv_q2_dual_ws_bytes(Mgu_, Kgu, W["C3_gate"].group, 0)),
+    Mgu_ = W["q2_g128_gate_17408x5120"].M
+    ws_pair = torch.zeros(max(1, qg.qgemv_q2_dual_ws_bytes(Mgu_, Kgu, W["q2_g128_gate_17408x5120"].group, 0)),
                           dtype=torch.uint8, device=dev)
 
     def k_gate_up():
-        qg.qgemv_q2_dual(W["C3_gate"], W["C3_up"], xq_gu, su_gu, sc_gu, y["C3_gate"], y["C3_up"], ws_pair)
+        qg.qgemv_q2_dual(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_gu, su_gu, sc_gu, y["q2_g128_gate_17408x5120"], y["q2_g128_up_17408x5120"], ws_pair)
 
     def k_down():
-        qg.qgemv_q2(W["C3_down"], xq_dn, su_dn, sc_dn, y["C3_down"], ws["C3_down"])
+        qg.qgemv_q2(W["q2_g128_down_5120x17408"], xq_dn, su_dn, sc_dn, y["q2_g128_down_5120x17408"], ws["q2_g128_down_5120x17408"])
 
     def k_lm_head():
         L4.gemv(xs4_d, y4)
@@ -177,7 +177,7 @@ def main():
     k_gate()
     k_up()
     torch.cuda.synchronize()
-    single = {n: y[n].clone() for n in ("C3_gate", "C3_up")}
+    single = {n: y[n].clone() for n in ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120")}
     step()
     torch.cuda.synchronize()
     for n in single:
@@ -269,12 +269,12 @@ def main():
     # g64 Q2 GEMV (with its quantiser), each back to back in a graph
     small = []
     if not args.no_breakdown:
-        q1, rs1, xs1 = synth.config_inputs("C1")
+        q1, rs1, xs1 = synth.config_inputs("q8row_256x512")
         W1 = qg.Q8RowWeight.from_host(q1, rs1, dev)
         xs1_d = torch.from_numpy(xs1).to(dev)
         y1 = torch.empty(q1.shape[0], dtype=torch.float32, device=dev)
-        c2 = synth.CONFIGS["C2"]
-        b2s, x2s = synth.config_inputs("C2")
+        c2 = synth.CONFIGS["q2_g64_4096x4096"]
+        b2s, x2s = synth.config_inputs("q2_g64_4096x4096")
         W2s = qg.Q2Weight.from_blocks(b2s, c2["M"], c2["K"], c2["group"], dev)
         x2s_d = torch.from_numpy(x2s).to(dev)
         xq2s = torch.empty(c2["K"], dtype=torch.int8, device=dev)
@@ -292,12 +292,12 @@ def main():
 
     kernels = {}
     for name, fn, nbytes, n in small + ([] if args.no_breakdown else [("act_quant_K5120", k_quant_gu, None, 50),
-                                ("q2_gate_17408x5120_g128", k_gate, q2_bytes["C3_gate"], 20),
-                                ("q2_up_17408x5120_g128", k_up, q2_bytes["C3_up"], 20),
+                                ("q2_gate_17408x5120_g128", k_gate, q2_bytes["q2_g128_gate_17408x5120"], 20),
+                                ("q2_up_17408x5120_g128", k_up, q2_bytes["q2_g128_up_17408x5120"], 20),
                                 ("q2_gate_up_pair_2x17408x5120_g128", k_gate_up,
-                                 q2_bytes["C3_gate"] + q2_bytes["C3_up"], 20),
+                                 q2_bytes["q2_g128_gate_17408x5120"] + q2_bytes["q2_g128_up_17408x5120"], 20),
                                 ("act_quant_K17408", k_quant_dn, None, 50),
-                                ("q2_down_5120x17408_g128", k_down, q2_bytes["C3_down"], 20),
+                                ("q2_down_5120x17408_g128", k_down, q2_bytes["q2_g128_down_5120x17408"], 20),
                                 ("q8row_lm_head_248320x5120", k_lm_head, lm_bytes, 10)]):
         us = kernel_us(fn, n)
         ent = {"us": round(us, 3)}
@@ -337,22 +337,22 @@ def main():
         h_d = torch.from_numpy(rng.standard_normal(Kgu, dtype=np.float32)).to(dev)
         nw_d = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(Kgu)).astype(np.float32)).to(dev)
         h_out = torch.empty(Kgu, dtype=torch.float32, device=dev)
-        Mgu = W["C3_gate"].M
+        Mgu = W["q2_g128_gate_17408x5120"].M
         ws_gu = torch.zeros(max(1, qg.qgemv_q2_dual_ws_bytes(Mgu, Kgu, 128, 0)), dtype=torch.uint8, device=dev)
         g_buf = torch.empty(Mgu, dtype=torch.float32, device=dev)
         u_buf = torch.empty(Mgu, dtype=torch.float32, device=dev)
 
         def ffn_fused():
             qg.qquant_rmsnorm_i8(h_d, nw_d, 1e-6, xq_gu, sc_gu, su_gu)
-            qg.qgemv_q2_gate_up_glu(W["C3_gate"], W["C3_up"], xq_gu, su_gu, sc_gu, qg.QG_GLU_SILU, g_buf,
+            qg.qgemv_q2_gate_up_glu(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_gu, su_gu, sc_gu, qg.QG_GLU_SILU, g_buf,
                                     xq_dn, sc_dn, su_dn)
-            qg.qgemv_q2_accum(W["C3_down"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["C3_down"])
+            qg.qgemv_q2_accum(W["q2_g128_down_5120x17408"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["q2_g128_down_5120x17408"])
 
         def ffn_dual_then_glu():  # the same block with the gated product as its own launches
             qg.qquant_rmsnorm_i8(h_d, nw_d, 1e-6, xq_gu, sc_gu, su_gu)
-            qg.qgemv_q2_dual(W["C3_gate"], W["C3_up"], xq_gu, su_gu, sc_gu, g_buf, u_buf, ws_gu)
+            qg.qgemv_q2_dual(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_gu, su_gu, sc_gu, g_buf, u_buf, ws_gu)
             qg.qquant_glu_i8(g_buf, u_buf, qg.QG_GLU_SILU, g_buf, xq_dn, sc_dn, su_dn)
-            qg.qgemv_q2_accum(W["C3_down"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["C3_down"])
+            qg.qgemv_q2_accum(W["q2_g128_down_5120x17408"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["q2_g128_down_5120x17408"])
 
         def step_fused():
             ffn_fused()
@@ -411,21 +411,21 @@ def main():
     if not args.no_breakdown:
         sustained = {}
         xs_by_k = {Kgu: (xq_gu, su_gu, sc_gu), Kdn: (xq_dn, su_dn, sc_dn)}
-        c2 = synth.CONFIGS["C2"]
-        b2, x2 = synth.config_inputs("C2")
+        c2 = synth.CONFIGS["q2_g64_4096x4096"]
+        b2, x2 = synth.config_inputs("q2_g64_4096x4096")
         W2 = qg.Q2Weight.from_blocks(b2, c2["M"], c2["K"], c2["group"], dev)
         xq2 = torch.empty(c2["K"], dtype=torch.int8, device=dev)
         sc2 = torch.empty(1, dtype=torch.float32, device=dev)
         su2 = torch.empty(c2["K"] // 64, dtype=torch.int32, device=dev)
         qg.qquant_act_i8(torch.from_numpy(x2).to(dev), xq2, sc2, su2)
         xs_by_k[c2["K"]] = (xq2, su2, sc2)
-        for label, W0, mode in [("C2 Q2 g64 4096x4096", W2, "single"),
-                                ("C2 Q2 g64 4096x4096, 16 per launch", W2, "batch"),
-                                ("C3 gate Q2 g128 17408x5120", W["C3_gate"], "single"),
-                                ("C3 gate|up dual Q2 g128 2x17408x5120", W["C3_gate"], "dual"),
-                                ("C3 gate Q2 g128 17408x5120, 16 per launch", W["C3_gate"], "batch"),
-                                ("C3 down Q2 g128 5120x17408", W["C3_down"], "single"),
-                                ("C3 down Q2 g128 5120x17408, 16 per launch", W["C3_down"], "batch")]:
+        for label, W0, mode in [("Q2 g64 4096x4096", W2, "single"),
+                                ("Q2 g64 4096x4096, 16 per launch", W2, "batch"),
+                                ("gate Q2 g128 17408x5120", W["q2_g128_gate_17408x5120"], "single"),
+                                ("gate|up dual Q2 g128 2x17408x5120", W["q2_g128_gate_17408x5120"], "dual"),
+                                ("gate Q2 g128 17408x5120, 16 per launch", W["q2_g128_gate_17408x5120"], "batch"),
+                                ("down Q2 g128 5120x17408", W["q2_g128_down_5120x17408"], "single"),
+                                ("down Q2 g128 5120x17408, 16 per launch", W["q2_g128_down_5120x17408"], "batch")]:
             dual = mode == "dual"
             nb_w = W0.M * (W0.K // W0.group) * (2 + W0.group // 4)
             ncopy = max(2, -(-(512 << 20) // nb_w))
@@ -473,9 +473,9 @@ def main():
     if not args.no_gemm:
         del L4
         torch.cuda.empty_cache()
-        c5 = synth.CONFIGS["C5"]
+        c5 = synth.CONFIGS["q8row_gemm_512x17408x5120"]
         nb5, M5, K5 = c5["nb"], c5["M"], c5["K"]
-        q5, rs5, xs5 = synth.config_inputs("C5")
+        q5, rs5, xs5 = synth.config_inputs("q8row_gemm_512x17408x5120")
         W5 = qg.Q8RowWeight.from_host(q5, rs5, dev)
         del q5
         xs5_d = torch.from_numpy(xs5).to(dev)
@@ -543,10 +543,10 @@ def main():
     # matrix (17408 x 5120 g128): row-batched quantiser, then int8 MFMA
     q2gemm = None
     if not args.no_gemm:
-        cg = synth.CONFIGS["C3_gate"]
+        cg = synth.CONFIGS["q2_g128_gate_17408x5120"]
         Mg, Kg, Gg = cg["M"], cg["K"], cg["group"]
         nbq = 512
-        Wq = W["C3_gate"]
+        Wq = W["q2_g128_gate_17408x5120"]
         Xq = torch.from_numpy(synth.rng_for(20260 + 950).standard_normal((nbq, Kg), dtype=np.float32)).to(dev)
         xq_r = torch.empty((nbq, Kg), dtype=torch.int8, device=dev)
         sc_r = torch.empty(nbq, dtype=torch.float32, device=dev)
@@ -578,7 +578,7 @@ def main():
         # the whole prefill FFN block over the same 512 tokens: RMSNorm+quant
         # rows -> gate, up products -> SiLU gate+quant rows -> down product
         # with the residual (as the qxmx page's ffn_forward_b)
-        Wd = W["C3_down"]
+        Wd = W["q2_g128_down_5120x17408"]
         Fd = Wd.K
         H = torch.from_numpy(synth.rng_for(20260 + 951).standard_normal((nbq, Kg), dtype=np.float32)).to(dev)
         Hout = torch.empty_like(H)
@@ -595,11 +595,11 @@ def main():
         ws_p = torch.empty(nws_p, dtype=torch.uint8, device=dev) if nws_p else None
 
         def k_pair():
-            qg.qgemm_q2_batched_dual(W["C3_gate"], W["C3_up"], xq_r, su_r, sc_r, G, U, ws=ws_p)
+            qg.qgemm_q2_batched_dual(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_r, su_r, sc_r, G, U, ws=ws_p)
 
         def ffn_prefill():
             qg.qquant_rmsnorm_i8_rows(H, nw, 1e-6, xq_r, sc_r, su_r)
-            qg.qgemm_q2_batched_dual(W["C3_gate"], W["C3_up"], xq_r, su_r, sc_r, G, U, ws=ws_p)
+            qg.qgemm_q2_batched_dual(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_r, su_r, sc_r, G, U, ws=ws_p)
             qg.qquant_glu_i8_rows(G, U, qg.QG_GLU_SILU, G, xq_f, sc_f, su_f)
             qg.qgemm_q2_batched(Wd, xq_f, su_f, sc_f, Hout, accum=H, ws=ws_d)
 
@@ -626,12 +626,12 @@ def main():
 
         def oracle_step():
             rq, rsc, _ = oracle.act_quant_i8(x_gu)
-            for name in ("C3_gate", "C3_up"):
+            for name in ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120"):
                 c = synth.CONFIGS[name]
                 oracle.q2_gemv(host[name][0], c["M"], c["K"], c["group"], rq, rsc)
             rq, rsc, _ = oracle.act_quant_i8(x_dn)
-            c = synth.CONFIGS["C3_down"]
-            oracle.q2_gemv(host["C3_down"][0], c["M"], c["K"], c["group"], rq, rsc)
+            c = synth.CONFIGS["q2_g128_down_5120x17408"]
+            oracle.q2_gemv(host["q2_g128_down_5120x17408"][0], c["M"], c["K"], c["group"], rq, rsc)
             oracle.q8row_gemv(q4, rs4, xs4)
 
         # whole steps until about 10 s of CPU work (at least one)

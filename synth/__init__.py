@@ -16,8 +16,8 @@ Formats produced (as the pages define them):
   2-bit codes.  Independent uniform codes 0..3, four per byte, make every
   code byte a uniform random byte, so the code bytes are drawn directly.
 
-Seeds: ``numpy.random.PCG64(seed)``; the default seed of a configuration is
-``20260 + config id``.
+Seeds: ``numpy.random.PCG64(seed)``; the default seed of a workload is
+``20260 + its seed id`` (``SEED_IDS``), plus 100 per FFN-matrix substream.
 """
 from __future__ import annotations
 
@@ -28,17 +28,21 @@ SEED_BASE = 20260
 # The five workloads.  Shapes follow the pages' engine (model width 5120,
 # FFN width 17408, a ~248K-row vocabulary projection).
 CONFIGS = {
-    "C1": dict(kind="q8row", M=256, K=512, rs=(0.001, 0.01)),
-    "C2": dict(kind="q2", M=4096, K=4096, group=64),
-    "C3_gate": dict(kind="q2", M=17408, K=5120, group=128),
-    "C3_up": dict(kind="q2", M=17408, K=5120, group=128),
-    "C3_down": dict(kind="q2", M=5120, K=17408, group=128),
-    "C4": dict(kind="q8row", M=248320, K=5120, rs=(0.0005, 0.005)),
-    "C5": dict(kind="q8gemm", nb=512, M=17408, K=5120, rs=(0.001, 0.01)),
+    "q8row_256x512": dict(kind="q8row", M=256, K=512, rs=(0.001, 0.01)),
+    "q2_g64_4096x4096": dict(kind="q2", M=4096, K=4096, group=64),
+    "q2_g128_gate_17408x5120": dict(kind="q2", M=17408, K=5120, group=128),
+    "q2_g128_up_17408x5120": dict(kind="q2", M=17408, K=5120, group=128),
+    "q2_g128_down_5120x17408": dict(kind="q2", M=5120, K=17408, group=128),
+    "q8row_lm_head_248320x5120": dict(kind="q8row", M=248320, K=5120, rs=(0.0005, 0.005)),
+    "q8row_gemm_512x17408x5120": dict(kind="q8gemm", nb=512, M=17408, K=5120, rs=(0.001, 0.01)),
 }
-CONFIG_IDS = {"C1": 1, "C2": 2, "C3_gate": 3, "C3_up": 3, "C3_down": 3, "C4": 4, "C5": 5}
-# distinct streams for the three C3 matrices
-_SUBSTREAM = {"C3_gate": 0, "C3_up": 1, "C3_down": 2}
+# Seed id of each workload: the default seed is SEED_BASE + id, plus 100 per
+# substream for the three FFN matrices, which share id 3.
+SEED_IDS = {"q8row_256x512": 1, "q2_g64_4096x4096": 2,
+            "q2_g128_gate_17408x5120": 3, "q2_g128_up_17408x5120": 3, "q2_g128_down_5120x17408": 3,
+            "q8row_lm_head_248320x5120": 4, "q8row_gemm_512x17408x5120": 5}
+# distinct streams for the three FFN matrices
+_SUBSTREAM = {"q2_g128_gate_17408x5120": 0, "q2_g128_up_17408x5120": 1, "q2_g128_down_5120x17408": 2}
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -46,7 +50,7 @@ def rng_for(seed: int) -> np.random.Generator:
 
 
 def default_seed(name: str) -> int:
-    return SEED_BASE + CONFIG_IDS[name] + 100 * _SUBSTREAM.get(name, 0)
+    return SEED_BASE + SEED_IDS[name] + 100 * _SUBSTREAM.get(name, 0)
 
 
 def q8row_inputs(M: int, K: int, rs_range=(0.001, 0.01), seed: int = 0, *,

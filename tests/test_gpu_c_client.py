@@ -23,7 +23,7 @@ CLIENT = os.path.join(HERE, "c_abi", "_build", "qgemv_c_client")
 @pytest.mark.parametrize("M2,K2,group,split", [(300, 1024, 128, 4), (4096, 4096, 64, 0)])
 def test_c_client_matches_oracle(tmp_path, M2, K2, group, split):
     assert os.path.exists(CLIENT), "the C client is not built (run __graft_entry__.build())"
-    q8, rs, xs = synth.config_inputs("C1")
+    q8, rs, xs = synth.config_inputs("q8row_256x512")
     M8, K8 = q8.shape
     blob, x2 = synth.q2_inputs(M2, K2, group, seed=81 + M2)
     inp, outp = tmp_path / "in.bin", tmp_path / "out.bin"

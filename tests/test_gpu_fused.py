@@ -86,10 +86,10 @@ def test_dual_equals_two_calls(M, K, group, split):
 def test_dual_c3_gate_up():
     """The FFN gate and up matrices of the 17408 x 5120 g128 workload, one activation."""
     m = qg()
-    c = synth.CONFIGS["C3_gate"]
+    c = synth.CONFIGS["q2_g128_gate_17408x5120"]
     M, K, group = c["M"], c["K"], c["group"]
-    bg, x = synth.config_inputs("C3_gate")
-    bu, _ = synth.config_inputs("C3_up")
+    bg, x = synth.config_inputs("q2_g128_gate_17408x5120")
+    bu, _ = synth.config_inputs("q2_g128_up_17408x5120")
     Wg = m.Q2Weight.from_blocks(bg, M, K, group)
     Wu = m.Q2Weight.from_blocks(bu, M, K, group)
     xq_h, sc_h, _, (xq, sc, suma) = gpu_act_quant(x)
@@ -100,7 +100,7 @@ def test_dual_c3_gate_up():
     rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 1200)]))
     for blob, y, name in ((bg, yg, "gate"), (bu, yu, "up")):
         yref, mass = oracle.q2_gemv(blob, M, K, group, xq_h, sc_h, rows=rows)
-        within(y[rows], yref, mass, what=f"C3 dual {name}")
+        within(y[rows], yref, mass, what=f"gate|up dual 17408x5120 {name}")
 
 
 def test_dual_same_weight_twice():
@@ -143,13 +143,13 @@ def test_accum_equals_gemv_then_add(M, K, group, split):
 
 def test_accum_c3_down_residual():
     """The 5120 x 17408 down projection added to a residual stream (auto split)."""
-    c = synth.CONFIGS["C3_down"]
+    c = synth.CONFIGS["q2_g128_down_5120x17408"]
     M, K, group = c["M"], c["K"], c["group"]
-    blob, x = synth.config_inputs("C3_down")
+    blob, x = synth.config_inputs("q2_g128_down_5120x17408")
     accum = synth.rng_for(552).standard_normal(M).astype(np.float32)
     rng = synth.rng_for(553)
     rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 600)]))
-    _accum_check(blob, M, K, group, x, accum, 0, rows=rows, what="C3 down + residual")
+    _accum_check(blob, M, K, group, x, accum, 0, rows=rows, what="down 5120x17408 + residual")
 
 
 def test_accum_zero_projection_returns_residual():

@@ -112,8 +112,8 @@ def test_gemm_zero_and_int8_min_rows():
 
 
 def test_gemm_config_c5_sampled_entries():
-    c = synth.CONFIGS["C5"]
-    q, rs, xs = synth.config_inputs("C5")
+    c = synth.CONFIGS["q8row_gemm_512x17408x5120"]
+    q, rs, xs = synth.config_inputs("q8row_gemm_512x17408x5120")
     nb, M, K = c["nb"], c["M"], c["K"]
     y = gpu_gemm(q, rs, xs, 0)
     assert np.all(np.isfinite(y))
@@ -121,7 +121,7 @@ def test_gemm_config_c5_sampled_entries():
     bs = np.concatenate([np.repeat(np.arange(nb), 4), rng.integers(0, nb, 20000)])
     os_ = np.concatenate([np.tile([0, 1, M - 2, M - 1], nb), rng.integers(0, M, 20000)])
     yref, mass = oracle.q8row_gemm(q, rs, xs, entries=(bs, os_))
-    within(y[bs, os_], yref, mass, "C5 sampled")
+    within(y[bs, os_], yref, mass, "GEMM 512x17408x5120 sampled")
 
 
 def test_gemm_workspace_too_small_is_rejected():

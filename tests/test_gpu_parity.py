@@ -111,10 +111,10 @@ def test_q8row_small_shapes(M, K):
 
 
 def test_q8row_config_c1_all_outputs():
-    q, rs, xs = synth.config_inputs("C1")
+    q, rs, xs = synth.config_inputs("q8row_256x512")
     y = gpu_q8row(q, rs, xs)
     yref, mass = oracle.q8row_gemv(q, rs, xs)
-    within(y, yref, mass, what="C1")
+    within(y, yref, mass, what="q8row 256x512")
 
 
 def test_q8row_int8_min_and_zero_rows():
@@ -133,7 +133,7 @@ def test_q8row_int8_min_and_zero_rows():
 
 
 def test_q8row_config_c4_sampled_rows():
-    q, rs, xs = synth.config_inputs("C4")
+    q, rs, xs = synth.config_inputs("q8row_lm_head_248320x5120")
     M = q.shape[0]
     y = gpu_q8row(q, rs, xs)
     assert np.all(np.isfinite(y))
@@ -141,7 +141,7 @@ def test_q8row_config_c4_sampled_rows():
     rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M),
                                      rng.integers(0, M, 6000)]))
     yref, mass = oracle.q8row_gemv(q, rs, xs, rows=rows)
-    within(y[rows], yref, mass, what="C4 sampled")
+    within(y[rows], yref, mass, what="lm_head 248320x5120 sampled")
 
 
 # ------------------------------------------------------------------ Q2 GEMV --
@@ -193,11 +193,11 @@ def test_q2_small_shapes(M, K, group):
 
 
 def test_q2_config_c2_all_outputs():
-    blob, x = synth.config_inputs("C2")
-    check_q2(blob, 4096, 4096, 64, x, what="C2")
+    blob, x = synth.config_inputs("q2_g64_4096x4096")
+    check_q2(blob, 4096, 4096, 64, x, what="Q2 g64 4096x4096")
 
 
-@pytest.mark.parametrize("name", ["C3_gate", "C3_up", "C3_down"])
+@pytest.mark.parametrize("name", ["q2_g128_gate_17408x5120", "q2_g128_up_17408x5120", "q2_g128_down_5120x17408"])
 def test_q2_config_c3_sampled_rows(name):
     c = synth.CONFIGS[name]
     blob, x = synth.config_inputs(name)

@@ -88,9 +88,9 @@ def test_q2_gemm_residual(in_place):
 
 def test_q2_gemm_c3_gate_prefill_sampled():
     """The 17408 x 5120 g128 gate matrix over 512 prefill tokens, sampled entries."""
-    c = synth.CONFIGS["C3_gate"]
+    c = synth.CONFIGS["q2_g128_gate_17408x5120"]
     M, K, group = c["M"], c["K"], c["group"]
-    blob, _ = synth.config_inputs("C3_gate")
+    blob, _ = synth.config_inputs("q2_g128_gate_17408x5120")
     nb = 512
     X = token_rows(nb, K, 6400)
     y, xq, sc = run_gemm(blob, M, K, group, X)
@@ -99,15 +99,15 @@ def test_q2_gemm_c3_gate_prefill_sampled():
     bs = np.concatenate([rng.integers(0, nb, 3000), np.full(64, nb - 1), np.zeros(64, np.int64)])
     os_ = np.concatenate([rng.integers(0, M, 3000), np.arange(M - 64, M), np.arange(64)])
     yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, entries=(bs, os_))
-    within(y[bs, os_], yref, mass, what="C3 gate prefill")
+    within(y[bs, os_], yref, mass, what="gate 17408x5120 prefill")
 
 
 def test_q2_gemm_c3_down_prefill_split_sampled():
     """The 5120 x 17408 g128 down matrix over 512 tokens: its tiles take a K split."""
-    c = synth.CONFIGS["C3_down"]
+    c = synth.CONFIGS["q2_g128_down_5120x17408"]
     M, K, group = c["M"], c["K"], c["group"]
     assert qg().qgemm_q2_batched_ws_bytes(M, K, group, 512) > 0
-    blob, _ = synth.config_inputs("C3_down")
+    blob, _ = synth.config_inputs("q2_g128_down_5120x17408")
     X = token_rows(512, K, 6450)
     acc = synth.rng_for(6451).standard_normal((512, M)).astype(np.float32)
     y, xq, sc = run_gemm(blob, M, K, group, X, accum=acc)
@@ -115,7 +115,7 @@ def test_q2_gemm_c3_down_prefill_split_sampled():
     bs = np.concatenate([rng.integers(0, 512, 1500), np.full(32, 511)])
     os_ = np.concatenate([rng.integers(0, M, 1500), np.arange(M - 32, M)])
     yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, accum=acc, entries=(bs, os_))
-    within(y[bs, os_], yref, mass + U32 / REL * np.abs(yref), what="C3 down prefill + residual")
+    within(y[bs, os_], yref, mass + U32 / REL * np.abs(yref), what="down 5120x17408 prefill + residual")
 
 
 @pytest.mark.parametrize("nb,M,K,group", [(40, 300, 1024, 64), (7, 64, 256, 128)])
