@@ -2,10 +2,14 @@
 """Benchmark of the weight-only-quantized decode hot path on one MI355X.
 
 A step is one pass of the batch-1 decode path at the pages' model shapes,
-captured once in a HIP graph and replayed:
-    quantise x (K=5120) -> Q2 g128 gate and up GEMVs 17408x5120 (one launch
-    for the pair) -> quantise h (K=17408) -> Q2 g128 down GEMV 5120x17408
-    (split-K partials and their reduce) -> q8_row lm_head GEMV 248320x5120.
+captured once in a HIP graph and replayed, three launches:
+    Q2 g128 gate and up GEMVs 17408x5120 (one launch for the pair, the f32
+    activation x (K=5120) quantised inside it) -> Q2 g128 down GEMV
+    5120x17408 (h, K=17408, quantised inside the launch; split-K partials
+    added by the last workgroup of each row tile) -> q8_row lm_head GEMV
+    248320x5120.
+The same step as six launches (the quantisers and the split reduce as
+launches of their own, the same bits) is timed beside it.
 `value` is the weight bytes the step streams (the formats' own bytes: 34 B
 per 128 Q2 weights, K+4 bytes per q8_row row) divided by the step time:
 batch-1 quantized GEMV weight GB/s.  Inputs are synthetic and seeded, already
@@ -17,9 +21,9 @@ kernel's roofline (HIP events on the launch stream), the CPU oracle timed
 on this host over the same step (cpu_baseline), and the second half of the
 metric, the batched prefill q8_row GEMM (nb=512 x 17408 x 5120, int8 MFMA
 with exact activation limbs), in algorithmic TFLOP/s (`prefill_gemm`), and
-the FFN block in its fused form (RMSNorm+quant, gate|up in one launch,
-SiLU-gate+quant, down with the residual in its epilogue) next to the
-main step (`fused_ffn`), each Q2 GEMV's streaming rate from HBM
+the FFN block in its fused form (RMSNorm+quant, gate|up with the SiLU gate,
+quant, down with the residual: two launches) next to the main step
+(`fused_ffn`), each Q2 GEMV's streaming rate from HBM
 over rotated weight copies launched back to back (`q2_sustained`), and the
 batched prefill Q2 product over 512 token rows (`prefill_q2_gemm`).
 
@@ -154,17 +158,37 @@ def main():
     def k_gate_up():
         qg.qgemv_q2_dual(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_gu, su_gu, sc_gu, y["q2_g128_gate_17408x5120"], y["q2_g128_up_17408x5120"], ws_pair)
 
+    Wdn = W["q2_g128_down_5120x17408"]
+    # the down projection's split: the in-launch form's automatic choice
+    # (its partials are added inside the launch); the six-launch form is run
+    # with the same split so that the two give the same bits
+    S_dn = qg.qgemv_q2_x_auto_split(Wdn.M, Wdn.K, Wdn.group)
+    ws_dn6 = torch.zeros(max(1, qg.qgemv_q2_ws_bytes(Wdn.M, Wdn.K, Wdn.group, S_dn)), dtype=torch.uint8, device=dev)
+    ws_dnx = qg.qgemv_q2_x_workspace(Wdn.M, Wdn.K, Wdn.group, S_dn, dev)
+
     def k_down():
-        qg.qgemv_q2(W["q2_g128_down_5120x17408"], xq_dn, su_dn, sc_dn, y["q2_g128_down_5120x17408"], ws["q2_g128_down_5120x17408"])
+        qg.qgemv_q2(Wdn, xq_dn, su_dn, sc_dn, y["q2_g128_down_5120x17408"], ws_dn6, S_dn)
+
+    def k_gate_up_x():  # the activation quantiser inside the pair launch
+        qg.qgemv_q2_dual_x(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xgu_d,
+                           y["q2_g128_gate_17408x5120"], y["q2_g128_up_17408x5120"])
+
+    def k_down_x():  # quantiser and split-K reduce inside the launch
+        qg.qgemv_q2_x(Wdn, xdn_d, y["q2_g128_down_5120x17408"], ws=ws_dnx, split_k=S_dn)
 
     def k_lm_head():
         L4.gemv(xs4_d, y4)
 
-    def step():
+    def step6():  # the same step as six launches: quantisers and the split reduce on their own
         k_quant_gu()
         k_gate_up()
         k_quant_dn()
         k_down()
+        k_lm_head()
+
+    def step():
+        k_gate_up_x()
+        k_down_x()
         k_lm_head()
 
     q2_bytes = {n: W[n].M * (W[n].K // W[n].group) * (2 + W[n].group // 4) for n in W}
@@ -178,11 +202,17 @@ def main():
     k_up()
     torch.cuda.synchronize()
     single = {n: y[n].clone() for n in ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120")}
-    step()
+    step6()
     torch.cuda.synchronize()
     for n in single:
         assert torch.equal(y[n], single[n]), f"the pair launch's {n} output differs from the single GEMV"
     ref = {n: y[n].clone() for n in y}
+    for n in y:
+        y[n].fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    for n in y:
+        assert torch.equal(y[n], ref[n]), f"the three-launch step's {n} output differs from the six-launch step"
     ref4 = y4.clone()
 
     def capture(fn, n=1):
@@ -224,6 +254,24 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s (wall {wall * 1e6 / args.steps:.1f} us/step)")
+
+    # the same step as six launches, timed the same way (context)
+    g_step6 = capture(step6)
+    for _ in range(3):
+        g_step6.replay()
+        torch.cuda.synchronize()
+        for n in y:
+            assert torch.equal(y[n], ref[n]), f"graph replay of the six-launch step's {n} differs"
+    for _ in range(args.warmup):
+        g_step6.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        g_step6.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_step6 = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    log(f"six-launch step {us_step6:.1f} us")
 
     # ---------------- per-kernel times (graph of n back-to-back launches)
     def kernel_us(fn, n):
@@ -298,6 +346,9 @@ def main():
                                  q2_bytes["q2_g128_gate_17408x5120"] + q2_bytes["q2_g128_up_17408x5120"], 20),
                                 ("act_quant_K17408", k_quant_dn, None, 50),
                                 ("q2_down_5120x17408_g128", k_down, q2_bytes["q2_g128_down_5120x17408"], 20),
+                                ("q2_gate_up_pair_x_2x17408x5120_g128", k_gate_up_x,
+                                 q2_bytes["q2_g128_gate_17408x5120"] + q2_bytes["q2_g128_up_17408x5120"], 20),
+                                ("q2_down_x_5120x17408_g128", k_down_x, q2_bytes["q2_g128_down_5120x17408"], 20),
                                 ("q8row_lm_head_248320x5120", k_lm_head, lm_bytes, 10)]):
         us = kernel_us(fn, n)
         ent = {"us": round(us, 3)}
@@ -342,66 +393,70 @@ def main():
         g_buf = torch.empty(Mgu, dtype=torch.float32, device=dev)
         u_buf = torch.empty(Mgu, dtype=torch.float32, device=dev)
 
-        def ffn_fused():
-            qg.qquant_rmsnorm_i8(h_d, nw_d, 1e-6, xq_gu, sc_gu, su_gu)
-            qg.qgemv_q2_gate_up_glu(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_gu, su_gu, sc_gu, qg.QG_GLU_SILU, g_buf,
-                                    xq_dn, sc_dn, su_dn)
-            qg.qgemv_q2_accum(W["q2_g128_down_5120x17408"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["q2_g128_down_5120x17408"])
+        Wg_, Wu_ = W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"]
+        ws_glu = qg.qgemv_q2_gate_up_glu_x_workspace(Mgu, dev)
 
-        def ffn_dual_then_glu():  # the same block with the gated product as its own launches
+        def ffn_x():  # two launches: the producers and the split reduce inside the GEMV launches
+            qg.qgemv_q2_gate_up_glu_x(Wg_, Wu_, h_d, qg.QG_GLU_SILU, g_buf, ws_glu, norm_w=nw_d, eps=1e-6)
+            qg.qgemv_q2_x(Wdn, g_buf, h_out, accum=h_d, ws=ws_dnx, split_k=S_dn)
+
+        def ffn_fused():  # five launches: the fused producers as launches of their own
             qg.qquant_rmsnorm_i8(h_d, nw_d, 1e-6, xq_gu, sc_gu, su_gu)
-            qg.qgemv_q2_dual(W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"], xq_gu, su_gu, sc_gu, g_buf, u_buf, ws_gu)
+            qg.qgemv_q2_gate_up_glu(Wg_, Wu_, xq_gu, su_gu, sc_gu, qg.QG_GLU_SILU, g_buf, xq_dn, sc_dn, su_dn)
+            qg.qgemv_q2_accum(Wdn, xq_dn, su_dn, sc_dn, h_d, h_out, ws_dn6, S_dn)
+
+        def ffn_dual_then_glu():  # the gated product as its own launches too
+            qg.qquant_rmsnorm_i8(h_d, nw_d, 1e-6, xq_gu, sc_gu, su_gu)
+            qg.qgemv_q2_dual(Wg_, Wu_, xq_gu, su_gu, sc_gu, g_buf, u_buf, ws_gu)
             qg.qquant_glu_i8(g_buf, u_buf, qg.QG_GLU_SILU, g_buf, xq_dn, sc_dn, su_dn)
-            qg.qgemv_q2_accum(W["q2_g128_down_5120x17408"], xq_dn, su_dn, sc_dn, h_d, h_out, ws["q2_g128_down_5120x17408"])
+            qg.qgemv_q2_accum(Wdn, xq_dn, su_dn, sc_dn, h_d, h_out, ws_dn6, S_dn)
 
-        def step_fused():
-            ffn_fused()
-            k_lm_head()
+        def timed_step(ffn):
+            def fn():
+                ffn()
+                k_lm_head()
+            h_out.fill_(float("nan"))
+            fn()
+            torch.cuda.synchronize()
+            if ref_h is not None:
+                assert torch.equal(h_out, ref_h), f"{ffn.__name__} differs from the other FFN forms"
+            g = capture(fn, 1)
+            for _ in range(3):
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(h_out, ref_h if ref_h is not None else h_out), "graph replay differs from eager"
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / args.steps
 
-        def step_dual_glu():
-            ffn_dual_then_glu()
-            k_lm_head()
-
-        step_fused()
+        ref_h = None
+        ffn_fused()
         torch.cuda.synchronize()
         ref_h = h_out.clone()
-        g_f = capture(step_fused, 1)
-        for _ in range(3):
-            g_f.replay()
-            torch.cuda.synchronize()
-            assert torch.equal(h_out, ref_h), "graph replay of the fused FFN differs from eager"
-        for _ in range(args.warmup):
-            g_f.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            g_f.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        us_fs = a.elapsed_time(b) * 1e3 / args.steps
-        step_dual_glu()
-        torch.cuda.synchronize()
-        assert torch.equal(h_out, ref_h), "the two fused forms differ"
-        g_d = capture(step_dual_glu, 1)
-        for _ in range(args.warmup):
-            g_d.replay()
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(args.steps):
-            g_d.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        us_dg = a.elapsed_time(b) * 1e3 / args.steps
+        us_x = timed_step(ffn_x)
+        us_fs = timed_step(ffn_fused)
+        us_dg = timed_step(ffn_dual_then_glu)
         fused = {"workload": "decode step with the FFN block fused: RMSNorm+quant -> gate|up Q2 GEMV with the "
                              "SiLU gate in its epilogue -> quant -> down Q2 GEMV + residual, then the q8_row lm_head",
-                 "us_per_step": round(us_fs, 2), "GB/s": round(step_bytes / us_fs / 1e3, 1),
-                 "frac_hbm_peak": round(step_bytes / us_fs / 1e3 / HBM_PEAK_GBS, 4),
-                 "launches": 6, "main_step_us_per_step": round(ms_per_step * 1e3, 2), "main_step_launches": 6,
+                 "us_per_step": round(us_x, 2), "GB/s": round(step_bytes / us_x / 1e3, 1),
+                 "frac_hbm_peak": round(step_bytes / us_x / 1e3 / HBM_PEAK_GBS, 4),
+                 "launches": 3,
+                 "form": "qgemv_q2_gate_up_glu_x (RMSNorm + quantiser in the launch, g and u meeting in a "
+                         "workspace) -> qgemv_q2_x (quantiser, split-K reduce and residual in the launch) -> lm_head",
+                 "producers_as_launches_us_per_step": round(us_fs, 2), "producers_as_launches_launches": 6,
                  "gated_product_as_own_launches_us_per_step": round(us_dg, 2),
+                 "main_step_us_per_step": round(ms_per_step * 1e3, 2), "main_step_launches": 3,
                  "step_weight_bytes": step_bytes,
-                 "note": "timed like the main step (graph replays, the lm_head evicting the last-level cache)"}
+                 "note": "timed like the main step (graph replays, the lm_head evicting the last-level cache); "
+                         "all forms give the same bits"}
         log(f"fused FFN: {fused}")
 
     # ---------------- Q2 GEMV streaming rate from HBM: copies of one matrix
@@ -666,8 +721,13 @@ def main():
         "config": {"workload": "decode_step_batch1: act-quant + Q2 g128 FFN (gate, up 17408x5120; "
                                "down 5120x17408) + q8_row lm_head 248320x5120",
                    "step_weight_bytes": step_bytes,
-                   "graph": "hipGraph of six launches: act-quant, gate|up pair, act-quant, down "
-                            "partials, split-K reduce, lm_head",
+                   "graph": "hipGraph of three launches: gate|up pair with the act-quant in the launch "
+                            "(qgemv_q2_dual_x), down with the act-quant and the split-K reduce in the launch "
+                            "(qgemv_q2_x), lm_head",
+                   "down_split_k": S_dn,
+                   "six_launch_form_us_per_step": round(us_step6, 2),
+                   "six_launch_form": "act-quant, gate|up pair, act-quant, down partials, split-K reduce, "
+                                      "lm_head (same bits)",
                    "parallelism": "single GPU"},
         "kernels": kernels,
         "roofline": roofline,

@@ -369,6 +369,95 @@ typedef struct {
  * or residual.                                                             */
 qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream);
 
+/* ---- The decode GEMVs with the activation quantiser in the same launch --
+ *
+ * Each workgroup of these launches quantises the f32 input vector itself by
+ * the rule of qquant_act_i8 (after the RMSNorm of qquant_rmsnorm_i8 when
+ * norm_w is given) and keeps the int8 vector in LDS, so the quantiser is not
+ * a launch of its own; a K split is added up by the last workgroup of each
+ * row tile, so it needs no reduce launch either.  Every output equals the
+ * multi-launch chain it replaces bit for bit.  What a launch saves is its
+ * fixed cost of a few microseconds, which at decode sizes is as much as
+ * streaming 10-20 MB of weights.
+ *   [AQ, PQ gpu_rmsnorm_quant; GV gemv_dpas8 + gemv_reduce; GD
+ *    gemv_dpas8_dual, tmatvec_accum; GU moe_gate_up]
+ * The vector is read by every workgroup while outputs are written, so it
+ * must not overlap any output.  Each workgroup holds its share of K (K
+ * divided by the split, in whole groups): at most 32768 values, or 16384
+ * when M >= 16384 (256 row tiles or more); with the RMSNorm K <= 16384.    */
+
+/* Split factor qgemv_q2_x uses for split_k = 0 (auto) on this shape: 1
+ * when the row tiles fill the GPU (M >= 8192), else the largest split whose
+ * workgroups still all run at once on the 256 CUs (the split costs no
+ * launch here).                                                           */
+int qgemv_q2_x_auto_split(int64_t M, int64_t K, int group);
+
+/* Bytes of workspace qgemv_q2_x needs for this shape and split (split_k 0 =
+ * qgemv_q2_x_auto_split): 0 without a split, else the arrival counters
+ * then the f32 partials.                                                  */
+size_t qgemv_q2_x_ws_bytes(int64_t M, int64_t K, int group, int split_k);
+
+/* Device: y = qgemv_q2(w, quantised x) (+ accum), one launch
+ *   x:         device, f32[K], 16-byte aligned, finite; must not overlap y,
+ *              accum or ws.
+ *   accum:     device, f32[M] residual added as in qgemv_q2_accum, or NULL;
+ *              may be y itself.
+ *   y:         device, f32[M], written.
+ *   ws:        device, >= qgemv_q2_x_ws_bytes(M, K, group, split_k) bytes,
+ *              16-byte aligned (may be NULL when that is 0).  It must be
+ *              all zero before the first call that uses it (allocate it
+ *              zero-filled, or clear it once); every call leaves it all
+ *              zero again, so one workspace serves calls of any shape and
+ *              split.  Calls sharing one ws must not overlap in time.
+ *   split_k:   0 = auto (qgemv_q2_x_auto_split), else 1..16.
+ * y equals qquant_act_i8(x) followed by qgemv_q2 (or qgemv_q2_accum) with
+ * the same split (given explicitly to both), bit for bit.
+ * QG_EINVAL: as qgemv_q2_accum, or null or misaligned x, a share of K
+ * above the limit above, x overlapping y, or a workspace overlapping x.   */
+qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x,
+                     const float *accum, float *y, void *ws, size_t ws_bytes,
+                     int split_k, void *stream);
+
+/* Device: the gate|up pair against one vector quantised in the launch
+ *   x:         device, f32[K], 16-byte aligned.
+ *   norm_w:    device, f32[K] RMSNorm weights (16-byte aligned), or NULL:
+ *              with it the quantised vector is the RMSNorm of
+ *              qquant_rmsnorm_i8 (x, norm_w, eps), K <= 16384.
+ *   y0, y1:    device, f32[M] each, written; must not overlap each other,
+ *              x or norm_w.
+ * y0, y1 equal qquant_act_i8 (or qquant_rmsnorm_i8) followed by
+ * qgemv_q2_dual with split_k = 1, bit for bit.  No workspace, no split.
+ * QG_EINVAL: as qgemv_q2_dual, or as qgemv_q2_x for x, or eps negative
+ * or not finite when norm_w is given.                                     */
+qg_status qgemv_q2_dual_x(const qg_q2_weight *w0, const qg_q2_weight *w1,
+                          const float *x, const float *norm_w, float eps,
+                          float *y0, float *y1, void *stream);
+
+/* Bytes of workspace qgemv_q2_gate_up_glu_x needs for M rows: the
+ * arrival counters, then g and u of each row tile.                        */
+size_t qgemv_q2_gate_up_glu_x_ws_bytes(int64_t M);
+
+/* Device: the gate|up pair with the gated product in its epilogue, against
+ * a vector quantised (optionally RMSNorm-ed) in the same launch
+ *   t = silu(g) * u (kind QG_GLU_SILU) or u * sigmoid(g) (QG_GLU_SIGMOID)
+ *   with g, u the qgemv_q2_dual_x outputs, which meet in ws: the second of
+ *   the two workgroups of a row tile (gate, up) to finish forms t.
+ *   t:         device, f32[M], written; must not overlap x or norm_w.
+ *   ws:        device, >= qgemv_q2_gate_up_glu_x_ws_bytes(M) bytes, 16-byte
+ *              aligned, all zero before the first call (allocate it
+ *              zero-filled); every call leaves it all zero again.  Calls
+ *              sharing one ws must not overlap in time.
+ * t equals qgemv_q2_dual_x followed by the gated product of
+ * qquant_glu_i8, bit for bit; feed it to qgemv_q2_x (the down projection,
+ * with the residual as accum) to finish the FFN block in two launches.
+ * Any M >= 1.  QG_EINVAL: as qgemv_q2_dual_x, or a bad kind, or a short,
+ * misaligned or overlapping workspace.                                    */
+qg_status qgemv_q2_gate_up_glu_x(const qg_q2_weight *w_gate,
+                                 const qg_q2_weight *w_up, const float *x,
+                                 const float *norm_w, float eps, int kind,
+                                 float *t, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 /* Device: the batched (prefill) Q2 product over nb token rows, on int8
  * MFMA   [QG, ffn_forward_b with gemm_gpu_v4]
  *   y[b, o] = act_scale[b] * sum_g d(o, g) * sum_{i in g} (code - 1) * xq[b, i]

@@ -40,7 +40,7 @@ def test_library_exports(name):
 
 def test_abi_and_status_strings():
     L = qg.lib()
-    assert L.qg_abi_version() == 5
+    assert L.qg_abi_version() == 6
     assert L.qg_status_string(0) == b"QG_OK"
     assert L.qg_status_string(1) == b"QG_EINVAL"
     assert L.qg_status_string(2) == b"QG_ELAUNCH"
@@ -309,3 +309,66 @@ def test_c_client_builds_against_the_header(tmp_path):
     import build_client
     out = build_client.build(str(tmp_path / "qgemv_c_client"))
     assert os.path.exists(out)
+
+
+def test_einval_paths_in_launch_quantiser():
+    """qgemv_q2_x, qgemv_q2_dual_x, qgemv_q2_gate_up_glu_x reject bad
+    arguments before any launch (the pointers are never dereferenced)."""
+    L = qg.lib()
+    P = ctypes.c_void_p
+    F = ctypes.c_float
+    a16 = P(0x10000)
+    w = qg.qg_q2_weight(0x100000, 0x200000, 128, 256, 64, 0)
+    w1 = qg.qg_q2_weight(0x300000, 0x400000, 128, 256, 64, 0)
+    X, Y, Y1, WS = P(0x500000), P(0x600000), P(0x700000), P(0x800000)
+    # workspace sizes: counters (tiles rounded up to 64 ints) then [S][Mp] f32
+    assert L.qgemv_q2_x_ws_bytes(128, 256, 64, 1) == 0
+    assert L.qgemv_q2_x_ws_bytes(128, 256, 64, 2) == 256 + 2 * 128 * 4
+    assert L.qgemv_q2_x_ws_bytes(5120, 17408, 128, 4) == 128 * 4 + 4 * 5120 * 4   # 80 tiles -> 128 counters
+    # auto split of the in-launch form: every (tile, split) workgroup in one round
+    assert L.qgemv_q2_x_auto_split(5120, 17408, 128) == 3      # 80 tiles x 3 = 240 workgroups
+    assert L.qgemv_q2_x_auto_split(17408, 5120, 128) == 1      # 272 tiles fill the GPU
+    assert L.qgemv_q2_x_auto_split(4096, 4096, 64) == 4        # 64 tiles x 4 = 256
+    assert L.qgemv_q2_x_auto_split(64, 512, 64) == 1           # 8 groups: no split
+    assert L.qgemv_q2_x_auto_split(64, 1024, 64) == 2
+    assert L.qgemv_q2_x_auto_split(1, 65536, 64) == 16
+    assert L.qgemv_q2_x_ws_bytes(5120, 17408, 128, 0) == 128 * 4 + 3 * 5120 * 4
+    # qgemv_q2_x
+    _einval(L.qgemv_q2_x(None, X, None, Y, None, 0, 1, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), None, None, Y, None, 0, 1, None))            # null x
+    _einval(L.qgemv_q2_x(ctypes.byref(w), P(0x500008), None, Y, None, 0, 1, None))     # x misaligned
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, None, None, 0, 1, None))            # null y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, P(0x500100), None, 0, 1, None))     # y inside x
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, P(0x600004), Y, None, 0, 1, None))        # accum over y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, None, 0, 17, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, None, 0, 2, None))               # no workspace
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, WS, 100, 2, None))               # too small
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x800008), 4096, 2, None))     # ws misaligned
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x500000), 4096, 2, None))     # ws over x
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x600000), 4096, 2, None))     # ws over y
+    big = qg.qg_q2_weight(0x100000, 0x200000, 128, 32768 + 64, 64, 0)
+    _einval(L.qgemv_q2_x(ctypes.byref(big), X, None, Y, None, 0, 1, None))             # K above 32768
+    wide = qg.qg_q2_weight(0x100000, 0x200000, 16384, 16384 + 128, 128, 0)
+    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, Y, None, 0, 1, None))            # share above 16384
+    assert L.qgemv_q2_gate_up_glu_x_ws_bytes(130) == 256 + 2 * 192 * 4
+    # qgemv_q2_dual_x
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), None, X, None, F(0), Y, Y1, None))
+    other = qg.qg_q2_weight(0x300000, 0x400000, 64, 256, 64, 0)
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(other), X, None, F(0), Y, Y1, None))
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), Y, None, None))
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), Y, P(0x600100), None))
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), Y, P(0x500000), None))
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(w1), X, P(0x900008), F(0), Y, Y1, None))
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(w1), X, P(0x900000), F(-1.0), Y, Y1, None))
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(w1), X, P(0x900000), F(float("nan")), Y, Y1, None))
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(w), ctypes.byref(w1), X, P(0x600000), F(0), Y, Y1, None))  # norm_w = y0
+    wn = qg.qg_q2_weight(0x100000, 0x200000, 128, 16384 + 64, 64, 0)
+    wn1 = qg.qg_q2_weight(0x300000, 0x400000, 128, 16384 + 64, 64, 0)
+    _einval(L.qgemv_q2_dual_x(ctypes.byref(wn), ctypes.byref(wn1), X, P(0x900000), F(0), Y, Y1, None))
+    # qgemv_q2_gate_up_glu_x
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 2, Y, WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, None, WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, P(0x500010), WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, None, 0, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, WS, 100, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, P(0x600000), 4096, None))

@@ -75,6 +75,14 @@ _SIGS = {
     "qgemv_q2_batch": (_I, [ctypes.POINTER(qg_q2_job), _I, _P]),
     "qgemv_q2_gate_up_glu": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _I, _P, _P,
                                   _P, _P, _P]),
+    "qgemv_q2_x_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
+    "qgemv_q2_x_auto_split": (_I, [_I64, _I64, _I]),
+    "qgemv_q2_x": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _SZ, _I, _P]),
+    "qgemv_q2_dual_x": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, ctypes.c_float,
+                             _P, _P, _P]),
+    "qgemv_q2_gate_up_glu_x_ws_bytes": (_SZ, [_I64]),
+    "qgemv_q2_gate_up_glu_x": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P,
+                                    ctypes.c_float, _I, _P, _P, _SZ, _P]),
     "qgemm_q2_batched": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "qgemm_q2_batched_ws_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "qgemm_q2_batched_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P,
@@ -390,6 +398,58 @@ def qgemv_q2_batch(jobs, stream=None):
                            _dev(sc, torch.float32, "act_scale"), _dev(accum, torch.float32, "accum"),
                            _dev(y, torch.float32, "y"))
     _check("qgemv_q2_batch", lib().qgemv_q2_batch(arr, len(jobs), _stream(stream)))
+
+
+def qgemv_q2_x_ws_bytes(M, K, group, split_k=0) -> int:
+    return lib().qgemv_q2_x_ws_bytes(M, K, group, split_k)
+
+
+def qgemv_q2_x_auto_split(M, K, group) -> int:
+    return lib().qgemv_q2_x_auto_split(M, K, group)
+
+
+def qgemv_q2_x_workspace(M, K, group, split_k=0, device="cuda"):
+    """A zero-filled workspace for qgemv_q2_x (it must start all zero; calls leave it so), or None."""
+    import torch
+    n = qgemv_q2_x_ws_bytes(M, K, group, split_k)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def qgemv_q2_x(w: Q2Weight, x, y, accum=None, ws=None, split_k=0, stream=None):
+    """y = Q2 GEMV of the f32 vector x, quantised inside the launch (+ accum); one launch.
+    ws: from qgemv_q2_x_workspace (all zero) when the split is above 1."""
+    import torch
+    d = w.desc()
+    _check("qgemv_q2_x", lib().qgemv_q2_x(
+        ctypes.byref(d), _dev(x, torch.float32, "x"), _dev(accum, torch.float32, "accum"),
+        _dev(y, torch.float32, "y"), _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), split_k,
+        _stream(stream)))
+
+
+def qgemv_q2_dual_x(w0: Q2Weight, w1: Q2Weight, x, y0, y1, norm_w=None, eps=0.0, stream=None):
+    """The gate|up pair against x quantised (after RMSNorm with norm_w, eps) inside the launch."""
+    import torch
+    d0, d1 = w0.desc(), w1.desc()
+    _check("qgemv_q2_dual_x", lib().qgemv_q2_dual_x(
+        ctypes.byref(d0), ctypes.byref(d1), _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w"),
+        float(eps), _dev(y0, torch.float32, "y0"), _dev(y1, torch.float32, "y1"), _stream(stream)))
+
+
+def qgemv_q2_gate_up_glu_x_workspace(M, device="cuda"):
+    """The zero-filled workspace qgemv_q2_gate_up_glu_x needs (calls leave it all zero)."""
+    import torch
+    return torch.zeros(lib().qgemv_q2_gate_up_glu_x_ws_bytes(M), dtype=torch.uint8, device=device)
+
+
+def qgemv_q2_gate_up_glu_x(w_gate: Q2Weight, w_up: Q2Weight, x, kind, t, ws, norm_w=None, eps=0.0, stream=None):
+    """t = silu(g)*u (kind 0) or u*sigmoid(g) (kind 1) of the gate|up pair, x quantised in the launch.
+    ws: from qgemv_q2_gate_up_glu_x_workspace."""
+    import torch
+    dg, du = w_gate.desc(), w_up.desc()
+    _check("qgemv_q2_gate_up_glu_x", lib().qgemv_q2_gate_up_glu_x(
+        ctypes.byref(dg), ctypes.byref(du), _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w"),
+        float(eps), int(kind), _dev(t, torch.float32, "t"), _dev(ws, torch.uint8, "ws"),
+        0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def qgemm_q2_batched_ws_bytes(M, K, group, nb) -> int:

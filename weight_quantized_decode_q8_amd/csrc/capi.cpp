@@ -57,7 +57,7 @@ const char *qg_status_string(qg_status s) {
 
 const char *qg_last_error(void) { return qg::g_msg; }
 
-int qg_abi_version(void) { return 5; }
+int qg_abi_version(void) { return 6; }
 
 qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
                       int64_t K, void *stream) {
@@ -294,6 +294,135 @@ qg_status qgemv_q2_gate_up_glu(const qg_q2_weight *w_gate, const qg_q2_weight *w
   call.split = 1;
   return qg::launched(qg::launch_q2_gate_up_glu(call, kind, t, xq_out, act_scale_out, suma_out, (hipStream_t)stream),
                       fn);
+}
+
+size_t qgemv_q2_x_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
+  if (M < 1 || K < 1 || (group != 64 && group != 128)) return 0;
+  const int S = split_k == 0 ? qg::q2x_auto_split(M, K, group) : split_k;
+  if (S <= 1 || S > qg::kMaxSplit) return 0;
+  return qg::q2x_cnt_bytes(M) + (size_t)S * (size_t)qg::round_up(M, 64) * sizeof(float);
+}
+
+// The f32 input vector of the in-launch quantiser: present, 16-byte
+// aligned, and each workgroup's share of K (K / split, in whole groups)
+// within what it holds.
+static qg_status check_x_input(const char *fn, const qg_q2_weight *w, const float *x, const float *norm_w,
+                               float eps, int S) {
+  if (!x) return fail(QG_EINVAL, "%s: null x", fn);
+  if (!aligned(x, 16) || (norm_w && !aligned(norm_w, 16)))
+    return fail(QG_EINVAL, "%s: x and norm_w must be 16-byte aligned", fn);
+  const int64_t ngroups = w->K / w->group;
+  const int64_t share = (ngroups + S - 1) / S * w->group;
+  const int64_t smax = qg::q2x_max_split_k(w->M);
+  if (share > smax)
+    return fail(QG_EINVAL, "%s: K=%lld over split %d gives %lld values per workgroup, above %lld for M=%lld", fn,
+                (long long)w->K, S, (long long)share, (long long)smax, (long long)w->M);
+  if (norm_w && w->K > qg::kQ2XNormMaxK)
+    return fail(QG_EINVAL, "%s: K=%lld above %d with the RMSNorm", fn, (long long)w->K, qg::kQ2XNormMaxK);
+  if (norm_w && !(eps >= 0.0f && eps <= 3.4e38f)) return fail(QG_EINVAL, "%s: eps must be finite and >= 0", fn);
+  return QG_OK;
+}
+
+qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *accum, float *y, void *ws, size_t ws_bytes,
+                     int split_k, void *stream) {
+  const char *fn = "qgemv_q2_x";
+  qg_status st = qg::check_q2_weight(w, fn);
+  if (st != QG_OK) return st;
+  if (split_k < 0 || split_k > qg::kMaxSplit) return fail(QG_EINVAL, "%s: split_k=%d outside 0..16", fn, split_k);
+  const int S = split_k == 0 ? qg::q2x_auto_split(w->M, w->K, w->group) : split_k;
+  if ((st = check_x_input(fn, w, x, nullptr, 0.0f, S)) != QG_OK) return st;
+  if (!y) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!aligned(y, 4) || (accum && !aligned(accum, 4))) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  if (accum && accum != y && overlap(accum, y, w->M))
+    return fail(QG_EINVAL, "%s: accum must be y itself or not overlap it", fn);
+  const size_t xbytes = (size_t)w->K * sizeof(float), ybytes = (size_t)w->M * sizeof(float);
+  if (bytes_overlap(x, xbytes, y, ybytes)) return fail(QG_EINVAL, "%s: x overlaps y", fn);
+  const size_t need = qgemv_q2_x_ws_bytes(w->M, w->K, w->group, S);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed for split %d", fn, ws ? ws_bytes : (size_t)0, need, S);
+  if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
+  if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, accum, ybytes) ||
+                   bytes_overlap(ws, need, x, xbytes)))
+    return fail(QG_EINVAL, "%s: workspace overlaps an output, the residual or x", fn);
+  qg::Q2XCall c{};
+  c.codes[0] = w->codes;
+  c.scales[0] = w->scales;
+  c.y[0] = y;
+  c.M = (int)w->M;
+  c.K = (int)w->K;
+  c.group = w->group;
+  c.x = x;
+  c.accum = accum;
+  c.ws = ws;
+  c.split = S;
+  c.glu = -1;
+  return qg::launched(qg::launch_q2_gemv_x(c, (hipStream_t)stream), fn);
+}
+
+int qgemv_q2_x_auto_split(int64_t M, int64_t K, int group) {
+  if (M < 1 || K < 1 || (group != 64 && group != 128)) return 1;
+  return qg::q2x_auto_split(M, K, group);
+}
+
+size_t qgemv_q2_gate_up_glu_x_ws_bytes(int64_t M) {
+  if (M < 1) return 0;
+  return qg::q2x_cnt_bytes(M) + 2 * (size_t)qg::round_up(M, 64) * sizeof(float);
+}
+
+static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_q2_weight *w1, const float *x,
+                               const float *norm_w, float eps, int glu, float *y0, float *y1, void *ws,
+                               size_t ws_bytes, void *stream) {
+  qg_status st = qg::check_q2_weight(w0, fn);
+  if (st != QG_OK) return st;
+  if ((st = qg::check_q2_weight(w1, fn)) != QG_OK) return st;
+  if (w1->M != w0->M || w1->K != w0->K || w1->group != w0->group)
+    return fail(QG_EINVAL, "%s: the two weights differ in shape or group", fn);
+  if ((st = check_x_input(fn, w0, x, norm_w, eps, 1)) != QG_OK) return st;
+  if (!y0 || (glu < 0 && !y1)) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!aligned(y0, 4) || (y1 && !aligned(y1, 4))) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  const size_t xbytes = (size_t)w0->K * sizeof(float), ybytes = (size_t)w0->M * sizeof(float);
+  if (glu < 0 && bytes_overlap(y0, ybytes, y1, ybytes)) return fail(QG_EINVAL, "%s: the two outputs overlap", fn);
+  if (bytes_overlap(x, xbytes, y0, ybytes) || bytes_overlap(norm_w, xbytes, y0, ybytes) ||
+      (glu < 0 && (bytes_overlap(x, xbytes, y1, ybytes) || bytes_overlap(norm_w, xbytes, y1, ybytes))))
+    return fail(QG_EINVAL, "%s: an output overlaps x or norm_w", fn);
+  if (glu >= 0) {
+    const size_t need = qgemv_q2_gate_up_glu_x_ws_bytes(w0->M);
+    if (!ws || ws_bytes < need) return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws ? ws_bytes : (size_t)0, need);
+    if (!aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
+    if (bytes_overlap(ws, need, y0, ybytes) || bytes_overlap(ws, need, x, xbytes) ||
+        bytes_overlap(ws, need, norm_w, xbytes))
+      return fail(QG_EINVAL, "%s: workspace overlaps t, x or norm_w", fn);
+  }
+  qg::Q2XCall c{};
+  c.codes[0] = w0->codes;
+  c.scales[0] = w0->scales;
+  c.codes[1] = w1->codes;
+  c.scales[1] = w1->scales;
+  c.y[0] = y0;
+  c.y[1] = glu < 0 ? y1 : nullptr;
+  c.M = (int)w0->M;
+  c.K = (int)w0->K;
+  c.group = w0->group;
+  c.x = x;
+  c.norm_w = norm_w;
+  c.eps = eps;
+  c.ws = glu >= 0 ? ws : nullptr;
+  c.split = 1;
+  c.glu = glu;
+  return qg::launched(qg::launch_q2_gemv_x(c, (hipStream_t)stream), fn);
+}
+
+qg_status qgemv_q2_dual_x(const qg_q2_weight *w0, const qg_q2_weight *w1, const float *x, const float *norm_w,
+                          float eps, float *y0, float *y1, void *stream) {
+  return pair_x_common("qgemv_q2_dual_x", w0, w1, x, norm_w, eps, -1, y0, y1, nullptr, 0, stream);
+}
+
+qg_status qgemv_q2_gate_up_glu_x(const qg_q2_weight *w_gate, const qg_q2_weight *w_up, const float *x,
+                                 const float *norm_w, float eps, int kind, float *t, void *ws, size_t ws_bytes,
+                                 void *stream) {
+  const char *fn = "qgemv_q2_gate_up_glu_x";
+  if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
+  return pair_x_common(fn, w_gate, w_up, x, norm_w, eps, kind, t, nullptr, ws, ws_bytes, stream);
 }
 
 qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream) {

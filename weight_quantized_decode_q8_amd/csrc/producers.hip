@@ -36,20 +36,6 @@
 namespace qg {
 namespace {
 
-__device__ inline float4 mul4(float4 a, float4 b) {
-  return make_float4(__fmul_rn(a.x, b.x), __fmul_rn(a.y, b.y), __fmul_rn(a.z, b.z), __fmul_rn(a.w, b.w));
-}
-
-__device__ inline float4 scale4(float4 a, float s) {
-  return make_float4(__fmul_rn(a.x, s), __fmul_rn(a.y, s), __fmul_rn(a.z, s), __fmul_rn(a.w, s));
-}
-
-// Correctly rounded binary32 square root: the binary64 root (correctly
-// rounded) rounded once more to binary32, which for sqrt gives the correctly
-// rounded binary32 result (53 >= 2 * 24 + 2).  The single-precision
-// hardware root is not correctly rounded.
-__device__ inline float sqrt_rn(float a) { return (float)sqrt((double)a); }
-
 __global__ __launch_bounds__(kQuantThreads) void rmsnorm_quant_kernel(
     const float4 *__restrict__ x4, const float4 *__restrict__ w4, int n4, float eps,
     int *__restrict__ xq4, float *__restrict__ act_scale, int *__restrict__ suma) {

@@ -1,0 +1,411 @@
+// q2_gemv_x.hip -- the decode Q2 GEMVs with the activation side in the same
+// launch: each workgroup quantises the f32 input vector itself (optionally
+// after an RMSNorm), and split-K partials are added by the last workgroup of
+// each row tile instead of a second kernel.
+//
+// What is computed is exactly what the two- or three-launch chains compute
+// (qxmx qxmx_gpu.cpp page: gpu_rmsnorm_quant or the plain quantiser, then
+// gemv_dpas8 and gemv_reduce; gemv_dpas8_dual for the gate|up pair; the
+// cortiq-engine 0.5.43 gpu_wgpu.rs page, moe_gate_up, for the gated product
+// in the epilogue):
+//   v      = x, or (x * inv) * w with inv = 1/sqrt(ms + eps) (RMSNorm)
+//   sc     = max|v| / 127, xq = clamp(round(v / sc)), suma = per-64 sums
+//   y[o]   = sc * sum_u d(o,u) * (sum_{i in u} code_i * xq_i - suma_u)
+// with the same per-wave group ranges, the same f32 accumulation order, the
+// same wave combine and the same split order as q2_gemv_t64_kernel and
+// q2_splitk_reduce_kernel, so every output equals the multi-launch chain
+// bit for bit.
+//
+// Why (MI355X): a kernel launch in a stream or graph costs a few
+// microseconds before its first bytes arrive, as much as streaming 10-20 MB,
+// and the decode FFN's quantisers and split reduce each paid it for a few
+// tens of KiB of work.  Quantising in every workgroup repeats that small
+// work (the vector is read from L2) but overlaps it with the workgroup's
+// first weight loads, which are issued before the prologue.
+//
+// Layout of the work: one row tile (64 rows, one per lane) per workgroup and
+// matrix, K split over the waves as in q2_gemv_t64_kernel.  The activation
+// words, which the plain kernel reads through the scalar cache, come from
+// LDS here (broadcast ds_read_b128: every lane reads the same address).  A
+// gate|up pair puts the two matrices on the two halves of the workgroup; a
+// shape whose plain dual kernel uses 16 waves per matrix runs each half's 8
+// waves over two of those waves' group ranges ("virtual waves"), each with
+// its own accumulator, so the sums and their combine order are unchanged.
+//
+// Split-K in one launch: each (tile, split) workgroup stores its partial and
+// then increments the tile's counter; the workgroup that sees the count S-1
+// adds the S partials in split order, setting them and the counter back to
+// zero: the workspace is all zero between calls, so one workspace serves
+// calls of any shape and split.  The gate|up pair with the gated product
+// meets the same way: each matrix's workgroup of a tile stores its g or u,
+// and the second to arrive forms t.  No workgroup
+// waits on another, so nothing can hang on a missing arrival.
+#include "gate_rule.h"
+#include "qg_internal.h"
+#include "quant_rule.h"
+
+namespace qg {
+namespace {
+
+constexpr unsigned kCodeMask = 0x03030303u;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate for lgkmcnt(0) alone (gfx9 encoding: vmcnt and
+// expcnt at their maxima, i.e. not waited for).
+constexpr int kLgkm0 = 0xC07F;
+
+// A workgroup barrier that makes this wave's LDS writes visible but leaves
+// its global loads in flight (__syncthreads() would also wait for those,
+// i.e. for the weight loads issued before the prologue).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Corrected dot of one unit: sum_{64 weights} code*xq - suma, the
+// activation words given as four 128-bit values.
+__device__ inline int unit_dot_v(const i32x4 c, const i32x4 x0, const i32x4 x1, const i32x4 x2, const i32x4 x3,
+                                 int sa) {
+  int p = 0;
+  p = __builtin_amdgcn_sdot4((int)((unsigned)c.x & kCodeMask), x0.x, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 2) & kCodeMask), x0.y, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 4) & kCodeMask), x0.z, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 6) & kCodeMask), x0.w, p, false);
+  p = __builtin_amdgcn_sdot4((int)((unsigned)c.y & kCodeMask), x1.x, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 2) & kCodeMask), x1.y, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 4) & kCodeMask), x1.z, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 6) & kCodeMask), x1.w, p, false);
+  p = __builtin_amdgcn_sdot4((int)((unsigned)c.z & kCodeMask), x2.x, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 2) & kCodeMask), x2.y, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 4) & kCodeMask), x2.z, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 6) & kCodeMask), x2.w, p, false);
+  p = __builtin_amdgcn_sdot4((int)((unsigned)c.w & kCodeMask), x3.x, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 2) & kCodeMask), x3.y, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 4) & kCodeMask), x3.z, p, false);
+  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 6) & kCodeMask), x3.w, p, false);
+  return p - sa;
+}
+
+__device__ inline float half_bits_to_f32(unsigned short h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ inline float scale_add(float acc, float sc, const float *accum, int o) {
+  const float y = __fmul_rn(acc, sc);
+  return accum ? __fadd_rn(y, accum[o]) : y;
+}
+
+struct XArgs {
+  const i32x4 *codes[2];
+  const unsigned short *scales[2];
+  const float4 *x;       // the f32 input vector [K]
+  const float4 *norm_w;  // RMSNorm weights [K] (PRO_NORM)
+  float eps;
+  float *y[2];           // outputs; EPI_GLU: t in y[0]
+  const float *accum;    // one matrix: residual or null
+  float *part;           // S > 1: partials [S][Mp]; EPI_GLU: g and u [2][Mp]
+  int *cnt;              // S > 1 or EPI_GLU: arrival counters [tiles]
+  int M, K, S, tiles;
+};
+
+enum { PRO_X = 0, PRO_NORM = 1 };
+enum { EPI_Y = 0, EPI_GLU_SILU = 1, EPI_GLU_SIGMOID = 2 };
+
+// Largest of every thread's m over an NT-thread workgroup (exact).
+template <int NT>
+__device__ inline float block_max_nt(float m, float *red) {
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  lds_barrier();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; w++) r = fmaxf(r, red[w]);
+  return r;
+}
+
+// The values two or more workgroups of a row tile exchange (split partials,
+// g and u) go through device-scope atomic swaps, which are performed at the
+// device's coherence point like the arrival counter itself, instead of plain
+// stores published by a device-scope release fence: that fence writes back
+// the whole L2 of the XCD, and with hundreds of workgroups it cost more than
+// the launch it replaces.
+__device__ inline void put(float *p, float v) {
+  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The value stored at p, which is left zero.
+__device__ inline float take(float *p) {
+  return __hip_atomic_exchange(p, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt immediate for vmcnt(0) alone.
+constexpr int kVm0 = 0x0F70;
+
+// Counts this workgroup's arrival on the tile's counter once its put()s
+// have completed; true for the last of n arrivals, whose take()s are issued
+// after it and so see every earlier arrival's values.
+__device__ inline bool arrive_last(int *cnt, int n) {
+  // the swaps must be performed before the count: wait for every vector
+  // memory operation of this wave (the compiler does not order relaxed
+  // atomics to different addresses, nor wait for a swap whose result is
+  // unused)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kVm0);
+  asm volatile("" ::: "memory");
+  int prev = 0;
+  if ((threadIdx.x & 63) == 0) prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0);
+  return prev == n - 1;
+}
+
+// grid = (row tiles x matrices, splits), one row tile of one matrix per
+// workgroup of W waves (the plain kernel's waves per tile).  RQ quads of
+// this split's share of the vector are held per thread.  UPG units per
+// scale group, GPB groups per load step.
+template <int UPG, int GPB, int W, int RQ, int PRO, int EPI>
+__global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
+  constexpr int NT = 64 * W;
+  constexpr int VPT = 1024 / NT;  // RMSNorm: threads of the 1024-thread order per thread
+  __shared__ i32x4 xl[RQ * NT / 4];  // xq of this split's units, 16 per entry
+  __shared__ int sl[RQ * NT / 16];    // their 64-wide sums
+  __shared__ float red[W - 1][64];
+  __shared__ float rmax[W];
+  __shared__ double rss[16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mat = (int)blockIdx.x >= a.tiles ? 1 : 0;
+  const int tile = (int)blockIdx.x - mat * a.tiles;
+  const int split = blockIdx.y, S = a.S;
+  const int M = a.M, K = a.K, Mp = a.tiles * 64;
+  const int nunits = K / 64, ngroups = nunits / UPG;
+
+  // Groups of this split (the plain kernel's partition), then of this wave:
+  // contiguous ranges.
+  const int gps = (ngroups + S - 1) / S;
+  const int gs0 = min(ngroups, split * gps);
+  const int gs1 = min(ngroups, gs0 + gps);
+  const int per = (gs1 - gs0 + W - 1) / W;
+  const int g0 = min(gs1, gs0 + wave * per);
+  const int g1 = min(gs1, g0 + per);
+  const int u0 = gs0 * UPG;  // first unit held in LDS
+
+  const i32x4 *cp = (mat ? a.codes[1] : a.codes[0]) + (size_t)tile * nunits * 64 + lane;
+  const unsigned short *sp = (mat ? a.scales[1] : a.scales[0]) + (size_t)tile * ngroups * 64 + lane;
+
+  // 1. This wave's first load step, then the vector: both round trips at
+  //    once (the prologue waits for the vector, hence for these loads too,
+  //    and then computes with the first weights already in registers).
+  i32x4 c[GPB * UPG];
+  unsigned short dh[GPB];
+  const bool pre = g0 + GPB <= g1;
+  if (pre) {
+#pragma unroll
+    for (int vv = 0; vv < GPB * UPG; vv++) c[vv] = __builtin_nontemporal_load(cp + (size_t)(g0 * UPG + vv) * 64);
+#pragma unroll
+    for (int j = 0; j < GPB; j++) dh[j] = __builtin_nontemporal_load(sp + (size_t)(g0 + j) * 64);
+  }
+  const int n4 = K / 4;
+  const int q0 = u0 * 16, q1 = gs1 * UPG * 16;  // quads of this split
+  float4 v[RQ];
+#pragma unroll
+  for (int r = 0; r < RQ; r++) {
+    const int i = q0 + tid + r * NT;
+    if (i < q1) v[r] = a.x[i];
+  }
+  float m = 0.0f;
+  if (PRO == PRO_X && S > 1)  // the rest of the vector, for its max only
+    for (int i = tid; i < n4; i += NT)
+      if (i < q0 || i >= q1) m = fmaxf(m, abs_max4(a.x[i]));
+
+  // 2. Prologue: the quantised vector of this split's units into LDS.
+  if (PRO == PRO_NORM) {
+    // RMSNorm exactly as rmsnorm_quant_kernel: its 1024 threads' binary64
+    // sums (thread t: quads t, t + 1024, ...), each wave's shuffle tree and
+    // the 16 wave sums added in order; here thread tid stands for threads
+    // tid + NT * j, j < VPT (S = 1, so q0 = 0 and quad tid + NT r belongs
+    // to thread tid + NT (r % VPT)).
+    double ss[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; j++) ss[j] = 0.0;
+#pragma unroll
+    for (int r = 0; r < RQ; r++)
+      if (tid + r * NT < n4)
+        ss[r % VPT] += ((double)v[r].x * (double)v[r].x + (double)v[r].y * (double)v[r].y) +
+                       ((double)v[r].z * (double)v[r].z + (double)v[r].w * (double)v[r].w);
+#pragma unroll
+    for (int j = 0; j < VPT; j++) {
+      for (int off = 32; off > 0; off >>= 1) ss[j] += __shfl_xor(ss[j], off);
+      if (lane == 0) rss[wave + W * j] = ss[j];
+    }
+    lds_barrier();
+    double tot = 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; k++) tot += rss[k];
+    const float ms = (float)(tot / (double)(4 * n4));
+    const float inv = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, a.eps)));
+    // the norm weights are loaded only now (from L2), so that they and the
+    // vector are not both held across the sum: fewer registers, more
+    // workgroups per CU
+#pragma unroll
+    for (int r = 0; r < RQ; r++)
+      if (tid + r * NT < n4) v[r] = mul4(scale4(v[r], inv), a.norm_w[tid + r * NT]);
+  }
+#pragma unroll
+  for (int r = 0; r < RQ; r++)
+    if (q0 + tid + r * NT < q1) m = fmaxf(m, abs_max4(v[r]));
+  const float amax = block_max_nt<NT>(m, rmax);
+  const float sc = __fdiv_rn(amax, 127.0f);
+  const float qinv = sc > 0.0f ? __fdiv_rn(1.0f, sc) : 0.0f;
+#pragma unroll
+  for (int r = 0; r < RQ; r++) {
+    const int i = tid + r * NT;  // quad of the split, counted from q0
+    if (q0 + i < q1) quant_quad(i, v[r], qinv, reinterpret_cast<int *>(xl), sl);
+  }
+  lds_barrier();
+
+  // 3. The GEMV over this wave's range, activations from LDS.
+  float acc = 0.0f;
+  int g = g0;
+  auto step = [&](int gg) {
+#pragma unroll
+    for (int j = 0; j < GPB; j++) {
+      int p = 0;
+#pragma unroll
+      for (int vv = 0; vv < UPG; vv++) {
+        const int ul = (gg + j) * UPG + vv - u0;
+        p += unit_dot_v(c[j * UPG + vv], xl[ul * 4], xl[ul * 4 + 1], xl[ul * 4 + 2], xl[ul * 4 + 3], sl[ul]);
+      }
+      acc = fmaf(half_bits_to_f32(dh[j]), (float)p, acc);
+    }
+  };
+  if (pre) {
+    step(g);
+    g += GPB;
+  }
+  for (; g + GPB <= g1; g += GPB) {
+#pragma unroll
+    for (int vv = 0; vv < GPB * UPG; vv++) c[vv] = __builtin_nontemporal_load(cp + (size_t)(g * UPG + vv) * 64);
+#pragma unroll
+    for (int j = 0; j < GPB; j++) dh[j] = __builtin_nontemporal_load(sp + (size_t)(g + j) * 64);
+    step(g);
+  }
+  for (; g < g1; g++) {
+    const unsigned short d1 = __builtin_nontemporal_load(sp + (size_t)g * 64);
+    int p = 0;
+#pragma unroll
+    for (int vv = 0; vv < UPG; vv++) {
+      const int ul = g * UPG + vv - u0;
+      p += unit_dot_v(__builtin_nontemporal_load(cp + (size_t)(g * UPG + vv) * 64), xl[ul * 4], xl[ul * 4 + 1],
+                      xl[ul * 4 + 2], xl[ul * 4 + 3], sl[ul]);
+    }
+    acc = fmaf(half_bits_to_f32(d1), (float)p, acc);
+  }
+
+  // 4. Combine the waves in order (the plain kernel's combine).
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int k = 0; k < W - 1; k++) acc += red[k][lane];
+  const int o = tile * 64 + lane;
+
+  if (EPI == EPI_Y) {
+    if (S == 1) {
+      if (o < M) a.y[mat][o] = scale_add(acc, sc, a.accum, o);
+      return;
+    }
+    // Split partial; the last arrival of this tile adds all of them in
+    // split order, leaving the workspace all zero again.
+    put(a.part + (size_t)split * Mp + o, acc);
+    if (!arrive_last(a.cnt + tile, S)) return;
+    float s = 0.0f;
+    for (int k = 0; k < S; k++) s += take(a.part + (size_t)k * Mp + o);
+    if (o < M) a.y[0][o] = scale_add(s, sc, a.accum, o);
+    if (lane == 0) __hip_atomic_store(a.cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // g or u of this tile, rounded as the GEMV rounds it; the second of the
+    // tile's two workgroups forms t = glu(g, u) and clears the workspace.
+    const float r = __fmul_rn(acc, sc);
+    put(a.part + (size_t)mat * Mp + o, r);
+    if (!arrive_last(a.cnt + tile, 2)) return;
+    const float other = take(a.part + (size_t)(1 - mat) * Mp + o);
+    (void)take(a.part + (size_t)mat * Mp + o);
+    if (o < M) a.y[0][o] = glu1<EPI == EPI_GLU_SILU ? 0 : 1>(mat ? other : r, mat ? r : other);
+    if (lane == 0) __hip_atomic_store(a.cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace
+
+int q2x_auto_split(int64_t M, int64_t K, int group) {
+  // The split costs no launch here, only a handshake per row tile, so K is
+  // split whenever the row tiles cannot fill the CUs: the largest split that
+  // still runs every (tile, split) workgroup in one round (one 16-wave
+  // workgroup per CU), keeping at least 8 scale groups per split.  Measured
+  // on the 5120 x 17408 g128 down projection inside the decode step: S = 3
+  // (240 workgroups) 216.7-217.2 us, S = 2 217.4-218.2, S = 4 (320, two
+  // rounds) 220.6-221.2, S = 1 219.9-220.6.
+  const int64_t tiles = (M + 63) / 64;
+  const int64_t ngroups = K / group;
+  if (tiles >= 128) return 1;
+  int S = 1;
+  while (S < kMaxSplit && tiles * (S + 1) <= 256 && ngroups / (S + 1) >= 8) S++;
+  return S;
+}
+
+hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
+  const int tiles = (c.M + 63) / 64;
+  const bool pair = c.codes[1] != nullptr;
+  XArgs a{};
+  for (int n = 0; n < (pair ? 2 : 1); n++) {
+    a.codes[n] = reinterpret_cast<const i32x4 *>(c.codes[n]);
+    a.scales[n] = reinterpret_cast<const unsigned short *>(c.scales[n]);
+    a.y[n] = c.y[n];
+  }
+  a.x = reinterpret_cast<const float4 *>(c.x);
+  a.norm_w = reinterpret_cast<const float4 *>(c.norm_w);
+  a.eps = c.eps;
+  a.accum = c.accum;
+  a.M = c.M;
+  a.K = c.K;
+  a.S = pair ? 1 : c.split;
+  a.tiles = tiles;
+  if (a.S > 1 || c.glu >= 0) {
+    a.cnt = reinterpret_cast<int *>(c.ws);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(c.ws) + q2x_cnt_bytes(c.M));
+  }
+  const bool norm = c.norm_w != nullptr;
+  // Waves per tile as the plain kernels: 8 when one matrix's row tiles fill
+  // the CUs, else 16; quads held per thread: 4 or 8 per split.
+  const int waves = tiles >= 256 ? 8 : 16;
+  const int gps = (c.K / c.group + a.S - 1) / a.S;
+  const int rq = (gps * c.group / 4 + 64 * waves - 1) / (64 * waves) <= 4 ? 4 : 8;
+  const dim3 grid(tiles * (pair ? 2 : 1), a.S);
+#define QXK(UPG, GPB, W, RQ, PRO, EPI) q2_gemv_x_kernel<UPG, GPB, W, RQ, PRO, EPI><<<grid, 64 * W, 0, stream>>>(a)
+#define QXE(UPG, GPB, W, RQ, PRO)                                      \
+  do {                                                                 \
+    if (c.glu < 0) QXK(UPG, GPB, W, RQ, PRO, EPI_Y);                   \
+    else if (c.glu == 0) QXK(UPG, GPB, W, RQ, PRO, EPI_GLU_SILU);      \
+    else QXK(UPG, GPB, W, RQ, PRO, EPI_GLU_SIGMOID);                   \
+  } while (0)
+#define QXP(UPG, GPB, W, RQ)                                           \
+  do {                                                                 \
+    if (norm) QXE(UPG, GPB, W, RQ, PRO_NORM); else QXE(UPG, GPB, W, RQ, PRO_X); \
+  } while (0)
+#define QXR(UPG, GPB, W)                                               \
+  do {                                                                 \
+    if (rq == 4) QXP(UPG, GPB, W, 4); else QXP(UPG, GPB, W, 8);        \
+  } while (0)
+  if (c.group == 64) {
+    if (waves == 8) QXR(1, 4, 8); else QXR(1, 4, 16);
+  } else {
+    if (waves == 8) QXR(2, 2, 8); else QXR(2, 2, 16);
+  }
+#undef QXK
+#undef QXE
+#undef QXP
+#undef QXR
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -62,6 +62,34 @@ struct Q2Call {
 };
 hipError_t launch_q2_gemv(const Q2Call &call, hipStream_t stream);
 
+// Q2 GEMVs that quantise their f32 input in the same launch (optionally
+// after an RMSNorm, for the gate|up pair), with split-K partials reduced by
+// the last workgroup of each row tile.  codes[1] non-null: the gate|up pair
+// (no split), written to y[0], y[1], or with glu >= 0 (0 silu, 1 sigmoid)
+// t = glu(g, u) to y[0], g and u meeting in ws.  One matrix: split S,
+// accum optional.  ws: the arrival counters (q2x_cnt_bytes) then [S][Mp]
+// (or [2][Mp]) f32, all zero between calls.
+inline size_t q2x_cnt_bytes(int64_t M) { return (size_t)round_up((M + 63) / 64, 64) * sizeof(int); }
+// Largest share of K one workgroup quantises (held in registers: 8 quads
+// per thread of its 8 or 16 waves), and the largest K with the RMSNorm.
+constexpr int kQ2XMaxK = 32768;
+constexpr int kQ2XNormMaxK = 16384;
+inline int64_t q2x_max_split_k(int64_t M) { return (M + 63) / 64 >= 256 ? 16384 : 32768; }
+struct Q2XCall {
+  const void *codes[2];
+  const void *scales[2];
+  float *y[2];
+  int M, K, group;
+  const float *x, *norm_w;
+  float eps;
+  const float *accum;
+  void *ws;
+  int split;
+  int glu;
+};
+hipError_t launch_q2_gemv_x(const Q2XCall &call, hipStream_t stream);
+int q2x_auto_split(int64_t M, int64_t K, int group);
+
 // Several independent Q2 GEMVs of one group size in one launch (no split).
 constexpr int kMaxQ2Jobs = QG_Q2_BATCH_MAX;
 struct Q2BatchCall {

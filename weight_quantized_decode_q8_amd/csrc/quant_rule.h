@@ -63,4 +63,20 @@ __device__ inline void quant_quad(int i, float4 v, float inv, int *__restrict__ 
   if ((i & 15) == 0) suma[i >> 4] = s;
 }
 
+// Element-wise binary32 products of a quad (each one rounding), for the
+// RMSNorm producers: v = (x * inv) * w.
+__device__ inline float4 mul4(float4 a, float4 b) {
+  return make_float4(__fmul_rn(a.x, b.x), __fmul_rn(a.y, b.y), __fmul_rn(a.z, b.z), __fmul_rn(a.w, b.w));
+}
+
+__device__ inline float4 scale4(float4 a, float s) {
+  return make_float4(__fmul_rn(a.x, s), __fmul_rn(a.y, s), __fmul_rn(a.z, s), __fmul_rn(a.w, s));
+}
+
+// Correctly rounded binary32 square root: the binary64 root (correctly
+// rounded) rounded once more to binary32, which for sqrt gives the correctly
+// rounded binary32 result (53 >= 2 * 24 + 2).  The single-precision
+// hardware root is not correctly rounded.
+__device__ inline float sqrt_rn(float a) { return (float)sqrt((double)a); }
+
 }  // namespace qg
