@@ -161,6 +161,37 @@ def test_canary_q8row_gemm(nb, M, K):
     check(y, ws)
 
 
+@pytest.mark.parametrize("M,K,group,split", [(1, 64, 64, 1), (100, 1088, 64, 3), (130, 640, 128, 0),
+                                             (5000, 2048, 128, 5), (16400, 256, 64, 1)])
+def test_canary_q2_in_launch_forms(M, K, group, split):
+    """qgemv_q2_x (its split partials and counters), qgemv_q2_dual_x and
+    qgemv_q2_gate_up_glu_x (g and u meeting in the workspace) on ragged
+    shapes: nothing written outside the outputs and workspaces, and the
+    workspaces left all zero."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    b0, x = synth.q2_inputs(M, K, group, seed=M + K + 7)
+    b1, _ = synth.q2_inputs(M, K, group, seed=M + K + 8)
+    W0 = qg.Q2Weight.from_blocks(b0, M, K, group)
+    W1 = qg.Q2Weight.from_blocks(b1, M, K, group)
+    xd = torch.from_numpy(x).cuda()
+    nw = torch.ones(K, device="cuda")
+    y, y1 = Guarded(M, torch.float32), Guarded(M, torch.float32)
+    ws = ws_guarded(qg.qgemv_q2_x_ws_bytes(M, K, group, split))
+    ws.t.zero_()
+    acc = torch.from_numpy(synth.rng_for(M).standard_normal(M).astype(np.float32)).cuda()
+    qg.qgemv_q2_x(W0, xd, y.t, accum=acc, ws=ws.t if ws.nbytes > 1 else None, split_k=split)
+    check(y, ws)
+    assert int(torch.count_nonzero(ws.t).item()) == 0
+    qg.qgemv_q2_dual_x(W0, W1, xd, y.t, y1.t, norm_w=nw if K <= 16384 else None, eps=1e-6)
+    check(y, y1)
+    wsg = ws_guarded(qg.lib().qgemv_q2_gate_up_glu_x_ws_bytes(M))
+    wsg.t.zero_()
+    qg.qgemv_q2_gate_up_glu_x(W0, W1, xd, qg.QG_GLU_SIGMOID, y.t, wsg.t)
+    check(y, wsg)
+    assert int(torch.count_nonzero(wsg.t).item()) == 0
+
+
 def test_canary_detects_a_stray_write():
     """The guard check itself: one byte changed just past (or just before) the
     buffer is reported."""

@@ -112,8 +112,19 @@ def test_graph_replays_fused_forms():
     xq3 = torch.empty(F, dtype=torch.int8, device=dev)
     sc3 = torch.empty(1, device=dev)
     su3 = torch.empty(F // 64, dtype=torch.int32, device=dev)
+    # the two-launch block: producers and split reduce inside the GEMV launches
+    # (workspaces zero-filled once; every replay must leave them zero again)
+    t4 = torch.empty(F, device=dev)
+    h4 = torch.empty(D, device=dev)
+    g5 = torch.empty(F, device=dev)
+    u5 = torch.empty(F, device=dev)
+    ws_glu = qg.qgemv_q2_gate_up_glu_x_workspace(F, dev)
+    ws_x = qg.qgemv_q2_x_workspace(D, F, 128, 3, dev)
 
     def path():
+        qg.qgemv_q2_gate_up_glu_x(Wg, Wu, h, qg.QG_GLU_SILU, t4, ws_glu, norm_w=nw, eps=1e-6)
+        qg.qgemv_q2_x(Wd, t4, h4, accum=h, ws=ws_x, split_k=3)
+        qg.qgemv_q2_dual_x(Wg, Wu, h, g5, u5, norm_w=nw, eps=1e-6)
         qg.qquant_rmsnorm_i8(h, nw, 1e-6, xq1, sc1, su1)
         qg.qgemv_q2_gate_up_glu(Wg, Wu, xq1, su1, sc1, qg.QG_GLU_SILU, t2, xq3, sc3, su3)
         qg.qgemv_q2_dual(Wg, Wu, xq1, su1, sc1, g, u, ws_gu, split_k=2)
@@ -122,7 +133,7 @@ def test_graph_replays_fused_forms():
         qg.qgemv_q2_batch([(W, xq1, su1, sc1, y) + ((h[:W.M],) if W.M <= D and n == 0 else ())
                            for n, (W, y) in enumerate(zip(Wx, ys))])
 
-    outs = (xq1, sc1, su1, g, u, t, xq2, sc2, su2, hout, t2, xq3, sc3, su3, *ys)
+    outs = (xq1, sc1, su1, g, u, t, xq2, sc2, su2, hout, t2, xq3, sc3, su3, *ys, t4, h4, g5, u5)
     path()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
@@ -143,6 +154,12 @@ def test_graph_replays_fused_forms():
         torch.cuda.synchronize()
         for n, (o, r) in enumerate(zip(outs, ref)):
             assert torch.equal(o, r), f"replay {rep}: output {n} differs from the eager result"
+        assert int(torch.count_nonzero(ws_glu).item()) == 0 and int(torch.count_nonzero(ws_x).item()) == 0, \
+            f"replay {rep}: a workspace was not left all zero"
+        # eager work on the same workspaces between replays
+        qg.qgemv_q2_x(Wd, t4, h4, accum=h, ws=ws_x, split_k=2)
+    torch.cuda.synchronize()
+    assert torch.equal(t4, t2), "the two-launch block's t differs from the fused kernel's"
 
 
 def test_graph_replays_prefill_forms():
