@@ -382,9 +382,9 @@ qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream);
  *   [AQ, PQ gpu_rmsnorm_quant; GV gemv_dpas8 + gemv_reduce; GD
  *    gemv_dpas8_dual, tmatvec_accum; GU moe_gate_up]
  * The vector is read by every workgroup while outputs are written, so it
- * must not overlap any output.  Each workgroup holds its share of K (K
- * divided by the split, in whole groups): at most 32768 values, or 16384
- * when M >= 16384 (256 row tiles or more); with the RMSNorm K <= 16384.    */
+ * must not overlap any output.  Each workgroup holds the whole vector: K
+ * is at most 32768, or 16384 when M >= 16384 (256 row tiles or more, the
+ * shapes run with 8 waves per tile) or with the RMSNorm.                  */
 
 /* Split factor qgemv_q2_x uses for split_k = 0 (auto) on this shape: 1
  * when the row tiles fill the GPU (M >= 8192), else the largest split whose
@@ -412,8 +412,8 @@ size_t qgemv_q2_x_ws_bytes(int64_t M, int64_t K, int group, int split_k);
  *   split_k:   0 = auto (qgemv_q2_x_auto_split), else 1..16.
  * y equals qquant_act_i8(x) followed by qgemv_q2 (or qgemv_q2_accum) with
  * the same split (given explicitly to both), bit for bit.
- * QG_EINVAL: as qgemv_q2_accum, or null or misaligned x, a share of K
- * above the limit above, x overlapping y, or a workspace overlapping x.   */
+ * QG_EINVAL: as qgemv_q2_accum, or null or misaligned x, K above the
+ * limit above, x overlapping y, or a workspace overlapping x.             */
 qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x,
                      const float *accum, float *y, void *ws, size_t ws_bytes,
                      int split_k, void *stream);

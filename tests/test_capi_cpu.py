@@ -349,7 +349,8 @@ def test_einval_paths_in_launch_quantiser():
     big = qg.qg_q2_weight(0x100000, 0x200000, 128, 32768 + 64, 64, 0)
     _einval(L.qgemv_q2_x(ctypes.byref(big), X, None, Y, None, 0, 1, None))             # K above 32768
     wide = qg.qg_q2_weight(0x100000, 0x200000, 16384, 16384 + 128, 128, 0)
-    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, Y, None, 0, 1, None))            # share above 16384
+    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, Y, None, 0, 1, None))            # K above 16384 at 8 waves
+    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, Y, WS, 1 << 20, 4, None))       # whatever the split
     assert L.qgemv_q2_gate_up_glu_x_ws_bytes(130) == 256 + 2 * 192 * 4
     # qgemv_q2_dual_x
     _einval(L.qgemv_q2_dual_x(ctypes.byref(w), None, X, None, F(0), Y, Y1, None))

@@ -64,7 +64,7 @@ def fused_single(W, x, split, accum=None, ws=None, in_place=False):
 
 SHAPES = [(1, 64, 64, 1), (64, 256, 64, 1), (130, 640, 128, 0), (300, 2048, 64, 4), (200, 4096, 128, 3),
           (70, 1536, 64, 16), (4100, 1024, 128, 0), (16448, 512, 64, 1), (777, 32768, 128, 1),
-          (777, 32768, 128, 5), (16448, 16384, 128, 1), (16448, 32768, 64, 2), (100, 8256, 64, 1)]
+          (777, 32768, 128, 5), (16448, 16384, 128, 1), (16448, 16384, 64, 2), (100, 8256, 64, 1), (64, 32768, 64, 0)]
 
 
 @pytest.mark.parametrize("M,K,group,split", SHAPES)

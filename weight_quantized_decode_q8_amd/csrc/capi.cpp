@@ -304,19 +304,15 @@ size_t qgemv_q2_x_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
 }
 
 // The f32 input vector of the in-launch quantiser: present, 16-byte
-// aligned, and each workgroup's share of K (K / split, in whole groups)
-// within what it holds.
+// aligned, and short enough for each workgroup to hold it.
 static qg_status check_x_input(const char *fn, const qg_q2_weight *w, const float *x, const float *norm_w,
-                               float eps, int S) {
+                               float eps) {
   if (!x) return fail(QG_EINVAL, "%s: null x", fn);
   if (!aligned(x, 16) || (norm_w && !aligned(norm_w, 16)))
     return fail(QG_EINVAL, "%s: x and norm_w must be 16-byte aligned", fn);
-  const int64_t ngroups = w->K / w->group;
-  const int64_t share = (ngroups + S - 1) / S * w->group;
-  const int64_t smax = qg::q2x_max_split_k(w->M);
-  if (share > smax)
-    return fail(QG_EINVAL, "%s: K=%lld over split %d gives %lld values per workgroup, above %lld for M=%lld", fn,
-                (long long)w->K, S, (long long)share, (long long)smax, (long long)w->M);
+  const int64_t kmax = qg::q2x_max_k(w->M);
+  if (w->K > kmax)
+    return fail(QG_EINVAL, "%s: K=%lld above %lld for M=%lld", fn, (long long)w->K, (long long)kmax, (long long)w->M);
   if (norm_w && w->K > qg::kQ2XNormMaxK)
     return fail(QG_EINVAL, "%s: K=%lld above %d with the RMSNorm", fn, (long long)w->K, qg::kQ2XNormMaxK);
   if (norm_w && !(eps >= 0.0f && eps <= 3.4e38f)) return fail(QG_EINVAL, "%s: eps must be finite and >= 0", fn);
@@ -330,7 +326,7 @@ qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *accum, 
   if (st != QG_OK) return st;
   if (split_k < 0 || split_k > qg::kMaxSplit) return fail(QG_EINVAL, "%s: split_k=%d outside 0..16", fn, split_k);
   const int S = split_k == 0 ? qg::q2x_auto_split(w->M, w->K, w->group) : split_k;
-  if ((st = check_x_input(fn, w, x, nullptr, 0.0f, S)) != QG_OK) return st;
+  if ((st = check_x_input(fn, w, x, nullptr, 0.0f)) != QG_OK) return st;
   if (!y) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (!aligned(y, 4) || (accum && !aligned(accum, 4))) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
   if (accum && accum != y && overlap(accum, y, w->M))
@@ -377,7 +373,7 @@ static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_
   if ((st = qg::check_q2_weight(w1, fn)) != QG_OK) return st;
   if (w1->M != w0->M || w1->K != w0->K || w1->group != w0->group)
     return fail(QG_EINVAL, "%s: the two weights differ in shape or group", fn);
-  if ((st = check_x_input(fn, w0, x, norm_w, eps, 1)) != QG_OK) return st;
+  if ((st = check_x_input(fn, w0, x, norm_w, eps)) != QG_OK) return st;
   if (!y0 || (glu < 0 && !y1)) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (!aligned(y0, 4) || (y1 && !aligned(y1, 4))) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
   const size_t xbytes = (size_t)w0->K * sizeof(float), ybytes = (size_t)w0->M * sizeof(float);

@@ -158,9 +158,9 @@ __device__ inline bool arrive_last(int *cnt, int n) {
 }
 
 // grid = (row tiles x matrices, splits), one row tile of one matrix per
-// workgroup of W waves (the plain kernel's waves per tile).  RQ quads of
-// this split's share of the vector are held per thread.  UPG units per
-// scale group, GPB groups per load step.
+// workgroup of W waves (the plain kernel's waves per tile).  RQ quads of the
+// vector are held per thread (K <= 4 * RQ * 64 * W).  UPG units per scale
+// group, GPB groups per load step.
 template <int UPG, int GPB, int W, int RQ, int PRO, int EPI>
 __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
   constexpr int NT = 64 * W;
@@ -192,38 +192,51 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
   const i32x4 *cp = (mat ? a.codes[1] : a.codes[0]) + (size_t)tile * nunits * 64 + lane;
   const unsigned short *sp = (mat ? a.scales[1] : a.scales[0]) + (size_t)tile * ngroups * 64 + lane;
 
-  // 1. This wave's first load step, then the vector: both round trips at
-  //    once (the prologue waits for the vector, hence for these loads too,
-  //    and then computes with the first weights already in registers).
-  i32x4 c[GPB * UPG];
-  unsigned short dh[GPB];
-  const bool pre = g0 + GPB <= g1;
-  if (pre) {
-#pragma unroll
-    for (int vv = 0; vv < GPB * UPG; vv++) c[vv] = __builtin_nontemporal_load(cp + (size_t)(g0 * UPG + vv) * 64);
-#pragma unroll
-    for (int j = 0; j < GPB; j++) dh[j] = __builtin_nontemporal_load(sp + (size_t)(g0 + j) * 64);
-  }
+  // 1. The whole vector first, then this wave's first load step of weights.
+  //    Every load is issued unconditionally, indices clamped into range (a
+  //    clamped quad repeats the vector's last one; a clamped weight load
+  //    repeats one of the wave's own), so the compiler counts them exactly:
+  //    the loads return in order, and the prologue waits for the vector
+  //    alone while the weights stream in.  (Issued after the vector, the
+  //    first quantiser pass measured 2 us faster per launch than with the
+  //    weights first, on HBM-cold weights.)
   const int n4 = K / 4;
   const int q0 = u0 * 16, q1 = gs1 * UPG * 16;  // quads of this split
   float4 v[RQ];
+  float4 w[PRO == PRO_NORM ? RQ : 1];
 #pragma unroll
   for (int r = 0; r < RQ; r++) {
-    const int i = q0 + tid + r * NT;
-    if (i < q1) v[r] = a.x[i];
+    const int i = min(tid + r * NT, n4 - 1);
+    v[r] = a.x[i];
+    if (PRO == PRO_NORM) w[r] = a.norm_w[i];
   }
+  i32x4 c[GPB * UPG];
+  unsigned short dh[GPB];
+  const bool pre = g0 + GPB <= g1;
+  auto prefetch = [&]() {
+    const int gl = max(g1 - 1, 0);
+#pragma unroll
+    for (int j = 0; j < GPB; j++)
+#pragma unroll
+      for (int vv = 0; vv < UPG; vv++)
+        c[j * UPG + vv] = __builtin_nontemporal_load(cp + (size_t)(min(g0 + j, gl) * UPG + vv) * 64);
+#pragma unroll
+    for (int j = 0; j < GPB; j++) dh[j] = __builtin_nontemporal_load(sp + (size_t)min(g0 + j, gl) * 64);
+  };
+  // With the RMSNorm the weights go out after the binary64 sum of squares,
+  // so that its temporaries and the weights are never live together (fewer
+  // registers, three workgroups per CU); loads issued after the weights
+  // would wait behind them, so the norm weights come with the vector.
+  if (PRO != PRO_NORM) prefetch();
   float m = 0.0f;
-  if (PRO == PRO_X && S > 1)  // the rest of the vector, for its max only
-    for (int i = tid; i < n4; i += NT)
-      if (i < q0 || i >= q1) m = fmaxf(m, abs_max4(a.x[i]));
 
   // 2. Prologue: the quantised vector of this split's units into LDS.
   if (PRO == PRO_NORM) {
     // RMSNorm exactly as rmsnorm_quant_kernel: its 1024 threads' binary64
     // sums (thread t: quads t, t + 1024, ...), each wave's shuffle tree and
     // the 16 wave sums added in order; here thread tid stands for threads
-    // tid + NT * j, j < VPT (S = 1, so q0 = 0 and quad tid + NT r belongs
-    // to thread tid + NT (r % VPT)).
+    // tid + NT * j, j < VPT (quad tid + NT r belongs to thread
+    // tid + NT (r % VPT)).
     double ss[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; j++) ss[j] = 0.0;
@@ -243,23 +256,19 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
     for (int k = 0; k < 16; k++) tot += rss[k];
     const float ms = (float)(tot / (double)(4 * n4));
     const float inv = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, a.eps)));
-    // the norm weights are loaded only now (from L2), so that they and the
-    // vector are not both held across the sum: fewer registers, more
-    // workgroups per CU
+    prefetch();
 #pragma unroll
-    for (int r = 0; r < RQ; r++)
-      if (tid + r * NT < n4) v[r] = mul4(scale4(v[r], inv), a.norm_w[tid + r * NT]);
+    for (int r = 0; r < RQ; r++) v[r] = mul4(scale4(v[r], inv), w[r]);
   }
 #pragma unroll
-  for (int r = 0; r < RQ; r++)
-    if (q0 + tid + r * NT < q1) m = fmaxf(m, abs_max4(v[r]));
+  for (int r = 0; r < RQ; r++) m = fmaxf(m, abs_max4(v[r]));
   const float amax = block_max_nt<NT>(m, rmax);
   const float sc = __fdiv_rn(amax, 127.0f);
   const float qinv = sc > 0.0f ? __fdiv_rn(1.0f, sc) : 0.0f;
 #pragma unroll
   for (int r = 0; r < RQ; r++) {
-    const int i = tid + r * NT;  // quad of the split, counted from q0
-    if (q0 + i < q1) quant_quad(i, v[r], qinv, reinterpret_cast<int *>(xl), sl);
+    const int i = tid + r * NT;
+    if (i >= q0 && i < q1) quant_quad(i - q0, v[r], qinv, reinterpret_cast<int *>(xl), sl);
   }
   lds_barrier();
 
@@ -376,10 +385,9 @@ hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
   }
   const bool norm = c.norm_w != nullptr;
   // Waves per tile as the plain kernels: 8 when one matrix's row tiles fill
-  // the CUs, else 16; quads held per thread: 4 or 8 per split.
+  // the CUs, else 16; quads of the vector held per thread: 4 or 8.
   const int waves = tiles >= 256 ? 8 : 16;
-  const int gps = (c.K / c.group + a.S - 1) / a.S;
-  const int rq = (gps * c.group / 4 + 64 * waves - 1) / (64 * waves) <= 4 ? 4 : 8;
+  const int rq = (c.K / 4 + 64 * waves - 1) / (64 * waves) <= 4 ? 4 : 8;
   const dim3 grid(tiles * (pair ? 2 : 1), a.S);
 #define QXK(UPG, GPB, W, RQ, PRO, EPI) q2_gemv_x_kernel<UPG, GPB, W, RQ, PRO, EPI><<<grid, 64 * W, 0, stream>>>(a)
 #define QXE(UPG, GPB, W, RQ, PRO)                                      \

@@ -70,11 +70,12 @@ hipError_t launch_q2_gemv(const Q2Call &call, hipStream_t stream);
 // accum optional.  ws: the arrival counters (q2x_cnt_bytes) then [S][Mp]
 // (or [2][Mp]) f32, all zero between calls.
 inline size_t q2x_cnt_bytes(int64_t M) { return (size_t)round_up((M + 63) / 64, 64) * sizeof(int); }
-// Largest share of K one workgroup quantises (held in registers: 8 quads
-// per thread of its 8 or 16 waves), and the largest K with the RMSNorm.
+// Largest K: every workgroup holds the whole vector in registers, 8 quads
+// per thread of its 8 (M >= 16384) or 16 waves; with the RMSNorm (the norm
+// weights held too) at most 16384.
 constexpr int kQ2XMaxK = 32768;
 constexpr int kQ2XNormMaxK = 16384;
-inline int64_t q2x_max_split_k(int64_t M) { return (M + 63) / 64 >= 256 ? 16384 : 32768; }
+inline int64_t q2x_max_k(int64_t M) { return (M + 63) / 64 >= 256 ? 16384 : 32768; }
 struct Q2XCall {
   const void *codes[2];
   const void *scales[2];
