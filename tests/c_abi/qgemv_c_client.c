@@ -11,7 +11,9 @@
  * q8 int8[M8][K8], rs f32[M8], xs f32[K8], the Q2 block blob
  * (qg_q2_blocks_bytes(M2, K2, group) bytes), x f32[K2].
  * Output file: y8 f32[M8], y2 f32[M2], xq int8[K2], act_scale f32,
- * suma int32[K2/64].
+ * suma int32[K2/64], y2x f32[M2] (the same Q2 GEMV by qgemv_q2_x: the
+ * quantiser and the split's reduce inside one launch, its workspace
+ * cleared once with hipMemset as the header asks).
  * Exit status 0 on success; otherwise a message names the failing call.
  */
 #include <stdint.h>
@@ -118,6 +120,15 @@ int main(int argc, char **argv) {
   w.reserved = 0;
   QG_OK_(qquant_act_i8(d_x2, K2, d_xq, d_sc, d_suma, (void *)stream));
   QG_OK_(qgemv_q2(&w, d_xq, d_suma, d_sc, d_y2, d_ws, ws_bytes, split, (void *)stream));
+  float *d_y2x = NULL;
+  void *d_wsx = NULL;
+  HIP_OK(hipMalloc((void **)&d_y2x, (size_t)M2 * 4));
+  const size_t wsx_bytes = qgemv_q2_x_ws_bytes(M2, K2, group, split);
+  if (wsx_bytes) {
+    HIP_OK(hipMalloc(&d_wsx, wsx_bytes));
+    HIP_OK(hipMemset(d_wsx, 0, wsx_bytes));
+  }
+  QG_OK_(qgemv_q2_x(&w, d_x2, NULL, d_y2x, d_wsx, wsx_bytes, split, (void *)stream));
   HIP_OK(hipStreamSynchronize(stream));
 
   float *y8 = malloc((size_t)M8 * 4), *y2 = malloc((size_t)M2 * 4), sc;
@@ -128,6 +139,8 @@ int main(int argc, char **argv) {
   HIP_OK(hipMemcpy(xq, d_xq, (size_t)K2, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(&sc, d_sc, 4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(suma, d_suma, (size_t)(K2 / 64) * 4, hipMemcpyDeviceToHost));
+  float *y2x = malloc((size_t)M2 * 4);
+  HIP_OK(hipMemcpy(y2x, d_y2x, (size_t)M2 * 4, hipMemcpyDeviceToHost));
   FILE *out = fopen(argv[2], "wb");
   if (!out) return 1;
   fwrite(y8, 4, (size_t)M8, out);
@@ -135,6 +148,7 @@ int main(int argc, char **argv) {
   fwrite(xq, 1, (size_t)K2, out);
   fwrite(&sc, 4, 1, out);
   fwrite(suma, 4, (size_t)(K2 / 64), out);
+  fwrite(y2x, 4, (size_t)M2, out);
   fclose(out);
   HIP_OK(hipStreamDestroy(stream));
   printf("qgemv C client: ok (q8_row %lldx%lld, Q2 g%d %lldx%lld split %d)\n", (long long)M8, (long long)K8, group,

@@ -1,7 +1,8 @@
 """The C-ABI used from plain C: the client program under tests/c_abi (built
 by __graft_entry__.build()) runs a q8_row GEMV and a Q2 GEMV with its
-activation quantiser and a K split, in its own process, on inputs this test
-writes; its outputs are held to the oracle (the quantiser bit for bit, the
+activation quantiser and a K split (and the same GEMV with the quantiser
+and the split's reduce inside one launch), in its own process, on inputs
+this test writes; its outputs are held to the oracle (the quantiser bit for bit, the
 GEMVs within |y - y_ref| <= 2e-5 * sum_i |w_i x_i|)."""
 import os
 import subprocess
@@ -47,6 +48,7 @@ def test_c_client_matches_oracle(tmp_path, M2, K2, group, split):
 
     y8, y2 = take(M8, np.float32), take(M2, np.float32)
     xq, sc, suma = take(K2, np.int8), take(1, np.float32)[0], take(K2 // 64, np.int32)
+    y2x = take(M2, np.float32)
     assert off == len(raw)
     rq, rsc, rsu = oracle.act_quant_i8(x2)
     assert np.array_equal(xq, rq) and sc == rsc and np.array_equal(suma, rsu)
@@ -54,3 +56,6 @@ def test_c_client_matches_oracle(tmp_path, M2, K2, group, split):
     assert np.all(np.abs(y8.astype(np.float64) - y8r) <= 2e-5 * m8), "q8_row GEMV from C outside bound"
     y2r, m2 = oracle.q2_gemv(blob, M2, K2, group, rq, rsc)
     assert np.all(np.abs(y2.astype(np.float64) - y2r) <= 2e-5 * m2), "Q2 GEMV from C outside bound"
+    assert np.all(np.abs(y2x.astype(np.float64) - y2r) <= 2e-5 * m2), "qgemv_q2_x from C outside bound"
+    if split:  # the same explicit split: the same bits as quantiser + qgemv_q2
+        assert np.array_equal(y2x.view(np.uint32), y2.view(np.uint32)), "qgemv_q2_x from C differs from qgemv_q2"
