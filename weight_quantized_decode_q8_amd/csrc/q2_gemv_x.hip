@@ -21,16 +21,14 @@
 // and the decode FFN's quantisers and split reduce each paid it for a few
 // tens of KiB of work.  Quantising in every workgroup repeats that small
 // work (the vector is read from L2) but overlaps it with the workgroup's
-// first weight loads, which are issued before the prologue.
+// first weight loads, which stream in during the prologue.
 //
-// Layout of the work: one row tile (64 rows, one per lane) per workgroup and
-// matrix, K split over the waves as in q2_gemv_t64_kernel.  The activation
-// words, which the plain kernel reads through the scalar cache, come from
-// LDS here (broadcast ds_read_b128: every lane reads the same address).  A
-// gate|up pair puts the two matrices on the two halves of the workgroup; a
-// shape whose plain dual kernel uses 16 waves per matrix runs each half's 8
-// waves over two of those waves' group ranges ("virtual waves"), each with
-// its own accumulator, so the sums and their combine order are unchanged.
+// Layout of the work: one row tile (64 rows, one per lane) of one matrix per
+// workgroup, with the plain kernel's waves per tile and K split over the
+// waves as in q2_gemv_t64_kernel; the gate|up pair is two matrices' tiles in
+// one grid.  The activation words, which the plain kernel reads through the
+// scalar cache, come from LDS here (broadcast ds_read_b128: every lane reads
+// the same address).
 //
 // Split-K in one launch: each (tile, split) workgroup stores its partial and
 // then increments the tile's counter; the workgroup that sees the count S-1
@@ -38,8 +36,8 @@
 // zero: the workspace is all zero between calls, so one workspace serves
 // calls of any shape and split.  The gate|up pair with the gated product
 // meets the same way: each matrix's workgroup of a tile stores its g or u,
-// and the second to arrive forms t.  No workgroup
-// waits on another, so nothing can hang on a missing arrival.
+// and the second to arrive forms t.  No workgroup waits on another, so
+// nothing can hang on a missing arrival.
 #include "gate_rule.h"
 #include "qg_internal.h"
 #include "quant_rule.h"
