@@ -241,3 +241,37 @@ def test_ffn_block_two_launches_equals_fused_chain():
     rows = np.arange(0, D, 37)
     yref, mass = oracle.q2_gemv_accum(bd, D, F, group, tq, tsc, resid, rows=rows)
     within(host(y)[rows], yref, mass + np.abs(yref) * 2.0 ** -24 / 2e-5, what="FFN block down")
+
+
+def test_decode_ffn_workloads_as_benched():
+    """The decode step's Q2 workloads (g128 gate and up 17408 x 5120, down
+    5120 x 17408, the seeded inputs and the launch configuration the bench
+    times: the pair with the quantiser inside, the down projection with the
+    quantiser and its automatic split inside): sampled rows against the fp64
+    oracle on the oracle's own quantised activations, every row against the
+    six-launch chain bit for bit."""
+    m = qg()
+    blobs, xs, Ws = {}, {}, {}
+    for n in ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120", "q2_g128_down_5120x17408"):
+        c = synth.CONFIGS[n]
+        blobs[n], xs[n] = synth.config_inputs(n)
+        Ws[n] = m.Q2Weight.from_blocks(blobs[n], c["M"], c["K"], c["group"])
+    Wg, Wu = Ws["q2_g128_gate_17408x5120"], Ws["q2_g128_up_17408x5120"]
+    Wd = Ws["q2_g128_down_5120x17408"]
+    x_gu, x_dn = xs["q2_g128_gate_17408x5120"], xs["q2_g128_down_5120x17408"]
+    yg, yu = _empty(Wg.M), _empty(Wg.M)
+    m.qgemv_q2_dual_x(Wg, Wu, dev(x_gu), yg, yu)
+    S = m.qgemv_q2_x_auto_split(Wd.M, Wd.K, Wd.group)
+    assert S == 3
+    yd = _empty(Wd.M)
+    m.qgemv_q2_x(Wd, dev(x_dn), yd, ws=m.qgemv_q2_x_workspace(Wd.M, Wd.K, Wd.group, 0), split_k=0)
+    yg, yu, yd = host(yg), host(yu), host(yd)
+    assert np.array_equal(bits(yg), bits(chain_single(Wg, x_gu, 1)))
+    assert np.array_equal(bits(yu), bits(chain_single(Wu, x_gu, 1)))
+    assert np.array_equal(bits(yd), bits(chain_single(Wd, x_dn, S)))
+    for name, W, x, y in (("q2_g128_gate_17408x5120", Wg, x_gu, yg), ("q2_g128_up_17408x5120", Wu, x_gu, yu),
+                          ("q2_g128_down_5120x17408", Wd, x_dn, yd)):
+        rq, rsc, _ = oracle.act_quant_i8(x)
+        rows = np.unique(np.concatenate([np.arange(0, W.M, 97), [W.M - 1]]))
+        yref, mass = oracle.q2_gemv(blobs[name], W.M, W.K, W.group, rq, rsc, rows=rows)
+        within(y[rows], yref, mass, what=name)
