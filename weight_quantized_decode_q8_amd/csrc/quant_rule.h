@@ -10,9 +10,9 @@
 // other binary32 evaluation of the rule.
 //
 // The vector is handled as float4 quads: thread t takes quads t, t + 1024,
-// ...; 16 consecutive threads cover one 64-wide group (the quad count and
-// kQuantThreads are multiples of 16, so a group's threads are active or idle
-// together).
+// ...; the 16 consecutive threads of one 16-lane row cover one 64-wide group
+// (the quad count and kQuantThreads are multiples of 16, so a group's
+// threads are active or idle together).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,17 +50,25 @@ __device__ inline float scale_and_inverse(float amax, float *act_scale) {
   return sc > 0.0f ? __fdiv_rn(1.0f, sc) : 0.0f;
 }
 
-// Quantise quad i (values v) into xq4[i]; the 16 threads of a group combine
-// their sums into suma[i / 16].
+// Running sum of s over the lanes of this lane's 16-lane row up to this
+// lane (DPP row shifts, no LDS traffic): the row's last lane holds the sum
+// of all 16.  Every lane of the row must be active.
+__device__ inline int row16_prefix_sum(int s) {
+  s += __builtin_amdgcn_update_dpp(0, s, 0x111, 0xF, 0xF, true);  // row_shr:1
+  s += __builtin_amdgcn_update_dpp(0, s, 0x112, 0xF, 0xF, true);  // row_shr:2
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xF, true);  // row_shr:4
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xF, true);  // row_shr:8
+  return s;
+}
+
+// Quantise quad i (values v) into xq4[i]; the 16 threads of a group (one
+// 16-lane row, since i and the thread index advance together in multiples
+// of 16) combine their sums into suma[i / 16].
 __device__ inline void quant_quad(int i, float4 v, float inv, int *__restrict__ xq4, int *__restrict__ suma) {
   const int a = quant1(v.x, inv), b = quant1(v.y, inv), c = quant1(v.z, inv), d = quant1(v.w, inv);
   xq4[i] = (a & 0xff) | ((b & 0xff) << 8) | ((c & 0xff) << 16) | ((unsigned)(d & 0xff) << 24);
-  int s = a + b + c + d;
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  s += __shfl_xor(s, 8);
-  if ((i & 15) == 0) suma[i >> 4] = s;
+  const int s = row16_prefix_sum(a + b + c + d);
+  if ((i & 15) == 15) suma[i >> 4] = s;
 }
 
 // Element-wise binary32 products of a quad (each one rounding), for the
