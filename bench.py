@@ -7,7 +7,8 @@ captured once in a HIP graph and replayed, three launches:
     activation x (K=5120) quantised inside it) -> Q2 g128 down GEMV
     5120x17408 (h, K=17408, quantised inside the launch; split-K partials
     added by the last workgroup of each row tile) -> q8_row lm_head GEMV
-    248320x5120.
+    248320x5120 (its last partial round of 40 row tiles split along K over
+    the whole GPU).
 The same step as six launches (the quantisers and the split reduce as
 launches of their own, the same bits) is timed beside it.
 `value` is the weight bytes the step streams (the formats' own bytes: 34 B
@@ -176,7 +177,14 @@ def main():
     def k_down_x():  # quantiser and split-K reduce inside the launch
         qg.qgemv_q2_x(Wdn, xdn_d, y["q2_g128_down_5120x17408"], ws=ws_dnx, split_k=S_dn)
 
+    # the lm_head's last partial round of row tiles (3880 = 15 x 256 + 40)
+    # split along K over the whole GPU (qgemv_q8row_balanced)
+    ws4 = L4.workspace(dev)
+
     def k_lm_head():
+        L4.gemv_balanced(xs4_d, y4, ws4)
+
+    def k_lm_head_plain():
         L4.gemv(xs4_d, y4)
 
     def step6():  # the same step as six launches: quantisers and the split reduce on their own
@@ -349,7 +357,8 @@ def main():
                                 ("q2_gate_up_pair_x_2x17408x5120_g128", k_gate_up_x,
                                  q2_bytes["q2_g128_gate_17408x5120"] + q2_bytes["q2_g128_up_17408x5120"], 20),
                                 ("q2_down_x_5120x17408_g128", k_down_x, q2_bytes["q2_g128_down_5120x17408"], 20),
-                                ("q8row_lm_head_248320x5120", k_lm_head, lm_bytes, 10)]):
+                                ("q8row_lm_head_248320x5120", k_lm_head, lm_bytes, 10),
+                                ("q8row_lm_head_248320x5120_plain_launch", k_lm_head_plain, lm_bytes, 10)]):
         us = kernel_us(fn, n)
         ent = {"us": round(us, 3)}
         if nbytes:
@@ -374,7 +383,7 @@ def main():
     torch.cuda.synchronize()
     dom_us = a.elapsed_time(b) * 1e3 / n_dom
     achieved = lm_bytes / dom_us / 1e3
-    roofline = {"bound": "hbm", "kernel": "q8row_gemv_t64 (lm_head 248320x5120)",
+    roofline = {"bound": "hbm", "kernel": "q8row_gemv_t64 (lm_head 248320x5120, balanced launch)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
                 "avg_launch_us": round(dom_us, 2), "algorithmic_bytes_per_launch": lm_bytes}
@@ -723,7 +732,7 @@ def main():
                    "step_weight_bytes": step_bytes,
                    "graph": "hipGraph of three launches: gate|up pair with the act-quant in the launch "
                             "(qgemv_q2_dual_x), down with the act-quant and the split-K reduce in the launch "
-                            "(qgemv_q2_x), lm_head",
+                            "(qgemv_q2_x), lm_head (qgemv_q8row_balanced)",
                    "down_split_k": S_dn,
                    "six_launch_form_us_per_step": round(us_step6, 2),
                    "six_launch_form": "act-quant, gate|up pair, act-quant, down partials, split-K reduce, "

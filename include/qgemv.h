@@ -117,6 +117,33 @@ qg_status qg_unpack_q8row(const void *packed, size_t packed_bytes,
 qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs,
                       float *y, int64_t M, int64_t K, void *stream);
 
+/* Bytes of workspace qgemv_q8row_balanced needs for this shape (0 when M
+ * gives whole rounds of row tiles over the 256 CUs, or less than one).    */
+size_t qgemv_q8row_balanced_ws_bytes(int64_t M, int64_t K);
+
+/* Device: the same GEMV as qgemv_q8row, with its last partial round of row
+ * tiles spread over the whole GPU   [Q8]
+ *   A launch of T = ceil(M/64) tiles runs T / 256 full rounds on the 256
+ *   CUs and then R = T mod 256 tiles on R CUs while the others idle (on
+ *   the 248320-row lm_head, 40 tiles costing 8.6 us).  Here each of those
+ *   R tiles is split along K into S pieces (R * S >= 256, S <= 16), one
+ *   workgroup each at the end of the grid, and the last piece of a tile to
+ *   finish adds the pieces' row sums in piece order.
+ *   ws:        device, >= qgemv_q8row_balanced_ws_bytes(M, K) bytes,
+ *              16-byte aligned (may be NULL when that is 0), all zero before
+ *              the first call that uses it (allocate it zero-filled); every
+ *              call leaves it all zero again.  Calls sharing one ws must not
+ *              overlap in time.
+ *   Other arguments as qgemv_q8row.  The outputs of the full rounds' tiles
+ *   equal qgemv_q8row's bit for bit; those of the R split tiles differ only
+ *   in the f32 summation order (the same bound holds).
+ * QG_EINVAL: as qgemv_q8row, or a short, misaligned or overlapping
+ * workspace.                                                              */
+qg_status qgemv_q8row_balanced(const void *qpacked, const float *rs,
+                               const float *xs, float *y, int64_t M,
+                               int64_t K, void *ws, size_t ws_bytes,
+                               void *stream);
+
 /* ======================================================================
  * Q2 weights  [Q2]
  *

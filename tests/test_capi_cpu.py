@@ -373,3 +373,22 @@ def test_einval_paths_in_launch_quantiser():
     _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, None, 0, None))
     _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, WS, 100, None))
     _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, P(0x600000), 4096, None))
+
+
+def test_q8row_balanced_sizes_and_einval():
+    L = qg.lib()
+    P = ctypes.c_void_p
+    # 248320 rows: 3880 tiles = 15 rounds of 256 + 40, split 7 ways
+    assert L.qgemv_q8row_balanced_ws_bytes(248320, 5120) == 256 + 40 * 7 * 64 * 4
+    assert L.qgemv_q8row_balanced_ws_bytes(100, 512) == 0          # under one round
+    assert L.qgemv_q8row_balanced_ws_bytes(64 * 512, 512) == 0     # whole rounds
+    assert L.qgemv_q8row_balanced_ws_bytes(64 * 257, 1024) == 256 + 1 * 16 * 64 * 4   # S capped at 16
+    assert L.qgemv_q8row_balanced_ws_bytes(64 * 257, 96) == 256 + 1 * 6 * 64 * 4      # S at most the chunks
+    a16 = P(0x10000)
+    _einval(L.qgemv_q8row_balanced(None, a16, a16, a16, 64, 64, None, 0, None))
+    _einval(L.qgemv_q8row_balanced(a16, a16, a16, a16, 64, 62, None, 0, None))
+    M = 64 * 257
+    _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, None, 0, None))
+    _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x500000), 100, None))
+    _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x500008), 1 << 20, None))
+    _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x400100), 1 << 20, None))

@@ -75,6 +75,8 @@ _SIGS = {
     "qgemv_q2_batch": (_I, [ctypes.POINTER(qg_q2_job), _I, _P]),
     "qgemv_q2_gate_up_glu": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _I, _P, _P,
                                   _P, _P, _P]),
+    "qgemv_q8row_balanced_ws_bytes": (_SZ, [_I64, _I64]),
+    "qgemv_q8row_balanced": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemv_q2_x_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
     "qgemv_q2_x_auto_split": (_I, [_I64, _I64, _I]),
     "qgemv_q2_x": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _SZ, _I, _P]),
@@ -179,6 +181,15 @@ def qgemv_q8row(qpacked, rs, xs, y, M: int, K: int, stream=None):
         _dev(xs, torch.float32, "xs"), _dev(y, torch.float32, "y"), M, K, _stream(stream)))
 
 
+def qgemv_q8row_balanced(qpacked, rs, xs, y, M: int, K: int, ws, stream=None):
+    """qgemv_q8row with the last partial round of row tiles split along K; ws all zero (calls leave it so)."""
+    import torch
+    _check("qgemv_q8row_balanced", lib().qgemv_q8row_balanced(
+        _dev(qpacked, torch.uint8, "qpacked"), _dev(rs, torch.float32, "rs"), _dev(xs, torch.float32, "xs"),
+        _dev(y, torch.float32, "y"), M, K, _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(),
+        _stream(stream)))
+
+
 @dataclass
 class Q8RowWeight:
     """A q8_row matrix resident on the device: T64 image + row scales."""
@@ -196,6 +207,16 @@ class Q8RowWeight:
 
     def gemv(self, xs, y, stream=None):
         qgemv_q8row(self.packed, self.rs, xs, y, self.M, self.K, stream)
+
+    def workspace(self, device="cuda"):
+        """The zero-filled workspace gemv_balanced needs (None when it needs none)."""
+        import torch
+        n = lib().qgemv_q8row_balanced_ws_bytes(self.M, self.K)
+        return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+    def gemv_balanced(self, xs, y, ws, stream=None):
+        """The same GEMV with the last partial round of row tiles split along K over the GPU."""
+        qgemv_q8row_balanced(self.packed, self.rs, xs, y, self.M, self.K, ws, stream)
 
 
 # -------------------------------------------------------------------- Q2 --

@@ -59,16 +59,56 @@ const char *qg_last_error(void) { return qg::g_msg; }
 
 int qg_abi_version(void) { return 6; }
 
-qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
-                      int64_t K, void *stream) {
-  const char *fn = "qgemv_q8row";
+static bool overlap(const float *a, const float *b, int64_t n) { return a < b + n && b < a + n; }
+
+// Byte ranges [a, a + na) and [b, b + nb) share a byte (null b: never).
+static bool bytes_overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+static qg_status q8row_args(const char *fn, const void *qpacked, const float *rs, const float *xs, float *y,
+                            int64_t M, int64_t K) {
   if (!qpacked || !rs || !xs || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (M < 1 || M > (1LL << 31) - 64) return fail(QG_EINVAL, "%s: bad M=%lld", fn, (long long)M);
   if (K < 4 || K % 4 != 0 || K > (1 << 30)) return fail(QG_EINVAL, "%s: K=%lld must be a positive multiple of 4", fn, (long long)K);
   if (!aligned(qpacked, 16)) return fail(QG_EINVAL, "%s: weight image not 16-byte aligned", fn);
   if (!aligned(xs, 16)) return fail(QG_EINVAL, "%s: xs not 16-byte aligned", fn);
   if (!aligned(rs, 4) || !aligned(y, 4)) return fail(QG_EINVAL, "%s: rs/y not 4-byte aligned", fn);
+  return QG_OK;
+}
+
+qg_status qgemv_q8row(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
+                      int64_t K, void *stream) {
+  const char *fn = "qgemv_q8row";
+  qg_status st = q8row_args(fn, qpacked, rs, xs, y, M, K);
+  if (st != QG_OK) return st;
   return qg::launched(qg::launch_q8row_gemv(qpacked, rs, xs, y, (int)M, (int)K, (hipStream_t)stream), fn);
+}
+
+size_t qgemv_q8row_balanced_ws_bytes(int64_t M, int64_t K) {
+  if (M < 1 || M > (1LL << 31) - 64 || K < 4 || K > (1 << 30)) return 0;
+  const qg::Q8TailSplit t = qg::q8row_tail_split(M, K);
+  if (t.tiles_split == 0) return 0;
+  return qg::q8_tail_cnt_bytes(t.tiles_split) + (size_t)t.tiles_split * t.S * 64 * sizeof(float);
+}
+
+qg_status qgemv_q8row_balanced(const void *qpacked, const float *rs, const float *xs, float *y, int64_t M,
+                               int64_t K, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "qgemv_q8row_balanced";
+  qg_status st = q8row_args(fn, qpacked, rs, xs, y, M, K);
+  if (st != QG_OK) return st;
+  const size_t need = qgemv_q8row_balanced_ws_bytes(M, K);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws ? ws_bytes : (size_t)0, need);
+  if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
+  const size_t ybytes = (size_t)M * sizeof(float), xbytes = (size_t)K * sizeof(float);
+  if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, xs, xbytes) ||
+                   bytes_overlap(ws, need, rs, ybytes)))
+    return fail(QG_EINVAL, "%s: workspace overlaps y, xs or rs", fn);
+  return qg::launched(
+      qg::launch_q8row_gemv_balanced(qpacked, rs, xs, y, (int)M, (int)K, ws, (hipStream_t)stream), fn);
 }
 
 qg_status qquant_act_i8(const float *x, int64_t K, int8_t *xq, float *act_scale, int32_t *suma,
@@ -159,15 +199,6 @@ size_t qgemv_q2_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
   const int S = split_k == 0 ? qg::q2_auto_split(M, K, group) : split_k;
   if (S <= 1 || S > qg::kMaxSplit) return 0;
   return (size_t)S * (size_t)qg::round_up(M, 64) * sizeof(float);
-}
-
-static bool overlap(const float *a, const float *b, int64_t n) { return a < b + n && b < a + n; }
-
-// Byte ranges [a, a + na) and [b, b + nb) share a byte (null b: never).
-static bool bytes_overlap(const void *a, size_t na, const void *b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
 }
 
 static qg_status q2_common(const char *fn, const qg_q2_weight *w, const qg_q2_weight *w1, const int8_t *xq,

@@ -38,6 +38,7 @@
 // meets the same way: each matrix's workgroup of a tile stores its g or u,
 // and the second to arrive forms t.  No workgroup waits on another, so
 // nothing can hang on a missing arrival.
+#include "arrival.h"
 #include "gate_rule.h"
 #include "qg_internal.h"
 #include "quant_rule.h"
@@ -119,40 +120,6 @@ __device__ inline float block_max_nt(float m, float *red) {
 #pragma unroll
   for (int w = 1; w < NT / 64; w++) r = fmaxf(r, red[w]);
   return r;
-}
-
-// The values two or more workgroups of a row tile exchange (split partials,
-// g and u) go through device-scope atomic swaps, which are performed at the
-// device's coherence point like the arrival counter itself, instead of plain
-// stores published by a device-scope release fence: that fence writes back
-// the whole L2 of the XCD, and with hundreds of workgroups it cost more than
-// the launch it replaces.
-__device__ inline void put(float *p, float v) {
-  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The value stored at p, which is left zero.
-__device__ inline float take(float *p) {
-  return __hip_atomic_exchange(p, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// s_waitcnt immediate for vmcnt(0) alone.
-constexpr int kVm0 = 0x0F70;
-
-// Counts this workgroup's arrival on the tile's counter once its put()s
-// have completed; true for the last of n arrivals, whose take()s are issued
-// after it and so see every earlier arrival's values.
-__device__ inline bool arrive_last(int *cnt, int n) {
-  // the swaps must be performed before the count: wait for every vector
-  // memory operation of this wave (the compiler does not order relaxed
-  // atomics to different addresses, nor wait for a swap whose result is
-  // unused)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kVm0);
-  asm volatile("" ::: "memory");
-  int prev = 0;
-  if ((threadIdx.x & 63) == 0) prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0);
-  return prev == n - 1;
 }
 
 // grid = (row tiles x matrices, splits), one row tile of one matrix per
@@ -328,7 +295,7 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
     float s = 0.0f;
     for (int k = 0; k < S; k++) s += take(a.part + (size_t)k * Mp + o);
     if (o < M) a.y[0][o] = scale_add(s, sc, a.accum, o);
-    if (lane == 0) __hip_atomic_store(a.cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    arrive_reset(a.cnt + tile);
   } else {
     // g or u of this tile, rounded as the GEMV rounds it; the second of the
     // tile's two workgroups forms t = glu(g, u) and clears the workspace.
@@ -338,7 +305,7 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
     const float other = take(a.part + (size_t)(1 - mat) * Mp + o);
     (void)take(a.part + (size_t)mat * Mp + o);
     if (o < M) a.y[0][o] = glu1<EPI == EPI_GLU_SILU ? 0 : 1>(mat ? other : r, mat ? r : other);
-    if (lane == 0) __hip_atomic_store(a.cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    arrive_reset(a.cnt + tile);
   }
 }
 

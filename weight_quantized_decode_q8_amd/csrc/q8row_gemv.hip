@@ -21,6 +21,21 @@
 // Rounding: each lane keeps 16 accumulators (one per byte position), so an
 // accumulator chain has K/16/8 terms, then a 16-way tree and an 8-way sum;
 // at K = 5120 the worst-case chain is about 50 roundings.
+//
+// Balanced form: a launch of T tiles on 256 CUs runs T / 256 full rounds and
+// then a partial one, in which R = T mod 256 tiles keep R CUs busy while the
+// rest idle (measured on the 248320-row lm_head: its last 40 tiles cost
+// 8.6 us of 196 against 1.8 us at the full-round rate).  The balanced launch
+// runs the T - R tiles of the full rounds as above and splits each of the R
+// others along K into S pieces, R * S >= 256, one per workgroup at the end of
+// the grid (measured: 190.6-191.8 us against 192.2-193.2 for the plain
+// launch; the pieces at the start of the grid, or split 16 ways, were slower
+// than the plain launch); the pieces' row sums meet in a workspace and the
+// last piece of a tile to arrive adds them in piece order (arrival.h).  Only the summation
+// order of those R tiles differs from the plain launch.
+#include <algorithm>
+
+#include "arrival.h"
 #include "qg_internal.h"
 
 namespace qg {
@@ -70,21 +85,43 @@ __device__ inline Chunk load_chunk(const i32x4 *p) {
   return Chunk{v.x, v.y, v.z, v.w};
 }
 
-// grid.x = number of 64-row tiles; block = kWaves wavefronts.
+// The split tail of the balanced launch: the tiles from tiles_full on are
+// cut into S pieces along K; part holds [tile - tiles_full][S][64] f32 row
+// sums, cnt one arrival counter per split tile.
+struct SplitTail {
+  int tiles_full, S;
+  float *part;
+  int *cnt;
+};
+
+// grid.x = number of 64-row tiles (kSplit: the full tiles, then S pieces of
+// each tile from tiles_full on); block = kWaves wavefronts.
+template <bool kSplit>
 __global__ __launch_bounds__(64 * kWaves) void q8row_gemv_t64_kernel(
     const i32x4 *__restrict__ qp, const float *__restrict__ rs, const float *__restrict__ xs,
-    float *__restrict__ y, int M, int K, int nchunk) {
+    float *__restrict__ y, int M, int K, int nchunk, SplitTail st) {
   __shared__ float red[kWaves - 1][64];
   const int lane = threadIdx.x & 63;
   // The wave index is uniform across the wavefront; saying so lets every
   // address derived from it (and from the chunk counter) live in SGPRs.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = blockIdx.x;
+  int tile = blockIdx.x;
+  // This workgroup's chunks: all of the tile's, or (split tail) piece `piece`.
+  int w0 = 0, w1 = nchunk, piece = 0;
+  const bool split = kSplit && tile >= st.tiles_full;
+  if (split) {
+    const int j = tile - st.tiles_full;
+    tile = st.tiles_full + j / st.S;
+    piece = j % st.S;
+    const int cps = (nchunk + st.S - 1) / st.S;
+    w0 = min(nchunk, piece * cps);
+    w1 = min(nchunk, w0 + cps);
+  }
 
   // Contiguous chunk range of this wave.
-  const int per = (nchunk + kWaves - 1) / kWaves;
-  const int c0 = min(nchunk, wave * per);
-  const int c1 = min(nchunk, c0 + per);
+  const int per = (w1 - w0 + kWaves - 1) / kWaves;
+  const int c0 = min(w1, w0 + wave * per);
+  const int c1 = min(w1, c0 + per);
   const int cfull = min(c1, K / kQ8Chunk);  // chunks lying wholly inside K
 
   const i32x4 *wp = qp + (size_t)tile * nchunk * 64 + lane;
@@ -117,12 +154,20 @@ __global__ __launch_bounds__(64 * kWaves) void q8row_gemv_t64_kernel(
 
   if (wave > 0) red[wave - 1][lane] = s;
   __syncthreads();
-  if (wave == 0) {
+  if (wave != 0) return;
 #pragma unroll
-    for (int w = 0; w < kWaves - 1; w++) s += red[w][lane];
-    const int o = tile * 64 + lane;
-    if (o < M) y[o] = s * rs[o];
+  for (int w = 0; w < kWaves - 1; w++) s += red[w][lane];
+  const int o = tile * 64 + lane;
+  if (split) {
+    const int t = tile - st.tiles_full;
+    float *pp = st.part + (size_t)t * st.S * 64 + lane;
+    put(pp + piece * 64, s);
+    if (!arrive_last(st.cnt + t, st.S)) return;
+    s = 0.0f;
+    for (int k = 0; k < st.S; k++) s += take(pp + k * 64);
+    arrive_reset(st.cnt + t);
   }
+  if (o < M) y[o] = s * rs[o];
 }
 
 }  // namespace
@@ -131,8 +176,38 @@ hipError_t launch_q8row_gemv(const void *qpacked, const float *rs, const float *
                              int M, int K, hipStream_t stream) {
   const int tiles = (M + 63) / 64;
   const int nchunk = (K + kQ8Chunk - 1) / kQ8Chunk;
-  q8row_gemv_t64_kernel<<<tiles, 64 * kWaves, 0, stream>>>(
-      reinterpret_cast<const i32x4 *>(qpacked), rs, xs, y, M, K, nchunk);
+  q8row_gemv_t64_kernel<false><<<tiles, 64 * kWaves, 0, stream>>>(
+      reinterpret_cast<const i32x4 *>(qpacked), rs, xs, y, M, K, nchunk, SplitTail{tiles, 1, nullptr, nullptr});
+  return hipGetLastError();
+}
+
+Q8TailSplit q8row_tail_split(int64_t M, int64_t K) {
+  const int64_t tiles = (M + 63) / 64;
+  const int64_t nchunk = (K + kQ8Chunk - 1) / kQ8Chunk;
+  Q8TailSplit t{(int)tiles, 0, 1};
+  const int64_t rest = tiles % kQ8Cus;
+  // Below one full round the whole launch is the tail: nothing to balance
+  // against (every tile already has a CU of its own).
+  if (tiles < kQ8Cus || rest == 0) return t;
+  int S = (int)((kQ8Cus + rest - 1) / rest);
+  S = (int)std::min<int64_t>({(int64_t)S, (int64_t)kQ8MaxTailSplit, nchunk});
+  if (S < 2) return t;
+  t.tiles_full = (int)(tiles - rest);
+  t.tiles_split = (int)rest;
+  t.S = S;
+  return t;
+}
+
+hipError_t launch_q8row_gemv_balanced(const void *qpacked, const float *rs, const float *xs, float *y, int M,
+                                      int K, void *ws, hipStream_t stream) {
+  const Q8TailSplit t = q8row_tail_split(M, K);
+  if (t.tiles_split == 0) return launch_q8row_gemv(qpacked, rs, xs, y, M, K, stream);
+  const int nchunk = (K + kQ8Chunk - 1) / kQ8Chunk;
+  SplitTail st{t.tiles_full, t.S, nullptr, nullptr};
+  st.cnt = static_cast<int *>(ws);
+  st.part = reinterpret_cast<float *>(static_cast<char *>(ws) + q8_tail_cnt_bytes(t.tiles_split));
+  q8row_gemv_t64_kernel<true><<<t.tiles_full + t.tiles_split * t.S, 64 * kWaves, 0, stream>>>(
+      reinterpret_cast<const i32x4 *>(qpacked), rs, xs, y, M, K, nchunk, st);
   return hipGetLastError();
 }
 

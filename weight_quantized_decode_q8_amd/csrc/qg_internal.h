@@ -41,6 +41,19 @@ hipError_t launch_silu_mul_pre(const float *g, const float *u, const float *col,
 
 hipError_t launch_q8row_gemv(const void *qpacked, const float *rs, const float *xs,
                              float *y, int M, int K, hipStream_t stream);
+// The balanced q8_row GEMV: the tiles past the last full round over the
+// kQ8Cus CUs are split along K into S pieces (tiles_split * S >= kQ8Cus,
+// S <= kQ8MaxTailSplit); ws holds one arrival counter per split tile
+// (q8_tail_cnt_bytes) then [tiles_split][S][64] f32, all zero between calls.
+constexpr int kQ8Cus = 256;
+constexpr int kQ8MaxTailSplit = 16;
+struct Q8TailSplit {
+  int tiles_full, tiles_split, S;
+};
+Q8TailSplit q8row_tail_split(int64_t M, int64_t K);
+inline size_t q8_tail_cnt_bytes(int64_t tiles_split) { return (size_t)round_up(tiles_split, 64) * sizeof(int); }
+hipError_t launch_q8row_gemv_balanced(const void *qpacked, const float *rs, const float *xs, float *y, int M,
+                                      int K, void *ws, hipStream_t stream);
 
 // One Q2 GEMV launch over one matrix, or two of one shape sharing the
 // activation (codes[1] non-null).  y[m] receive the results; with split > 1
