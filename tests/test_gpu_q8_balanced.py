@@ -88,3 +88,36 @@ def test_balanced_canary(M, K):
     W.gemv_balanced(dev(xs), y.t, ws.t)
     check(y, ws)
     assert int(torch.count_nonzero(ws.t).item()) == 0
+
+
+def test_balanced_graph_replays():
+    """Captured in a HIP graph and replayed with eager calls on the same
+    workspace in between: every replay gives the eager result bit for bit and
+    leaves the workspace all zero."""
+    import torch
+    M, K = 64 * 300 + 17, 2052
+    q, rs, xs = synth.q8row_inputs(M, K, seed=77)
+    W = qg().Q8RowWeight.from_host(q, rs)
+    ws = W.workspace()
+    xd = dev(xs)
+    y = torch.empty(M, device="cuda")
+    W.gemv_balanced(xd, y, ws)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        W.gemv_balanced(xd, y, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        W.gemv_balanced(xd, y, ws)
+    for rep in range(4):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {rep} differs from the eager result"
+        assert int(torch.count_nonzero(ws).item()) == 0, f"replay {rep} left the workspace non-zero"
+        W.gemv_balanced(xd, y, ws)  # eager call on the same workspace between replays
