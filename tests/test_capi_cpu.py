@@ -346,6 +346,8 @@ def test_einval_paths_in_launch_quantiser():
     _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x800008), 4096, 2, None))     # ws misaligned
     _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x500000), 4096, 2, None))     # ws over x
     _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x600000), 4096, 2, None))     # ws over y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x100100), 4096, 2, None))     # ws over the codes
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x200040), 4096, 2, None))     # ws over the scales
     big = qg.qg_q2_weight(0x100000, 0x200000, 128, 32768 + 64, 64, 0)
     _einval(L.qgemv_q2_x(ctypes.byref(big), X, None, Y, None, 0, 1, None))             # K above 32768
     wide = qg.qg_q2_weight(0x100000, 0x200000, 16384, 16384 + 128, 128, 0)
@@ -392,3 +394,4 @@ def test_q8row_balanced_sizes_and_einval():
     _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x500000), 100, None))
     _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x500008), 1 << 20, None))
     _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x400100), 1 << 20, None))
+    _einval(L.qgemv_q8row_balanced(P(0x1000000), P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x1000400), 1 << 20, None))

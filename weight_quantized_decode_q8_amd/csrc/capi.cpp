@@ -104,9 +104,10 @@ qg_status qgemv_q8row_balanced(const void *qpacked, const float *rs, const float
     return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws ? ws_bytes : (size_t)0, need);
   if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
   const size_t ybytes = (size_t)M * sizeof(float), xbytes = (size_t)K * sizeof(float);
+  const size_t wbytes = (size_t)qg::round_up(M, 64) * (size_t)qg::round_up(K, 16);
   if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, xs, xbytes) ||
-                   bytes_overlap(ws, need, rs, ybytes)))
-    return fail(QG_EINVAL, "%s: workspace overlaps y, xs or rs", fn);
+                   bytes_overlap(ws, need, rs, ybytes) || bytes_overlap(ws, need, qpacked, wbytes)))
+    return fail(QG_EINVAL, "%s: workspace overlaps y, xs, rs or the weight image", fn);
   return qg::launched(
       qg::launch_q8row_gemv_balanced(qpacked, rs, xs, y, (int)M, (int)K, ws, (hipStream_t)stream), fn);
 }
@@ -334,6 +335,13 @@ size_t qgemv_q2_x_ws_bytes(int64_t M, int64_t K, int group, int split_k) {
   return qg::q2x_cnt_bytes(M) + (size_t)S * (size_t)qg::round_up(M, 64) * sizeof(float);
 }
 
+// Byte range [p, p + n) overlaps one of the Q2 weight's device planes.
+static bool overlaps_q2_planes(const void *p, size_t n, const qg_q2_weight *w) {
+  const size_t rows = (size_t)qg::round_up(w->M, 64);
+  return bytes_overlap(p, n, w->codes, rows * (size_t)(w->K / 4)) ||
+         bytes_overlap(p, n, w->scales, rows * (size_t)(w->K / w->group) * 2);
+}
+
 // The f32 input vector of the in-launch quantiser: present, 16-byte
 // aligned, and short enough for each workgroup to hold it.
 static qg_status check_x_input(const char *fn, const qg_q2_weight *w, const float *x, const float *norm_w,
@@ -369,8 +377,8 @@ qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *accum, 
     return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed for split %d", fn, ws ? ws_bytes : (size_t)0, need, S);
   if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
   if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, accum, ybytes) ||
-                   bytes_overlap(ws, need, x, xbytes)))
-    return fail(QG_EINVAL, "%s: workspace overlaps an output, the residual or x", fn);
+                   bytes_overlap(ws, need, x, xbytes) || overlaps_q2_planes(ws, need, w)))
+    return fail(QG_EINVAL, "%s: workspace overlaps an output, the residual, x or the weights", fn);
   qg::Q2XCall c{};
   c.codes[0] = w->codes;
   c.scales[0] = w->scales;
@@ -417,8 +425,9 @@ static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_
     if (!ws || ws_bytes < need) return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws ? ws_bytes : (size_t)0, need);
     if (!aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
     if (bytes_overlap(ws, need, y0, ybytes) || bytes_overlap(ws, need, x, xbytes) ||
-        bytes_overlap(ws, need, norm_w, xbytes))
-      return fail(QG_EINVAL, "%s: workspace overlaps t, x or norm_w", fn);
+        bytes_overlap(ws, need, norm_w, xbytes) || overlaps_q2_planes(ws, need, w0) ||
+        overlaps_q2_planes(ws, need, w1))
+      return fail(QG_EINVAL, "%s: workspace overlaps t, x, norm_w or the weights", fn);
   }
   qg::Q2XCall c{};
   c.codes[0] = w0->codes;
