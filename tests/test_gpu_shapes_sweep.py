@@ -170,3 +170,77 @@ def test_sweep_q2_batch_jobs(case):
             yref, mass = oracle.q2_gemv_accum(blob, M, K, group, rq, rsc, acc)
             err = np.abs(y.cpu().numpy().astype(np.float64) - yref)
             assert np.all(err <= REL * mass + 2.0 ** -24 * np.abs(yref)), f"batch job with residual {M}x{K}"
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_sweep_q2_in_launch_forms(case):
+    """qgemv_q2_x (random split, residual or not), qgemv_q2_dual_x and
+    qgemv_q2_gate_up_glu_x (with or without the RMSNorm) on random shapes, one
+    shared workspace per form across the sweep's calls: each output against
+    the oracle on the oracle's own quantised vector, the workspaces left zero."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(36000 + case)
+    group = int(r.choice([64, 128]))
+    M = int(r.integers(1, 1400))
+    K = group * int(r.integers(1, 60))
+    split = int(r.integers(0, 17))
+    blob, x = synth.q2_inputs(M, K, group, seed=36500 + case)
+    b1, _ = synth.q2_inputs(M, K, group, seed=36700 + case)
+    W = qg.Q2Weight.from_blocks(blob, M, K, group)
+    W1 = qg.Q2Weight.from_blocks(b1, M, K, group)
+    xd = torch.from_numpy(x).cuda()
+    rq, rsc, _ = oracle.act_quant_i8(x)
+    ws = qg.qgemv_q2_x_workspace(M, K, group, split)
+    acc = synth.rng_for(36900 + case).standard_normal(M).astype(np.float32) if case % 2 else None
+    y = torch.empty(M, device="cuda")
+    qg.qgemv_q2_x(W, xd, y, accum=None if acc is None else torch.from_numpy(acc).cuda(), ws=ws, split_k=split)
+    if acc is None:
+        yref, mass = oracle.q2_gemv(blob, M, K, group, rq, rsc)
+    else:
+        yref, mass = oracle.q2_gemv_accum(blob, M, K, group, rq, rsc, acc)
+        mass = mass + (2.0 ** -24 / REL) * np.abs(yref)
+    _within(y.cpu().numpy(), yref, mass, f"qgemv_q2_x M={M} K={K} g{group} split={split}")
+    if ws is not None:
+        assert int(torch.count_nonzero(ws).item()) == 0
+    norm = (case % 3 == 0) and K <= 16384
+    nw = (1.0 + 0.1 * synth.rng_for(37000 + case).standard_normal(K)).astype(np.float32)
+    if norm:
+        _, rq, rsc, _ = oracle.rmsnorm_quant_i8(x, nw, 1e-6)
+    y0, y1 = torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
+    qg.qgemv_q2_dual_x(W, W1, xd, y0, y1, norm_w=torch.from_numpy(nw).cuda() if norm else None, eps=1e-6)
+    for b, yy, nm in ((blob, y0, "gate"), (b1, y1, "up")):
+        yref, mass = oracle.q2_gemv(b, M, K, group, rq, rsc)
+        _within(yy.cpu().numpy(), yref, mass, f"qgemv_q2_dual_x {nm} M={M} K={K} g{group} norm={norm}")
+    # the gated product of those two outputs, formed in the launch: the same
+    # bits as the product of the dual outputs by the producers' rule
+    wsg = qg.qgemv_q2_gate_up_glu_x_workspace(M)
+    t = torch.empty(M, device="cuda")
+    kind = int(case % 2)
+    qg.qgemv_q2_gate_up_glu_x(W, W1, xd, kind, t, wsg, norm_w=torch.from_numpy(nw).cuda() if norm else None, eps=1e-6)
+    Mp = -(-M // 64) * 64  # the oracle's producer quantises whole groups: pad g, u with zeros
+    gp, up = np.zeros(Mp, np.float32), np.zeros(Mp, np.float32)
+    gp[:M], up[:M] = y0.cpu().numpy(), y1.cpu().numpy()
+    tref = oracle.glu_quant_i8(gp, up, kind)[0][:M]
+    assert np.array_equal(t.cpu().numpy().view(np.uint32), tref.view(np.uint32)), "gated product differs"
+    assert int(torch.count_nonzero(wsg).item()) == 0
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_sweep_q8row_balanced(case):
+    """qgemv_q8row_balanced on random row counts past one full round of 256
+    tiles and random K (tails included): every output against the oracle."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    r = synth.rng_for(38000 + case)
+    M = 64 * 256 + int(r.integers(1, 64 * 300))
+    K = 4 * int(r.integers(1, 400))
+    q, rs, xs = synth.q8row_inputs(M, K, rng=r)
+    W = qg.Q8RowWeight.from_host(q, rs)
+    ws = W.workspace()
+    y = torch.empty(M, device="cuda")
+    W.gemv_balanced(torch.from_numpy(xs).cuda(), y, ws)
+    yref, mass = oracle.q8row_gemv(q, rs, xs)
+    _within(y.cpu().numpy(), yref, mass, f"q8row balanced M={M} K={K}")
+    if ws is not None:
+        assert int(torch.count_nonzero(ws).item()) == 0
