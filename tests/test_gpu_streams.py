@@ -72,3 +72,56 @@ def test_concurrent_streams_match_sequential():
         torch.cuda.synchronize()
         for n, (o, r) in enumerate(zip(outs, ref)):
             assert torch.equal(o, r), f"round {rep}: output {n} differs under concurrent streams"
+
+
+def test_concurrent_streams_one_launch_forms():
+    """The one-launch split forms on three streams at once, each stream with
+    its own workspaces: qgemv_q2_x with split 3 and a residual, the gate|up
+    pair with the SiLU gate and the RMSNorm inside, and the balanced q8_row
+    launch; every output as the one-at-a-time result, bit for bit."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+
+    dev = "cuda"
+    D, F = 1024, 4096
+    Wd = [qg.Q2Weight.from_blocks(synth.q2_inputs(D, F, 128, seed=95 + n)[0], D, F, 128) for n in range(3)]
+    Wg = qg.Q2Weight.from_blocks(synth.q2_inputs(F, D, 128, seed=99)[0], F, D, 128)
+    Wu = qg.Q2Weight.from_blocks(synth.q2_inputs(F, D, 128, seed=100)[0], F, D, 128)
+    r = synth.rng_for(101)
+    xs = [torch.from_numpy(r.standard_normal(F).astype(np.float32)).to(dev) for _ in range(3)]
+    hs = [torch.from_numpy(r.standard_normal(D).astype(np.float32)).to(dev) for _ in range(3)]
+    nw = torch.from_numpy((1.0 + 0.1 * r.standard_normal(D)).astype(np.float32)).to(dev)
+    q8, rs8, xs8 = synth.q8row_inputs(64 * 300 + 9, 1028, seed=102)
+    W8 = qg.Q8RowWeight.from_host(q8, rs8)
+    xs8_d = torch.from_numpy(xs8).to(dev)
+    ys = [torch.empty(D, device=dev) for _ in range(3)]
+    ts = [torch.empty(F, device=dev) for _ in range(3)]
+    y8 = [torch.empty(W8.M, device=dev) for _ in range(3)]
+    wsx = [qg.qgemv_q2_x_workspace(D, F, 128, 3, dev) for _ in range(3)]
+    wsg = [qg.qgemv_q2_gate_up_glu_x_workspace(F, dev) for _ in range(3)]
+    ws8 = [W8.workspace(dev) for _ in range(3)]
+
+    def work(n, s):
+        qg.qgemv_q2_x(Wd[n], xs[n], ys[n], accum=hs[n], ws=wsx[n], split_k=3, stream=s)
+        qg.qgemv_q2_gate_up_glu_x(Wg, Wu, hs[n], qg.QG_GLU_SILU, ts[n], wsg[n], norm_w=nw, eps=1e-6, stream=s)
+        W8.gemv_balanced(xs8_d, y8[n], ws8[n], stream=s)
+
+    outs = ys + ts + y8
+    cur = torch.cuda.current_stream()
+    for n in range(3):
+        work(n, cur)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        for _ in range(4):
+            for n, s in enumerate(streams):
+                work(n, s)
+        torch.cuda.synchronize()
+        for k, (o, rr) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, rr), f"round {rep}: output {k} differs under concurrent streams"
+    for w in wsx + wsg + ws8:
+        assert int(torch.count_nonzero(w).item()) == 0
