@@ -338,8 +338,11 @@ def main():
         su2s = torch.empty(c2["K"] // 64, dtype=torch.int32, device=dev)
         y2s = torch.empty(c2["M"], dtype=torch.float32, device=dev)
         qg.qquant_act_i8(x2s_d, xq2s, sc2s, su2s)
+        ws2s_x = qg.qgemv_q2_x_workspace(c2["M"], c2["K"], c2["group"], 0, dev)
         small = [("q8row_256x512", lambda: W1.gemv(xs1_d, y1), q1.shape[0] * (q1.shape[1] + 4), 50),
                  ("q2_4096x4096_g64", lambda: qg.qgemv_q2(W2s, xq2s, su2s, sc2s, y2s), 4096 * 64 * 18, 50),
+                 ("q2_4096x4096_g64_x", lambda: qg.qgemv_q2_x(W2s, x2s_d, y2s, ws=ws2s_x, split_k=0),
+                  4096 * 64 * 18, 50),
                  ("act_quant_K4096", lambda: qg.qquant_act_i8(x2s_d, xq2s, sc2s, su2s), None, 50)]
         # the column prescale act = silu(g) u col at the down projection's K
         gp, up_, cp = (torch.from_numpy(a).to(dev) for a in synth.gate_inputs(1, 17408, seed=20260 + 960))
