@@ -16,8 +16,9 @@
 //    a unit 1 KiB contiguous, and the scale plane 128 B contiguous;
 //  - the codes' bit order inside a unit (fixed by the repack) makes
 //    (word >> 2a) & 0x03030303 four code bytes that line up with one
-//    natural-order int8 activation word: 7 bit ops + 4 v_dot4_i32_i8 per
-//    16 weights, no shuffles and no lookup tables;
+//    natural-order int8 activation word; fields 1 and 3 are used in place
+//    as 4 x code (q2_unit.h): 5 bit ops + 4 v_dot4_i32_i8 per 16 weights,
+//    no shuffles and no lookup tables;
 //  - the activation words and suma are wave-uniform: scalar loads into
 //    SGPRs, used directly as the dot4 operand;
 //  - K is split over the workgroup's 8 or 16 waves (LDS combine) and, for
@@ -40,12 +41,11 @@
 // launchers guarantee: waves per tile and the automatic split depend only on
 // one matrix's shape.
 #include "gate_rule.h"
+#include "q2_unit.h"
 #include "qg_internal.h"
 
 namespace qg {
 namespace {
-
-constexpr unsigned kCodeMask = 0x03030303u;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 // Wave-uniform reads (activation words, suma) through the constant address
@@ -55,25 +55,7 @@ typedef const __attribute__((address_space(4))) int uniform_i32;
 
 // Corrected dot of one unit: sum_{64 weights} code*xq - suma.
 __device__ inline int unit_dot(const i32x4 c, const uniform_i32x4 *xw, int sa) {
-  const i32x4 x0 = xw[0], x1 = xw[1], x2 = xw[2], x3 = xw[3];
-  int p = 0;
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.x & kCodeMask), x0.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 2) & kCodeMask), x0.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 4) & kCodeMask), x0.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 6) & kCodeMask), x0.w, p, false);
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.y & kCodeMask), x1.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 2) & kCodeMask), x1.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 4) & kCodeMask), x1.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 6) & kCodeMask), x1.w, p, false);
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.z & kCodeMask), x2.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 2) & kCodeMask), x2.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 4) & kCodeMask), x2.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 6) & kCodeMask), x2.w, p, false);
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.w & kCodeMask), x3.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 2) & kCodeMask), x3.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 4) & kCodeMask), x3.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 6) & kCodeMask), x3.w, p, false);
-  return p - sa;
+  return q2_unit_dot(c, xw[0], xw[1], xw[2], xw[3], sa);
 }
 
 // IEEE binary16 -> f32 by the hardware convert (exact, subnormals included).

@@ -40,13 +40,13 @@
 // nothing can hang on a missing arrival.
 #include "arrival.h"
 #include "gate_rule.h"
+#include "q2_unit.h"
 #include "qg_internal.h"
 #include "quant_rule.h"
 
 namespace qg {
 namespace {
 
-constexpr unsigned kCodeMask = 0x03030303u;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediate for lgkmcnt(0) alone (gfx9 encoding: vmcnt and
@@ -65,24 +65,7 @@ __device__ inline void lds_barrier() {
 // activation words given as four 128-bit values.
 __device__ inline int unit_dot_v(const i32x4 c, const i32x4 x0, const i32x4 x1, const i32x4 x2, const i32x4 x3,
                                  int sa) {
-  int p = 0;
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.x & kCodeMask), x0.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 2) & kCodeMask), x0.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 4) & kCodeMask), x0.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.x >> 6) & kCodeMask), x0.w, p, false);
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.y & kCodeMask), x1.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 2) & kCodeMask), x1.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 4) & kCodeMask), x1.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.y >> 6) & kCodeMask), x1.w, p, false);
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.z & kCodeMask), x2.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 2) & kCodeMask), x2.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 4) & kCodeMask), x2.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.z >> 6) & kCodeMask), x2.w, p, false);
-  p = __builtin_amdgcn_sdot4((int)((unsigned)c.w & kCodeMask), x3.x, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 2) & kCodeMask), x3.y, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 4) & kCodeMask), x3.z, p, false);
-  p = __builtin_amdgcn_sdot4((int)(((unsigned)c.w >> 6) & kCodeMask), x3.w, p, false);
-  return p - sa;
+  return q2_unit_dot(c, x0, x1, x2, x3, sa);
 }
 
 __device__ inline float half_bits_to_f32(unsigned short h) {
