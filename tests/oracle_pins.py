@@ -142,6 +142,27 @@ def pin_act_quant_tie(orc):
     assert list(suma) == g["suma"]
 
 
+def _bits(v):
+    return int(np.asarray(v, np.float32).reshape(()).view(np.uint32))
+
+
+def _from_bits(b):
+    return np.array([int(b, 16)], np.uint32).view(np.float32)[0]
+
+
+def pin_act_quant_reciprocal(orc):
+    """Reciprocal then multiply, as the page writes it: a division by the
+    scale would turn the 84 of this vector into 85."""
+    g = _golden("act_quant_reciprocal.json")
+    x = np.zeros(g["K"], np.float32)
+    x[: len(g["x_head_bits"])] = [_from_bits(b) for b in g["x_head_bits"]]
+    xq, sc, suma = orc.act_quant_i8(x)
+    assert list(xq[: len(g["xq_head"])]) == g["xq_head"], xq[:4]
+    assert np.all(xq[len(g["xq_head"]):] == 0)
+    assert _bits(sc) == int(g["act_scale_bits"], 16), hex(_bits(sc))
+    assert list(suma) == g["suma"]
+
+
 def pin_act_quant_invariants(orc):
     rng = np.random.Generator(np.random.PCG64(14))
     for K, scale in [(64, 1.0), (128, 3e-3), (4096, 1.0), (5120, 250.0), (17408, 1.0)]:
@@ -417,6 +438,37 @@ def pin_rmsnorm_two_level(orc):
     assert v[0] == inv and v[1] == np.float32(np.float32(7.0) * inv)
     assert np.array_equal(xq, np.tile(np.array([18, 127], np.int8), K // 2))
     assert list(suma) == [32 * (18 + 127)] * (K // 64)
+
+
+def _rmsnorm_golden(orc, name, x, w):
+    g = _golden(name)
+    v, xq, sc, suma = orc.rmsnorm_quant_i8(x, w, g["eps"])
+    n = len(g["v_bits_head"])
+    assert [_bits(a) for a in v[:n]] == [int(b, 16) for b in g["v_bits_head"]], [hex(_bits(a)) for a in v[:n]]
+    assert _bits(sc) == int(g["act_scale_bits"], 16), hex(_bits(sc))
+    assert list(xq[: len(g["xq_head"])]) == g["xq_head"], xq[:4]
+    assert list(suma) == g["suma"], suma
+    return v, xq
+
+
+def pin_rmsnorm_sum_of_squares_binary64(orc):
+    """x = [4096, 1 x 1023]: the binary64 sum of squares is 16778239 where a
+    binary32 one stays at 2^24, and the scale tells the two apart."""
+    K = 1024
+    x = np.ones(K, np.float32)
+    x[0] = 4096.0
+    v, xq = _rmsnorm_golden(orc, "rmsnorm_sum_of_squares.json", x, np.ones(K, np.float32))
+    assert np.all(v[1:] == v[1]) and np.all(xq[1:] == 0)
+
+
+def pin_rmsnorm_product_order(orc):
+    """x alternating 1, 7 and w alternating 1, 1.5: (x*inv)*w rounds the 7s
+    to 0x40066666, x*(inv*w) to 0x40066667."""
+    K = 128
+    x = np.tile(np.array([1.0, 7.0], np.float32), K // 2)
+    w = np.tile(np.array([1.0, 1.5], np.float32), K // 2)
+    v, xq = _rmsnorm_golden(orc, "rmsnorm_product_order.json", x, w)
+    assert np.array_equal(v, np.tile(v[:2], K // 2)) and np.array_equal(xq, np.tile(xq[:2], K // 2))
 
 
 def pin_rmsnorm_pow2(orc):

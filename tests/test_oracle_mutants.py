@@ -60,6 +60,11 @@ MUTANTS = {
     "silu_pre column dropped": ("                v = v * col[i];", "                v = v;"),
     "silu_pre column by row": ("                v = v * col[i];", "                v = v * col[r];"),
     "silu_pre up from row 0": ("float v = s * u[k];", "float v = s * u[i];"),
+    "quant divides by the scale": ("float v = roundf(x[i] * inv);", "float v = roundf(x[i] / sc);"),
+    "rms sum of squares in binary32": ("double ss = 0.0;\n    for (int64_t i = 0; i < K; i++) ss += (double)x[i] * (double)x[i];",
+                                       "float ss = 0.0f;\n    for (int64_t i = 0; i < K; i++) ss += x[i] * x[i];"),
+    "rms weight folded into inv": ("float xi = x[i] * inv;\n        v[i] = xi * w[i];",
+                                   "float iw = inv * w[i];\n        v[i] = x[i] * iw;"),
     "q2 gemm token row ignored": ("qo_q2_gemv(blob, M, K, group, xq + b * K, sc[b], &o, 1, &yj, &mj);",
                                   "qo_q2_gemv(blob, M, K, group, xq, sc[b], &o, 1, &yj, &mj);"),
     "q2 gemm scale of token 0": ("qo_q2_gemv(blob, M, K, group, xq + b * K, sc[b], &o, 1, &yj, &mj);",

@@ -9,7 +9,9 @@
 // cortiq-engine 0.5.43 gpu_wgpu.rs page, moe_gate_up, for the gated product
 // in the epilogue):
 //   v      = x, or (x * inv) * w with inv = 1/sqrt(ms + eps) (RMSNorm)
-//   sc     = max|v| / 127, xq = clamp(round(v / sc)), suma = per-64 sums
+//   sc     = max|v| / 127, inv = 1 / sc (0 when sc is 0), both rounded to
+//            binary32, xq = clamp(round(v * inv)): one product per value,
+//            never a division by sc; suma = per-64 sums
 //   y[o]   = sc * sum_u d(o,u) * (sum_{i in u} code_i * xq_i - suma_u)
 // with the same per-wave group ranges, the same f32 accumulation order, the
 // same wave combine and the same split order as q2_gemv_t64_kernel and
