@@ -15,7 +15,8 @@
  *    is no fallback path of any kind.
  *  - Sizes are int64_t element counts unless the name says bytes.
  *  - Entry points are re-entrant and keep no global state besides the
- *    thread-local error message.
+ *    thread-local error message and the static device scratch of
+ *    qgemv_q2_noalloc.
  *
  * Sources of the operations (page and function; the pages are third-party
  * source files of LLM inference engines):
@@ -297,6 +298,27 @@ int qgemv_q2_auto_split(int64_t M, int64_t K, int group);
 qg_status qgemv_q2(const qg_q2_weight *w, const int8_t *xq,
                    const int32_t *suma, const float *act_scale, float *y,
                    void *ws, size_t ws_bytes, int split_k, void *stream);
+
+/* Device: qgemv_q2 with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The split-K partials go to a
+ * static device array of QG_STATIC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (looked up on the first call on
+ * a device; nothing is allocated, on that call or any other).
+ *   Arguments as qgemv_q2; the current device must be the stream's.
+ *   y equals qgemv_q2 with the same split_k bit for bit.
+ * Every call on one GPU shares that GPU's scratch, and it keeps the last
+ * call's partials: calls that overlap in time on one GPU (other streams,
+ * other threads) race and give wrong results; calls in order on one stream
+ * are safe.  Nothing in it must start at zero.
+ * QG_EINVAL: as qgemv_q2, or the split's partials (split * round_up(M, 64)
+ * floats, qgemv_q2_ws_bytes) exceed QG_STATIC_SCRATCH_BYTES.
+ * QG_ELAUNCH: the scratch's device address cannot be found, or a launch
+ * fails.                                                                  */
+#define QG_STATIC_SCRATCH_BYTES (1u << 20)
+qg_status qgemv_q2_noalloc(const qg_q2_weight *w, const int8_t *xq,
+                           const int32_t *suma, const float *act_scale,
+                           float *y, int split_k, void *stream);
 
 /* Test entry: qgemv_q2 that also writes the exact int32 unit dots
  *   dots[o][u] = sum_{i in unit u} (code - 1) * xq_i   (device,

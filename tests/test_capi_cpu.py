@@ -173,6 +173,17 @@ def test_einval_paths():
     _einval(L.qgemv_q2(ctypes.byref(w), a16, a16, a16, a16, a16, 100, 4, None))       # too small
     _einval(L.qgemv_q2(ctypes.byref(w), P(0x10004), a16, a16, a16, None, 0, 1, None))  # xq misaligned
     _einval(L.qgemv_q2_dots(ctypes.byref(w), a16, a16, a16, a16, None, None, 0, 1, None))
+    # the entry point without a workspace: the same checks, and splits whose
+    # partials exceed the static scratch (16 * 16448 floats > 1 MiB)
+    for b in bad:
+        _einval(L.qgemv_q2_noalloc(ctypes.byref(b), a16, a16, a16, a16, 1, None))
+    _einval(L.qgemv_q2_noalloc(None, a16, a16, a16, a16, 1, None))
+    _einval(L.qgemv_q2_noalloc(ctypes.byref(w), a16, a16, a16, a16, 17, None))
+    _einval(L.qgemv_q2_noalloc(ctypes.byref(w), a16, a16, a16, a16, -1, None))
+    wbig = qg.qg_q2_weight(0x10000, 0x20000, 16400, 4096, 64, 0)
+    assert L.qgemv_q2_ws_bytes(16400, 4096, 64, 16) == 16 * 16448 * 4 > (1 << 20)
+    _einval(L.qgemv_q2_noalloc(ctypes.byref(wbig), a16, a16, a16, a16, 16, None))
+    assert b"static scratch" in L.qg_last_error()
     # residual epilogue: null accum, accum partly overlapping y
     _einval(L.qgemv_q2_accum(ctypes.byref(w), a16, a16, a16, None, a16, None, 0, 1, None))
     _einval(L.qgemv_q2_accum(ctypes.byref(w), a16, a16, a16, P(0x10010), a16, None, 0, 1, None))

@@ -67,6 +67,7 @@ _SIGS = {
     "qgemv_q2_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
     "qgemv_q2_auto_split": (_I, [_I64, _I64, _I]),
     "qgemv_q2": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _SZ, _I, _P]),
+    "qgemv_q2_noalloc": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _I, _P]),
     "qgemv_q2_dots": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qgemv_q2_accum": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qgemv_q2_dual_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
@@ -355,6 +356,16 @@ def qgemv_q2(w: Q2Weight, xq, suma, act_scale, y, ws=None, split_k=0, stream=Non
         ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
         _dev(act_scale, torch.float32, "act_scale"), _dev(y, torch.float32, "y"),
         wsp, 0 if ws is None else ws.numel(), split_k, _stream(stream)))
+
+
+def qgemv_q2_noalloc(w: Q2Weight, xq, suma, act_scale, y, split_k=0, stream=None):
+    """qgemv_q2 with its split-K partials in the library's static device
+    scratch: no workspace, no allocation.  Calls overlapping on one GPU race."""
+    import torch
+    d = w.desc()
+    _check("qgemv_q2_noalloc", lib().qgemv_q2_noalloc(
+        ctypes.byref(d), _dev(xq, torch.int8, "xq"), _dev(suma, torch.int32, "suma"),
+        _dev(act_scale, torch.float32, "act_scale"), _dev(y, torch.float32, "y"), split_k, _stream(stream)))
 
 
 def qgemv_q2_dots(w: Q2Weight, xq, suma, act_scale, y, dots, ws=None, split_k=0, stream=None):

@@ -262,6 +262,27 @@ qg_status qgemv_q2(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma,
                    split_k, stream);
 }
 
+qg_status qgemv_q2_noalloc(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
+                           float *y, int split_k, void *stream) {
+  const char *fn = "qgemv_q2_noalloc";
+  qg_status st = qg::check_q2_weight(w, fn);
+  if (st != QG_OK) return st;
+  if (split_k < 0 || split_k > qg::kMaxSplit) return fail(QG_EINVAL, "%s: split_k=%d outside 0..16", fn, split_k);
+  const size_t need = qgemv_q2_ws_bytes(w->M, w->K, w->group, split_k);
+  if (need > qg::kStaticScratchBytes)
+    return fail(QG_EINVAL, "%s: split %d of %lld rows needs %zu bytes of partials; the static scratch holds %zu", fn,
+                split_k == 0 ? qg::q2_auto_split(w->M, w->K, w->group) : split_k, (long long)w->M, need,
+                qg::kStaticScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) {
+    hipError_t e = qg::static_scratch(&ws);
+    if (e != hipSuccess) return fail(QG_ELAUNCH, "%s: no device address for the static scratch: %s", fn,
+                                     hipGetErrorString(e));
+  }
+  return q2_common(fn, w, nullptr, xq, suma, act_scale, nullptr, y, nullptr, nullptr, ws,
+                   need > 0 ? qg::kStaticScratchBytes : 0, split_k, stream);
+}
+
 qg_status qgemv_q2_dots(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
                         float *y, int32_t *dots, void *ws, size_t ws_bytes, int split_k, void *stream) {
   if (!dots) return fail(QG_EINVAL, "qgemv_q2_dots: null dots");

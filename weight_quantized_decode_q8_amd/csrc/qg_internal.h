@@ -118,6 +118,13 @@ hipError_t launch_q2_batch(const Q2BatchCall *jobs, int njobs, int group, hipStr
 
 int q2_auto_split(int64_t M, int64_t K, int group);
 
+// The static device scratch of the entry point that allocates nothing
+// (static_scratch.hip): kStaticScratchBytes per device, 256-byte aligned.
+// static_scratch() returns its device address on the current device (looked
+// up once per device; no allocation).
+constexpr size_t kStaticScratchBytes = QG_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void **ptr);
+
 // Gate|up Q2 GEMV (call.codes[0], [1]; no split) with t = glu(g, u) (kind 0
 // silu, 1 sigmoid) in its epilogue, each tile's max|t| in suma_out[tile],
 // then the quantiser's second step over t into xq_out, act_scale_out and
