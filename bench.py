@@ -91,6 +91,169 @@ def read_traffic():
         return None
 
 
+def measure_achievable(qg, torch, dev, stream, log):
+    """What this GPU reaches: a streaming read of a 4 GiB buffer (16-byte
+    non-temporal loads, the best of several grid sizes) and register-only
+    matrix-core loops (int8 16x16x64, fp16 16x16x32), with the shader clock
+    read from s_memtime against the wall clock during the loops."""
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    best = None
+    sweep = {}
+    for loads in (4, 8, 16):
+        for wg in (1024, 2048, 4096, 8192, 16384, 32768):
+            sink = torch.zeros(wg, dtype=torch.int32, device=dev)
+            qg.qg_probe_stream_read(buf, 0x5EED1E55, sink, wg, loads)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            reps = 5
+            a.record(stream)
+            for _ in range(reps):
+                qg.qg_probe_stream_read(buf, 0x5EED1E55, sink, wg, loads)
+            b.record(stream)
+            torch.cuda.synchronize()
+            gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+            sweep[f"{loads}x{wg}"] = round(gbs, 1)
+            if best is None or gbs > best[0]:
+                best = (gbs, wg, loads)
+    del buf
+    out["stream_read"] = {"GB/s": round(best[0], 1), "frac_hbm_spec": round(best[0] / HBM_PEAK_GBS, 4),
+                          "workgroups": best[1], "loads_in_flight": best[2], "bytes": nbytes,
+                          "sweep_GB/s": sweep,
+                          "note": "qg_probe_stream_read: one pass over 4 GiB, 16-byte non-temporal loads, "
+                                  "4-16 in flight per lane, 512-thread workgroups, 1024-32768 of them (best)"}
+    khz = qg.qg_probe_wall_clock_khz()
+    wgs, iters = 2048, 400
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    for kind, name, ops_per, spec in ((0, "mfma_i8", 32768, INT8_DENSE_TOPS), (1, "mfma_f16", 16384, FP16_DENSE_TFLOPS)):
+        qg.qg_probe_mfma(kind, iters, wgs, sink, clocks)  # the clock settles under load
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        qg.qg_probe_mfma(kind, iters, wgs, sink, clocks)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3
+        ops = wgs * 4 * 8 * iters * ops_per
+        cyc, ticks = (int(v) for v in clocks.cpu())
+        mhz = cyc / (ticks / khz * 1e3) if ticks else None
+        rate = ops / us / 1e6
+        out[name] = {"T/s": round(rate, 1), "frac_dense_spec": round(rate / spec, 4), "us": round(us, 1),
+                     "shader_clock_MHz": round(mhz, 0) if mhz else None,
+                     "note": f"qg_probe_mfma kind {kind}: {wgs} workgroups x 4 waves x 8 independent chains x "
+                             f"{iters} rounds, register operands only"}
+    out["wall_clock_kHz"] = khz
+    return out
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_oracle_baseline(oracle, synth, host, q4, rs4, xs4, x_gu, x_dn, step_bytes, log):
+    """The fp64 C oracle on this host: whole decode steps with the rows of
+    each matrix spread over the host threads this process may use (at most
+    16, the host share of one GPU), plus each workload on one thread, and a
+    sample of the batched GEMM's outputs.  A baseline, not a target."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, avail))
+    names = ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120", "q2_g128_down_5120x17408")
+    cfg = {n: synth.CONFIGS[n] for n in names}
+
+    def chunks(M):
+        cuts = np.linspace(0, M, threads + 1).astype(np.int64)
+        return [np.arange(a, b, dtype=np.int64) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+
+    pool = ThreadPoolExecutor(max_workers=threads)
+
+    def oracle_step():  # the ctypes calls release the interpreter lock: one row range per thread
+        rq, rsc, _ = oracle.act_quant_i8(x_gu)
+        rd, rdsc, _ = oracle.act_quant_i8(x_dn)
+        jobs = []
+        for n in names:
+            c = cfg[n]
+            xq, sc = (rd, rdsc) if n.startswith("q2_g128_down") else (rq, rsc)
+            for r in chunks(c["M"]):
+                jobs.append(pool.submit(oracle.q2_gemv, host[n][0], c["M"], c["K"], c["group"], xq, sc, r))
+        for r in chunks(q4.shape[0]):
+            jobs.append(pool.submit(oracle.q8row_gemv, q4, rs4, xs4, r))
+        for j in jobs:
+            j.result()
+
+    c0 = time.perf_counter()
+    passes = 0
+    while passes == 0 or time.perf_counter() - c0 < 10.0:
+        oracle_step()
+        passes += 1
+    cpu_s = (time.perf_counter() - c0) / passes
+    pool.shutdown()
+
+    def timed(fn, budget=1.0):
+        t0 = time.perf_counter()
+        n = 0
+        while n == 0 or time.perf_counter() - t0 < budget:
+            fn()
+            n += 1
+        return (time.perf_counter() - t0) / n
+
+    single = {}
+    q1, rs1, xs1 = synth.config_inputs("q8row_256x512")
+    s1 = timed(lambda: oracle.q8row_gemv(q1, rs1, xs1), 0.5)
+    single["q8row_256x512"] = {"ms": round(s1 * 1e3, 4), "GB/s": round(q1.shape[0] * (q1.shape[1] + 4) / s1 / 1e9, 3)}
+    b2, x2 = synth.config_inputs("q2_g64_4096x4096")
+    s2 = timed(lambda: oracle.q2_gemv(b2, 4096, 4096, 64, *oracle.act_quant_i8(x2)[:2]), 1.0)
+    single["q2_g64_4096x4096"] = {"ms": round(s2 * 1e3, 3), "GB/s": round(4096 * 64 * 18 / s2 / 1e9, 3)}
+    for n in names:
+        c = cfg[n]
+        x = x_dn if n.startswith("q2_g128_down") else x_gu
+        s3 = timed(lambda: oracle.q2_gemv(host[n][0], c["M"], c["K"], c["group"], *oracle.act_quant_i8(x)[:2]), 1.0)
+        single[n] = {"ms": round(s3 * 1e3, 2),
+                     "GB/s": round(c["M"] * (c["K"] // c["group"]) * (2 + c["group"] // 4) / s3 / 1e9, 3)}
+    # the lm_head and the batched GEMM on samples of their rows / outputs
+    rows4 = np.arange(0, q4.shape[0], 64, dtype=np.int64)
+    s4 = timed(lambda: oracle.q8row_gemv(q4, rs4, xs4, rows4), 0.5)
+    single["q8row_lm_head_248320x5120"] = {
+        "ms_extrapolated": round(s4 * q4.shape[0] / rows4.size * 1e3, 1),
+        "GB/s": round(rows4.size * (q4.shape[1] + 4) / s4 / 1e9, 3), "sample": f"{rows4.size} rows (every 64th)"}
+    c5 = synth.CONFIGS["q8row_gemm_512x17408x5120"]
+    rng = np.random.Generator(np.random.PCG64(20260 + 970))
+    q5 = rng.integers(-127, 128, size=(256, c5["K"]), dtype=np.int8)
+    rs5 = rng.uniform(0.001, 0.01, 256).astype(np.float32)
+    xs5 = rng.standard_normal((64, c5["K"]), dtype=np.float32)
+    bs = np.repeat(np.arange(64, dtype=np.int64), 256)
+    os_ = np.tile(np.arange(256, dtype=np.int64), 64)
+    s5 = timed(lambda: oracle.q8row_gemm(q5, rs5, xs5, entries=(bs, os_)), 0.5)
+    gflops = 2 * bs.size * c5["K"] / s5 / 1e9
+    single["q8row_gemm_512x17408x5120"] = {
+        "GFLOP/s": round(gflops, 3),
+        "s_extrapolated": round(2 * c5["nb"] * c5["M"] * c5["K"] / (gflops * 1e9), 1),
+        "sample": "64 x 256 outputs of the same K (random rows of the workload's distributions)"}
+    cpu = {"value": round(step_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "seconds_per_step": round(cpu_s, 4), "passes": passes,
+           "sample": f"{passes} whole decode steps (all six kernels' work) by the fp64 C oracle, the rows of "
+                     f"each matrix split over {threads} host threads, mean per step",
+           "host_cpus_visible": avail, "os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model(),
+           "single_thread": single}
+    log(f"cpu oracle: {cpu}")
+    return cpu
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -407,8 +570,16 @@ def main():
 
         Wg_, Wu_ = W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"]
         ws_glu = qg.qgemv_q2_gate_up_glu_x_workspace(Mgu, dev)
+        tmax_d = torch.empty((Mgu + 63) // 64, dtype=torch.float32, device=dev)
 
-        def ffn_x():  # two launches: the producers and the split reduce inside the GEMV launches
+        def ffn_x():  # two launches: the producers and the split reduce inside the GEMV launches;
+            # the gate|up launch hands max|t| per row tile to the down launch, whose
+            # workgroups then read only their own split of t
+            qg.qgemv_q2_gate_up_glu_x(Wg_, Wu_, h_d, qg.QG_GLU_SILU, g_buf, ws_glu, norm_w=nw_d, eps=1e-6,
+                                      tmax=tmax_d)
+            qg.qgemv_q2_x(Wdn, g_buf, h_out, accum=h_d, ws=ws_dnx, split_k=S_dn, xmax=tmax_d)
+
+        def ffn_x_whole_max():  # the same, each down workgroup finding max|t| over all of t
             qg.qgemv_q2_gate_up_glu_x(Wg_, Wu_, h_d, qg.QG_GLU_SILU, g_buf, ws_glu, norm_w=nw_d, eps=1e-6)
             qg.qgemv_q2_x(Wdn, g_buf, h_out, accum=h_d, ws=ws_dnx, split_k=S_dn)
 
@@ -454,6 +625,7 @@ def main():
         torch.cuda.synchronize()
         ref_h = h_out.clone()
         us_x = timed_step(ffn_x)
+        us_xw = timed_step(ffn_x_whole_max)
         us_fs = timed_step(ffn_fused)
         us_dg = timed_step(ffn_dual_then_glu)
         fused = {"workload": "decode step with the FFN block fused: RMSNorm+quant -> gate|up Q2 GEMV with the "
@@ -462,7 +634,9 @@ def main():
                  "frac_hbm_peak": round(step_bytes / us_x / 1e3 / HBM_PEAK_GBS, 4),
                  "launches": 3,
                  "form": "qgemv_q2_gate_up_glu_x (RMSNorm + quantiser in the launch, g and u meeting in a "
-                         "workspace) -> qgemv_q2_x (quantiser, split-K reduce and residual in the launch) -> lm_head",
+                         "workspace, max|t| per row tile out) -> qgemv_q2_x (the quantiser on its split of t with "
+                         "the tiles' max, split-K reduce and residual in the launch) -> lm_head",
+                 "whole_vector_max_us_per_step": round(us_xw, 2),
                  "producers_as_launches_us_per_step": round(us_fs, 2), "producers_as_launches_launches": 6,
                  "gated_product_as_own_launches_us_per_step": round(us_dg, 2),
                  "main_step_us_per_step": round(ms_per_step * 1e3, 2), "main_step_launches": 3,
@@ -686,33 +860,17 @@ def main():
         del Xq, xq_r, y_r, H, Hout, G, U, xq_f
         torch.cuda.empty_cache()
 
+    # ---------------- achievable peaks of this GPU (measurement probes)
+    achievable = None
+    if not args.no_breakdown:
+        achievable = measure_achievable(qg, torch, dev, stream, log)
+        log(f"achievable: {achievable}")
+
     # ---------------- CPU oracle over the same step, on this host
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-
-        def oracle_step():
-            rq, rsc, _ = oracle.act_quant_i8(x_gu)
-            for name in ("q2_g128_gate_17408x5120", "q2_g128_up_17408x5120"):
-                c = synth.CONFIGS[name]
-                oracle.q2_gemv(host[name][0], c["M"], c["K"], c["group"], rq, rsc)
-            rq, rsc, _ = oracle.act_quant_i8(x_dn)
-            c = synth.CONFIGS["q2_g128_down_5120x17408"]
-            oracle.q2_gemv(host["q2_g128_down_5120x17408"][0], c["M"], c["K"], c["group"], rq, rsc)
-            oracle.q8row_gemv(q4, rs4, xs4)
-
-        # whole steps until about 10 s of CPU work (at least one)
-        c0 = time.perf_counter()
-        passes = 0
-        while passes == 0 or time.perf_counter() - c0 < 10.0:
-            oracle_step()
-            passes += 1
-        cpu_s = (time.perf_counter() - c0) / passes
-        cpu = {"value": round(step_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "seconds_per_step": round(cpu_s, 3), "passes": passes,
-               "sample": f"{passes} whole decode steps (all six kernels' work) by the fp64 C oracle, "
-                         "single thread, mean per step"}
-        log(f"cpu oracle: {cpu}")
+        cpu = cpu_oracle_baseline(oracle, synth, host, q4, rs4, xs4, x_gu, x_dn, step_bytes, log)
 
     out = {
         "metric": "batch-1 quantized GEMV weight GB/s (% of HBM peak); prefill GEMM TFLOP/s",
@@ -744,6 +902,13 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "achievable": achievable,
+        "context_pages": {
+            "what": "the pages' own throughput figure for their Q2 GEMV (2-bit weights x int8 activations, "
+                    "ESIMD/XMX DPAS, split-K) on an Intel Xe2 B70-class GPU: 240-468 GB/s of weight bytes "
+                    "(qxmx qxmx_gpu.cpp page, the comment above gemv_dpas8); another machine, shapes not stated",
+            "GB/s_low": 240.0, "GB/s_high": 468.0,
+            "this_step_GB/s": round(value, 1)},
         "prefill_gemm": gemm,
         "prefill_q2_gemm": q2gemm,
         "fused_ffn": fused,

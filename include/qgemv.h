@@ -449,6 +449,15 @@ size_t qgemv_q2_x_ws_bytes(int64_t M, int64_t K, int group, int split_k);
 /* Device: y = qgemv_q2(w, quantised x) (+ accum), one launch
  *   x:         device, f32[K], 16-byte aligned, finite; must not overlap y,
  *              accum or ws.
+ *   xmax, nxmax: NULL and 0, or device f32[nxmax] (1 <= nxmax <=
+ *              QG_Q2X_MAX_PARTS, 4-byte aligned) whose largest entry is
+ *              max_i |x_i|, for instance the tmax that
+ *              qgemv_q2_gate_up_glu_x wrote along with x = t.  Then each
+ *              workgroup reads only its own split's part of x instead of
+ *              the whole vector to find the scale.  act_scale is always
+ *              max/127 of the max used, so given a wrong max the result
+ *              is that of the quantiser with that scale (codes clamped to
+ *              [-128, 127]), never an out-of-bounds access.
  *   accum:     device, f32[M] residual added as in qgemv_q2_accum, or NULL;
  *              may be y itself.
  *   y:         device, f32[M], written.
@@ -463,7 +472,9 @@ size_t qgemv_q2_x_ws_bytes(int64_t M, int64_t K, int group, int split_k);
  * the same split (given explicitly to both), bit for bit.
  * QG_EINVAL: as qgemv_q2_accum, or null or misaligned x, K above the
  * limit above, x overlapping y, or a workspace overlapping x.             */
+#define QG_Q2X_MAX_PARTS 512
 qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x,
+                     const float *xmax, int64_t nxmax,
                      const float *accum, float *y, void *ws, size_t ws_bytes,
                      int split_k, void *stream);
 
@@ -492,6 +503,10 @@ size_t qgemv_q2_gate_up_glu_x_ws_bytes(int64_t M);
  *   with g, u the qgemv_q2_dual_x outputs, which meet in ws: the second of
  *   the two workgroups of a row tile (gate, up) to finish forms t.
  *   t:         device, f32[M], written; must not overlap x or norm_w.
+ *   tmax:      device, f32[ceil(M/64)] (4-byte aligned), or NULL: receives
+ *              max |t| over each 64-row tile, so that max_o |t_o| is the
+ *              largest entry (pass it to qgemv_q2_x as xmax); must not
+ *              overlap t, x, norm_w or ws.
  *   ws:        device, >= qgemv_q2_gate_up_glu_x_ws_bytes(M) bytes, 16-byte
  *              aligned, all zero before the first call (allocate it
  *              zero-filled); every call leaves it all zero again.  Calls
@@ -504,8 +519,8 @@ size_t qgemv_q2_gate_up_glu_x_ws_bytes(int64_t M);
 qg_status qgemv_q2_gate_up_glu_x(const qg_q2_weight *w_gate,
                                  const qg_q2_weight *w_up, const float *x,
                                  const float *norm_w, float eps, int kind,
-                                 float *t, void *ws, size_t ws_bytes,
-                                 void *stream);
+                                 float *t, float *tmax, void *ws,
+                                 size_t ws_bytes, void *stream);
 
 /* Device: the batched (prefill) Q2 product over nb token rows, on int8
  * MFMA   [QG, ffn_forward_b with gemm_gpu_v4]

@@ -1,0 +1,55 @@
+/*
+ * qgemv_probes.h -- measurement probes of libqgemv.so.  They are not part
+ * of the product path: the benchmark calls them to measure what this GPU
+ * actually reaches (HBM read rate, matrix-core rate, shader clock), to
+ * quote next to the published peaks the library's kernels are rated
+ * against.  Same conventions as qgemv.h (device pointers, a hipStream_t
+ * as void *, QG_EINVAL before any launch, QG_ELAUNCH on a failed launch).
+ */
+#ifndef QGEMV_PROBES_H
+#define QGEMV_PROBES_H
+
+#include <stddef.h>
+
+#include "qgemv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Device: reads the first bytes/16*16 bytes of buf once, with 16-byte
+ * non-temporal loads, `loads` (4, 8 or 16) in flight per lane, over
+ * `workgroups` workgroups of 512 threads (grid-stride).  Writes nothing unless a workgroup's folded
+ * value equals `sentinel` (then sink[workgroup] = that value): pick a
+ * sentinel the data cannot fold to, and time the launch.
+ *   buf:  device, 16-byte aligned, >= 16 bytes.
+ *   sink: device, unsigned[workgroups].
+ * QG_EINVAL: null or misaligned pointer, bytes < 16, workgroups outside
+ * 1..2^20, loads not 4, 8 or 16.                                          */
+qg_status qg_probe_stream_read(const void *buf, size_t bytes,
+                               unsigned sentinel, unsigned *sink,
+                               int workgroups, int loads, void *stream);
+
+/* Device: `workgroups` workgroups of 4 waves, each wave running `iters`
+ * rounds of 8 independent matrix-core products on register operands:
+ * kind 0 = v_mfma_i32_16x16x64_i8 (32768 int8 ops each), kind 1 =
+ * v_mfma_f32_16x16x32_f16 (16384 fp16 flops each).
+ *   sink:   device, f32[workgroups * 256], written (keeps the work live).
+ *   clocks: device, uint64[2]: the shader-clock cycles (s_memtime) and the
+ *           constant-rate wall-clock ticks (s_memrealtime, rate from
+ *           qg_probe_wall_clock_khz) that wave 0 of workgroup 0 spent in
+ *           its loop.
+ * QG_EINVAL: bad kind, iters < 1, workgroups outside 1..65536, null or
+ * misaligned pointer.                                                     */
+qg_status qg_probe_mfma(int kind, int iters, int workgroups, float *sink,
+                        unsigned long long *clocks, void *stream);
+
+/* Host: the current device's wall-clock counter rate in kHz (the unit of
+ * qg_probe_mfma's clocks[1]).  QG_ELAUNCH if the runtime cannot say.     */
+qg_status qg_probe_wall_clock_khz(int *khz);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_PROBES_H */

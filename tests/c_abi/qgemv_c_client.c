@@ -128,7 +128,7 @@ int main(int argc, char **argv) {
     HIP_OK(hipMalloc(&d_wsx, wsx_bytes));
     HIP_OK(hipMemset(d_wsx, 0, wsx_bytes));
   }
-  QG_OK_(qgemv_q2_x(&w, d_x2, NULL, d_y2x, d_wsx, wsx_bytes, split, (void *)stream));
+  QG_OK_(qgemv_q2_x(&w, d_x2, NULL, 0, NULL, d_y2x, d_wsx, wsx_bytes, split, (void *)stream));
   HIP_OK(hipStreamSynchronize(stream));
 
   float *y8 = malloc((size_t)M8 * 4), *y2 = malloc((size_t)M2 * 4), sc;

@@ -40,7 +40,7 @@ def test_library_exports(name):
 
 def test_abi_and_status_strings():
     L = qg.lib()
-    assert L.qg_abi_version() == 6
+    assert L.qg_abi_version() == 7
     assert L.qg_status_string(0) == b"QG_OK"
     assert L.qg_status_string(1) == b"QG_EINVAL"
     assert L.qg_status_string(2) == b"QG_ELAUNCH"
@@ -345,25 +345,32 @@ def test_einval_paths_in_launch_quantiser():
     assert L.qgemv_q2_x_auto_split(1, 65536, 64) == 16
     assert L.qgemv_q2_x_ws_bytes(5120, 17408, 128, 0) == 128 * 4 + 3 * 5120 * 4
     # qgemv_q2_x
-    _einval(L.qgemv_q2_x(None, X, None, Y, None, 0, 1, None))
-    _einval(L.qgemv_q2_x(ctypes.byref(w), None, None, Y, None, 0, 1, None))            # null x
-    _einval(L.qgemv_q2_x(ctypes.byref(w), P(0x500008), None, Y, None, 0, 1, None))     # x misaligned
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, None, None, 0, 1, None))            # null y
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, P(0x500100), None, 0, 1, None))     # y inside x
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, P(0x600004), Y, None, 0, 1, None))        # accum over y
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, None, 0, 17, None))
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, None, 0, 2, None))               # no workspace
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, WS, 100, 2, None))               # too small
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x800008), 4096, 2, None))     # ws misaligned
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x500000), 4096, 2, None))     # ws over x
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x600000), 4096, 2, None))     # ws over y
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x100100), 4096, 2, None))     # ws over the codes
-    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, Y, P(0x200040), 4096, 2, None))     # ws over the scales
+    _einval(L.qgemv_q2_x(None, X, None, 0, None, Y, None, 0, 1, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), None, None, 0, None, Y, None, 0, 1, None))            # null x
+    _einval(L.qgemv_q2_x(ctypes.byref(w), P(0x500008), None, 0, None, Y, None, 0, 1, None))     # x misaligned
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, None, None, 0, 1, None))            # null y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, P(0x500100), None, 0, 1, None))     # y inside x
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, P(0x600004), Y, None, 0, 1, None))        # accum over y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, None, 0, 17, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, None, 0, 2, None))               # no workspace
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, WS, 100, 2, None))               # too small
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, P(0x800008), 4096, 2, None))     # ws misaligned
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, P(0x500000), 4096, 2, None))     # ws over x
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, P(0x600000), 4096, 2, None))     # ws over y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, P(0x100100), 4096, 2, None))     # ws over the codes
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 0, None, Y, P(0x200040), 4096, 2, None))     # ws over the scales
+    # partial maxima of |x|: both or neither, 1..512 of them, aligned, apart from y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, P(0xa00000), 0, None, Y, None, 0, 1, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, None, 4, None, Y, None, 0, 1, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, P(0xa00000), 513, None, Y, None, 0, 1, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, P(0xa00002), 4, None, Y, None, 0, 1, None))
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, P(0x600010), 4, None, Y, None, 0, 1, None))       # xmax over y
+    _einval(L.qgemv_q2_x(ctypes.byref(w), X, P(0x800010), 4, None, Y, P(0x800000), 4096, 2, None))  # over ws
     big = qg.qg_q2_weight(0x100000, 0x200000, 128, 32768 + 64, 64, 0)
-    _einval(L.qgemv_q2_x(ctypes.byref(big), X, None, Y, None, 0, 1, None))             # K above 32768
+    _einval(L.qgemv_q2_x(ctypes.byref(big), X, None, 0, None, Y, None, 0, 1, None))             # K above 32768
     wide = qg.qg_q2_weight(0x100000, 0x200000, 16384, 16384 + 128, 128, 0)
-    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, Y, None, 0, 1, None))            # K above 16384 at 8 waves
-    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, Y, WS, 1 << 20, 4, None))       # whatever the split
+    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, 0, None, Y, None, 0, 1, None))            # K above 16384 at 8 waves
+    _einval(L.qgemv_q2_x(ctypes.byref(wide), X, None, 0, None, Y, WS, 1 << 20, 4, None))       # whatever the split
     assert L.qgemv_q2_gate_up_glu_x_ws_bytes(130) == 256 + 2 * 192 * 4
     # qgemv_q2_dual_x
     _einval(L.qgemv_q2_dual_x(ctypes.byref(w), None, X, None, F(0), Y, Y1, None))
@@ -380,12 +387,17 @@ def test_einval_paths_in_launch_quantiser():
     wn1 = qg.qg_q2_weight(0x300000, 0x400000, 128, 16384 + 64, 64, 0)
     _einval(L.qgemv_q2_dual_x(ctypes.byref(wn), ctypes.byref(wn1), X, P(0x900000), F(0), Y, Y1, None))
     # qgemv_q2_gate_up_glu_x
-    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 2, Y, WS, 4096, None))
-    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, None, WS, 4096, None))
-    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, P(0x500010), WS, 4096, None))
-    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, None, 0, None))
-    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, WS, 100, None))
-    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, P(0x600000), 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 2, Y, None, WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, None, None, WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, P(0x500010), None, WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, None, None, 0, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, None, WS, 100, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, None, P(0x600000), 4096, None))
+    # tmax: aligned, apart from t, x and the workspace
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, P(0xa00002), WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, P(0x600008), WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, P(0x500008), WS, 4096, None))
+    _einval(L.qgemv_q2_gate_up_glu_x(ctypes.byref(w), ctypes.byref(w1), X, None, F(0), 0, Y, WS, WS, 4096, None))
 
 
 def test_q8row_balanced_sizes_and_einval():

@@ -275,3 +275,116 @@ def test_decode_ffn_workloads_as_benched():
         rows = np.unique(np.concatenate([np.arange(0, W.M, 97), [W.M - 1]]))
         yref, mass = oracle.q2_gemv(blobs[name], W.M, W.K, W.group, rq, rsc, rows=rows)
         within(y[rows], yref, mass, what=name)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_gate_up_glu_x_t_within_oracle_bound(kind):
+    """t of the fused gate|up launch (RMSNorm + quantiser inside, the gated
+    product in the epilogue) held directly to the fp64 oracle at the decode
+    shape (g128, 17408 x 5120), every row.  The oracle gives g, u (fp64, on
+    its own quantised activation) and their yardsticks m_g, m_u; with
+    |g - g_ref| <= 2e-5 m_g and |u - u_ref| <= 2e-5 m_u, the mean value
+    theorem bounds t = u * f(g) (f = silu, |f'| < 1.1; or f = sigmoid,
+    |f'| <= 1/4) by
+        |dt| <= c (|u_ref| + du) dg + (|f(g_ref)| + c dg) du + 6 ulp(t_ref),
+    the last term the binary32 evaluation of exp, 1 + e, the quotient and
+    the product (four roundings)."""
+    m = qg()
+    M, K, group = 17408, 5120, 128
+    bg, x = synth.q2_inputs(M, K, group, seed=7700)
+    bu, _ = synth.q2_inputs(M, K, group, seed=7701)
+    Wg, Wu = m.Q2Weight.from_blocks(bg, M, K, group), m.Q2Weight.from_blocks(bu, M, K, group)
+    rng = np.random.Generator(np.random.PCG64(7702))
+    nw = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    eps = 1e-6
+    t = _empty(M)
+    m.qgemv_q2_gate_up_glu_x(Wg, Wu, dev(x), kind, t, m.qgemv_q2_gate_up_glu_x_workspace(M),
+                             norm_w=dev(nw), eps=eps)
+    t = host(t).astype(np.float64)
+    _, xq, sc, _ = oracle.rmsnorm_quant_i8(x, nw, eps)
+    g, mg = oracle.q2_gemv(bg, M, K, group, xq, sc)
+    u, mu = oracle.q2_gemv(bu, M, K, group, xq, sc)
+    sig = 1.0 / (1.0 + np.exp(-g))
+    f, c = (g * sig, 1.1) if kind == 0 else (sig, 0.25)
+    t_ref = u * f
+    dg, du = 2e-5 * mg, 2e-5 * mu
+    bound = c * (np.abs(u) + du) * dg + (np.abs(f) + c * dg) * du + 6.0 * 2.0 ** -24 * np.abs(t_ref)
+    err = np.abs(t - t_ref)
+    assert np.all(np.isfinite(t))
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} of {M} t outside the bound; worst ratio "
+                           f"{np.max(err / bound):.3f}")
+
+
+@pytest.mark.parametrize("M,K,group,kind", [(130, 640, 128, 0), (300, 2048, 128, 1), (16448, 512, 64, 0),
+                                            (17408, 5120, 128, 0)])
+def test_gate_up_glu_x_tmax_is_each_tiles_max(M, K, group, kind):
+    """tmax[tile] = max |t| over the tile's rows, bit for bit, and t itself is
+    the same as without tmax."""
+    torch = _torch()
+    m = qg()
+    Wg, Wu, x = _pair(M, K, group, 7800 + M)
+    tiles = -(-M // 64)
+    ws = m.qgemv_q2_gate_up_glu_x_workspace(M)
+    t0 = _empty(M)
+    m.qgemv_q2_gate_up_glu_x(Wg, Wu, dev(x), kind, t0, ws)
+    t1 = _empty(M)
+    tmax = torch.full((tiles,), float("nan"), dtype=torch.float32, device="cuda")
+    m.qgemv_q2_gate_up_glu_x(Wg, Wu, dev(x), kind, t1, ws, tmax=tmax)
+    t0, t1, tmax = host(t0), host(t1), host(tmax)
+    assert np.array_equal(bits(t0), bits(t1))
+    pad = np.zeros(tiles * 64, np.float32)
+    pad[:M] = np.abs(t1)
+    assert np.array_equal(bits(tmax), bits(pad.reshape(tiles, 64).max(axis=1)))
+    assert int(torch.count_nonzero(ws).item()) == 0
+
+
+@pytest.mark.parametrize("M,K,group,split", [(1, 64, 64, 1), (65, 192, 64, 3), (300, 2048, 128, 0),
+                                             (129, 4096, 64, 16), (4096, 4096, 64, 0), (5120, 17408, 128, 0),
+                                             (5120, 17408, 128, 1), (64, 32768, 64, 5)])
+@pytest.mark.parametrize("nparts", [1, 7, 512])
+def test_q2_x_with_partial_maxima_equals_whole_vector(M, K, group, split, nparts):
+    """Given partial maxima of |x| (here over nparts ragged chunks), each
+    workgroup reads only its split of x: y is bit-identical to the launch
+    that finds the max over the whole vector, residual included."""
+    torch = _torch()
+    m = qg()
+    blob, x = synth.q2_inputs(M, K, group, seed=7900 + M + K + split)
+    W = m.Q2Weight.from_blocks(blob, M, K, group)
+    rng = np.random.Generator(np.random.PCG64(7901 + M))
+    resid = rng.standard_normal(M).astype(np.float32)
+    cuts = np.linspace(0, K, min(nparts, K) + 1).astype(int)
+    parts = np.array([np.max(np.abs(x[a:b])) for a, b in zip(cuts[:-1], cuts[1:])], np.float32)
+    ws = m.qgemv_q2_x_workspace(M, K, group, split)
+    y0, y1 = _empty(M), _empty(M)
+    m.qgemv_q2_x(W, dev(x), y0, accum=dev(resid), ws=ws, split_k=split)
+    m.qgemv_q2_x(W, dev(x), y1, accum=dev(resid), ws=ws, split_k=split, xmax=dev(parts))
+    assert np.array_equal(bits(host(y0)), bits(host(y1)))
+    assert ws is None or int(torch.count_nonzero(ws).item()) == 0
+
+
+def test_ffn_block_with_tile_maxima_equals_two_launches():
+    """The decode FFN block with the gate|up launch's tile maxima handed to
+    the down projection (which then reads only its split of t): y bit-
+    identical to the block without them, at the pages' model shapes."""
+    torch = _torch()
+    m = qg()
+    D, F, group = 5120, 17408, 128
+    Wg, Wu, _ = _pair(F, D, group, 7600)
+    bd, _ = synth.q2_inputs(D, F, group, seed=7602)
+    Wd = m.Q2Weight.from_blocks(bd, D, F, group)
+    rng = np.random.Generator(np.random.PCG64(7603))
+    h = rng.standard_normal(D).astype(np.float32)
+    nw = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    eps = 1e-6
+    ws_g = m.qgemv_q2_gate_up_glu_x_workspace(F)
+    ws_d = m.qgemv_q2_x_workspace(D, F, group, 0)
+    ys = []
+    for use_parts in (False, True):
+        t = _empty(F)
+        tmax = torch.empty(F // 64, dtype=torch.float32, device="cuda") if use_parts else None
+        m.qgemv_q2_gate_up_glu_x(Wg, Wu, dev(h), 0, t, ws_g, norm_w=dev(nw), eps=eps, tmax=tmax)
+        y = dev(h)
+        m.qgemv_q2_x(Wd, t, y, accum=y, ws=ws_d, split_k=0, xmax=tmax)
+        ys.append(host(y))
+    assert np.array_equal(bits(ys[0]), bits(ys[1]))

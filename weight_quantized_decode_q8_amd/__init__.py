@@ -80,12 +80,12 @@ _SIGS = {
     "qgemv_q8row_balanced": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemv_q2_x_ws_bytes": (_SZ, [_I64, _I64, _I, _I]),
     "qgemv_q2_x_auto_split": (_I, [_I64, _I64, _I]),
-    "qgemv_q2_x": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _SZ, _I, _P]),
+    "qgemv_q2_x": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _I64, _P, _P, _P, _SZ, _I, _P]),
     "qgemv_q2_dual_x": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, ctypes.c_float,
                              _P, _P, _P]),
     "qgemv_q2_gate_up_glu_x_ws_bytes": (_SZ, [_I64]),
     "qgemv_q2_gate_up_glu_x": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P,
-                                    ctypes.c_float, _I, _P, _P, _SZ, _P]),
+                                    ctypes.c_float, _I, _P, _P, _P, _SZ, _P]),
     "qgemm_q2_batched": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "qgemm_q2_batched_ws_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "qgemm_q2_batched_dual": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P, _P, _P, _P,
@@ -95,6 +95,10 @@ _SIGS = {
     "qgemm_q8row_batched": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "qgemm_q8row_batched_silu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "qact_silu_mul_pre": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
+    # measurement probes (include/qgemv_probes.h), not the product path
+    "qg_probe_stream_read": (_I, [_P, _SZ, ctypes.c_uint, _P, _I, _I, _P]),
+    "qg_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P]),
+    "qg_probe_wall_clock_khz": (_I, [ctypes.POINTER(ctypes.c_int)]),
 }
 
 _lib = None
@@ -447,13 +451,16 @@ def qgemv_q2_x_workspace(M, K, group, split_k=0, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
-def qgemv_q2_x(w: Q2Weight, x, y, accum=None, ws=None, split_k=0, stream=None):
+def qgemv_q2_x(w: Q2Weight, x, y, accum=None, ws=None, split_k=0, stream=None, xmax=None):
     """y = Q2 GEMV of the f32 vector x, quantised inside the launch (+ accum); one launch.
-    ws: from qgemv_q2_x_workspace (all zero) when the split is above 1."""
+    ws: from qgemv_q2_x_workspace (all zero) when the split is above 1.
+    xmax: None, or a float32 device tensor of partial maxima of |x| (the tmax
+    of qgemv_q2_gate_up_glu_x), so each workgroup reads only its split of x."""
     import torch
     d = w.desc()
     _check("qgemv_q2_x", lib().qgemv_q2_x(
-        ctypes.byref(d), _dev(x, torch.float32, "x"), _dev(accum, torch.float32, "accum"),
+        ctypes.byref(d), _dev(x, torch.float32, "x"), _dev(xmax, torch.float32, "xmax"),
+        0 if xmax is None else xmax.numel(), _dev(accum, torch.float32, "accum"),
         _dev(y, torch.float32, "y"), _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), split_k,
         _stream(stream)))
 
@@ -473,14 +480,17 @@ def qgemv_q2_gate_up_glu_x_workspace(M, device="cuda"):
     return torch.zeros(lib().qgemv_q2_gate_up_glu_x_ws_bytes(M), dtype=torch.uint8, device=device)
 
 
-def qgemv_q2_gate_up_glu_x(w_gate: Q2Weight, w_up: Q2Weight, x, kind, t, ws, norm_w=None, eps=0.0, stream=None):
+def qgemv_q2_gate_up_glu_x(w_gate: Q2Weight, w_up: Q2Weight, x, kind, t, ws, norm_w=None, eps=0.0, stream=None,
+                           tmax=None):
     """t = silu(g)*u (kind 0) or u*sigmoid(g) (kind 1) of the gate|up pair, x quantised in the launch.
-    ws: from qgemv_q2_gate_up_glu_x_workspace."""
+    ws: from qgemv_q2_gate_up_glu_x_workspace.  tmax: None, or a float32 device
+    tensor of ceil(M/64) entries that receives max|t| of each row tile."""
     import torch
     dg, du = w_gate.desc(), w_up.desc()
     _check("qgemv_q2_gate_up_glu_x", lib().qgemv_q2_gate_up_glu_x(
         ctypes.byref(dg), ctypes.byref(du), _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w"),
-        float(eps), int(kind), _dev(t, torch.float32, "t"), _dev(ws, torch.uint8, "ws"),
+        float(eps), int(kind), _dev(t, torch.float32, "t"), _dev(tmax, torch.float32, "tmax"),
+        _dev(ws, torch.uint8, "ws"),
         0 if ws is None else ws.numel(), _stream(stream)))
 
 
@@ -540,3 +550,27 @@ def qgemm_q8row_batched_silu(qpacked, rs, g, u, col, y, nb: int, M: int, K: int,
         _dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), _dev(col, torch.float32, "col"),
         _dev(y, torch.float32, "y"), nb, M, K, xs_limbs,
         _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+# ---- measurement probes (include/qgemv_probes.h): not the product path ----
+def qg_probe_stream_read(buf, sentinel, sink, workgroups, loads=8, stream=None):
+    """Read the uint8 device tensor buf once (16-byte non-temporal loads, `loads` in flight per lane);
+    sink: int32[workgroups]."""
+    import torch
+    _check("qg_probe_stream_read", lib().qg_probe_stream_read(
+        _dev(buf, torch.uint8, "buf"), buf.numel(), sentinel & 0xFFFFFFFF, _dev(sink, torch.int32, "sink"),
+        int(workgroups), int(loads), _stream(stream)))
+
+
+def qg_probe_mfma(kind, iters, workgroups, sink, clocks, stream=None):
+    """Matrix-core loop: kind 0 int8 16x16x64, 1 fp16 16x16x32; sink f32[workgroups*256], clocks int64[2]."""
+    import torch
+    _check("qg_probe_mfma", lib().qg_probe_mfma(
+        int(kind), int(iters), int(workgroups), _dev(sink, torch.float32, "sink"),
+        _dev(clocks, torch.int64, "clocks"), _stream(stream)))
+
+
+def qg_probe_wall_clock_khz():
+    khz = ctypes.c_int(0)
+    _check("qg_probe_wall_clock_khz", lib().qg_probe_wall_clock_khz(ctypes.byref(khz)))
+    return khz.value

@@ -57,7 +57,7 @@ const char *qg_status_string(qg_status s) {
 
 const char *qg_last_error(void) { return qg::g_msg; }
 
-int qg_abi_version(void) { return 6; }
+int qg_abi_version(void) { return 7; }
 
 static bool overlap(const float *a, const float *b, int64_t n) { return a < b + n && b < a + n; }
 
@@ -379,8 +379,8 @@ static qg_status check_x_input(const char *fn, const qg_q2_weight *w, const floa
   return QG_OK;
 }
 
-qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *accum, float *y, void *ws, size_t ws_bytes,
-                     int split_k, void *stream) {
+qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *xmax, int64_t nxmax, const float *accum,
+                     float *y, void *ws, size_t ws_bytes, int split_k, void *stream) {
   const char *fn = "qgemv_q2_x";
   qg_status st = qg::check_q2_weight(w, fn);
   if (st != QG_OK) return st;
@@ -393,13 +393,21 @@ qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *accum, 
     return fail(QG_EINVAL, "%s: accum must be y itself or not overlap it", fn);
   const size_t xbytes = (size_t)w->K * sizeof(float), ybytes = (size_t)w->M * sizeof(float);
   if (bytes_overlap(x, xbytes, y, ybytes)) return fail(QG_EINVAL, "%s: x overlaps y", fn);
+  if ((xmax == nullptr) != (nxmax == 0))
+    return fail(QG_EINVAL, "%s: xmax and nxmax must be both given or NULL and 0", fn);
+  if (xmax && (nxmax < 1 || nxmax > QG_Q2X_MAX_PARTS))
+    return fail(QG_EINVAL, "%s: nxmax=%lld outside 1..%d", fn, (long long)nxmax, QG_Q2X_MAX_PARTS);
+  if (xmax && !aligned(xmax, 4)) return fail(QG_EINVAL, "%s: misaligned xmax", fn);
+  const size_t pbytes = (size_t)nxmax * sizeof(float);
+  if (xmax && bytes_overlap(xmax, pbytes, y, ybytes)) return fail(QG_EINVAL, "%s: xmax overlaps y", fn);
   const size_t need = qgemv_q2_x_ws_bytes(w->M, w->K, w->group, S);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QG_EINVAL, "%s: workspace %zu bytes < %zu needed for split %d", fn, ws ? ws_bytes : (size_t)0, need, S);
   if (need > 0 && !aligned(ws, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", fn);
   if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, accum, ybytes) ||
-                   bytes_overlap(ws, need, x, xbytes) || overlaps_q2_planes(ws, need, w)))
-    return fail(QG_EINVAL, "%s: workspace overlaps an output, the residual, x or the weights", fn);
+                   bytes_overlap(ws, need, x, xbytes) || bytes_overlap(ws, need, xmax, pbytes) ||
+                   overlaps_q2_planes(ws, need, w)))
+    return fail(QG_EINVAL, "%s: workspace overlaps an output, the residual, x, xmax or the weights", fn);
   qg::Q2XCall c{};
   c.codes[0] = w->codes;
   c.scales[0] = w->scales;
@@ -408,6 +416,8 @@ qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *accum, 
   c.K = (int)w->K;
   c.group = w->group;
   c.x = x;
+  c.xmax = xmax;
+  c.nxmax = (int)nxmax;
   c.accum = accum;
   c.ws = ws;
   c.split = S;
@@ -426,8 +436,8 @@ size_t qgemv_q2_gate_up_glu_x_ws_bytes(int64_t M) {
 }
 
 static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_q2_weight *w1, const float *x,
-                               const float *norm_w, float eps, int glu, float *y0, float *y1, void *ws,
-                               size_t ws_bytes, void *stream) {
+                               const float *norm_w, float eps, int glu, float *y0, float *y1, float *tmax,
+                               void *ws, size_t ws_bytes, void *stream) {
   qg_status st = qg::check_q2_weight(w0, fn);
   if (st != QG_OK) return st;
   if ((st = qg::check_q2_weight(w1, fn)) != QG_OK) return st;
@@ -449,6 +459,13 @@ static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_
         bytes_overlap(ws, need, norm_w, xbytes) || overlaps_q2_planes(ws, need, w0) ||
         overlaps_q2_planes(ws, need, w1))
       return fail(QG_EINVAL, "%s: workspace overlaps t, x, norm_w or the weights", fn);
+    if (tmax) {
+      const size_t tb = (size_t)((w0->M + 63) / 64) * sizeof(float);
+      if (!aligned(tmax, 4)) return fail(QG_EINVAL, "%s: misaligned tmax", fn);
+      if (bytes_overlap(tmax, tb, y0, ybytes) || bytes_overlap(tmax, tb, x, xbytes) ||
+          bytes_overlap(tmax, tb, norm_w, xbytes) || bytes_overlap(tmax, tb, ws, need))
+        return fail(QG_EINVAL, "%s: tmax overlaps t, x, norm_w or the workspace", fn);
+    }
   }
   qg::Q2XCall c{};
   c.codes[0] = w0->codes;
@@ -466,20 +483,21 @@ static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_
   c.ws = glu >= 0 ? ws : nullptr;
   c.split = 1;
   c.glu = glu;
+  c.tmax = glu >= 0 ? tmax : nullptr;
   return qg::launched(qg::launch_q2_gemv_x(c, (hipStream_t)stream), fn);
 }
 
 qg_status qgemv_q2_dual_x(const qg_q2_weight *w0, const qg_q2_weight *w1, const float *x, const float *norm_w,
                           float eps, float *y0, float *y1, void *stream) {
-  return pair_x_common("qgemv_q2_dual_x", w0, w1, x, norm_w, eps, -1, y0, y1, nullptr, 0, stream);
+  return pair_x_common("qgemv_q2_dual_x", w0, w1, x, norm_w, eps, -1, y0, y1, nullptr, nullptr, 0, stream);
 }
 
 qg_status qgemv_q2_gate_up_glu_x(const qg_q2_weight *w_gate, const qg_q2_weight *w_up, const float *x,
-                                 const float *norm_w, float eps, int kind, float *t, void *ws, size_t ws_bytes,
-                                 void *stream) {
+                                 const float *norm_w, float eps, int kind, float *t, float *tmax, void *ws,
+                                 size_t ws_bytes, void *stream) {
   const char *fn = "qgemv_q2_gate_up_glu_x";
   if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
-  return pair_x_common(fn, w_gate, w_up, x, norm_w, eps, kind, t, nullptr, ws, ws_bytes, stream);
+  return pair_x_common(fn, w_gate, w_up, x, norm_w, eps, kind, t, nullptr, tmax, ws, ws_bytes, stream);
 }
 
 qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream) {

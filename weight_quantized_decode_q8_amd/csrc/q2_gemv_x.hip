@@ -89,10 +89,16 @@ struct XArgs {
   const float *accum;    // one matrix: residual or null
   float *part;           // S > 1: partials [S][Mp]; EPI_GLU: g and u [2][Mp]
   int *cnt;              // S > 1 or EPI_GLU: arrival counters [tiles]
-  int M, K, S, tiles;
+  const float *xmax;     // PRO_PARTS: nxmax partial maxima of |x|
+  float *tmax;           // EPI_GLU: max|t| of each row tile, or null
+  int M, K, S, tiles, nxmax;
 };
 
-enum { PRO_X = 0, PRO_NORM = 1 };
+// PRO_PARTS: the caller gives max|x| as partial maxima (at most
+// kMaxXParts, e.g. the per-tile max|t| the gate|up launch wrote), so a
+// workgroup loads only its own split's part of the vector.
+enum { PRO_X = 0, PRO_NORM = 1, PRO_PARTS = 2 };
+constexpr int kPartsPerLane = kQ2XMaxParts / 64;
 enum { EPI_Y = 0, EPI_GLU_SILU = 1, EPI_GLU_SIGMOID = 2 };
 
 // Largest of every thread's m over an NT-thread workgroup (exact).
@@ -142,7 +148,8 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
   const i32x4 *cp = (mat ? a.codes[1] : a.codes[0]) + (size_t)tile * nunits * 64 + lane;
   const unsigned short *sp = (mat ? a.scales[1] : a.scales[0]) + (size_t)tile * ngroups * 64 + lane;
 
-  // 1. The whole vector first, then this wave's first load step of weights.
+  // 1. The whole vector (PRO_PARTS: this split's quads and the partial
+  //    maxima) first, then this wave's first load step of weights.
   //    Every load is issued unconditionally, indices clamped into range (a
   //    clamped quad repeats the vector's last one; a clamped weight load
   //    repeats one of the wave's own), so the compiler counts them exactly:
@@ -152,13 +159,19 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
   //    weights first, on HBM-cold weights.)
   const int n4 = K / 4;
   const int q0 = u0 * 16, q1 = gs1 * UPG * 16;  // quads of this split
+  const int qbase = PRO == PRO_PARTS ? q0 : 0;  // quad held by thread tid at r = 0
   float4 v[RQ];
   float4 w[PRO == PRO_NORM ? RQ : 1];
 #pragma unroll
   for (int r = 0; r < RQ; r++) {
-    const int i = min(tid + r * NT, n4 - 1);
+    const int i = min(qbase + tid + r * NT, n4 - 1);
     v[r] = a.x[i];
     if (PRO == PRO_NORM) w[r] = a.norm_w[i];
+  }
+  float pm[PRO == PRO_PARTS ? kPartsPerLane : 1];
+  if (PRO == PRO_PARTS) {
+#pragma unroll
+    for (int k = 0; k < kPartsPerLane; k++) pm[k] = a.xmax[min(lane + 64 * k, a.nxmax - 1)];
   }
   i32x4 c[GPB * UPG];
   unsigned short dh[GPB];
@@ -210,14 +223,23 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
 #pragma unroll
     for (int r = 0; r < RQ; r++) v[r] = mul4(scale4(v[r], inv), w[r]);
   }
+  float amax;
+  if (PRO == PRO_PARTS) {
+    // every wave takes the max of the parts itself: no barrier
 #pragma unroll
-  for (int r = 0; r < RQ; r++) m = fmaxf(m, abs_max4(v[r]));
-  const float amax = block_max_nt<NT>(m, rmax);
+    for (int k = 0; k < kPartsPerLane; k++) m = fmaxf(m, pm[k]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    amax = m;
+  } else {
+#pragma unroll
+    for (int r = 0; r < RQ; r++) m = fmaxf(m, abs_max4(v[r]));
+    amax = block_max_nt<NT>(m, rmax);
+  }
   const float sc = __fdiv_rn(amax, 127.0f);
   const float qinv = sc > 0.0f ? __fdiv_rn(1.0f, sc) : 0.0f;
 #pragma unroll
   for (int r = 0; r < RQ; r++) {
-    const int i = tid + r * NT;
+    const int i = qbase + tid + r * NT;
     if (i >= q0 && i < q1) quant_quad(i - q0, v[r], qinv, reinterpret_cast<int *>(xl), sl);
   }
   lds_barrier();
@@ -289,8 +311,17 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
     if (!arrive_last(a.cnt + tile, 2)) return;
     const float other = take(a.part + (size_t)(1 - mat) * Mp + o);
     (void)take(a.part + (size_t)mat * Mp + o);
-    if (o < M) a.y[0][o] = glu1<EPI == EPI_GLU_SILU ? 0 : 1>(mat ? other : r, mat ? r : other);
+    float tm = 0.0f;
+    if (o < M) {
+      const float tv = glu1<EPI == EPI_GLU_SILU ? 0 : 1>(mat ? other : r, mat ? r : other);
+      a.y[0][o] = tv;
+      tm = fabsf(tv);
+    }
     arrive_reset(a.cnt + tile);
+    if (a.tmax) {
+      for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
+      if (lane == 0) a.tmax[tile] = tm;
+    }
   }
 }
 
@@ -329,15 +360,25 @@ hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
   a.K = c.K;
   a.S = pair ? 1 : c.split;
   a.tiles = tiles;
+  a.xmax = c.xmax;
+  a.nxmax = c.nxmax;
+  a.tmax = c.tmax;
   if (a.S > 1 || c.glu >= 0) {
     a.cnt = reinterpret_cast<int *>(c.ws);
     a.part = reinterpret_cast<float *>(static_cast<char *>(c.ws) + q2x_cnt_bytes(c.M));
   }
   const bool norm = c.norm_w != nullptr;
+  const bool parts = c.xmax != nullptr;
   // Waves per tile as the plain kernels: 8 when one matrix's row tiles fill
-  // the CUs, else 16; quads of the vector held per thread: 4 or 8.
+  // the CUs, else 16; quads of the vector held per thread: 4 or 8 (the whole
+  // vector), or 2, 4 or 8 (one split's quads, with the partial maxima).
   const int waves = tiles >= 256 ? 8 : 16;
-  const int rq = (c.K / 4 + 64 * waves - 1) / (64 * waves) <= 4 ? 4 : 8;
+  const int ugroup = c.group / 64;
+  const int ngroups = c.K / c.group;
+  const int split_quads = (ngroups + a.S - 1) / a.S * ugroup * 16;
+  const int hold = parts ? split_quads : c.K / 4;
+  const int per_thread = (hold + 64 * waves - 1) / (64 * waves);
+  const int rq = parts && per_thread <= 2 ? 2 : per_thread <= 4 ? 4 : 8;
   const dim3 grid(tiles * (pair ? 2 : 1), a.S);
 #define QXK(UPG, GPB, W, RQ, PRO, EPI) q2_gemv_x_kernel<UPG, GPB, W, RQ, PRO, EPI><<<grid, 64 * W, 0, stream>>>(a)
 #define QXE(UPG, GPB, W, RQ, PRO)                                      \
@@ -350,9 +391,14 @@ hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
   do {                                                                 \
     if (norm) QXE(UPG, GPB, W, RQ, PRO_NORM); else QXE(UPG, GPB, W, RQ, PRO_X); \
   } while (0)
+#define QXQ(UPG, GPB, W, RQ) QXK(UPG, GPB, W, RQ, PRO_PARTS, EPI_Y)
 #define QXR(UPG, GPB, W)                                               \
   do {                                                                 \
-    if (rq == 4) QXP(UPG, GPB, W, 4); else QXP(UPG, GPB, W, 8);        \
+    if (parts) {                                                       \
+      if (rq == 2) QXQ(UPG, GPB, W, 2);                                \
+      else if (rq == 4) QXQ(UPG, GPB, W, 4);                           \
+      else QXQ(UPG, GPB, W, 8);                                        \
+    } else if (rq == 4) QXP(UPG, GPB, W, 4); else QXP(UPG, GPB, W, 8); \
   } while (0)
   if (c.group == 64) {
     if (waves == 8) QXR(1, 4, 8); else QXR(1, 4, 16);
@@ -362,6 +408,7 @@ hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
 #undef QXK
 #undef QXE
 #undef QXP
+#undef QXQ
 #undef QXR
   return hipGetLastError();
 }

@@ -88,6 +88,8 @@ inline size_t q2x_cnt_bytes(int64_t M) { return (size_t)round_up((M + 63) / 64, 
 // weights held too) at most 16384.
 constexpr int kQ2XMaxK = 32768;
 constexpr int kQ2XNormMaxK = 16384;
+// Largest number of partial maxima of |x| a caller may give (8 per lane).
+constexpr int kQ2XMaxParts = QG_Q2X_MAX_PARTS;
 inline int64_t q2x_max_k(int64_t M) { return (M + 63) / 64 >= 256 ? 16384 : 32768; }
 struct Q2XCall {
   const void *codes[2];
@@ -100,6 +102,9 @@ struct Q2XCall {
   void *ws;
   int split;
   int glu;
+  const float *xmax;  // one matrix: partial maxima of |x| (nxmax of them), or null
+  int nxmax;
+  float *tmax;        // glu: max|t| per row tile, or null
 };
 hipError_t launch_q2_gemv_x(const Q2XCall &call, hipStream_t stream);
 int q2x_auto_split(int64_t M, int64_t K, int group);
