@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel timing table (for counter runs)")
+    ap.add_argument("--timeline-only", action="store_true",
+                    help="only the per-workgroup timeline of the fused FFN launches")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -146,6 +148,76 @@ def measure_achievable(qg, torch, dev, stream, log):
                      "note": f"qg_probe_mfma kind {kind}: {wgs} workgroups x 4 waves x 8 independent chains x "
                              f"{iters} rounds, register operands only"}
     out["wall_clock_kHz"] = khz
+    return out
+
+
+def ffn_timeline(qg, torch, dev, W, Wdn, L4, xs4_d, y4, ws4, S_dn, capture, log, reps=8):
+    """Where the fused decode FFN's microseconds go: the gate|up launch (RMSNorm
+    + quantiser, SiLU gate, tile maxima) and the down launch (quantiser on its
+    split of t, split-K reduce, residual), each workgroup stamping the device
+    wall clock at its start, after its prologue, when its tile result is
+    summed over its waves, and at its exit.  Timed inside a graph right after
+    the lm_head, so the weights come from HBM as in the decode step."""
+    import numpy as np
+
+    khz = qg.qg_probe_wall_clock_khz()
+    Wg, Wu = W["q2_g128_gate_17408x5120"], W["q2_g128_up_17408x5120"]
+    F, D = Wg.M, Wg.K
+    rng = np.random.Generator(np.random.PCG64(20260 + 901))
+    h = torch.from_numpy(rng.standard_normal(D, dtype=np.float32)).to(dev)
+    nw = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)).to(dev)
+    t = torch.empty(F, dtype=torch.float32, device=dev)
+    tmax = torch.empty((F + 63) // 64, dtype=torch.float32, device=dev)
+    hout = torch.empty(D, dtype=torch.float32, device=dev)
+    ws_g = qg.qgemv_q2_gate_up_glu_x_workspace(F, dev)
+    ws_d = qg.qgemv_q2_x_workspace(Wdn.M, Wdn.K, Wdn.group, S_dn, dev)
+    n_g = 2 * ((F + 63) // 64)
+    n_d = ((Wdn.M + 63) // 64) * S_dn
+    st_g = torch.zeros(4 * n_g, dtype=torch.int64, device=dev)
+    st_d = torch.zeros(4 * n_d, dtype=torch.int64, device=dev)
+
+    def fn():
+        L4.gemv_balanced(xs4_d, y4, ws4)
+        qg.qg_probe_q2_gate_up_glu_x_stamped(Wg, Wu, h, qg.QG_GLU_SILU, t, ws_g, st_g, norm_w=nw, eps=1e-6,
+                                             tmax=tmax)
+        qg.qg_probe_q2_x_stamped(Wdn, t, hout, st_d, accum=h, ws=ws_d, split_k=S_dn, xmax=tmax)
+
+    g = capture(fn)
+    runs = []
+    for _ in range(reps):
+        g.replay()
+        torch.cuda.synchronize()
+        runs.append((st_g.cpu().numpy().reshape(-1, 4).astype(np.float64),
+                     st_d.cpu().numpy().reshape(-1, 4).astype(np.float64)))
+    us = 1e3 / khz  # microseconds per tick
+
+    def kernel_stats(a, t0):
+        a = (a - t0) * us
+        q = lambda v, p: round(float(np.percentile(v, p)), 2)
+        return {"workgroups": int(a.shape[0]),
+                "start_us": {"first": q(a[:, 0], 0), "median": q(a[:, 0], 50), "last": q(a[:, 0], 100)},
+                "prologue_us": {"median": q(a[:, 1] - a[:, 0], 50), "max": q(a[:, 1] - a[:, 0], 100)},
+                "tile_result_us": {"median": q(a[:, 2] - a[:, 0], 50), "max": q(a[:, 2] - a[:, 0], 100),
+                                   "last_at": q(a[:, 2], 100)},
+                "exit_last_at_us": q(a[:, 3], 100),
+                "span_us": round(float(a[:, 3].max() - a[:, 0].min()), 2)}
+
+    out = {}
+    spans = []
+    for i, (a, b) in enumerate(runs[2:]):  # the first replays warm the clock
+        t0 = a[:, 0].min()
+        kg, kd = kernel_stats(a, t0), kernel_stats(b, t0)
+        gap = round(float((b[:, 0].min() - a[:, 3].max()) * us), 2)
+        spans.append((kg["span_us"], kd["span_us"], gap))
+        out = {"gate_up_glu_x": kg, "down_x": kd, "gap_between_us": gap}
+    sp = np.array(spans)
+    out["replays"] = len(spans)
+    out["span_us_median"] = {"gate_up_glu_x": round(float(np.median(sp[:, 0])), 2),
+                             "down_x": round(float(np.median(sp[:, 1])), 2),
+                             "gap_between": round(float(np.median(sp[:, 2])), 2)}
+    out["note"] = ("device wall clock (s_memrealtime) per workgroup, relative to the first gate|up workgroup's "
+                   "start, last replay shown in full; spans are first start to last exit of each launch")
+    log(f"FFN timeline: {out}")
     return out
 
 
@@ -554,6 +626,13 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
                 "avg_launch_us": round(dom_us, 2), "algorithmic_bytes_per_launch": lm_bytes}
 
+    timeline = None
+    if not args.no_breakdown or args.timeline_only:
+        timeline = ffn_timeline(qg, torch, dev, W, Wdn, L4, xs4_d, y4, ws4, S_dn, capture, log)
+    if args.timeline_only:
+        print(json.dumps({"ffn_timeline": timeline}), flush=True)
+        return
+
     # ---------------- fused FFN block: the same three matrices with the fused
     # producers, gate and up in one launch and the residual in the down
     # projection's epilogue
@@ -726,8 +805,12 @@ def main():
         def k_gemm():
             qg.qgemm_q8row_batched(W5.packed, W5.rs, xs5_d, y5, nb5, M5, K5, ws5, xs_limbs=0)
 
+        def k_gemm3():
+            qg.qgemm_q8row_batched(W5.packed, W5.rs, xs5_d, y5, nb5, M5, K5, ws5, xs_limbs=3)
+
         k_gemm()
         g_us, g_cold = steady_us(k_gemm, 1, reps=20)
+        g3_us, _ = steady_us(k_gemm3, 1, reps=20)
         flop = 2 * nb5 * M5 * K5
         tflops = flop / g_us / 1e6
         gemm = {"workload": f"batched prefill q8_row GEMM nb={nb5} M={M5} K={K5} (xs limbs: auto)",
@@ -735,7 +818,11 @@ def main():
                 "algorithmic_flop": flop, "us_cold": round(g_cold, 2),
                 "frac_fp16_dense_peak": round(tflops / FP16_DENSE_TFLOPS, 4),
                 "frac_int8_dense_peak_hw": round(2 * tflops / INT8_DENSE_TOPS, 4),
-                "note": "2 int8 limbs per activation on these N(0,1) rows: hardware int8 ops = 2x algorithmic"}
+                "note": "2 int8 limbs per activation on these N(0,1) rows: hardware int8 ops = 2x algorithmic",
+                "accuracy": "auto picks 2 limbs here; the 2e-5 bound then rests on the rounding errors of "
+                            "different elements cancelling, which holds for dense weight rows (the contract in "
+                            "include/qgemv.h); with 3 limbs the bound is certain wherever condition (C) holds",
+                "limbs3_us": round(g3_us, 2), "limbs3_TFLOP/s": round(flop / g3_us / 1e6, 1)}
         # The same product fed by the column prescale of the q8_row FFN: act =
         # silu(g) u col formed inside the product's prep, against the prescale
         # launch followed by the product.
@@ -912,6 +999,7 @@ def main():
         "prefill_gemm": gemm,
         "prefill_q2_gemm": q2gemm,
         "fused_ffn": fused,
+        "ffn_timeline": timeline,
         "q2_sustained": sustained,
     }
     print(json.dumps(out), flush=True)

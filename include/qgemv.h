@@ -591,6 +591,26 @@ size_t qgemm_q2_batched_dual_ws_bytes(int64_t M, int64_t K, int group, int64_t n
  *      2^(e_b+8) <= 0.9e-5 * sum_i |xs[b,i]| / sqrt(K) (the 16-bit error
  *      then stays well inside 2e-5 * sum_i |w_i xs_i| for q8_row weights),
  *      else 3 limbs.
+ * Accuracy contract.  Row b's fixed point rounds each xs[b, i] by at most
+ * u_b = 2^(e_b - 1) (3 limbs) or 257 * 2^(e_b - 1) (2 limbs: the dropped
+ * low limb is at most 128 * 2^e_b in magnitude); everything after
+ * that is exact (int32 limb sums) up to six binary32 roundings of the
+ * output.  So, with A[o, b] = sum_i |q[o, i]| and S[o, b] = sum_i
+ * |q[o, i] * xs[b, i]|, output (b, o) is certain to meet
+ * |y - y_exact| <= 2e-5 * rs[o] * S[o, b] whenever
+ *     u_b * A[o, b] <= 1.9e-5 * S[o, b]                        (C)
+ * for the limb count used.  With 3 limbs (C) holds for dense weight rows
+ * against activation rows without extreme outliers (uniform int8 rows and
+ * N(0,1) xs: u_b * A is 1/35 to 1/70 of 1.9e-5 * S).  With 2 limbs (C) does
+ * not hold in general: auto's 2-limb choice rests on the rounding errors
+ * of different elements partly cancelling, which holds (at six standard
+ * deviations) for weight rows whose mass is spread, E|q| / sqrt(E q^2) >=
+ * 0.8, as in dense int8 matrices.  Outside (C) -- e.g. a weight row with
+ * one or a few non-zeros on activations far below the row maximum
+ * (|xs| below about 0.5 % of max|xs_b| with 3 limbs) -- no fixed-point
+ * form of this product meets the bound; such rows need the per-element
+ * floating arithmetic of the q8_row GEMV (qgemv_q8row, per row b).
+ * A row of xs holding an infinity or NaN gives NaN for all its outputs.
  * Arguments:
  *   qpacked: device, T64 image of q [M][K] (16-byte aligned);
  *   rs: device f32[M];  xs: device f32[nb][K] row-major (16-byte aligned);

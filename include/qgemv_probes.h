@@ -48,6 +48,32 @@ qg_status qg_probe_mfma(int kind, int iters, int workgroups, float *sink,
  * qg_probe_mfma's clocks[1]).  QG_ELAUNCH if the runtime cannot say.     */
 qg_status qg_probe_wall_clock_khz(int *khz);
 
+/* Device: the timeline of one launch -- qgemv_q2_x and
+ * qgemv_q2_gate_up_glu_x exactly as in qgemv.h (same kernels, same
+ * results), with every workgroup recording the device wall clock
+ * (s_memrealtime, qg_probe_wall_clock_khz) at four points: its start,
+ * the end of its prologue (the quantised vector in LDS), the moment its
+ * row tile's partial (or g / u) is summed over its waves, and its exit.
+ *   stamps: device, uint64[4 * workgroups], 8-byte aligned; workgroup
+ *           (x, y) of the grid writes entries 4 * (y * gx + x) + 0..3.
+ *           The grid is ceil(M/64) x S (S = the split actually used) for
+ *           qgemv_q2_x and 2 * ceil(M/64) x 1 for the pair (gate tiles
+ *           first).
+ * Arguments and errors otherwise as the product entry points.             */
+qg_status qg_probe_q2_x_stamped(const qg_q2_weight *w, const float *x,
+                                const float *xmax, int64_t nxmax,
+                                const float *accum, float *y, void *ws,
+                                size_t ws_bytes, int split_k,
+                                unsigned long long *stamps, void *stream);
+qg_status qg_probe_q2_gate_up_glu_x_stamped(const qg_q2_weight *w_gate,
+                                            const qg_q2_weight *w_up,
+                                            const float *x,
+                                            const float *norm_w, float eps,
+                                            int kind, float *t, float *tmax,
+                                            void *ws, size_t ws_bytes,
+                                            unsigned long long *stamps,
+                                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,3 +153,81 @@ def test_gemm_largest_k_extreme_values():
         y = gpu_gemm(q, rs, xs, limbs)
         yref, mass = oracle.q8row_gemm(q, rs, xs)
         within(y, yref, mass, f"largest K, limbs={limbs}")
+
+
+# ---- the accuracy contract: sparse weight rows ------------------------------
+def _sparse_case(nb, M, K, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    n1 = min(1024, M // 3)
+    q[: 2 * n1] = 0
+    for o in range(n1):                                    # one-hot rows
+        q[o, rng.integers(0, K)] = rng.choice([-1, 1]) * rng.integers(1, 128)
+    for o in range(n1, 2 * n1):                            # one non-zero per 64
+        cols = np.arange(0, K, 64) + rng.integers(0, 64, K // 64)
+        q[o, cols] = rng.integers(-127, 128, K // 64)
+    rs = rng.uniform(0.001, 0.01, M).astype(np.float32)
+    return q, rs, rng, n1
+
+
+def _contract_u(xs_row, limbs):
+    from test_gemm_error_model import exponent
+    e = exponent(xs_row)
+    return 2.0 ** (e - 1) * (257 if limbs == 2 else 1)
+
+
+def test_gemm_sparse_rows_inside_contract_c5_shape():
+    """One-hot rows and rows with one non-zero per 64 at the batched
+    workload's shape (512 x 17408 x 5120), 3 limbs, activation rows whose
+    entries are at least a fifth of the row maximum: condition (C) of the
+    contract holds for every sampled output (checked here), and so must the
+    2e-5 bound."""
+    nb, M, K = 512, 17408, 5120
+    q, rs, rng, n1 = _sparse_case(nb, M, K, 9200)
+    xs = (rng.choice([-1.0, 1.0], (nb, K)) * rng.uniform(0.2, 1.0, (nb, K))
+          * rng.uniform(0.1, 10.0, (nb, 1))).astype(np.float32)
+    y = gpu_gemm(q, rs, xs, 3)
+    bs = np.concatenate([rng.integers(0, nb, 6000), rng.integers(0, nb, 2000)])
+    os_ = np.concatenate([rng.integers(0, 2 * n1, 6000), rng.integers(2 * n1, M, 2000)])
+    yref, mass = oracle.q8row_gemm(q, rs, xs, entries=(bs, os_))
+    A = np.abs(q.astype(np.int64)).sum(axis=1)
+    u = np.array([_contract_u(xs[b], 3) for b in range(nb)])
+    assert np.all(rs[os_].astype(np.float64) * u[bs] * A[os_] <= 1.9e-5 * mass), "case outside (C)"
+    within(y[bs, os_], yref, mass, "sparse rows, 3 limbs")
+
+
+@pytest.mark.skip(reason="outside the accuracy contract of qgemm_q8row_batched: one-hot weight rows whose "
+                         "non-zero meets an activation far below its row's maximum break condition (C) for every "
+                         "fixed-point limb count, and the fixed point then leaves the 2e-5 bound (the CPU error "
+                         "model in test_gemm_error_model.py shows it); kept as the recorded out-of-class case")
+def test_gemm_auto_one_hot_rows_on_small_activations_outside_contract():
+    nb, M, K = 512, 17408, 5120
+    rng = np.random.Generator(np.random.PCG64(9201))
+    xs = rng.standard_normal((nb, K)).astype(np.float32)
+    q = np.zeros((M, K), np.int8)
+    for o in range(M):
+        q[o, int(np.argmin(np.abs(xs[o % nb])))] = 127
+    rs = rng.uniform(0.001, 0.01, M).astype(np.float32)
+    y = gpu_gemm(q, rs, xs, 0)
+    os_ = np.arange(0, M, 7)
+    bs = os_ % nb
+    yref, mass = oracle.q8row_gemm(q, rs, xs, entries=(bs, os_))
+    within(y[bs, os_], yref, mass, "one-hot rows on the smallest activations, auto")
+
+
+@pytest.mark.parametrize("limbs", [0, 2, 3])
+def test_gemm_non_finite_rows_give_nan(limbs):
+    """A row of xs holding an infinity or a NaN gives NaN for all its
+    outputs; the other rows are unaffected and within the bound."""
+    nb, M, K = 130, 300, 640
+    q, rs, xs = synth.q8gemm_inputs(nb, M, K, seed=9202)
+    xs = xs.copy()
+    xs[3, 17] = np.inf
+    xs[70, 5] = -np.inf
+    xs[129, 600] = np.nan
+    y = gpu_gemm(q, rs, xs, limbs)
+    bad = [3, 70, 129]
+    assert np.all(np.isnan(y[bad]))
+    good = np.setdiff1d(np.arange(nb), bad)
+    yref, mass = oracle.q8row_gemm(q, rs, xs[good])
+    within(y[good], yref, mass, f"finite rows beside non-finite ones, limbs={limbs}")

@@ -99,6 +99,9 @@ _SIGS = {
     "qg_probe_stream_read": (_I, [_P, _SZ, ctypes.c_uint, _P, _I, _I, _P]),
     "qg_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P]),
     "qg_probe_wall_clock_khz": (_I, [ctypes.POINTER(ctypes.c_int)]),
+    "qg_probe_q2_x_stamped": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _I64, _P, _P, _P, _SZ, _I, _P, _P]),
+    "qg_probe_q2_gate_up_glu_x_stamped": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P,
+                                               ctypes.c_float, _I, _P, _P, _P, _SZ, _P, _P]),
 }
 
 _lib = None
@@ -574,3 +577,25 @@ def qg_probe_wall_clock_khz():
     khz = ctypes.c_int(0)
     _check("qg_probe_wall_clock_khz", lib().qg_probe_wall_clock_khz(ctypes.byref(khz)))
     return khz.value
+
+
+def qg_probe_q2_x_stamped(w: Q2Weight, x, y, stamps, accum=None, ws=None, split_k=0, xmax=None, stream=None):
+    """qgemv_q2_x with four wall-clock stamps per workgroup into the int64 device tensor stamps."""
+    import torch
+    d = w.desc()
+    _check("qg_probe_q2_x_stamped", lib().qg_probe_q2_x_stamped(
+        ctypes.byref(d), _dev(x, torch.float32, "x"), _dev(xmax, torch.float32, "xmax"),
+        0 if xmax is None else xmax.numel(), _dev(accum, torch.float32, "accum"), _dev(y, torch.float32, "y"),
+        _dev(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), split_k, _dev(stamps, torch.int64, "stamps"),
+        _stream(stream)))
+
+
+def qg_probe_q2_gate_up_glu_x_stamped(w_gate: Q2Weight, w_up: Q2Weight, x, kind, t, ws, stamps, norm_w=None,
+                                      eps=0.0, tmax=None, stream=None):
+    """qgemv_q2_gate_up_glu_x with four wall-clock stamps per workgroup."""
+    import torch
+    dg, du = w_gate.desc(), w_up.desc()
+    _check("qg_probe_q2_gate_up_glu_x_stamped", lib().qg_probe_q2_gate_up_glu_x_stamped(
+        ctypes.byref(dg), ctypes.byref(du), _dev(x, torch.float32, "x"), _dev(norm_w, torch.float32, "norm_w"),
+        float(eps), int(kind), _dev(t, torch.float32, "t"), _dev(tmax, torch.float32, "tmax"),
+        _dev(ws, torch.uint8, "ws"), ws.numel(), _dev(stamps, torch.int64, "stamps"), _stream(stream)))

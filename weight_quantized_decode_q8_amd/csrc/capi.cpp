@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include "qg_internal.h"
+#include "qgemv_probes.h"
 
 namespace qg {
 
@@ -379,9 +380,9 @@ static qg_status check_x_input(const char *fn, const qg_q2_weight *w, const floa
   return QG_OK;
 }
 
-qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *xmax, int64_t nxmax, const float *accum,
-                     float *y, void *ws, size_t ws_bytes, int split_k, void *stream) {
-  const char *fn = "qgemv_q2_x";
+static qg_status q2_x_impl(const char *fn, const qg_q2_weight *w, const float *x, const float *xmax, int64_t nxmax,
+                           const float *accum, float *y, void *ws, size_t ws_bytes, int split_k,
+                           unsigned long long *stamps, void *stream) {
   qg_status st = qg::check_q2_weight(w, fn);
   if (st != QG_OK) return st;
   if (split_k < 0 || split_k > qg::kMaxSplit) return fail(QG_EINVAL, "%s: split_k=%d outside 0..16", fn, split_k);
@@ -422,7 +423,20 @@ qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *xmax, i
   c.ws = ws;
   c.split = S;
   c.glu = -1;
+  c.stamps = stamps;
   return qg::launched(qg::launch_q2_gemv_x(c, (hipStream_t)stream), fn);
+}
+
+qg_status qgemv_q2_x(const qg_q2_weight *w, const float *x, const float *xmax, int64_t nxmax, const float *accum,
+                     float *y, void *ws, size_t ws_bytes, int split_k, void *stream) {
+  return q2_x_impl("qgemv_q2_x", w, x, xmax, nxmax, accum, y, ws, ws_bytes, split_k, nullptr, stream);
+}
+
+qg_status qg_probe_q2_x_stamped(const qg_q2_weight *w, const float *x, const float *xmax, int64_t nxmax,
+                                const float *accum, float *y, void *ws, size_t ws_bytes, int split_k,
+                                unsigned long long *stamps, void *stream) {
+  if (!stamps || !aligned(stamps, 8)) return fail(QG_EINVAL, "qg_probe_q2_x_stamped: null or misaligned stamps");
+  return q2_x_impl("qg_probe_q2_x_stamped", w, x, xmax, nxmax, accum, y, ws, ws_bytes, split_k, stamps, stream);
 }
 
 int qgemv_q2_x_auto_split(int64_t M, int64_t K, int group) {
@@ -437,7 +451,7 @@ size_t qgemv_q2_gate_up_glu_x_ws_bytes(int64_t M) {
 
 static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_q2_weight *w1, const float *x,
                                const float *norm_w, float eps, int glu, float *y0, float *y1, float *tmax,
-                               void *ws, size_t ws_bytes, void *stream) {
+                               void *ws, size_t ws_bytes, void *stream, unsigned long long *stamps = nullptr) {
   qg_status st = qg::check_q2_weight(w0, fn);
   if (st != QG_OK) return st;
   if ((st = qg::check_q2_weight(w1, fn)) != QG_OK) return st;
@@ -484,6 +498,7 @@ static qg_status pair_x_common(const char *fn, const qg_q2_weight *w0, const qg_
   c.split = 1;
   c.glu = glu;
   c.tmax = glu >= 0 ? tmax : nullptr;
+  c.stamps = stamps;
   return qg::launched(qg::launch_q2_gemv_x(c, (hipStream_t)stream), fn);
 }
 
@@ -498,6 +513,15 @@ qg_status qgemv_q2_gate_up_glu_x(const qg_q2_weight *w_gate, const qg_q2_weight 
   const char *fn = "qgemv_q2_gate_up_glu_x";
   if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
   return pair_x_common(fn, w_gate, w_up, x, norm_w, eps, kind, t, nullptr, tmax, ws, ws_bytes, stream);
+}
+
+qg_status qg_probe_q2_gate_up_glu_x_stamped(const qg_q2_weight *w_gate, const qg_q2_weight *w_up, const float *x,
+                                            const float *norm_w, float eps, int kind, float *t, float *tmax,
+                                            void *ws, size_t ws_bytes, unsigned long long *stamps, void *stream) {
+  const char *fn = "qg_probe_q2_gate_up_glu_x_stamped";
+  if (!stamps || !aligned(stamps, 8)) return fail(QG_EINVAL, "%s: null or misaligned stamps", fn);
+  if (kind != QG_GLU_SILU && kind != QG_GLU_SIGMOID) return fail(QG_EINVAL, "%s: kind %d is not SILU or SIGMOID", fn, kind);
+  return pair_x_common(fn, w_gate, w_up, x, norm_w, eps, kind, t, nullptr, tmax, ws, ws_bytes, stream, stamps);
 }
 
 qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream) {

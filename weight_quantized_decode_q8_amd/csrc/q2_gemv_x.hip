@@ -46,6 +46,15 @@
 #include "qg_internal.h"
 #include "quant_rule.h"
 
+// g128 groups per load step: the gate|up pair, and the one-matrix form fed
+// partial maxima (the down projection, whose waves hold 2-3 groups each).
+#ifndef QG_X_PAIR_GPB
+#define QG_X_PAIR_GPB 2
+#endif
+#ifndef QG_X_PARTS_GPB
+#define QG_X_PARTS_GPB 2
+#endif
+
 namespace qg {
 namespace {
 
@@ -91,8 +100,17 @@ struct XArgs {
   int *cnt;              // S > 1 or EPI_GLU: arrival counters [tiles]
   const float *xmax;     // PRO_PARTS: nxmax partial maxima of |x|
   float *tmax;           // EPI_GLU: max|t| of each row tile, or null
+  unsigned long long *stamps;  // measurement only: 4 wall-clock stamps per workgroup, or null
   int M, K, S, tiles, nxmax;
 };
+
+// Measurement stamps (the timeline probe): the wall clock at the
+// workgroup's start, after its prologue, when its tile result is ready and
+// at its exit, by thread 0.  Null in every product call.
+__device__ inline void stamp(const XArgs &a, int k) {
+  if (a.stamps && threadIdx.x == 0)
+    a.stamps[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 4 + k] = wall_clock64();
+}
 
 // PRO_PARTS: the caller gives max|x| as partial maxima (at most
 // kMaxXParts, e.g. the per-tile max|t| the gate|up launch wrote), so a
@@ -127,6 +145,7 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
   __shared__ float rmax[W];
   __shared__ double rss[16];
 
+  stamp(a, 0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mat = (int)blockIdx.x >= a.tiles ? 1 : 0;
@@ -243,6 +262,7 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
     if (i >= q0 && i < q1) quant_quad(i - q0, v[r], qinv, reinterpret_cast<int *>(xl), sl);
   }
   lds_barrier();
+  stamp(a, 1);
 
   // 3. The GEMV over this wave's range, activations from LDS.
   float acc = 0.0f;
@@ -289,26 +309,35 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
 #pragma unroll
   for (int k = 0; k < W - 1; k++) acc += red[k][lane];
   const int o = tile * 64 + lane;
+  stamp(a, 2);
 
   if (EPI == EPI_Y) {
     if (S == 1) {
       if (o < M) a.y[mat][o] = scale_add(acc, sc, a.accum, o);
+      stamp(a, 3);
       return;
     }
     // Split partial; the last arrival of this tile adds all of them in
     // split order, leaving the workspace all zero again.
     put(a.part + (size_t)split * Mp + o, acc);
-    if (!arrive_last(a.cnt + tile, S)) return;
+    if (!arrive_last(a.cnt + tile, S)) {
+      stamp(a, 3);
+      return;
+    }
     float s = 0.0f;
     for (int k = 0; k < S; k++) s += take(a.part + (size_t)k * Mp + o);
     if (o < M) a.y[0][o] = scale_add(s, sc, a.accum, o);
     arrive_reset(a.cnt + tile);
+    stamp(a, 3);
   } else {
     // g or u of this tile, rounded as the GEMV rounds it; the second of the
     // tile's two workgroups forms t = glu(g, u) and clears the workspace.
     const float r = __fmul_rn(acc, sc);
     put(a.part + (size_t)mat * Mp + o, r);
-    if (!arrive_last(a.cnt + tile, 2)) return;
+    if (!arrive_last(a.cnt + tile, 2)) {
+      stamp(a, 3);
+      return;
+    }
     const float other = take(a.part + (size_t)(1 - mat) * Mp + o);
     (void)take(a.part + (size_t)mat * Mp + o);
     float tm = 0.0f;
@@ -322,6 +351,7 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
       for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
       if (lane == 0) a.tmax[tile] = tm;
     }
+    stamp(a, 3);
   }
 }
 
@@ -363,6 +393,7 @@ hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
   a.xmax = c.xmax;
   a.nxmax = c.nxmax;
   a.tmax = c.tmax;
+  a.stamps = c.stamps;
   if (a.S > 1 || c.glu >= 0) {
     a.cnt = reinterpret_cast<int *>(c.ws);
     a.part = reinterpret_cast<float *>(static_cast<char *>(c.ws) + q2x_cnt_bytes(c.M));
@@ -391,7 +422,7 @@ hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
   do {                                                                 \
     if (norm) QXE(UPG, GPB, W, RQ, PRO_NORM); else QXE(UPG, GPB, W, RQ, PRO_X); \
   } while (0)
-#define QXQ(UPG, GPB, W, RQ) QXK(UPG, GPB, W, RQ, PRO_PARTS, EPI_Y)
+#define QXQ(UPG, GPB, W, RQ) QXK(UPG, (UPG == 2 ? QG_X_PARTS_GPB : 2 * QG_X_PARTS_GPB), W, RQ, PRO_PARTS, EPI_Y)
 #define QXR(UPG, GPB, W)                                               \
   do {                                                                 \
     if (parts) {                                                       \
@@ -403,7 +434,7 @@ hipError_t launch_q2_gemv_x(const Q2XCall &c, hipStream_t stream) {
   if (c.group == 64) {
     if (waves == 8) QXR(1, 4, 8); else QXR(1, 4, 16);
   } else {
-    if (waves == 8) QXR(2, 2, 8); else QXR(2, 2, 16);
+    if (waves == 8) QXR(2, QG_X_PAIR_GPB, 8); else QXR(2, QG_X_PAIR_GPB, 16);
   }
 #undef QXK
 #undef QXE

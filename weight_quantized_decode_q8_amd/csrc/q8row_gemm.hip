@@ -108,7 +108,8 @@ __device__ __forceinline__ void store_limbs(const float (&xv)[16], int e, i32x4 
     lim[0][w] = lim[1][w] = lim[2][w] = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      int v = (int)rintf(ldexpf(xv[w * 4 + j], -e));  // exact scaling, then nearest
+      const float xs = ldexpf(xv[w * 4 + j], -e);  // exact scaling
+      int v = isfinite(xs) ? (int)rintf(xs) : 0;     // nearest (a non-finite row is flagged)
       const int lo = ((v + 128) & 255) - 128;
       v = (v - lo) >> 8;
       const int mi = ((v + 128) & 255) - 128;
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
 
   float xh[kPrepHeld][16];
   float amax = 0.0f, asum = 0.0f;
+  bool bad = false;  // an infinity or NaN in the row
   if (held) {
 #pragma unroll
     for (int h = 0; h < kPrepHeld; h++) load_chunk<kSilu>(row, tid + h * kPrepThreads, K, live, xh[h]);
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
       for (int j = 0; j < 16; j++) {
         amax = fmaxf(amax, fabsf(xh[h][j]));
         asum += fabsf(xh[h][j]);
+        bad |= !isfinite(xh[h][j]);
       }
   } else {
     for (int c = tid; c < nchunk_k; c += kPrepThreads) {
@@ -163,9 +166,11 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
       for (int j = 0; j < 16; j++) {
         amax = fmaxf(amax, fabsf(xv[j]));
         asum += fabsf(xv[j]);
+        bad |= !isfinite(xv[j]);
       }
     }
   }
+  bad = __syncthreads_or(bad) != 0;
   for (int off = 32; off > 0; off >>= 1) {
     amax = fmaxf(amax, __shfl_xor(amax, off));
     asum += __shfl_xor(asum, off);
@@ -179,14 +184,16 @@ __global__ __launch_bounds__(kPrepThreads) void gemm_prep_kernel(const float *__
     amax = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
     asum = (red_sum[0] + red_sum[1]) + (red_sum[2] + red_sum[3]);
     int e = 0;
-    if (amax > 0.0f) {
+    if (!bad && amax > 0.0f) {  // amax finite: e within a few steps of ilogb(amax) - 22
       e = ilogbf(amax) - 22;
       while (amax > ldexpf((float)kR3, e)) e++;
       while (amax <= ldexpf((float)kR3, e - 1)) e--;
     }
     xexp[b] = e;
     const float thresh = 0.9e-5f * asum / sqrtf((float)K);
-    need3[b] = (amax > 0.0f && ldexpf(1.0f, e + 8) > thresh) ? 1 : 0;
+    // bit 0: the row needs the third limb; bit 1: the row is not finite (its
+    // limbs are meaningless and the epilogue writes NaN for its outputs)
+    need3[b] = bad ? 3 : (amax > 0.0f && ldexpf(1.0f, e + 8) > thresh) ? 1 : 0;
     sh_e = e;
   }
   __syncthreads();
@@ -260,7 +267,8 @@ struct GemmShape {
 template <int L, int TN>
 __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w, const float *__restrict__ rs,
                                           const i32x4 *__restrict__ xl, const i32x4 *__restrict__ zero_blk,
-                                          const int *__restrict__ xexp, float *__restrict__ y, int nb, int M,
+                                          const int *__restrict__ xexp, const int *__restrict__ need3,
+                                          float *__restrict__ y, int nb, int M,
                                           int nchunk_w, int nchunk, int nbt64, int ot, int b0) {
   using S = GemmShape<L, TN>;
   // Stage buffer `buf` holds the A pieces, then the B pieces.
@@ -444,7 +452,12 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
       const float4 v4 = *reinterpret_cast<const float4 *>(ep + gr * S::kRowStride + col);
       const int e = xexp[b] + (L == 2 ? 8 : 0);
       float *dst = y + (size_t)b * M + o;
-      if (vec && o + 3 < M) {
+      if (need3[b] & 2) {  // an infinity or NaN in this xs row
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          if (o + k < M) dst[k] = nan;
+      } else if (vec && o + 3 < M) {
         const float4 r4 = *reinterpret_cast<const float4 *>(rs + o);
         *reinterpret_cast<float4 *>(dst) = make_float4(ldexpf(v4.x * r4.x, e), ldexpf(v4.y * r4.y, e),
                                                        ldexpf(v4.z * r4.z, e), ldexpf(v4.w * r4.w, e));
@@ -486,14 +499,14 @@ __global__ __launch_bounds__(kThreads, 1) void q8row_gemm_kernel(
   bool three = limbs == 3;
   if (limbs == 0) {
     const int lane = threadIdx.x & 63;
-    const int f = need3[g0 + lane] | need3[g0 + 64 + lane];
+    const int f = (need3[g0 + lane] | need3[g0 + 64 + lane]) & 1;
     three = __builtin_amdgcn_ballot_w64(f != 0) != 0;
   }
   if (three) {
-    gemm_pass<3, 64>(lds, w, rs, xl, zero_blk, xexp, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0);
-    gemm_pass<3, 64>(lds, w, rs, xl, zero_blk, xexp, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0 + 64);
+    gemm_pass<3, 64>(lds, w, rs, xl, zero_blk, xexp, need3, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0);
+    gemm_pass<3, 64>(lds, w, rs, xl, zero_blk, xexp, need3, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0 + 64);
   } else {
-    gemm_pass<2, 128>(lds, w, rs, xl, zero_blk, xexp, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0);
+    gemm_pass<2, 128>(lds, w, rs, xl, zero_blk, xexp, need3, y, nb, M, nchunk_w, nchunk, nbt64, ot, g0);
   }
 }
 

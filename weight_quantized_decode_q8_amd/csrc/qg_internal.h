@@ -105,6 +105,7 @@ struct Q2XCall {
   const float *xmax;  // one matrix: partial maxima of |x| (nxmax of them), or null
   int nxmax;
   float *tmax;        // glu: max|t| per row tile, or null
+  unsigned long long *stamps;  // measurement only (the timeline probe), else null
 };
 hipError_t launch_q2_gemv_x(const Q2XCall &call, hipStream_t stream);
 int q2x_auto_split(int64_t M, int64_t K, int group);
