@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel timing table (for counter runs)")
+    ap.add_argument("--down-split", type=int, default=0,
+                    help="split of the down projection's one-launch form (0: the library's choice)")
     ap.add_argument("--timeline-only", action="store_true",
                     help="only the per-workgroup timeline of the fused FFN launches")
     ap.add_argument("--calib-copy", action="store_true",
@@ -398,7 +400,7 @@ def main():
     # the down projection's split: the in-launch form's automatic choice
     # (its partials are added inside the launch); the six-launch form is run
     # with the same split so that the two give the same bits
-    S_dn = qg.qgemv_q2_x_auto_split(Wdn.M, Wdn.K, Wdn.group)
+    S_dn = args.down_split or qg.qgemv_q2_x_auto_split(Wdn.M, Wdn.K, Wdn.group)
     ws_dn6 = torch.zeros(max(1, qg.qgemv_q2_ws_bytes(Wdn.M, Wdn.K, Wdn.group, S_dn)), dtype=torch.uint8, device=dev)
     ws_dnx = qg.qgemv_q2_x_workspace(Wdn.M, Wdn.K, Wdn.group, S_dn, dev)
 
@@ -479,24 +481,49 @@ def main():
             assert torch.equal(y[n], ref[n]), f"graph replay of {n} differs from eager"
         assert torch.equal(y4, ref4), "graph replay of lm_head differs from eager"
 
-    # ---------------- timed region: K steps
-    for _ in range(args.warmup):
-        g_step.replay()
-    torch.cuda.synchronize()
+    # ---------------- timed region: K steps, captured back to back in one
+    # graph (as a model's decode graph holds its layers' launches back to
+    # back); every step streams all its weights again.  A graph launch ends
+    # with a release to the host and the next one starts with an acquire, a
+    # few microseconds per launch: the same K steps as K launches of a
+    # one-step graph are timed beside it.
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        g_step.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    def time_graph(g_warm, g_main, per_replay_steps=None):
+        """Microseconds per step: warmup graph, then the timed graph between
+        events (per_replay_steps: the one-step graph replayed that many times)."""
+        nonlocal_wall[0] = 0.0
+        if g_warm is not None:
+            g_warm.replay()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        ev0.record(stream)
+        if per_replay_steps is None:
+            g_main.replay()
+        else:
+            for _ in range(per_replay_steps):
+                g_main.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        nonlocal_wall[0] = time.perf_counter() - w0
+        return ev0.elapsed_time(ev1) * 1e3 / args.steps
+
+    nonlocal_wall = [0.0]
+    g_steps = capture(step, args.steps)
+    g_warm = capture(step, args.warmup) if args.warmup > 0 else None
+    us_main = time_graph(g_warm, g_steps)
+    wall = nonlocal_wall[0]
+    for n in y:
+        assert torch.equal(y[n], ref[n]), f"the {args.steps}-step graph's {n} differs from eager"
+    assert torch.equal(y4, ref4), "the K-step graph's lm_head differs from eager"
+    ms_per_step = us_main / 1e3
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s (wall {wall * 1e6 / args.steps:.1f} us/step)")
+    us_one_step_graphs = time_graph(None, g_step, args.steps)
+    log(f"step {us_main:.1f} us, {value:.0f} GB/s (wall {wall * 1e6 / args.steps:.1f} us/step); "
+        f"as {args.steps} one-step graph launches {us_one_step_graphs:.1f} us")
+    del g_warm
 
     # the same step as six launches, timed the same way (context)
     g_step6 = capture(step6)
@@ -505,15 +532,9 @@ def main():
         torch.cuda.synchronize()
         for n in y:
             assert torch.equal(y[n], ref[n]), f"graph replay of the six-launch step's {n} differs"
-    for _ in range(args.warmup):
-        g_step6.replay()
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        g_step6.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    us_step6 = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    g_steps6 = capture(step6, args.steps)
+    us_step6 = time_graph(None, g_steps6)
+    del g_steps6
     log(f"six-launch step {us_step6:.1f} us")
 
     # ---------------- per-kernel times (graph of n back-to-back launches)
@@ -687,17 +708,11 @@ def main():
                 g.replay()
                 torch.cuda.synchronize()
                 assert torch.equal(h_out, ref_h if ref_h is not None else h_out), "graph replay differs from eager"
-            for _ in range(args.warmup):
-                g.replay()
-            torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.steps):
-                g.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e3 / args.steps
+            gk = capture(fn, args.steps)
+            us = time_graph(g, gk)
+            assert torch.equal(h_out, ref_h if ref_h is not None else h_out), "the K-step graph differs from eager"
+            del gk
+            return us
 
         ref_h = None
         ffn_fused()
@@ -982,6 +997,9 @@ def main():
                             "(qgemv_q2_dual_x), down with the act-quant and the split-K reduce in the launch "
                             "(qgemv_q2_x), lm_head (qgemv_q8row_balanced)",
                    "down_split_k": S_dn,
+                   "timing": f"the {args.steps} timed steps captured back to back in one graph (a model's decode "
+                             "graph holds its launches back to back); every step streams all its weights",
+                   "one_step_graph_launches_us_per_step": round(us_one_step_graphs, 2),
                    "six_launch_form_us_per_step": round(us_step6, 2),
                    "six_launch_form": "act-quant, gate|up pair, act-quant, down partials, split-K reduce, "
                                       "lm_head (same bits)",

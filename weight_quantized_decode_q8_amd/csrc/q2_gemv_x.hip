@@ -194,7 +194,6 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
   }
   i32x4 c[GPB * UPG];
   unsigned short dh[GPB];
-  const bool pre = g0 + GPB <= g1;
   auto prefetch = [&]() {
     const int gl = max(g1 - 1, 0);
 #pragma unroll
@@ -264,42 +263,55 @@ __global__ __launch_bounds__(64 * W) void q2_gemv_x_kernel(XArgs a) {
   lds_barrier();
   stamp(a, 1);
 
-  // 3. The GEMV over this wave's range, activations from LDS.
+  // 3. The GEMV over this wave's range, activations from LDS.  Two register
+  //    buffers of GPB groups: the next step's loads are issued before the
+  //    current step is computed, so a wave always has a step of weights in
+  //    flight.  Groups are added in the same order as in the plain kernel.
+  //    A step past the wave's range loads clamped indices (a repeat of its
+  //    last group) and computes only its groups in range.
   float acc = 0.0f;
-  int g = g0;
-  auto step = [&](int gg) {
+  i32x4 c2[GPB * UPG];
+  unsigned short dh2[GPB];
+  auto load_into = [&](i32x4 (&cc)[GPB * UPG], unsigned short (&dd)[GPB], int gs) {
+    const int gl = max(g1 - 1, 0);
+#pragma unroll
+    for (int j = 0; j < GPB; j++)
+#pragma unroll
+      for (int vv = 0; vv < UPG; vv++)
+        cc[j * UPG + vv] = __builtin_nontemporal_load(cp + (size_t)(min(gs + j, gl) * UPG + vv) * 64);
+#pragma unroll
+    for (int j = 0; j < GPB; j++) dd[j] = __builtin_nontemporal_load(sp + (size_t)min(gs + j, gl) * 64);
+  };
+  auto compute = [&](const i32x4 (&cc)[GPB * UPG], const unsigned short (&dd)[GPB], int gs) {
 #pragma unroll
     for (int j = 0; j < GPB; j++) {
-      int p = 0;
+      if (gs + j < g1) {
+        int p = 0;
 #pragma unroll
-      for (int vv = 0; vv < UPG; vv++) {
-        const int ul = (gg + j) * UPG + vv - u0;
-        p += unit_dot_v(c[j * UPG + vv], xl[ul * 4], xl[ul * 4 + 1], xl[ul * 4 + 2], xl[ul * 4 + 3], sl[ul]);
+        for (int vv = 0; vv < UPG; vv++) {
+          const int ul = (gs + j) * UPG + vv - u0;
+          p += unit_dot_v(cc[j * UPG + vv], xl[ul * 4], xl[ul * 4 + 1], xl[ul * 4 + 2], xl[ul * 4 + 3], sl[ul]);
+        }
+        acc = fmaf(half_bits_to_f32(dd[j]), (float)p, acc);
       }
-      acc = fmaf(half_bits_to_f32(dh[j]), (float)p, acc);
     }
   };
-  if (pre) {
-    step(g);
-    g += GPB;
-  }
-  for (; g + GPB <= g1; g += GPB) {
-#pragma unroll
-    for (int vv = 0; vv < GPB * UPG; vv++) c[vv] = __builtin_nontemporal_load(cp + (size_t)(g * UPG + vv) * 64);
-#pragma unroll
-    for (int j = 0; j < GPB; j++) dh[j] = __builtin_nontemporal_load(sp + (size_t)(g + j) * 64);
-    step(g);
-  }
-  for (; g < g1; g++) {
-    const unsigned short d1 = __builtin_nontemporal_load(sp + (size_t)g * 64);
-    int p = 0;
-#pragma unroll
-    for (int vv = 0; vv < UPG; vv++) {
-      const int ul = g * UPG + vv - u0;
-      p += unit_dot_v(__builtin_nontemporal_load(cp + (size_t)(g * UPG + vv) * 64), xl[ul * 4], xl[ul * 4 + 1],
-                      xl[ul * 4 + 2], xl[ul * 4 + 3], sl[ul]);
+  const int nsteps = (g1 - g0 + GPB - 1) / GPB;
+  for (int st = 0, gs = g0; st < nsteps; st += 2, gs += 2 * GPB) {
+    if (st + 1 < nsteps) {
+      load_into(c2, dh2, gs + GPB);
+      compute(c, dh, gs);
+    } else {
+      compute(c, dh, gs);
+      break;
     }
-    acc = fmaf(half_bits_to_f32(d1), (float)p, acc);
+    if (st + 2 < nsteps) {
+      load_into(c, dh, gs + 2 * GPB);
+      compute(c2, dh2, gs + GPB);
+    } else {
+      compute(c2, dh2, gs + GPB);
+      break;
+    }
   }
 
   // 4. Combine the waves in order (the plain kernel's combine).
