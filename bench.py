@@ -718,10 +718,14 @@ def main():
         ffn_fused()
         torch.cuda.synchronize()
         ref_h = h_out.clone()
-        us_x = timed_step(ffn_x)
-        us_xw = timed_step(ffn_x_whole_max)
-        us_fs = timed_step(ffn_fused)
-        us_dg = timed_step(ffn_dual_then_glu)
+        # the forms measured in turn, three rounds, median per form (the clock drifts
+        # by a microsecond or two over a run)
+        rounds = {f: [] for f in (ffn_x, ffn_x_whole_max, ffn_fused, ffn_dual_then_glu)}
+        for _ in range(3):
+            for f in rounds:
+                rounds[f].append(timed_step(f))
+        med = {f: sorted(v)[1] for f, v in rounds.items()}
+        us_x, us_xw, us_fs, us_dg = med[ffn_x], med[ffn_x_whole_max], med[ffn_fused], med[ffn_dual_then_glu]
         fused = {"workload": "decode step with the FFN block fused: RMSNorm+quant -> gate|up Q2 GEMV with the "
                              "SiLU gate in its epilogue -> quant -> down Q2 GEMV + residual, then the q8_row lm_head",
                  "us_per_step": round(us_x, 2), "GB/s": round(step_bytes / us_x / 1e3, 1),
