@@ -418,3 +418,22 @@ def test_q8row_balanced_sizes_and_einval():
     _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x500008), 1 << 20, None))
     _einval(L.qgemv_q8row_balanced(a16, P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x400100), 1 << 20, None))
     _einval(L.qgemv_q8row_balanced(P(0x1000000), P(0x200000), P(0x300000), P(0x400000), M, 1024, P(0x1000400), 1 << 20, None))
+
+
+def test_probe_entry_points_einval():
+    """The measurement probes validate their arguments before any launch."""
+    L = qg.lib()
+    P = ctypes.c_void_p
+    _einval(L.qg_probe_stream_read(None, 1 << 20, 1, P(0x1000), 64, 8, None))
+    _einval(L.qg_probe_stream_read(P(0x1008), 1 << 20, 1, P(0x1000), 64, 8, None))   # misaligned
+    _einval(L.qg_probe_stream_read(P(0x1000), 8, 1, P(0x2000), 64, 8, None))         # under 16 bytes
+    _einval(L.qg_probe_stream_read(P(0x1000), 1 << 20, 1, P(0x2000), 64, 5, None))   # loads not 4/8/16
+    _einval(L.qg_probe_mfma(2, 10, 64, P(0x1000), P(0x2000), None))
+    _einval(L.qg_probe_mfma(0, 0, 64, P(0x1000), P(0x2000), None))
+    _einval(L.qg_probe_mfma(0, 10, 64, P(0x1000), P(0x2004), None))                 # clocks misaligned
+    w = qg.qg_q2_weight(0x100000, 0x200000, 128, 256, 64, 0)
+    _einval(L.qg_probe_q2_x_stamped(ctypes.byref(w), P(0x500000), None, 0, None, P(0x600000), None, 0, 1,
+                                    None, None))                                      # no stamps
+    _einval(L.qg_probe_q2_gate_up_glu_x_stamped(ctypes.byref(w), ctypes.byref(w), P(0x500000), None,
+                                                ctypes.c_float(0.0), 0, P(0x600000), None, P(0x800000), 4096,
+                                                P(0x900004), None))                  # stamps misaligned

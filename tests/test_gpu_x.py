@@ -388,3 +388,55 @@ def test_ffn_block_with_tile_maxima_equals_two_launches():
         m.qgemv_q2_x(Wd, t, y, accum=y, ws=ws_d, split_k=0, xmax=tmax)
         ys.append(host(y))
     assert np.array_equal(bits(ys[0]), bits(ys[1]))
+
+
+def test_stamped_launches_equal_product_launches():
+    """The timeline probe's stamped entry points run the product kernels: the
+    same bits as qgemv_q2_gate_up_glu_x / qgemv_q2_x, and every workgroup's
+    four stamps in order (start <= prologue <= tile sum <= exit)."""
+    torch = _torch()
+    m = qg()
+    F, D, group = 1152, 512, 128
+    Wg, Wu, x = _pair(F, D, group, 7960)
+    bd, _ = synth.q2_inputs(D, F, group, seed=7961)
+    Wd = m.Q2Weight.from_blocks(bd, D, F, group)
+    ws = m.qgemv_q2_gate_up_glu_x_workspace(F)
+    tiles = -(-F // 64)
+    t0, t1 = _empty(F), _empty(F)
+    tm0 = torch.empty(tiles, device="cuda")
+    tm1 = torch.empty(tiles, device="cuda")
+    m.qgemv_q2_gate_up_glu_x(Wg, Wu, dev(x), 0, t0, ws, tmax=tm0)
+    st_g = torch.zeros(4 * 2 * tiles, dtype=torch.int64, device="cuda")
+    m.qg_probe_q2_gate_up_glu_x_stamped(Wg, Wu, dev(x), 0, t1, ws, st_g, tmax=tm1)
+    S = m.qgemv_q2_x_auto_split(D, F, group)
+    wsd = m.qgemv_q2_x_workspace(D, F, group, S)
+    y0, y1 = _empty(D), _empty(D)
+    m.qgemv_q2_x(Wd, t0, y0, ws=wsd, split_k=S, xmax=tm0)
+    st_d = torch.zeros(4 * (-(-D // 64)) * S, dtype=torch.int64, device="cuda")
+    m.qg_probe_q2_x_stamped(Wd, t1, y1, st_d, ws=wsd, split_k=S, xmax=tm1)
+    assert np.array_equal(bits(host(t0)), bits(host(t1))) and np.array_equal(bits(host(y0)), bits(host(y1)))
+    for st in (st_g, st_d):
+        a = host(st).reshape(-1, 4)
+        assert np.all(a > 0) and np.all(np.diff(a, axis=1) >= 0)
+
+
+def test_peak_probes_run():
+    """The measurement probes run and report plausible figures: the streaming
+    read writes nothing (the sentinel is never met), the MFMA loops fill their
+    sink and report a shader clock between 0.5 and 3 GHz."""
+    import torch
+    m = qg()
+    buf = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    m.qg_probe_stream_read(buf, 0x5EED1E55, sink, 2048, 8)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(sink).item()) == 0
+    khz = m.qg_probe_wall_clock_khz()
+    assert khz > 0
+    for kind in (0, 1):
+        s = torch.zeros(64 * 256, dtype=torch.float32, device="cuda")
+        clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+        m.qg_probe_mfma(kind, 50, 64, s, clocks)
+        torch.cuda.synchronize()
+        cyc, ticks = (int(v) for v in clocks.cpu())
+        assert ticks > 0 and 0.5e6 < cyc / (ticks / khz) < 3e6

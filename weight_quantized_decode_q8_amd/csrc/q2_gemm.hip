@@ -55,7 +55,13 @@ constexpr int kWC = 2;         // wave groups along tokens
 constexpr int kWaves = kWR * kWC;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBB = kTN / kWC / 16;  // 16-token blocks per wave (4)
-constexpr int kStages = 4;
+// LDS ring depth in units: the loads of units u + kStages - 2 and
+// u + kStages - 1 go out while units u and u + 1 are multiplied.
+#ifndef QG_Q2GEMM_STAGES
+#define QG_Q2GEMM_STAGES 4
+#endif
+constexpr int kStages = QG_Q2GEMM_STAGES;
+static_assert(kStages % 2 == 0 && kStages >= 4, "two units per barrier");
 constexpr int kABytes = kTM * 16;    // one unit of codes for the tile's rows (4352)
 constexpr int kBBytes = kTN * 64;    // one unit of xq for the tile's tokens (8192)
 constexpr int kDBytes = kTM * 2;     // the unit's group scales for the tile's rows (544)
@@ -65,6 +71,19 @@ constexpr int kAWaveLoads = (kTM + 63) / 64;  // 5, the last one 16 lanes wide
 constexpr int kDDwords = kDBytes / 4;         // 136: waves 5, 6 and 8 lanes of wave 7
 
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Waits until at most n of this wave's vector memory operations are
+// outstanding (n uniform; s_waitcnt takes an immediate).
+__device__ inline void wait_vm_at_most(int n) {
+  switch (n) {
+#define QG_VM(k) \
+  case k: __builtin_amdgcn_s_waitcnt(vmcnt_imm(k)); break;
+    QG_VM(1) QG_VM(2) QG_VM(3) QG_VM(4) QG_VM(5) QG_VM(6) QG_VM(7) QG_VM(8) QG_VM(9) QG_VM(10) QG_VM(11)
+    QG_VM(12) QG_VM(13) QG_VM(14) QG_VM(15) QG_VM(16) QG_VM(17) QG_VM(18) QG_VM(19) QG_VM(20) QG_VM(21)
+#undef QG_VM
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+  }
+}
 
 // LDS slot of token t's 16-byte chunk k within a stage's xq part.
 __device__ inline int b_slot(int t, int k) { return t * 4 + (k ^ ((t >> 2) & 3)); }
@@ -241,15 +260,21 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   };
 
   // K loop over the ring, two units per barrier: while units u, u+1 are
-  // multiplied, the loads of u+2, u+3 are in flight into the buffers that
-  // u-2, u-1 used.
-  if (u_lo < u_hi) issue_stage(u_lo);
-  if (u_lo + 1 < u_hi) issue_stage(u_lo + 1);
+  // multiplied, the loads of u+2 ... u+kStages-1 are in flight, the last two
+  // of them into the buffers that u-2, u-1 used.  A wave's loads complete in
+  // order, so it waits until only the stages after u+1 are outstanding
+  // (this wave's loads per stage: the token pieces, plus the codes for
+  // waves 0-4, the scales for waves 5-7 and the sums for waves 3-4).
+  const int nl = 1 + (wave < kAWaveLoads ? 1 : 0) + (wave >= 5 ? 1 : 0) + ((wave == 3 || wave == 4) ? 1 : 0);
+#pragma unroll
+  for (int k = 0; k < kStages - 2; k++)
+    if (u_lo + k < u_hi) issue_stage(u_lo + k);
   for (int u = u_lo; u < u_hi; u += 2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    const int after = max(0, min(kStages - 4, u_hi - (u + 2)));  // stages issued after u + 1
+    wait_vm_at_most(after * nl);
     asm volatile("s_barrier" ::: "memory");  // every wave's loads of u, u+1 are in LDS
-    if (u + 2 < u_hi) issue_stage(u + 2);
-    if (u + 3 < u_hi) issue_stage(u + 3);
+    if (u + kStages - 2 < u_hi) issue_stage(u + kStages - 2);
+    if (u + kStages - 1 < u_hi) issue_stage(u + kStages - 1);
     const int b0u = u % kStages, b1u = (u + 1) % kStages;
     i32x4 nc[kBB];
     if (UPG == 2) {  // one g128 group: units u, u+1 (K is a multiple of 128)
