@@ -769,6 +769,8 @@ def main():
             nb_w = W0.M * (W0.K // W0.group) * (2 + W0.group // 4)
             ncopy = max(2, -(-(512 << 20) // nb_w))
             ncopy += ncopy % 2
+            if mode == "batch":  # whole launches of 16: a launch of fewer matrices streams slower
+                ncopy = -(-ncopy // qg.QG_Q2_BATCH_MAX) * qg.QG_Q2_BATCH_MAX
             copies = [W0] + [qg.Q2Weight(W0.codes.clone(), W0.scales.clone(), W0.M, W0.K, W0.group)
                              for _ in range(ncopy - 1)]
             xq_c, su_c, sc_c = xs_by_k[W0.K]
