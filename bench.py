@@ -99,7 +99,8 @@ def measure_achievable(qg, torch, dev, stream, log):
     """What this GPU reaches: a streaming read of a 4 GiB buffer (16-byte
     non-temporal loads, the best of several grid sizes) and register-only
     matrix-core loops (int8 16x16x64, fp16 16x16x32), with the shader clock
-    read from s_memtime against the wall clock during the loops."""
+    read from s_memtime against the wall clock during the loops; whether
+    vector-ALU work hides behind matrix-core work; the LDS read rate."""
     out = {}
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -149,6 +150,44 @@ def measure_achievable(qg, torch, dev, stream, log):
                      "shader_clock_MHz": round(mhz, 0) if mhz else None,
                      "note": f"qg_probe_mfma kind {kind}: {wgs} workgroups x 4 waves x 8 independent chains x "
                              f"{iters} rounds, register operands only"}
+    # vector-ALU work beside matrix-core work: 8 int8 MFMA chains per wave,
+    # 4 independent f32 FMAs after each MFMA, 2 waves per SIMD (the batched
+    # products' occupancy); each kind alone, then both
+    wg_mv, it_mv = 1024, 200
+    sink = torch.empty(wg_mv * 512, dtype=torch.float32, device=dev)
+    mv = {}
+    for key, mf, nf in (("mfma", 1, 0), ("fma", 0, 4), ("both", 1, 4)):
+        qg.qg_probe_mfma_valu(mf, nf, it_mv, wg_mv, 2, sink)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        qg.qg_probe_mfma_valu(mf, nf, it_mv, wg_mv, 2, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        mv[key] = a.elapsed_time(b) * 1e3
+    lo, hi = min(mv["mfma"], mv["fma"]), max(mv["mfma"], mv["fma"])
+    out["mfma_valu"] = {"us_mfma_alone": round(mv["mfma"], 1), "us_fma_alone": round(mv["fma"], 1),
+                        "us_both": round(mv["both"], 1),
+                        "added_frac": round((mv["both"] - hi) / lo, 3),
+                        "note": "qg_probe_mfma_valu: 8 int8 16x16x64 MFMA chains per wave, 4 independent f32 FMAs "
+                                "after each MFMA, 2 waves per SIMD; added_frac 0: the faster kind hides behind the "
+                                "slower, 1: their times add"}
+    # LDS read rate: 16-byte reads, one workgroup of 16 waves per CU
+    it_l, waves_l = 2000, 16
+    sink_i = torch.empty(256 * 64 * waves_l, dtype=torch.int32, device=dev)
+    qg.qg_probe_lds_read(16, it_l, 256, waves_l, sink_i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    qg.qg_probe_lds_read(16, it_l, 256, waves_l, sink_i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us_l = a.elapsed_time(b) * 1e3
+    per_cu = it_l * 8 * 64 * 16 * waves_l
+    out["lds_read"] = {"GB/s_per_CU": round(per_cu / us_l / 1e3, 1), "us": round(us_l, 1),
+                       "note": "qg_probe_lds_read: 16-byte conflict-free LDS reads, 16 waves on each of 256 CUs"}
     out["wall_clock_kHz"] = khz
     return out
 

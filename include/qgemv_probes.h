@@ -44,6 +44,37 @@ qg_status qg_probe_stream_read(const void *buf, size_t bytes,
 qg_status qg_probe_mfma(int kind, int iters, int workgroups, float *sink,
                         unsigned long long *clocks, void *stream);
 
+/* Device: whether vector-ALU work hides behind matrix-core work.
+ * `workgroups` workgroups of 256 * waves_per_simd threads (waves_per_simd
+ * waves on each SIMD), each wave running `iters` rounds of 8 independent
+ * v_mfma_i32_16x16x64_i8 chains (mfma = 1) each followed by `fmas`
+ * independent f32 FMAs (0, 2, 4 or 8), or the FMAs alone (mfma = 0,
+ * fmas > 0).  Time the launch: if the two kinds overlapped, mfma + fmas
+ * would take as long as the slower alone; if they add, as long as both.
+ *   sink: device, f32[sink_elems], sink_elems >= workgroups * 256 *
+ *         waves_per_simd; the first that many are written.
+ * QG_EINVAL: mfma not 0/1, fmas not 0/2/4/8, both zero, iters < 1,
+ * workgroups outside 1..65536, waves_per_simd outside 1..4, null or
+ * misaligned sink, sink_elems too small.                                  */
+qg_status qg_probe_mfma_valu(int mfma, int fmas, int iters, int workgroups,
+                             int waves_per_simd, float *sink,
+                             size_t sink_elems, void *stream);
+
+/* Device: the LDS read rate.  `workgroups` workgroups of 64 * waves
+ * threads, each wave running `iters` rounds of 8 LDS reads of
+ * bytes_per_lane (4, 8 or 16) bytes per lane, consecutive lanes at
+ * consecutive addresses of a 64 KiB LDS buffer (no bank conflicts); one
+ * workgroup per CU when the grid is the CU count.  Bytes read per
+ * workgroup: iters * 8 * 64 * bytes_per_lane * waves.
+ *   sink: device, int32[sink_elems], sink_elems >= workgroups * 64 *
+ *         waves; the first that many are written.
+ * QG_EINVAL: bytes_per_lane not 4/8/16, iters < 1, workgroups outside
+ * 1..65536, waves outside 1..16, null or misaligned sink, sink_elems too
+ * small.                                                                  */
+qg_status qg_probe_lds_read(int bytes_per_lane, int iters, int workgroups,
+                            int waves, int *sink, size_t sink_elems,
+                            void *stream);
+
 /* Host: the current device's wall-clock counter rate in kHz (the unit of
  * qg_probe_mfma's clocks[1]).  QG_ELAUNCH if the runtime cannot say.     */
 qg_status qg_probe_wall_clock_khz(int *khz);

@@ -437,3 +437,12 @@ def test_probe_entry_points_einval():
     _einval(L.qg_probe_q2_gate_up_glu_x_stamped(ctypes.byref(w), ctypes.byref(w), P(0x500000), None,
                                                 ctypes.c_float(0.0), 0, P(0x600000), None, P(0x800000), 4096,
                                                 P(0x900004), None))                  # stamps misaligned
+    _einval(L.qg_probe_mfma_valu(2, 4, 10, 64, 2, P(0x1000), 64 * 512, None))    # mfma not 0/1
+    _einval(L.qg_probe_mfma_valu(1, 3, 10, 64, 2, P(0x1000), 64 * 512, None))    # fmas not 0/2/4/8
+    _einval(L.qg_probe_mfma_valu(0, 0, 10, 64, 2, P(0x1000), 64 * 512, None))    # nothing to run
+    _einval(L.qg_probe_mfma_valu(1, 4, 10, 64, 5, P(0x1000), 64 * 1280, None))   # 5 waves per SIMD
+    _einval(L.qg_probe_mfma_valu(1, 4, 10, 64, 2, P(0x1000), 64 * 512 - 1, None))  # sink too small
+    _einval(L.qg_probe_lds_read(12, 10, 64, 8, P(0x1000), 64 * 512, None))       # 12 bytes per lane
+    _einval(L.qg_probe_lds_read(16, 10, 64, 17, P(0x1000), 64 * 64 * 17, None))  # 17 waves
+    _einval(L.qg_probe_lds_read(16, 10, 64, 8, P(0x1002), 64 * 512, None))       # sink misaligned
+    _einval(L.qg_probe_lds_read(16, 10, 64, 8, P(0x1000), 64 * 512 - 1, None))   # sink too small

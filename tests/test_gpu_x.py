@@ -440,3 +440,14 @@ def test_peak_probes_run():
         torch.cuda.synchronize()
         cyc, ticks = (int(v) for v in clocks.cpu())
         assert ticks > 0 and 0.5e6 < cyc / (ticks / khz) < 3e6
+    # matrix-core + vector-ALU loops and the LDS read loop fill their sinks
+    for mf, nf in ((1, 0), (1, 4), (0, 4)):
+        s = torch.full((64 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+        m.qg_probe_mfma_valu(mf, nf, 20, 64, 2, s)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(s).all().item())
+    for w in (4, 8, 16):
+        si = torch.full((64 * 64 * 8,), -1, dtype=torch.int32, device="cuda")
+        m.qg_probe_lds_read(w, 20, 64, 8, si)
+        torch.cuda.synchronize()
+        assert int((si == -1).sum().item()) < si.numel()

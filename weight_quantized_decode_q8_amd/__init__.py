@@ -99,6 +99,8 @@ _SIGS = {
     "qg_probe_stream_read": (_I, [_P, _SZ, ctypes.c_uint, _P, _I, _I, _P]),
     "qg_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P]),
     "qg_probe_wall_clock_khz": (_I, [ctypes.POINTER(ctypes.c_int)]),
+    "qg_probe_mfma_valu": (_I, [_I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "qg_probe_lds_read": (_I, [_I, _I, _I, _I, _P, _SZ, _P]),
     "qg_probe_q2_x_stamped": (_I, [ctypes.POINTER(qg_q2_weight), _P, _P, _I64, _P, _P, _P, _SZ, _I, _P, _P]),
     "qg_probe_q2_gate_up_glu_x_stamped": (_I, [ctypes.POINTER(qg_q2_weight), ctypes.POINTER(qg_q2_weight), _P, _P,
                                                ctypes.c_float, _I, _P, _P, _P, _SZ, _P, _P]),
@@ -571,6 +573,23 @@ def qg_probe_mfma(kind, iters, workgroups, sink, clocks, stream=None):
     _check("qg_probe_mfma", lib().qg_probe_mfma(
         int(kind), int(iters), int(workgroups), _dev(sink, torch.float32, "sink"),
         _dev(clocks, torch.int64, "clocks"), _stream(stream)))
+
+
+def qg_probe_mfma_valu(mfma, fmas, iters, workgroups, waves_per_simd, sink, stream=None):
+    """Matrix-core and vector-ALU work together or apart (qgemv_probes.h);
+    sink: float32[workgroups * 256 * waves_per_simd]."""
+    import torch
+    _check("qg_probe_mfma_valu", lib().qg_probe_mfma_valu(
+        int(mfma), int(fmas), int(iters), int(workgroups), int(waves_per_simd),
+        _dev(sink, torch.float32, "sink"), sink.numel(), _stream(stream)))
+
+
+def qg_probe_lds_read(bytes_per_lane, iters, workgroups, waves, sink, stream=None):
+    """LDS read rate probe (qgemv_probes.h); sink: int32[workgroups * 64 * waves]."""
+    import torch
+    _check("qg_probe_lds_read", lib().qg_probe_lds_read(
+        int(bytes_per_lane), int(iters), int(workgroups), int(waves),
+        _dev(sink, torch.int32, "sink"), sink.numel(), _stream(stream)))
 
 
 def qg_probe_wall_clock_khz():

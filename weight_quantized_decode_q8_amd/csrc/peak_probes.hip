@@ -17,6 +17,13 @@
 //    records the shader-clock count (s_memtime) and the constant-rate
 //    wall-clock count (s_memrealtime) around its loop, which gives the
 //    clock.
+//  - mfma_valu_kernel: 8 independent int8 MFMA chains per wave, each MFMA
+//    followed (by scheduling-group barriers) by a fixed number of
+//    independent f32 FMAs, or either kind alone: whether the vector ALU's
+//    work hides behind the matrix pipe's on this chip or adds to it.
+//  - lds_read_kernel: every lane reads 4, 8 or 16 bytes of LDS per
+//    instruction, consecutive lanes at consecutive addresses (no bank
+//    conflicts): the LDS read rate per CU.
 #include <hip/hip_runtime.h>
 
 #include "qg_internal.h"
@@ -98,6 +105,76 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float *sink, 
   }
 }
 
+constexpr int kMvChains = 8;
+constexpr int kMvFloats = 32;
+
+// MF: issue the MFMAs; NF: f32 FMAs per MFMA slot (0, 2, 4 or 8).
+template <bool MF, int NF>
+__global__ __launch_bounds__(1024) void mfma_valu_kernel(int iters, float *sink) {
+  const int lane = threadIdx.x & 63;
+  const i32x4 a = {lane, lane * 3, lane ^ 5, 7}, b = {lane + 1, 2, lane * 5, 9};
+  i32x4 acc[kMvChains];
+#pragma unroll
+  for (int c = 0; c < kMvChains; c++)
+    acc[c] = i32x4{lane + c, 3 * lane + c + 1, 5 * lane + 2 * c + 2, 7 * lane + 3 * c + 3};
+  float f[kMvFloats];
+#pragma unroll
+  for (int j = 0; j < kMvFloats; j++) f[j] = (float)(lane + j) * 0.001f;
+  const float x = 1.0001f + lane * 1e-7f;
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int c = 0; c < kMvChains; c++) {
+      if (MF) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < NF; k++) {
+        const int j = (c * NF + k) % kMvFloats;
+        f[j] = fmaf(f[j], x, 0.5f);
+      }
+    }
+    // one MFMA, then its FMAs, in program order (not clustered by the
+    // scheduler)
+#pragma unroll
+    for (int c = 0; c < kMvChains; c++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MF ? 1 : 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NF, 0);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMvChains; c++) s += (float)(acc[c].x + acc[c].y + acc[c].z + acc[c].w);
+#pragma unroll
+  for (int j = 0; j < kMvFloats; j++) s += f[j];
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+constexpr int kLdsProbeBytes = 65536;
+
+template <int W>
+__global__ __launch_bounds__(1024) void lds_read_kernel(int iters, int *sink) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsProbeBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kLdsProbeBytes / 4; i += blockDim.x) reinterpret_cast<int *>(lds)[i] = i * 7;
+  __syncthreads();
+  int acc = 0;
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      // W bytes per lane at consecutive addresses, wrapped inside the buffer
+      const int o = ((((wave * 8 + k) * 64 + lane) * W) + it * 64) & (kLdsProbeBytes - W);
+      if (W == 16) {
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(lds + o);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      } else if (W == 8) {
+        const int2 v = *reinterpret_cast<const int2 *>(lds + o);
+        acc ^= v.x ^ v.y;
+      } else {
+        acc ^= *reinterpret_cast<const int *>(lds + o);
+      }
+    }
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + tid] = acc;
+}
+
 }  // namespace
 }  // namespace qg
 
@@ -132,6 +209,40 @@ qg_status qg_probe_mfma(int kind, int iters, int workgroups, float *sink, unsign
     mfma_loop_kernel<1><<<workgroups, 256, 0, (hipStream_t)stream>>>(iters, sink, clocks);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? QG_OK : fail(QG_ELAUNCH, "qg_probe_mfma: %s", hipGetErrorString(e));
+}
+
+qg_status qg_probe_mfma_valu(int mfma, int fmas, int iters, int workgroups, int waves_per_simd, float *sink,
+                             size_t sink_elems, void *stream) {
+  if ((mfma != 0 && mfma != 1) || (fmas != 0 && fmas != 2 && fmas != 4 && fmas != 8) || (!mfma && !fmas) ||
+      iters < 1 || workgroups < 1 || workgroups > (1 << 16) || waves_per_simd < 1 || waves_per_simd > 4 || !sink ||
+      (reinterpret_cast<uintptr_t>(sink) & 3) || sink_elems < (size_t)workgroups * 256 * waves_per_simd)
+    return fail(QG_EINVAL, "qg_probe_mfma_valu: bad argument");
+  const dim3 grid(workgroups), block(256 * waves_per_simd);
+  const hipStream_t s = (hipStream_t)stream;
+#define QG_MV(M, N) \
+  if (mfma == M && fmas == N) mfma_valu_kernel<M, N><<<grid, block, 0, s>>>(iters, sink);
+  QG_MV(1, 0) QG_MV(1, 2) QG_MV(1, 4) QG_MV(1, 8) QG_MV(0, 2) QG_MV(0, 4) QG_MV(0, 8)
+#undef QG_MV
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QG_OK : fail(QG_ELAUNCH, "qg_probe_mfma_valu: %s", hipGetErrorString(e));
+}
+
+qg_status qg_probe_lds_read(int bytes_per_lane, int iters, int workgroups, int waves, int *sink, size_t sink_elems,
+                            void *stream) {
+  if ((bytes_per_lane != 4 && bytes_per_lane != 8 && bytes_per_lane != 16) || iters < 1 || workgroups < 1 ||
+      workgroups > (1 << 16) || waves < 1 || waves > 16 || !sink || (reinterpret_cast<uintptr_t>(sink) & 3) ||
+      sink_elems < (size_t)workgroups * 64 * waves)
+    return fail(QG_EINVAL, "qg_probe_lds_read: bad argument");
+  const dim3 grid(workgroups), block(64 * waves);
+  const hipStream_t s = (hipStream_t)stream;
+  if (bytes_per_lane == 16)
+    lds_read_kernel<16><<<grid, block, 0, s>>>(iters, sink);
+  else if (bytes_per_lane == 8)
+    lds_read_kernel<8><<<grid, block, 0, s>>>(iters, sink);
+  else
+    lds_read_kernel<4><<<grid, block, 0, s>>>(iters, sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QG_OK : fail(QG_ELAUNCH, "qg_probe_lds_read: %s", hipGetErrorString(e));
 }
 
 qg_status qg_probe_wall_clock_khz(int *khz) {
