@@ -19,17 +19,27 @@
 //    per token column, as in the GEMV (sum code*xq - sum xq).
 //  - int32 accumulation over a scale group's units (exact), started from
 //    -suma so that closing the group is one convert and one f32 FMA per
-//    output with d(o, g), as the GEMV does per group; this per-group VALU
-//    work, not the MFMA, is what the kernel's time is made of.
+//    output with d(o, g), as the GEMV does per group.  On gfx950 the vector
+//    ALU's time adds to the matrix pipe's instead of hiding behind it, so the
+//    design counts vector instructions: per wave and g128 group, 136 for the
+//    closes, 42 for the code unpack, about 10 for addresses, beside 34 MFMAs.
 //  - tile 272 weight rows x 128 tokens per 8-wave workgroup (17408 = 64 x
-//    272: 256 workgroups at the FFN width and 512 tokens), waves 4 (rows) x
-//    2 (tokens), so each code word is unpacked by two waves rather than
-//    four; operands go global -> LDS directly (global_load_lds) through
-//    a 4-stage ring, two units per barrier, each stage also carrying the
-//    unit's group scales and suma, so the loop issues no other global load;
-//    the token pieces are stored with an XOR swizzle so the 128-bit fragment
-//    reads hit distinct LDS banks; workgroups sharing a weight tile are
-//    dispatched to one XCD.
+//    272: 256 workgroups at the FFN width and 512 tokens).  Wave w owns row
+//    blocks 2w and 2w + 1 across all 8 token blocks, plus row block 16 by
+//    token block w (17 MFMA tiles per wave, every SIMD the same work), so
+//    each code word is unpacked by one wave and feeds 8 MFMAs.
+//  - the start values -suma of every (group, token) of the workgroup are
+//    built once into an LDS table, each already repeated for the 4 rows a
+//    lane's accumulator holds, so a group's restart reads them with one
+//    128-bit LDS read instead of vector adds and moves.
+//  - a group is closed during the next group's first unit, tile by tile
+//    just before the tile's accumulator restarts; its scales are read into
+//    registers at the end of its last unit.
+//  - operands go global -> LDS directly (global_load_lds) through a 4-stage
+//    ring, two units per barrier, each stage also carrying the unit's group
+//    scales, so the loop issues no other global load; the token pieces are
+//    stored with an XOR swizzle so the 128-bit fragment reads hit distinct
+//    LDS banks; workgroups sharing a weight tile are dispatched to one XCD.
 //  - a pair launch (the page's gemm_gpu_v4_dual: gate and up against the same
 //    token rows) runs both matrices' workgroups in one grid, blockIdx.y
 //    choosing the matrix; every output is computed exactly as in a
@@ -37,6 +47,8 @@
 //  - shapes whose tiles cannot fill the CUs (the 5120-row down projection:
 //    76 tiles) split K into f32 partials [S][nb][M], added in fixed order by
 //    a second kernel; (row tile, split) pairs are spread evenly over XCDs.
+//    A split holds at most kMaxGroupsPerWg scale groups (the start-value
+//    table's size), so long rows are split further.
 #include "qg_internal.h"
 
 namespace qg {
@@ -49,46 +61,29 @@ typedef const __attribute__((address_space(1))) void global_void;
 constexpr int kOB = 17;        // 16-row MFMA blocks per tile
 constexpr int kTM = 16 * kOB;  // 272 weight rows per tile
 constexpr int kTN = 128;       // tokens per tile
-constexpr int kWR = 4;         // wave groups along rows: blocks 0-4, 5-8, 9-12, 13-16
-constexpr int kOBW = 5;        // most row blocks of one wave
-constexpr int kWC = 2;         // wave groups along tokens
-constexpr int kWaves = kWR * kWC;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBB = kTN / kWC / 16;  // 16-token blocks per wave (4)
-// LDS ring depth in units: the loads of units u + kStages - 2 and
-// u + kStages - 1 go out while units u and u + 1 are multiplied.
-#ifndef QG_Q2GEMM_STAGES
-#define QG_Q2GEMM_STAGES 4
-#endif
-constexpr int kStages = QG_Q2GEMM_STAGES;
-static_assert(kStages % 2 == 0 && kStages >= 4, "two units per barrier");
+constexpr int kBB = kTN / 16;  // 16-token blocks per tile (8)
+constexpr int kOBW = 2;        // row blocks of one wave (2w, 2w+1), besides its tile of block 16
+constexpr int kStages = 4;     // LDS ring depth in units (two per barrier)
 constexpr int kABytes = kTM * 16;    // one unit of codes for the tile's rows (4352)
 constexpr int kBBytes = kTN * 64;    // one unit of xq for the tile's tokens (8192)
 constexpr int kDBytes = kTM * 2;     // the unit's group scales for the tile's rows (544)
-constexpr int kSBytes = kTN * 4;     // the unit's suma for the tile's tokens (512)
-constexpr int kStageBytes = kABytes + kBBytes + kDBytes + kSBytes;
+constexpr int kStageBytes = kABytes + kBBytes + kDBytes;
 constexpr int kAWaveLoads = (kTM + 63) / 64;  // 5, the last one 16 lanes wide
 constexpr int kDDwords = kDBytes / 4;         // 136: waves 5, 6 and 8 lanes of wave 7
-
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-// Waits until at most n of this wave's vector memory operations are
-// outstanding (n uniform; s_waitcnt takes an immediate).
-__device__ inline void wait_vm_at_most(int n) {
-  switch (n) {
-#define QG_VM(k) \
-  case k: __builtin_amdgcn_s_waitcnt(vmcnt_imm(k)); break;
-    QG_VM(1) QG_VM(2) QG_VM(3) QG_VM(4) QG_VM(5) QG_VM(6) QG_VM(7) QG_VM(8) QG_VM(9) QG_VM(10) QG_VM(11)
-    QG_VM(12) QG_VM(13) QG_VM(14) QG_VM(15) QG_VM(16) QG_VM(17) QG_VM(18) QG_VM(19) QG_VM(20) QG_VM(21)
-#undef QG_VM
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-  }
-}
-
-// LDS slot of token t's 16-byte chunk k within a stage's xq part.
-__device__ inline int b_slot(int t, int k) { return t * 4 + (k ^ ((t >> 2) & 3)); }
+// The -suma start values of a workgroup's scale groups, each broadcast to the
+// 4 rows a lane's accumulator holds: 16 bytes per (group, token).
+constexpr int kMaxGroupsPerWg = 48;
+constexpr int kNcBytes = kMaxGroupsPerWg * kTN * 16;
+constexpr int kLdsBytes = kStages * kStageBytes + kNcBytes;
 
 __device__ inline float half_bits_to_f32(unsigned short h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+template <bool B>
+struct BC {
+  static constexpr bool value = B;
+};
 
 // The two weight matrices of a pair launch (gate and up against one set of
 // token rows); a one-matrix launch uses entry 0 only.
@@ -103,7 +98,7 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
     Q2Pair pair_args, const int8_t *__restrict__ xq, const int *__restrict__ suma,
     const float *__restrict__ act_scale, const float *accum, int nb, int M, int K, int n_ot, int n_bt, int n_split,
     float *__restrict__ part) {
-  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   // Matrix of this workgroup (blockIdx.y); its partials follow the first
   // matrix's [S][nb][M] block.
   const int job = blockIdx.y;
@@ -126,224 +121,217 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wq = wave % kWC, wh = wave / kWC;
-  const int ob0 = wh == 0 ? 0 : 1 + 4 * wh;  // first row block of this wave
-  const int nob = wh == 0 ? kOBW : 4;
   const int o0 = ot * kTM, b0 = bt * kTN;
   const int m_tiles = (M + 63) / 64;
   const int nunits = K / 64;
   const int ngroups = nunits / UPG;
-  // K split into S ranges of contiguous scale groups: this workgroup's
-  // units are [u_lo, u_hi).
+  // K split into S ranges of contiguous scale groups (at most
+  // kMaxGroupsPerWg each): this workgroup's groups are [g_lo, g_hi), its
+  // units [u_lo, u_hi).
   const int gps = (ngroups + S - 1) / S;
-  const int u_lo = min(ngroups, split * gps) * UPG;
-  const int u_hi = min(ngroups, split * gps + gps) * UPG;
+  const int g_lo = min(ngroups, split * gps), g_hi = min(ngroups, split * gps + gps);
+  const int u_lo = g_lo * UPG, u_hi = g_hi * UPG;
   const int kc = lane >> 4, r16 = lane & 15;
 
-  // Load sources, formed once; a unit step moves each by 64 (codes, in
-  // 16-byte units) or 64 bytes (xq).  Rows past the image and tokens past nb
-  // read the last valid row or token: their results are never stored.
-  const i32x4 *a_src = nullptr;
+  // Load sources: a uniform base plus a 32-bit per-lane byte offset, formed
+  // once; a unit step moves the base by 1024 bytes (codes) or 64 bytes (xq).
+  // Rows past the image and tokens past nb read the last valid row or token:
+  // their results are never stored.
+  unsigned a_vo = 0, b_vo = 0, d_vo = 0;
   {
     const int p = min(64 * wave + lane, kTM - 1);
     const int o = min(o0 + p, m_tiles * 64 - 1);
-    a_src = codes + (size_t)(o >> 6) * nunits * 64 + (o & 63);
+    a_vo = (unsigned)(((o >> 6) * nunits * 64 + (o & 63)) * 16);
   }
-  const int8_t *b_src;
   {
     const int p = 64 * wave + lane;  // slot 0..511
     const int t = p >> 2, s = p & 3;
     const int k = s ^ ((t >> 2) & 3);
     const int b = min(b0 + t, nb - 1);
-    b_src = xq + (size_t)b * K + k * 16;
+    b_vo = (unsigned)(b * K + k * 16);
   }
-  // Per-unit group data, also moved by DMA (4 bytes per lane) so that the
-  // loop has no global loads of its own: the scales of the unit's group for
-  // rows 2j, 2j+1 of the tile in dword j (waves 5-7), and the unit's suma for
-  // each token (waves 3-4).
-  const unsigned short *d_src = nullptr;
+  // The scales of the unit's group for rows 2j, 2j+1 of the tile in dword j
+  // (waves 5-7), also moved by DMA, so the loop has no global loads of its own.
   if (wave >= 5) {
     const int j = min(64 * (wave - 5) + lane, kDDwords - 1);
     const int o = min(o0 + 2 * j, m_tiles * 64 - 2);
-    d_src = scales + (size_t)(o >> 6) * ngroups * 64 + (o & 63);
+    d_vo = (unsigned)(((o >> 6) * ngroups * 64 + (o & 63)) * 2);
   }
-  const int *s_src = nullptr;
-  if (wave == 3 || wave == 4) {
-    const int t = 64 * (wave - 3) + lane;
-    s_src = suma + (size_t)min(b0 + t, nb - 1) * nunits;
-  }
-  auto stage_a = [&](int buf) { return lds + buf * kStageBytes; };
-  auto stage_b = [&](int buf) { return lds + buf * kStageBytes + kABytes; };
-  auto stage_d = [&](int buf) { return lds + buf * kStageBytes + kABytes + kBBytes; };
-  auto stage_s = [&](int buf) { return lds + buf * kStageBytes + kABytes + kBBytes + kDBytes; };
-  auto issue_stage = [&](int u) {
-    const int buf = u % kStages;
+  const char *a_base = reinterpret_cast<const char *>(codes);
+  const char *b_base = reinterpret_cast<const char *>(xq);
+  const char *d_base = reinterpret_cast<const char *>(scales);
+  // A unit's uniform byte offset, opaque to the loop optimiser so that the
+  // addresses stay uniform base + 32-bit lane offset (no per-lane pointers).
+  auto uoff = [](int x) { return (size_t)(unsigned)__builtin_amdgcn_readfirstlane(x); };
+  auto issue_stage = [&](int u, int buf) {
+    char *st = lds + buf * kStageBytes;
     if (wave < kAWaveLoads && (wave < kAWaveLoads - 1 || lane < kTM - 64 * (kAWaveLoads - 1)))
-      __builtin_amdgcn_global_load_lds((global_void *)(a_src + (size_t)u * 64), (lds_void *)(stage_a(buf) + 1024 * wave),
-                                       16, 0, 0);
-    __builtin_amdgcn_global_load_lds((global_void *)(b_src + (size_t)u * 64), (lds_void *)(stage_b(buf) + 1024 * wave),
-                                     16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void *)(a_base + uoff(u * 1024) + a_vo),
+                                       (lds_void *)(st + 1024 * wave), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void *)(b_base + uoff(u * 64) + b_vo),
+                                     (lds_void *)(st + kABytes + 1024 * wave), 16, 0, 0);
     if (wave >= 5 && (wave < 7 || lane < kDDwords - 128))
-      __builtin_amdgcn_global_load_lds((global_void *)(d_src + (size_t)(u / UPG) * 64),
-                                       (lds_void *)(stage_d(buf) + 256 * (wave - 5)), 4, 0, 0);
-    if (wave == 3 || wave == 4)
-      __builtin_amdgcn_global_load_lds((global_void *)(s_src + u), (lds_void *)(stage_s(buf) + 256 * (wave - 3)), 4, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds((global_void *)(d_base + uoff((u / UPG) * 128) + d_vo),
+                                       (lds_void *)(st + kABytes + kBBytes + 256 * (wave - 5)), 4, 0, 0);
   };
+  // The first two units' loads go out before the table below is built.
+  if (u_lo < u_hi) issue_stage(u_lo, 0);
+  if (u_lo + 1 < u_hi) issue_stage(u_lo + 1, 1);
+
+  // -suma of every (group, token) of this workgroup, as 4 equal int32 (the
+  // start value of the group's accumulators, one per row a lane holds).
+  char *nctab = lds + kStages * kStageBytes;
+  for (int e = tid; e < (g_hi - g_lo) * kTN; e += kThreads) {
+    const int g = e / kTN, t = e % kTN;
+    const int *sp = suma + (size_t)min(b0 + t, nb - 1) * nunits + (g_lo + g) * UPG;
+    int sum = sp[0];
+    if (UPG == 2) sum += sp[1];
+    *reinterpret_cast<i32x4 *>(nctab + (size_t)e * 16) = i32x4{-sum, -sum, -sum, -sum};
+  }
+
+  // Tiles of a wave: row blocks 2w and 2w + 1 by the 8 token blocks
+  // (tile 8 a + c), and row block 16 by token block w (tile 16): 17 MFMA
+  // tiles per wave, each code word unpacked by one wave.
+  const int a_off = ((2 * wave) * 16 + r16) * 16 + kc * 4;  // + 256 for row block 2w + 1
+  const int a16_off = (16 * 16 + r16) * 16 + kc * 4;
+  // token t's 16-byte chunk k of a stage's xq sits in slot t * 4 + (k ^ ((t >> 2) & 3))
+  const int b_off = kABytes + (r16 * 4 + (kc ^ ((r16 >> 2) & 3))) * 16;  // + 1024 per token block
+  const int d_off = kABytes + kBBytes + 2 * ((2 * wave) * 16 + 4 * kc);  // + 32 for row block 2w + 1
+  const int d16_off = kABytes + kBBytes + 2 * (16 * 16 + 4 * kc);
+  const int nc_off = r16 * 16;                                          // + 256 per token block
 
   // Per tile an exact int32 accumulator for the current scale group and the
   // f32 sum over closed groups.  A group's first MFMA starts from -suma of
   // the group's tokens instead of 0, so the int32 result is already
-  // sum (code - 1) * xq and closing the group is one convert and one FMA.
-  i32x4 acc[kOBW][kBB];
-  float facc[kOBW][kBB][4];
+  // sum (code - 1) * xq and closing the group is one convert and one FMA per
+  // output.  A group is closed during the next group's first unit, tile by
+  // tile just before the tile's accumulator restarts; its scales are read
+  // into registers at the end of its last unit, before the ring reuses the
+  // stage.
+  constexpr int kTiles = kOBW * kBB + 1;
+  i32x4 acc[kTiles];
+  float facc[kTiles][4];
+  uint2 dq[kOBW + 1];
 #pragma unroll
-  for (int a = 0; a < kOBW; a++)
+  for (int j = 0; j < kTiles; j++) {
+    acc[j] = i32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int c = 0; c < kBB; c++) {
-      acc[a][c] = i32x4{0, 0, 0, 0};
+    for (int v = 0; v < 4; v++) facc[j][v] = 0.0f;
+  }
 #pragma unroll
-      for (int v = 0; v < 4; v++) facc[a][c][v] = 0.0f;
-    }
+  for (int a = 0; a <= kOBW; a++) dq[a] = make_uint2(0u, 0u);
 
-  // -suma of a group for this lane's token in each token block; the group's
-  // units sit in stage buffers buf0 and (g128) buf1.
-  auto group_start = [&](int buf0, int buf1, i32x4 (&nc)[kBB]) {
+  // facc += d * acc for tile j, whose rows' scales are in dq[a].
+  auto close_tile = [&](int j, int a) {
+    const float d0 = half_bits_to_f32(dq[a].x & 0xffff), d1 = half_bits_to_f32(dq[a].x >> 16);
+    const float d2 = half_bits_to_f32(dq[a].y & 0xffff), d3 = half_bits_to_f32(dq[a].y >> 16);
+    facc[j][0] = fmaf(d0, (float)acc[j].x, facc[j][0]);
+    facc[j][1] = fmaf(d1, (float)acc[j].y, facc[j][1]);
+    facc[j][2] = fmaf(d2, (float)acc[j].z, facc[j][2]);
+    facc[j][3] = fmaf(d3, (float)acc[j].w, facc[j][3]);
+  };
+  auto unpack = [](unsigned w) {
+    return i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                 (int)((w >> 6) & 0x03030303u)};
+  };
+  // One unit in stage buffer buf of group g (relative to g_lo).  FIRST: the
+  // group's first unit (the previous group closes, the accumulators restart
+  // from -suma); LAST: the group's last unit (its scales are kept).
+  auto unit = [&](int buf, int g, auto first_c, auto last_c) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    const char *st = lds + buf * kStageBytes;
+    const char *nc = nctab + g * (kTN * 16) + nc_off;
+    const i32x4 af0 = unpack(*reinterpret_cast<const unsigned *>(st + a_off));
+    const i32x4 af1 = unpack(*reinterpret_cast<const unsigned *>(st + a_off + 256));
 #pragma unroll
     for (int c = 0; c < kBB; c++) {
-      const int t = wq * (kTN / kWC) + c * 16 + r16;
-      int sum = *reinterpret_cast<const int *>(stage_s(buf0) + 4 * t);
-      if (UPG == 2) sum += *reinterpret_cast<const int *>(stage_s(buf1) + 4 * t);
-      nc[c] = i32x4{-sum, -sum, -sum, -sum};
-    }
-  };
-  // Close a group whose scales sit in stage buffer buf: facc += d * acc.
-  auto close_group = [&](int buf) {
-#pragma unroll
-    for (int a = 0; a < kOBW; a++) {
-      if (a < nob) {
-        const uint2 dq = *reinterpret_cast<const uint2 *>(stage_d(buf) + 2 * ((ob0 + a) * 16 + 4 * kc));
-        const float d[4] = {half_bits_to_f32(dq.x & 0xffff), half_bits_to_f32(dq.x >> 16),
-                            half_bits_to_f32(dq.y & 0xffff), half_bits_to_f32(dq.y >> 16)};
-#pragma unroll
-        for (int c = 0; c < kBB; c++) {
-          facc[a][c][0] = fmaf(d[0], (float)acc[a][c].x, facc[a][c][0]);
-          facc[a][c][1] = fmaf(d[1], (float)acc[a][c].y, facc[a][c][1]);
-          facc[a][c][2] = fmaf(d[2], (float)acc[a][c].z, facc[a][c][2]);
-          facc[a][c][3] = fmaf(d[3], (float)acc[a][c].w, facc[a][c][3]);
-        }
+      const i32x4 bf = *reinterpret_cast<const i32x4 *>(st + b_off + 1024 * c);
+      if constexpr (FIRST) {
+        const i32x4 n = *reinterpret_cast<const i32x4 *>(nc + 256 * c);
+        close_tile(c, 0);
+        close_tile(kBB + c, 1);
+        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af0, bf, n, 0, 0, 0);
+        acc[kBB + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af1, bf, n, 0, 0, 0);
+      } else {
+        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af0, bf, acc[c], 0, 0, 0);
+        acc[kBB + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af1, bf, acc[kBB + c], 0, 0, 0);
       }
     }
-  };
-
-  // One unit: B fragments of the wave's token blocks, then per row block the
-  // code word unpacked into an A fragment and one MFMA per token block; the
-  // group's first unit starts each accumulator from nc.
-  auto compute_unit = [&](int buf, bool first, const i32x4 (&nc)[kBB]) {
-    i32x4 bf[kBB];
-#pragma unroll
-    for (int c = 0; c < kBB; c++) {
-      const int t = wq * (kTN / kWC) + c * 16 + r16;
-      bf[c] = *reinterpret_cast<const i32x4 *>(stage_b(buf) + b_slot(t, kc) * 16);
-    }
-#pragma unroll
-    for (int a = 0; a < kOBW; a++) {
-      if (a < nob) {
-        const unsigned w = *reinterpret_cast<const unsigned *>(stage_a(buf) + ((ob0 + a) * 16 + r16) * 16 + kc * 4);
-        const i32x4 af = {(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-                          (int)((w >> 6) & 0x03030303u)};
-#pragma unroll
-        for (int c = 0; c < kBB; c++)
-          acc[a][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c], first ? nc[c] : acc[a][c], 0, 0, 0);
+    {
+      const i32x4 af = unpack(*reinterpret_cast<const unsigned *>(st + a16_off));
+      const i32x4 bf = *reinterpret_cast<const i32x4 *>(st + b_off + 1024 * wave);
+      if constexpr (FIRST) {
+        const i32x4 n = *reinterpret_cast<const i32x4 *>(nc + 256 * wave);
+        close_tile(kTiles - 1, kOBW);
+        acc[kTiles - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, n, 0, 0, 0);
+      } else {
+        acc[kTiles - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[kTiles - 1], 0, 0, 0);
       }
     }
+    if constexpr (LAST) {
+      dq[0] = *reinterpret_cast<const uint2 *>(st + d_off);
+      dq[1] = *reinterpret_cast<const uint2 *>(st + d_off + 32);
+      dq[2] = *reinterpret_cast<const uint2 *>(st + d16_off);
+    }
   };
 
-  // K loop over the ring, two units per barrier: while units u, u+1 are
-  // multiplied, the loads of u+2 ... u+kStages-1 are in flight, the last two
-  // of them into the buffers that u-2, u-1 used.  A wave's loads complete in
-  // order, so it waits until only the stages after u+1 are outstanding
-  // (this wave's loads per stage: the token pieces, plus the codes for
-  // waves 0-4, the scales for waves 5-7 and the sums for waves 3-4).
-  const int nl = 1 + (wave < kAWaveLoads ? 1 : 0) + (wave >= 5 ? 1 : 0) + ((wave == 3 || wave == 4) ? 1 : 0);
-#pragma unroll
-  for (int k = 0; k < kStages - 2; k++)
-    if (u_lo + k < u_hi) issue_stage(u_lo + k);
+  // K loop over the ring, one window of two units per barrier: after the
+  // barrier that makes the loads of units u, u + 1 (stage buffers B0,
+  // B0 + 1) visible -- the first one also the table above -- the loads of
+  // u + 2, u + 3 go out into the buffers the previous window used, and u,
+  // u + 1 are multiplied.
   for (int u = u_lo; u < u_hi; u += 2) {
-    const int after = max(0, min(kStages - 4, u_hi - (u + 2)));  // stages issued after u + 1
-    wait_vm_at_most(after * nl);
-    asm volatile("s_barrier" ::: "memory");  // every wave's loads of u, u+1 are in LDS
-    if (u + kStages - 2 < u_hi) issue_stage(u + kStages - 2);
-    if (u + kStages - 1 < u_hi) issue_stage(u + kStages - 1);
-    const int b0u = u % kStages, b1u = (u + 1) % kStages;
-    i32x4 nc[kBB];
-    if (UPG == 2) {  // one g128 group: units u, u+1 (K is a multiple of 128)
-      group_start(b0u, b1u, nc);
-      compute_unit(b0u, true, nc);
-      compute_unit(b1u, false, nc);
-      close_group(b1u);
+    const int B0 = (u - u_lo) & 2;
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+    if (u + 2 < u_hi) issue_stage(u + 2, B0 ^ 2);
+    if (u + 3 < u_hi) issue_stage(u + 3, (B0 ^ 2) + 1);
+    const int g = (u - u_lo) / UPG;
+    if constexpr (UPG == 2) {  // one g128 group: units u, u + 1 (K is a multiple of 128)
+      unit(B0, g, BC<true>{}, BC<false>{});
+      unit(B0 + 1, g, BC<false>{}, BC<true>{});
     } else {  // two g64 groups
-      group_start(b0u, b0u, nc);
-      compute_unit(b0u, true, nc);
-      close_group(b0u);
-      if (u + 1 < u_hi) {
-        group_start(b1u, b1u, nc);
-        compute_unit(b1u, true, nc);
-        close_group(b1u);
-      }
+      unit(B0, g, BC<true>{}, BC<true>{});
+      if (u + 1 < u_hi) unit(B0 + 1, g + 1, BC<true>{}, BC<true>{});
     }
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  close_tile(kTiles - 1, kOBW);
+#pragma unroll
+  for (int c = 0; c < kBB; c++) {
+    close_tile(c, 0);
+    close_tile(kBB + c, 1);
+  }
 
   // Epilogue: y[b, o] = act_scale[b] * acc (+ accum[b, o]), two roundings;
   // with a K split, the f32 partial sums go to part[split][b][o] instead.
   const bool vec = (M & 3) == 0;
-  if (S > 1) {
 #pragma unroll
-    for (int c = 0; c < kBB; c++) {
-      const int b = b0 + wq * (kTN / kWC) + c * 16 + r16;
-      if (b >= nb) continue;
+  for (int j = 0; j < kTiles; j++) {
+    const int blk = j < kTiles - 1 ? 2 * wave + j / kBB : 16;
+    const int c = j < kTiles - 1 ? j % kBB : wave;
+    const int b = b0 + c * 16 + r16;
+    const int o = o0 + blk * 16 + 4 * kc;
+    if (b >= nb || o >= M) continue;
+    float r[4];
+    if (S > 1) {
 #pragma unroll
-      for (int a = 0; a < kOBW; a++) {
-        if (a >= nob) continue;
-        const int o = o0 + (ob0 + a) * 16 + 4 * kc;
-        if (o >= M) continue;
-        float *dst = part + ((size_t)split * nb + b) * M + o;
-        if (vec && o + 3 < M) {
-          *reinterpret_cast<float4 *>(dst) = make_float4(facc[a][c][0], facc[a][c][1], facc[a][c][2], facc[a][c][3]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; v++)
-            if (o + v < M) dst[v] = facc[a][c][v];
-        }
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int c = 0; c < kBB; c++) {
-    const int b = b0 + wq * (kTN / kWC) + c * 16 + r16;
-    if (b >= nb) continue;
-    const float sc = act_scale[b];
-#pragma unroll
-    for (int a = 0; a < kOBW; a++) {
-      if (a >= nob) continue;
-      const int o = o0 + (ob0 + a) * 16 + 4 * kc;
-      if (o >= M) continue;
-      float r[4];
+      for (int v = 0; v < 4; v++) r[v] = facc[j][v];
+    } else {
+      const float sc = act_scale[b];
 #pragma unroll
       for (int v = 0; v < 4; v++) {
-        r[v] = __fmul_rn(facc[a][c][v], sc);
+        r[v] = __fmul_rn(facc[j][v], sc);
         if (accum && o + v < M) r[v] = __fadd_rn(r[v], accum[(size_t)b * M + o + v]);
       }
-      float *dst = y + (size_t)b * M + o;
-      if (vec && o + 3 < M) {
-        *reinterpret_cast<float4 *>(dst) = make_float4(r[0], r[1], r[2], r[3]);
-      } else {
+    }
+    float *dst = S > 1 ? part + ((size_t)split * nb + b) * M + o : y + (size_t)b * M + o;
+    if (vec && o + 3 < M) {
+      *reinterpret_cast<float4 *>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; v++)
-          if (o + v < M) dst[v] = r[v];
-      }
+      for (int v = 0; v < 4; v++)
+        if (o + v < M) dst[v] = r[v];
     }
   }
 }
@@ -377,7 +365,10 @@ int q2_gemm_split(int64_t M, int64_t K, int group, int64_t nb) {
   int64_t S = 256 / tiles;
   if (S > ngroups) S = ngroups;
   if (S > 16) S = 16;
-  return S < 1 ? 1 : (int)S;
+  if (S < 1) S = 1;
+  // every split's groups fit the workgroup's table of start values
+  while ((ngroups + S - 1) / S > kMaxGroupsPerWg) S++;
+  return (int)S;
 }
 
 hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, int group, const int8_t *xq,
