@@ -118,6 +118,26 @@ def test_q2_gemm_c3_down_prefill_split_sampled():
     within(y[bs, os_], yref, mass + U32 / REL * np.abs(yref), what="down 5120x17408 prefill + residual")
 
 
+@pytest.mark.parametrize("K,group", [(32768, 128), (16384, 64)])
+def test_q2_gemm_long_rows_split_by_group_table(K, group):
+    """Rows so long that a split of the occupancy rule would hold more scale
+    groups than a workgroup's table of start values (48): the product splits
+    K further (S = 6 here, against 4 from occupancy), sampled entries and the
+    edges held to the oracle's bound."""
+    nb, M = 512, 4352  # 16 row tiles x 4 token tiles: occupancy alone gives S = 4
+    groups = K // group
+    S = qg().qgemm_q2_batched_ws_bytes(M, K, group, nb) // (nb * M * 4)
+    assert S >= 5 and -(-groups // S) <= 48, (S, groups)
+    blob, _ = synth.q2_inputs(M, K, group, seed=6480 + group)
+    X = token_rows(nb, K, 6481 + group)
+    y, xq, sc = run_gemm(blob, M, K, group, X)
+    rng = synth.rng_for(6482 + group)
+    bs = np.concatenate([rng.integers(0, nb, 1200), np.full(32, nb - 1), np.zeros(32, np.int64)])
+    os_ = np.concatenate([rng.integers(0, M, 1200), np.arange(M - 32, M), np.arange(32)])
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, entries=(bs, os_))
+    within(y[bs, os_], yref, mass, what=f"long rows {M}x{K} g{group}")
+
+
 @pytest.mark.parametrize("nb,M,K,group", [(40, 300, 1024, 64), (7, 64, 256, 128)])
 def test_q2_gemm_split_small_shapes(nb, M, K, group):
     """Few tiles: K is split (several splits, short last split)."""
