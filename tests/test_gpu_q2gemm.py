@@ -138,9 +138,11 @@ def test_q2_gemm_long_rows_split_by_group_table(K, group):
     within(y[bs, os_], yref, mass, what=f"long rows {M}x{K} g{group}")
 
 
-@pytest.mark.parametrize("nb,M,K,group", [(40, 300, 1024, 64), (7, 64, 256, 128)])
+@pytest.mark.parametrize("nb,M,K,group", [(40, 300, 1024, 64), (7, 64, 256, 128), (5, 100, 5120, 128)])
 def test_q2_gemm_split_small_shapes(nb, M, K, group):
-    """Few tiles: K is split (several splits, short last split)."""
+    """Few tiles: K is split (several splits, short last split; at 100 x 5120
+    g128, 40 groups over 16 splits of 3 leave the last two splits empty, and
+    their zero partials must not disturb the sum)."""
     assert qg().qgemm_q2_batched_ws_bytes(M, K, group, nb) > 0
     blob, _ = synth.q2_inputs(M, K, group, seed=6460 + M)
     X = token_rows(nb, K, 6470 + nb)
