@@ -55,6 +55,7 @@ namespace qg {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void global_void;
 
@@ -327,7 +328,10 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
     }
     float *dst = S > 1 ? part + ((size_t)split * nb + b) * M + o : y + (size_t)b * M + o;
     if (vec && o + 3 < M) {
-      *reinterpret_cast<float4 *>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+      if (S > 1)  // partials: read back at once by the reduce kernel, kept in the caches
+        *reinterpret_cast<float4 *>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+      else  // the output: streamed out (every workgroup stores at once, at the end)
+        __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, reinterpret_cast<f32x4 *>(dst));
     } else {
 #pragma unroll
       for (int v = 0; v < 4; v++)

@@ -41,6 +41,7 @@ namespace qg {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKS = 64;        // K bytes per pipeline stage (one MFMA depth)
 constexpr int kCPS = kKS / 16; // 16-byte chunks per stage
@@ -459,8 +460,10 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
           if (o + k < M) dst[k] = nan;
       } else if (vec && o + 3 < M) {
         const float4 r4 = *reinterpret_cast<const float4 *>(rs + o);
-        *reinterpret_cast<float4 *>(dst) = make_float4(ldexpf(v4.x * r4.x, e), ldexpf(v4.y * r4.y, e),
-                                                       ldexpf(v4.z * r4.z, e), ldexpf(v4.w * r4.w, e));
+        // streamed out: every workgroup stores its rows at once, at the end
+        __builtin_nontemporal_store(f32x4{ldexpf(v4.x * r4.x, e), ldexpf(v4.y * r4.y, e),
+                                          ldexpf(v4.z * r4.z, e), ldexpf(v4.w * r4.w, e)},
+                                    reinterpret_cast<f32x4 *>(dst));
       } else {
         if (o < M) dst[0] = ldexpf(v4.x * rs[o], e);
         if (o + 1 < M) dst[1] = ldexpf(v4.y * rs[o + 1], e);
