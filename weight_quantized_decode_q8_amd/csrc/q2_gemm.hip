@@ -342,14 +342,36 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
 
 
 // y[b, o] = act_scale[b] * sum_s part[s][b][o] (+ accum[b, o]), the splits
-// added in fixed order.
+// added in fixed order.  V4: four consecutive outputs of one row per thread
+// (M a multiple of 4, accum 16-byte aligned), as 16-byte loads and a
+// streaming store; the same arithmetic per output.
 // blockIdx.y selects the matrix of a pair launch: its partials start at
 // part + y * S * n and its output is y0 or y1.
+template <bool V4>
 __global__ __launch_bounds__(256) void q2_gemm_reduce_kernel(const float *__restrict__ part, int S, size_t n, int M,
                                                             const float *__restrict__ act_scale, const float *accum,
                                                             float *y0, float *y1) {
   float *y = blockIdx.y ? y1 : y0;
   part += (size_t)blockIdx.y * S * n;
+  if (V4) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < S; k++) {
+      const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (size_t)k * n + i);
+      s[0] += p.x, s[1] += p.y, s[2] += p.z, s[3] += p.w;
+    }
+    const float sc = act_scale[i / M];
+    float r[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) r[v] = __fmul_rn(s[v], sc);
+    if (accum) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(accum + i);
+      r[0] = __fadd_rn(r[0], a.x), r[1] = __fadd_rn(r[1], a.y), r[2] = __fadd_rn(r[2], a.z), r[3] = __fadd_rn(r[3], a.w);
+    }
+    __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, reinterpret_cast<f32x4 *>(y + i));
+    return;
+  }
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.0f;
@@ -398,8 +420,13 @@ hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const size_t n = (size_t)nb * M;
-  const dim3 rgrid((unsigned)((n + 255) / 256), njobs);
-  q2_gemm_reduce_kernel<<<rgrid, 256, 0, stream>>>(part, S, n, M, act_scale, accum, pa.y[0], pa.y[1]);
+  if (M % 4 == 0 && (reinterpret_cast<uintptr_t>(accum) & 15) == 0) {
+    const dim3 rgrid((unsigned)((n / 4 + 255) / 256), njobs);
+    q2_gemm_reduce_kernel<true><<<rgrid, 256, 0, stream>>>(part, S, n, M, act_scale, accum, pa.y[0], pa.y[1]);
+  } else {
+    const dim3 rgrid((unsigned)((n + 255) / 256), njobs);
+    q2_gemm_reduce_kernel<false><<<rgrid, 256, 0, stream>>>(part, S, n, M, act_scale, accum, pa.y[0], pa.y[1]);
+  }
   return hipGetLastError();
 }
 
