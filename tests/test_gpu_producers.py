@@ -147,8 +147,10 @@ def test_rmsnorm_quant_rows_bit_exact(nb, K):
 
 
 @pytest.mark.parametrize("kind", [0, 1])
-@pytest.mark.parametrize("nb,K", [(1, 64), (7, 1088), (48, 17408)])
+@pytest.mark.parametrize("nb,K", [(1, 64), (7, 1088), (48, 17408), (64, 1088), (72, 17408), (64, 18496)])
 def test_glu_quant_rows_bit_exact(kind, nb, K):
+    """Below 64 rows the two-launch form, from 64 rows one workgroup per row
+    holding its t in LDS (K <= 18432; 18496 takes the two-launch form)."""
     torch = _torch()
     rng = synth.rng_for(4300 + nb + kind)
     G = (rng.standard_normal((nb, K)) * 2.5).astype(np.float32)
@@ -163,3 +165,25 @@ def test_glu_quant_rows_bit_exact(kind, nb, K):
         rt, rxq, rsc, rsu = oracle.glu_quant_i8(G[b], U[b], kind)
         assert same_bits(t[b], rt), f"row {b}: t differs"
         assert_quant_equal((xq[b], sc[b], suma[b]), (rxq, rsc, rsu), f"glu row {b}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_glu_quant_rows_in_place(kind):
+    """The one-launch batch form with t written over g, then over u."""
+    torch = _torch()
+    nb, K = 96, 5120
+    rng = synth.rng_for(4400 + kind)
+    G = (rng.standard_normal((nb, K)) * 2.5).astype(np.float32)
+    U = rng.standard_normal((nb, K)).astype(np.float32)
+    for over in ("g", "u"):
+        g_d, u_d = dev(G), dev(U)
+        t = g_d if over == "g" else u_d
+        xq = torch.empty((nb, K), dtype=torch.int8, device="cuda")
+        sc = torch.empty(nb, dtype=torch.float32, device="cuda")
+        suma = torch.empty((nb, K // 64), dtype=torch.int32, device="cuda")
+        qg().qquant_glu_i8_rows(g_d, u_d, kind, t, xq, sc, suma)
+        th, xq, sc, suma = host(t), host(xq), host(sc), host(suma)
+        for b in (0, 1, nb // 2, nb - 1):
+            rt, rxq, rsc, rsu = oracle.glu_quant_i8(G[b], U[b], kind)
+            assert same_bits(th[b], rt), f"row {b}: t over {over} differs"
+            assert_quant_equal((xq[b], sc[b], suma[b]), (rxq, rsc, rsu), f"glu row {b}, t over {over}")

@@ -27,8 +27,11 @@
 // quantiser: its passes re-read x and w from L2 (a few tens of KiB) instead
 // of holding them, so any K the quantiser takes works.  The gated product
 // spends about a hundred binary64 operations per element on exp, too much
-// for one CU at K = 17408, so it is two launches: the product over the
-// whole GPU (with per-workgroup maxima), then one workgroup quantising t.
+// for one CU at K = 17408, so for one vector it is two launches: the product
+// over the whole GPU (with per-workgroup maxima), then one workgroup
+// quantising t.  A batch of 64 or more rows runs one workgroup per row in
+// one launch, each holding its row of t in LDS between the product and the
+// quantiser.
 #include "qg_internal.h"
 #include "gate_rule.h"
 #include "quant_rule.h"
@@ -127,6 +130,40 @@ __global__ __launch_bounds__(kQuantThreads) void quant_from_parts_kernel(const f
   for (int i = threadIdx.x; i < n4; i += kQuantThreads) quant_quad(i, t4[i], qinv, xq4, suma);
 }
 
+// The gated product and its quantiser for a batch of token rows in one
+// launch: one workgroup per row computes the row's t (written out, and kept
+// in LDS), its max|t|, then quantises t from LDS.  A batch of rows fills the
+// GPU with the product's exponentials, so the single-row form's split over
+// the whole GPU is not needed; t is not read back from memory.  Rows of up to
+// kGluRowMaxQuads quads.
+constexpr int kGluRowMaxQuads = 4608;  // K <= 18432: 72 KiB of LDS
+
+template <int KIND>
+__global__ __launch_bounds__(kQuantThreads) void glu_quant_rows_kernel(const float4 *g4, const float4 *u4, float4 *t4,
+                                                                       int n4, int *__restrict__ xq4,
+                                                                       float *__restrict__ act_scale,
+                                                                       int *__restrict__ suma) {
+  __shared__ float4 tl[kGluRowMaxQuads];
+  __shared__ float red_max[kQuantThreads / 64];
+  const size_t row = blockIdx.x;
+  g4 += row * n4;
+  u4 += row * n4;
+  t4 += row * n4;
+  xq4 += row * n4;
+  suma += row * (n4 / 16);
+  act_scale += row;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n4; i += kQuantThreads) {
+    const float4 t = glu4<KIND>(g4[i], u4[i]);  // t may be g or u: each quad read, then written, by one thread
+    t4[i] = t;
+    tl[i] = t;
+    m = fmaxf(m, abs_max4(t));
+  }
+  // block_max's barrier also makes every thread's tl writes visible
+  const float qinv = scale_and_inverse(block_max(m, red_max), act_scale);
+  for (int i = threadIdx.x; i < n4; i += kQuantThreads) quant_quad(i, tl[i], qinv, xq4, suma);
+}
+
 // Column prescale: act[r][i] = silu(g[r][i]) * u[r][i] * col[i] (col null:
 // 1).  Workgroup `blk` of the grid-stride loop takes chunk blk % nck of row
 // blk / nck, 256 consecutive elements (VEC: quads) of that row; act may be g
@@ -196,6 +233,15 @@ hipError_t launch_glu_quant(const float *g, const float *u, int rows, int K, int
   float4 *t4 = reinterpret_cast<float4 *>(t);
   int *s = reinterpret_cast<int *>(suma);
   const int n4 = K / 4;
+  if (rows >= 64 && n4 <= kGluRowMaxQuads) {  // a batch of rows: one launch
+    if (kind == 0)
+      glu_quant_rows_kernel<0><<<rows, kQuantThreads, 0, stream>>>(g4, u4, t4, n4, reinterpret_cast<int *>(xq),
+                                                                    act_scale, s);
+    else
+      glu_quant_rows_kernel<1><<<rows, kQuantThreads, 0, stream>>>(g4, u4, t4, n4, reinterpret_cast<int *>(xq),
+                                                                    act_scale, s);
+    return hipGetLastError();
+  }
   const int nparts = (n4 + kGluThreads - 1) / kGluThreads;
   const dim3 grid(nparts, rows);
   if (kind == 0)
