@@ -39,6 +39,10 @@
 namespace qg {
 namespace {
 
+// HELD: rows of at most 2 * kQuantThreads quads, each thread's quads of x
+// and w read once into registers for all three passes (the same arithmetic
+// in the same order as re-reading them).
+template <bool HELD>
 __global__ __launch_bounds__(kQuantThreads) void rmsnorm_quant_kernel(
     const float4 *__restrict__ x4, const float4 *__restrict__ w4, int n4, float eps,
     int *__restrict__ xq4, float *__restrict__ act_scale, int *__restrict__ suma) {
@@ -51,12 +55,31 @@ __global__ __launch_bounds__(kQuantThreads) void rmsnorm_quant_kernel(
   suma += row * (n4 / 16);
   act_scale += row;
 
+  float4 xh[2], wh[2];
+  if (HELD) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int i = min(tid + h * kQuantThreads, n4 - 1);
+      xh[h] = x4[i];
+      wh[h] = w4[i];
+    }
+  }
+  // f(i, x4[i], w4[i]) for this thread's quads i = tid, tid + kQuantThreads, ...
+  auto each = [&](auto f) {
+    if (HELD) {
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        if (tid + h * kQuantThreads < n4) f(tid + h * kQuantThreads, xh[h], wh[h]);
+    } else {
+      for (int i = tid; i < n4; i += kQuantThreads) f(i, x4[i], w4[i]);
+    }
+  };
+
   double ss = 0.0;
-  for (int i = tid; i < n4; i += kQuantThreads) {
-    const float4 v = x4[i];
+  each([&](int, float4 v, float4) {
     ss += ((double)v.x * (double)v.x + (double)v.y * (double)v.y) +
           ((double)v.z * (double)v.z + (double)v.w * (double)v.w);
-  }
+  });
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   if ((tid & 63) == 0) red_ss[tid >> 6] = ss;
   __syncthreads();
@@ -67,9 +90,9 @@ __global__ __launch_bounds__(kQuantThreads) void rmsnorm_quant_kernel(
   const float inv = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
 
   float m = 0.0f;
-  for (int i = tid; i < n4; i += kQuantThreads) m = fmaxf(m, abs_max4(mul4(scale4(x4[i], inv), w4[i])));
+  each([&](int, float4 v, float4 w) { m = fmaxf(m, abs_max4(mul4(scale4(v, inv), w))); });
   const float qinv = scale_and_inverse(block_max(m, red_max), act_scale);
-  for (int i = tid; i < n4; i += kQuantThreads) quant_quad(i, mul4(scale4(x4[i], inv), w4[i]), qinv, xq4, suma);
+  each([&](int i, float4 v, float4 w) { quant_quad(i, mul4(scale4(v, inv), w), qinv, xq4, suma); });
 }
 
 template <int KIND>
@@ -220,9 +243,14 @@ hipError_t launch_quant_from_parts(const float *t, int rows, int K, int nparts, 
 
 hipError_t launch_rmsnorm_quant(const float *x, const float *w, int rows, int K, float eps, int8_t *xq,
                                 float *act_scale, int32_t *suma, hipStream_t stream) {
-  rmsnorm_quant_kernel<<<rows, kQuantThreads, 0, stream>>>(
-      reinterpret_cast<const float4 *>(x), reinterpret_cast<const float4 *>(w), K / 4, eps,
-      reinterpret_cast<int *>(xq), act_scale, reinterpret_cast<int *>(suma));
+  if (K / 4 <= 2 * kQuantThreads)
+    rmsnorm_quant_kernel<true><<<rows, kQuantThreads, 0, stream>>>(
+        reinterpret_cast<const float4 *>(x), reinterpret_cast<const float4 *>(w), K / 4, eps,
+        reinterpret_cast<int *>(xq), act_scale, reinterpret_cast<int *>(suma));
+  else
+    rmsnorm_quant_kernel<false><<<rows, kQuantThreads, 0, stream>>>(
+        reinterpret_cast<const float4 *>(x), reinterpret_cast<const float4 *>(w), K / 4, eps,
+        reinterpret_cast<int *>(xq), act_scale, reinterpret_cast<int *>(suma));
   return hipGetLastError();
 }
 
