@@ -527,8 +527,11 @@ qg_status qgemv_q2_gate_up_glu_x(const qg_q2_weight *w_gate,
  *   y[b, o] = act_scale[b] * sum_g d(o, g) * sum_{i in g} (code - 1) * xq[b, i]
  *             (+ accum[b, o])
  *   w:         host struct of the device planes (scales 8-byte aligned).
- *   xq, suma, act_scale: device, as written by qquant_act_i8_rows:
- *              int8[nb][K], int32[nb][K/64], f32[nb].
+ *   xq, act_scale: device, as written by qquant_act_i8_rows: int8[nb][K]
+ *              (16-byte aligned), f32[nb].
+ *   suma:      the row quantiser's group sums (int32[nb][K/64]) in the
+ *              GEMV's calling convention; not read (the product multiplies
+ *              code - 1 directly), may be NULL.
  *   accum:     device, f32[nb][M] residual, or NULL; may be y itself,
  *              otherwise must not overlap it.
  *   y:         device, f32[nb][M] (token-major), 16-byte aligned, written.

@@ -118,16 +118,34 @@ def test_q2_gemm_c3_down_prefill_split_sampled():
     within(y[bs, os_], yref, mass + U32 / REL * np.abs(yref), what="down 5120x17408 prefill + residual")
 
 
+@pytest.mark.parametrize("M,in_place", [(17000, True), (16999, False)])
+def test_q2_gemm_residual_one_split_ragged(M, in_place):
+    """A residual on a product that takes no K split (63 row tiles x 3 token
+    tiles), ragged in rows and tokens, in place and not, with M % 4 == 0 (16-byte
+    output stores) and not: the residual of every output is read before the
+    workgroup's first store, so y may be the residual itself."""
+    nb, K, group = 300, 1024, 128
+    assert qg().qgemm_q2_batched_ws_bytes(M, K, group, nb) == 0
+    blob, _ = synth.q2_inputs(M, K, group, seed=6460 + M)
+    X = token_rows(nb, K, 6461)
+    acc = (synth.rng_for(6462).standard_normal((nb, M)) * 3).astype(np.float32)
+    y, xq, sc = run_gemm(blob, M, K, group, X, accum=acc, in_place=in_place)
+    rng = synth.rng_for(6463)
+    bs = np.concatenate([rng.integers(0, nb, 2000), np.full(64, nb - 1), np.zeros(64, np.int64), np.full(64, 255)])
+    os_ = np.concatenate([rng.integers(0, M, 2000), np.arange(M - 64, M), np.arange(64), np.arange(M - 64, M)])
+    yref, mass = oracle.q2_gemm(blob, M, K, group, xq, sc, accum=acc, entries=(bs, os_))
+    within(y[bs, os_], yref, mass + U32 / REL * np.abs(yref), what=f"q2 gemm {M} rows + residual, no split")
+
+
 @pytest.mark.parametrize("K,group", [(32768, 128), (16384, 64)])
-def test_q2_gemm_long_rows_split_by_group_table(K, group):
-    """Rows so long that a split of the occupancy rule would hold more scale
-    groups than a workgroup's table of start values (48): the product splits
-    K further (S = 6 here, against 4 from occupancy), sampled entries and the
-    edges held to the oracle's bound."""
-    nb, M = 512, 4352  # 16 row tiles x 4 token tiles: occupancy alone gives S = 4
+def test_q2_gemm_long_rows_split(K, group):
+    """Long rows over a K split of the occupancy rule (16 row tiles x 4 token
+    tiles: S = 4, 64 scale groups per split), sampled entries and the edges
+    held to the oracle's bound."""
+    nb, M = 512, 4352
     groups = K // group
     S = qg().qgemm_q2_batched_ws_bytes(M, K, group, nb) // (nb * M * 4)
-    assert S >= 5 and -(-groups // S) <= 48, (S, groups)
+    assert S == 4 and groups // S == 64, (S, groups)
     blob, _ = synth.q2_inputs(M, K, group, seed=6480 + group)
     X = token_rows(nb, K, 6481 + group)
     y, xq, sc = run_gemm(blob, M, K, group, X)

@@ -572,15 +572,15 @@ size_t qgemm_q2_batched_ws_bytes(int64_t M, int64_t K, int group, int64_t nb) {
 qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq, const int32_t *suma, const float *act_scale,
                            const float *accum, float *y, int64_t nb, void *ws, size_t ws_bytes, void *stream) {
   const char *fn = "qgemm_q2_batched";
+  (void)suma;  // the product forms code - 1 in its operand
   qg_status st = qg::check_q2_weight(w, fn);
   if (st != QG_OK) return st;
-  if (!xq || !suma || !act_scale || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!xq || !act_scale || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (nb < 1 || nb > (1 << 24)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
   if (nb * w->M > (1LL << 40) || nb * w->K > (1LL << 40)) return fail(QG_EINVAL, "%s: problem too large", fn);
   if (!aligned(w->scales, 8)) return fail(QG_EINVAL, "%s: scales plane not 8-byte aligned", fn);
   if (!aligned(xq, 16) || !aligned(y, 16)) return fail(QG_EINVAL, "%s: xq and y must be 16-byte aligned", fn);
-  if (!aligned(suma, 4) || !aligned(act_scale, 4) || (accum && !aligned(accum, 4)))
-    return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  if (!aligned(act_scale, 4) || (accum && !aligned(accum, 4))) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
   if (accum && accum != y && overlap(accum, y, nb * w->M))
     return fail(QG_EINVAL, "%s: accum must be y itself or not overlap it", fn);
   const size_t need = qgemm_q2_batched_ws_bytes(w->M, w->K, w->group, nb);
@@ -590,8 +590,8 @@ qg_status qgemm_q2_batched(const qg_q2_weight *w, const int8_t *xq, const int32_
   const size_t ybytes = (size_t)nb * w->M * sizeof(float);
   if (need > 0 && (bytes_overlap(ws, need, y, ybytes) || bytes_overlap(ws, need, accum, ybytes)))
     return fail(QG_EINVAL, "%s: workspace overlaps the output or the residual", fn);
-  return qg::launched(qg::launch_q2_gemm(w->codes, w->scales, (int)w->M, (int)w->K, w->group, xq, suma, act_scale,
-                                         accum, y, (int)nb, static_cast<float *>(ws), (hipStream_t)stream),
+  return qg::launched(qg::launch_q2_gemm(w->codes, w->scales, (int)w->M, (int)w->K, w->group, xq, act_scale, accum,
+                                         y, (int)nb, static_cast<float *>(ws), (hipStream_t)stream),
                       fn);
 }
 
@@ -603,19 +603,20 @@ qg_status qgemm_q2_batched_dual(const qg_q2_weight *w0, const qg_q2_weight *w1, 
                                 const int32_t *suma, const float *act_scale, float *y0, float *y1, int64_t nb,
                                 void *ws, size_t ws_bytes, void *stream) {
   const char *fn = "qgemm_q2_batched_dual";
+  (void)suma;  // the product forms code - 1 in its operand
   qg_status st = qg::check_q2_weight(w0, fn);
   if (st != QG_OK) return st;
   st = qg::check_q2_weight(w1, fn);
   if (st != QG_OK) return st;
   if (w0->M != w1->M || w0->K != w1->K || w0->group != w1->group)
     return fail(QG_EINVAL, "%s: the two matrices differ in shape or group", fn);
-  if (!xq || !suma || !act_scale || !y0 || !y1) return fail(QG_EINVAL, "%s: null pointer", fn);
+  if (!xq || !act_scale || !y0 || !y1) return fail(QG_EINVAL, "%s: null pointer", fn);
   if (nb < 1 || nb > (1 << 24)) return fail(QG_EINVAL, "%s: bad nb=%lld", fn, (long long)nb);
   if (nb * w0->M > (1LL << 40) || nb * w0->K > (1LL << 40)) return fail(QG_EINVAL, "%s: problem too large", fn);
   if (!aligned(w0->scales, 8) || !aligned(w1->scales, 8)) return fail(QG_EINVAL, "%s: scales plane not 8-byte aligned", fn);
   if (!aligned(xq, 16) || !aligned(y0, 16) || !aligned(y1, 16))
     return fail(QG_EINVAL, "%s: xq, y0 and y1 must be 16-byte aligned", fn);
-  if (!aligned(suma, 4) || !aligned(act_scale, 4)) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
+  if (!aligned(act_scale, 4)) return fail(QG_EINVAL, "%s: misaligned pointer", fn);
   if (overlap(y0, y1, nb * w0->M)) return fail(QG_EINVAL, "%s: the two outputs overlap", fn);
   const size_t need = qgemm_q2_batched_dual_ws_bytes(w0->M, w0->K, w0->group, nb);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -624,7 +625,7 @@ qg_status qgemm_q2_batched_dual(const qg_q2_weight *w0, const qg_q2_weight *w1, 
   const size_t ybytes = (size_t)nb * w0->M * sizeof(float);
   if (need > 0 && (bytes_overlap(ws, need, y0, ybytes) || bytes_overlap(ws, need, y1, ybytes)))
     return fail(QG_EINVAL, "%s: workspace overlaps an output", fn);
-  return qg::launched(qg::launch_q2_gemm(w0->codes, w0->scales, (int)w0->M, (int)w0->K, w0->group, xq, suma,
+  return qg::launched(qg::launch_q2_gemm(w0->codes, w0->scales, (int)w0->M, (int)w0->K, w0->group, xq,
                                          act_scale, nullptr, y0, (int)nb, static_cast<float *>(ws),
                                          (hipStream_t)stream, w1->codes, w1->scales, y1),
                       fn);

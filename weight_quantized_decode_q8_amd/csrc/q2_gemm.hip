@@ -10,28 +10,25 @@
 //
 // gfx950 design:
 //  - v_mfma_i32_16x16x64_i8, one MFMA depth = one 64-wide unit.  The A
-//    operand is the weights' 2-bit codes used as unsigned bytes 0..3: a lane
+//    operand is the weights' codes as signed bytes code - 1 (-1..2): a lane
 //    (row lane % 16, k chunk lane / 16) needs word (lane / 16) of its row's
-//    unit, and (word >> 2a) & 0x03030303 is dword a of its 16-byte fragment
-//    in natural k order (the T64 code order), so A costs 4 bytes per lane
-//    per 16 x 64 block: a quarter of an int8 weight operand.
-//  - B is xq as stored, [nb][K]; the "- 1" is the group's suma[b] subtracted
-//    per token column, as in the GEMV (sum code*xq - sum xq).
-//  - int32 accumulation over a scale group's units (exact), started from
-//    -suma so that closing the group is one convert and one f32 FMA per
+//    unit; (word >> 2a) & 0x03030303 holds the 4 codes of dword a of its
+//    16-byte fragment in natural k order (the T64 code order), and one
+//    v_perm_b32 with those codes as byte selectors into 0x020100ff turns them
+//    into code - 1.  A costs 4 bytes per lane per 16 x 64 block: a quarter
+//    of an int8 weight operand.  B is xq as stored, [nb][K].
+//  - int32 accumulation over a scale group's units: exactly
+//    sum (code - 1) * xq, the GEMV's corrected group dot (its sum code * xq
+//    minus suma), so closing the group is one convert and one f32 FMA per
 //    output with d(o, g), as the GEMV does per group.  On gfx950 the vector
 //    ALU's time adds to the matrix pipe's instead of hiding behind it, so the
 //    design counts vector instructions: per wave and g128 group, 136 for the
-//    closes, 42 for the code unpack, about 10 for addresses, beside 34 MFMAs.
+//    closes, 66 for the code unpack, about 10 for addresses, beside 34 MFMAs.
 //  - tile 272 weight rows x 128 tokens per 8-wave workgroup (17408 = 64 x
 //    272: 256 workgroups at the FFN width and 512 tokens).  Wave w owns row
 //    blocks 2w and 2w + 1 across all 8 token blocks, plus row block 16 by
 //    token block w (17 MFMA tiles per wave, every SIMD the same work), so
 //    each code word is unpacked by one wave and feeds 8 MFMAs.
-//  - the start values -suma of every (group, token) of the workgroup are
-//    built once into an LDS table, each already repeated for the 4 rows a
-//    lane's accumulator holds, so a group's restart reads them with one
-//    128-bit LDS read instead of vector adds and moves.
 //  - a group is closed during the next group's first unit, tile by tile
 //    just before the tile's accumulator restarts; its scales are read into
 //    registers at the end of its last unit.
@@ -47,8 +44,6 @@
 //  - shapes whose tiles cannot fill the CUs (the 5120-row down projection:
 //    76 tiles) split K into f32 partials [S][nb][M], added in fixed order by
 //    a second kernel; (row tile, split) pairs are spread evenly over XCDs.
-//    A split holds at most kMaxGroupsPerWg scale groups (the start-value
-//    table's size), so long rows are split further.
 #include "qg_internal.h"
 
 namespace qg {
@@ -73,11 +68,7 @@ constexpr int kDBytes = kTM * 2;     // the unit's group scales for the tile's r
 constexpr int kStageBytes = kABytes + kBBytes + kDBytes;
 constexpr int kAWaveLoads = (kTM + 63) / 64;  // 5, the last one 16 lanes wide
 constexpr int kDDwords = kDBytes / 4;         // 136: waves 5, 6 and 8 lanes of wave 7
-// The -suma start values of a workgroup's scale groups, each broadcast to the
-// 4 rows a lane's accumulator holds: 16 bytes per (group, token).
-constexpr int kMaxGroupsPerWg = 48;
-constexpr int kNcBytes = kMaxGroupsPerWg * kTN * 16;
-constexpr int kLdsBytes = kStages * kStageBytes + kNcBytes;
+constexpr int kLdsBytes = kStages * kStageBytes;
 
 __device__ inline float half_bits_to_f32(unsigned short h) { return (float)__builtin_bit_cast(_Float16, h); }
 
@@ -96,7 +87,7 @@ struct Q2Pair {
 
 template <int UPG>
 __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
-    Q2Pair pair_args, const int8_t *__restrict__ xq, const int *__restrict__ suma,
+    Q2Pair pair_args, const int8_t *__restrict__ xq,
     const float *__restrict__ act_scale, const float *accum, int nb, int M, int K, int n_ot, int n_bt, int n_split,
     float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
@@ -126,9 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   const int m_tiles = (M + 63) / 64;
   const int nunits = K / 64;
   const int ngroups = nunits / UPG;
-  // K split into S ranges of contiguous scale groups (at most
-  // kMaxGroupsPerWg each): this workgroup's groups are [g_lo, g_hi), its
-  // units [u_lo, u_hi).
+  // K split into S ranges of contiguous scale groups: this workgroup's
+  // groups are [g_lo, g_hi), its units [u_lo, u_hi).
   const int gps = (ngroups + S - 1) / S;
   const int g_lo = min(ngroups, split * gps), g_hi = min(ngroups, split * gps + gps);
   const int u_lo = g_lo * UPG, u_hi = g_hi * UPG;
@@ -175,20 +165,9 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
       __builtin_amdgcn_global_load_lds((global_void *)(d_base + uoff((u / UPG) * 128) + d_vo),
                                        (lds_void *)(st + kABytes + kBBytes + 256 * (wave - 5)), 4, 0, 0);
   };
-  // The first two units' loads go out before the table below is built.
+  // The first two units' loads.
   if (u_lo < u_hi) issue_stage(u_lo, 0);
   if (u_lo + 1 < u_hi) issue_stage(u_lo + 1, 1);
-
-  // -suma of every (group, token) of this workgroup, as 4 equal int32 (the
-  // start value of the group's accumulators, one per row a lane holds).
-  char *nctab = lds + kStages * kStageBytes;
-  for (int e = tid; e < (g_hi - g_lo) * kTN; e += kThreads) {
-    const int g = e / kTN, t = e % kTN;
-    const int *sp = suma + (size_t)min(b0 + t, nb - 1) * nunits + (g_lo + g) * UPG;
-    int sum = sp[0];
-    if (UPG == 2) sum += sp[1];
-    *reinterpret_cast<i32x4 *>(nctab + (size_t)e * 16) = i32x4{-sum, -sum, -sum, -sum};
-  }
 
   // Tiles of a wave: row blocks 2w and 2w + 1 by the 8 token blocks
   // (tile 8 a + c), and row block 16 by token block w (tile 16): 17 MFMA
@@ -199,13 +178,11 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   const int b_off = kABytes + (r16 * 4 + (kc ^ ((r16 >> 2) & 3))) * 16;  // + 1024 per token block
   const int d_off = kABytes + kBBytes + 2 * ((2 * wave) * 16 + 4 * kc);  // + 32 for row block 2w + 1
   const int d16_off = kABytes + kBBytes + 2 * (16 * 16 + 4 * kc);
-  const int nc_off = r16 * 16;                                          // + 256 per token block
 
   // Per tile an exact int32 accumulator for the current scale group and the
-  // f32 sum over closed groups.  A group's first MFMA starts from -suma of
-  // the group's tokens instead of 0, so the int32 result is already
-  // sum (code - 1) * xq and closing the group is one convert and one FMA per
-  // output.  A group is closed during the next group's first unit, tile by
+  // f32 sum over closed groups.  A group's first MFMA starts from 0; closing
+  // the group is one convert and one FMA per output.  A group is closed
+  // during the next group's first unit, tile by
   // tile just before the tile's accumulator restarts; its scales are read
   // into registers at the end of its last unit, before the ring reuses the
   // stage.
@@ -231,25 +208,29 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
     facc[j][2] = fmaf(d2, (float)acc[j].z, facc[j][2]);
     facc[j][3] = fmaf(d3, (float)acc[j].w, facc[j][3]);
   };
+  // code - 1 as a signed byte: byte j of 0x020100ff is code j - 1 (v_perm_b32
+  // with the codes as selectors 0..3 picks it)
   auto unpack = [](unsigned w) {
-    return i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-                 (int)((w >> 6) & 0x03030303u)};
+    constexpr unsigned lut = 0x020100ffu;
+    return i32x4{(int)__builtin_amdgcn_perm(0u, lut, w & 0x03030303u),
+                 (int)__builtin_amdgcn_perm(0u, lut, (w >> 2) & 0x03030303u),
+                 (int)__builtin_amdgcn_perm(0u, lut, (w >> 4) & 0x03030303u),
+                 (int)__builtin_amdgcn_perm(0u, lut, (w >> 6) & 0x03030303u)};
   };
   // One unit in stage buffer buf of group g (relative to g_lo).  FIRST: the
   // group's first unit (the previous group closes, the accumulators restart
-  // from -suma); LAST: the group's last unit (its scales are kept).
+  // from 0); LAST: the group's last unit (its scales are kept).
   auto unit = [&](int buf, int g, auto first_c, auto last_c) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     const char *st = lds + buf * kStageBytes;
-    const char *nc = nctab + g * (kTN * 16) + nc_off;
     const i32x4 af0 = unpack(*reinterpret_cast<const unsigned *>(st + a_off));
     const i32x4 af1 = unpack(*reinterpret_cast<const unsigned *>(st + a_off + 256));
 #pragma unroll
     for (int c = 0; c < kBB; c++) {
       const i32x4 bf = *reinterpret_cast<const i32x4 *>(st + b_off + 1024 * c);
       if constexpr (FIRST) {
-        const i32x4 n = *reinterpret_cast<const i32x4 *>(nc + 256 * c);
+        const i32x4 n = i32x4{0, 0, 0, 0};
         close_tile(c, 0);
         close_tile(kBB + c, 1);
         acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af0, bf, n, 0, 0, 0);
@@ -263,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
       const i32x4 af = unpack(*reinterpret_cast<const unsigned *>(st + a16_off));
       const i32x4 bf = *reinterpret_cast<const i32x4 *>(st + b_off + 1024 * wave);
       if constexpr (FIRST) {
-        const i32x4 n = *reinterpret_cast<const i32x4 *>(nc + 256 * wave);
+        const i32x4 n = i32x4{0, 0, 0, 0};
         close_tile(kTiles - 1, kOBW);
         acc[kTiles - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, n, 0, 0, 0);
       } else {
@@ -279,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
 
   // K loop over the ring, one window of two units per barrier: after the
   // barrier that makes the loads of units u, u + 1 (stage buffers B0,
-  // B0 + 1) visible -- the first one also the table above -- the loads of
+  // B0 + 1) visible, the loads of
   // u + 2, u + 3 go out into the buffers the previous window used, and u,
   // u + 1 are multiplied.
   for (int u = u_lo; u < u_hi; u += 2) {
@@ -306,7 +287,26 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
 
   // Epilogue: y[b, o] = act_scale[b] * acc (+ accum[b, o]), two roundings;
   // with a K split, the f32 partial sums go to part[split][b][o] instead.
+  // Every tile's act_scale and residual values are read before the first
+  // store (a wait for a load also waits for the stores before it); each
+  // output's residual is read by the lane that writes it, so y may be accum.
   const bool vec = (M & 3) == 0;
+  float scl[kBB + 1];
+  float res[kTiles][4];
+  if (S == 1) {
+#pragma unroll
+    for (int c = 0; c <= kBB; c++) scl[c] = act_scale[min(b0 + (c < kBB ? c : wave) * 16 + r16, nb - 1)];
+#pragma unroll
+    for (int j = 0; j < kTiles; j++) {
+      const int blk = j < kTiles - 1 ? 2 * wave + j / kBB : 16;
+      const int c = j < kTiles - 1 ? j % kBB : wave;
+      const int b = b0 + c * 16 + r16;
+      const int o = o0 + blk * 16 + 4 * kc;
+#pragma unroll
+      for (int v = 0; v < 4; v++)
+        res[j][v] = (accum && b < nb && o + v < M) ? accum[(size_t)b * M + o + v] : 0.0f;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kTiles; j++) {
     const int blk = j < kTiles - 1 ? 2 * wave + j / kBB : 16;
@@ -319,11 +319,11 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 4; v++) r[v] = facc[j][v];
     } else {
-      const float sc = act_scale[b];
+      const float sc = scl[j < kTiles - 1 ? c : kBB];
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         r[v] = __fmul_rn(facc[j][v], sc);
-        if (accum && o + v < M) r[v] = __fadd_rn(r[v], accum[(size_t)b * M + o + v]);
+        if (accum) r[v] = __fadd_rn(r[v], res[j][v]);
       }
     }
     float *dst = S > 1 ? part + ((size_t)split * nb + b) * M + o : y + (size_t)b * M + o;
@@ -392,13 +392,11 @@ int q2_gemm_split(int64_t M, int64_t K, int group, int64_t nb) {
   if (S > ngroups) S = ngroups;
   if (S > 16) S = 16;
   if (S < 1) S = 1;
-  // every split's groups fit the workgroup's table of start values
-  while ((ngroups + S - 1) / S > kMaxGroupsPerWg) S++;
   return (int)S;
 }
 
 hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, int group, const int8_t *xq,
-                          const int32_t *suma, const float *act_scale, const float *accum, float *y, int nb,
+                          const float *act_scale, const float *accum, float *y, int nb,
                           float *part, hipStream_t stream, const void *codes1, const void *scales1, float *y1) {
   const int n_ot = (M + kTM - 1) / kTM;
   const int n_bt = (nb + kTN - 1) / kTN;
@@ -412,11 +410,10 @@ hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, i
   pa.codes[1] = codes1 ? reinterpret_cast<const i32x4 *>(codes1) : pa.codes[0];
   pa.scales[1] = scales1 ? reinterpret_cast<const unsigned short *>(scales1) : pa.scales[0];
   pa.y[1] = y1 ? y1 : y;
-  const int *sa = reinterpret_cast<const int *>(suma);
   if (group == 64)
-    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(pa, xq, sa, act_scale, accum, nb, M, K, n_ot, n_bt, S, part);
+    q2_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(pa, xq, act_scale, accum, nb, M, K, n_ot, n_bt, S, part);
   else
-    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(pa, xq, sa, act_scale, accum, nb, M, K, n_ot, n_bt, S, part);
+    q2_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(pa, xq, act_scale, accum, nb, M, K, n_ot, n_bt, S, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const size_t n = (size_t)nb * M;

@@ -148,7 +148,7 @@ int q2_gemm_split(int64_t M, int64_t K, int group, int64_t nb);
 // codes1 non-null: a pair launch, the second matrix (same M, K, group) into
 // y1 with its partials after the first's ([2][S][nb][M]); accum then null.
 hipError_t launch_q2_gemm(const void *codes, const void *scales, int M, int K, int group, const int8_t *xq,
-                          const int32_t *suma, const float *act_scale, const float *accum, float *y, int nb,
+                          const float *act_scale, const float *accum, float *y, int nb,
                           float *part, hipStream_t stream, const void *codes1 = nullptr,
                           const void *scales1 = nullptr, float *y1 = nullptr);
 
