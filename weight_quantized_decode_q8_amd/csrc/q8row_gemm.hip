@@ -244,6 +244,14 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void global_void;
 
+// A workgroup barrier for LDS traffic only: waits for this wave's LDS
+// accesses (lgkmcnt(0)), not for its global stores, which __syncthreads()
+// would also wait for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
+
 template <int L, int TN>
 struct GemmShape {
   static constexpr int kWB = TN / kWC;                // xs rows per wave
@@ -263,6 +271,15 @@ struct GemmShape {
       kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
 };
 
+// LDS of the ring or the epilogue's transpose, whichever is larger, for
+// either pass shape; then the epilogue's row scales rs[o0 .. o0 + 272) and
+// the exponents and flags of the pass's xs rows, moved into LDS at the start
+// of the pass.
+constexpr int kGemmMain = GemmShape<2, 128>::kLdsBytes > GemmShape<3, 64>::kLdsBytes
+                              ? GemmShape<2, 128>::kLdsBytes
+                              : GemmShape<3, 64>::kLdsBytes;
+constexpr int kEpiConstBytes = (kTM + 2 * 128) * 4;
+
 // One pass of the K loop plus the epilogue for weight block `ot` and the TN
 // xs rows starting at b0, with L limbs.  `lds` is the workgroup's buffer.
 template <int L, int TN>
@@ -272,6 +289,9 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
                                           float *__restrict__ y, int nb, int M,
                                           int nchunk_w, int nchunk, int nbt64, int ot, int b0) {
   using S = GemmShape<L, TN>;
+  float *rs_l = reinterpret_cast<float *>(lds + kGemmMain);  // [kTM]
+  int *exp_l = reinterpret_cast<int *>(rs_l + kTM);      // [TN]
+  int *need_l = exp_l + TN;                              // [TN]
   // Stage buffer `buf` holds the A pieces, then the B pieces.
   auto As = [&](int buf) { return reinterpret_cast<i32x4 *>(lds + buf * S::kStageBytes); };
   auto Bs = [&](int buf) { return As(buf) + S::kAPieces; };
@@ -402,6 +422,25 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
   // into the two buffers that steps s-2, s-1 used.
   const int nsteps = nchunk / kCPS;
   static_assert(S::kStages == 4, "the ring below holds two pairs of stages");
+  // The epilogue's constants go to LDS by DMA ahead of the ring's loads (the
+  // loop's first wait covers them), so that its stores are never followed by
+  // a wait for a load: rs by waves 0-4, the exponents and flags by the next.
+  {
+    constexpr int kRsWaves = (kTM + 63) / 64;
+    constexpr int kBW = TN / 64;
+    if (wave < kRsWaves) {
+      const int i = 64 * wave + lane;
+      if (i < kTM)
+        __builtin_amdgcn_global_load_lds((global_void *)(rs + min(o0 + i, M - 1)),
+                                         (lds_void *)(rs_l + 64 * wave), 4, 0, 0);
+    } else if (wave < kRsWaves + kBW) {
+      const int j = wave - kRsWaves;
+      __builtin_amdgcn_global_load_lds((global_void *)(xexp + b0 + 64 * j + lane), (lds_void *)(exp_l + 64 * j), 4, 0, 0);
+    } else if (wave < kRsWaves + 2 * kBW) {
+      const int j = wave - kRsWaves - kBW;
+      __builtin_amdgcn_global_load_lds((global_void *)(need3 + b0 + 64 * j + lane), (lds_void *)(need_l + 64 * j), 4, 0, 0);
+    }
+  }
   if (0 < nsteps) issue_stage(0);
   if (1 < nsteps) issue_stage(1);
   for (int step = 0; step < nsteps; step += 2) {
@@ -444,40 +483,39 @@ __device__ __forceinline__ void gemm_pass(char *lds, const i32x4 *__restrict__ w
             make_float4(vv[0], vv[1], vv[2], vv[3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     for (int f = tid; f < S::kEpiRows * (kTM / 4); f += kThreads) {
       const int gr = f / (kTM / 4), col = (f % (kTM / 4)) * 4;
       const int b = b0 + (gr / 16) * S::kWB + c * 16 + (gr % 16);
       const int o = o0 + col;
       if (b >= nb || o >= M) continue;
       const float4 v4 = *reinterpret_cast<const float4 *>(ep + gr * S::kRowStride + col);
-      const int e = xexp[b] + (L == 2 ? 8 : 0);
+      const int bl = b - b0;
+      const int e = exp_l[bl] + (L == 2 ? 8 : 0);
       float *dst = y + (size_t)b * M + o;
-      if (need3[b] & 2) {  // an infinity or NaN in this xs row
+      if (need_l[bl] & 2) {  // an infinity or NaN in this xs row
         const float nan = __builtin_nanf("");
 #pragma unroll
         for (int k = 0; k < 4; k++)
           if (o + k < M) dst[k] = nan;
       } else if (vec && o + 3 < M) {
-        const float4 r4 = *reinterpret_cast<const float4 *>(rs + o);
+        const float4 r4 = *reinterpret_cast<const float4 *>(rs_l + col);
         // streamed out: every workgroup stores its rows at once, at the end
         __builtin_nontemporal_store(f32x4{ldexpf(v4.x * r4.x, e), ldexpf(v4.y * r4.y, e),
                                           ldexpf(v4.z * r4.z, e), ldexpf(v4.w * r4.w, e)},
                                     reinterpret_cast<f32x4 *>(dst));
       } else {
-        if (o < M) dst[0] = ldexpf(v4.x * rs[o], e);
-        if (o + 1 < M) dst[1] = ldexpf(v4.y * rs[o + 1], e);
-        if (o + 2 < M) dst[2] = ldexpf(v4.z * rs[o + 2], e);
-        if (o + 3 < M) dst[3] = ldexpf(v4.w * rs[o + 3], e);
+        if (o < M) dst[0] = ldexpf(v4.x * rs_l[col], e);
+        if (o + 1 < M) dst[1] = ldexpf(v4.y * rs_l[col + 1], e);
+        if (o + 2 < M) dst[2] = ldexpf(v4.z * rs_l[col + 2], e);
+        if (o + 3 < M) dst[3] = ldexpf(v4.w * rs_l[col + 3], e);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
-constexpr int kGemmLds = GemmShape<2, 128>::kLdsBytes > GemmShape<3, 64>::kLdsBytes
-                             ? GemmShape<2, 128>::kLdsBytes
-                             : GemmShape<3, 64>::kLdsBytes;
+constexpr int kGemmLds = kGemmMain + kEpiConstBytes;
 
 // One workgroup per (weight block of 272 rows, group of 128 xs rows).  The
 // group is computed with 2 limbs in one pass of 128 rows, or with 3 limbs in
