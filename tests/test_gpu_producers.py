@@ -117,6 +117,25 @@ def test_glu_extreme_gates(kind):
     assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu extremes kind={kind}")
 
 
+@pytest.mark.parametrize("kind", [0, 1])
+def test_glu_gate_sweep_vs_oracle(kind):
+    """Gates spread evenly over the binary32 bit patterns of [-110, 110]
+    (both signs, from 1e-30 up: exp(-g) from 1 through overflow and
+    underflow): t, the codes, the scale and the group sums bit-exact against
+    the oracle."""
+    K = 65536
+    pos_lo = int(np.array([1e-30], np.float32).view(np.uint32)[0])
+    pos_hi = int(np.array([110.0], np.float32).view(np.uint32)[0])
+    bits = np.linspace(pos_lo, pos_hi, K // 2).astype(np.uint32)
+    g = np.concatenate([bits.view(np.float32), -bits.view(np.float32)])
+    g = g[synth.rng_for(4140 + kind).permutation(K)].astype(np.float32)
+    u = synth.rng_for(4142 + kind).standard_normal(K).astype(np.float32)
+    rt, rxq, rsc, rsuma = oracle.glu_quant_i8(g, u, kind)
+    t, xq, sc, suma = gpu_glu(g, u, kind)
+    assert same_bits(t, rt), f"t: {int((t.view(np.uint32) != rt.view(np.uint32)).sum())} differ"
+    assert_quant_equal((xq, sc, suma), (rxq, rsc, rsuma), f"glu sweep kind={kind}")
+
+
 @pytest.mark.parametrize("mode", ["in_u", "in_g"])
 def test_glu_output_modes(mode):
     rng = synth.rng_for(4130)
