@@ -869,8 +869,10 @@ def main():
             qg.qgemm_q8row_batched(W5.packed, W5.rs, xs5_d, y5, nb5, M5, K5, ws5, xs_limbs=3)
 
         k_gemm()
-        g_us, g_cold = steady_us(k_gemm, 1, reps=20)
-        g3_us, _ = steady_us(k_gemm3, 1, reps=20)
+        # ten calls per graph, as the other prefill legs: the figure is the
+        # call's own time, without a graph launch per call
+        g_us, g_cold = steady_us(k_gemm, 10, reps=4)
+        g3_us, _ = steady_us(k_gemm3, 10, reps=4)
         flop = 2 * nb5 * M5 * K5
         tflops = flop / g_us / 1e6
         gemm = {"workload": f"batched prefill q8_row GEMM nb={nb5} M={M5} K={K5} (xs limbs: auto)",
@@ -896,8 +898,8 @@ def main():
             qg.qact_silu_mul_pre(g5, u5, c5c, act5)
             qg.qgemm_q8row_batched(W5.packed, W5.rs, act5, y5, nb5, M5, K5, ws5, xs_limbs=0)
 
-        us_f, _ = steady_us(k_gemm_silu, 1, reps=20)
-        us_t, _ = steady_us(k_two_step, 1, reps=20)
+        us_f, _ = steady_us(k_gemm_silu, 10, reps=4)
+        us_t, _ = steady_us(k_two_step, 10, reps=4)
         gemm["silu_fused"] = {"workload": f"the same product of act = silu(g) u col (g, u [{nb5}][{K5}])",
                               "us": round(us_f, 2), "TFLOP/s": round(flop / us_f / 1e6, 1),
                               "two_step_us": round(us_t, 2),
@@ -913,10 +915,10 @@ def main():
         try:
             Wi = torch.randint(-127, 128, (M5, K5), dtype=torch.int8, device=dev)
             Xi = torch.randint(-127, 128, (2 * nb5, K5), dtype=torch.int8, device=dev).t()
-            us_i8, _ = steady_us(lambda: torch._int_mm(Wi, Xi), 1, reps=10)
+            us_i8, _ = steady_us(lambda: torch._int_mm(Wi, Xi), 10, reps=2)
             Wh = Wi.to(torch.float16)
             Xh = torch.randn(nb5, K5, dtype=torch.float16, device=dev)
-            us_h, _ = steady_us(lambda: torch.mm(Xh, Wh.t()), 1, reps=10)
+            us_h, _ = steady_us(lambda: torch.mm(Xh, Wh.t()), 10, reps=2)
             gemm["vendor_context"] = {
                 "int8_mm_17408x5120x1024_us": round(us_i8, 2),
                 "fp16_mm_512x5120x17408_us": round(us_h, 2),
