@@ -118,7 +118,7 @@ def test_q2_gemm_c3_down_prefill_split_sampled():
     within(y[bs, os_], yref, mass + U32 / REL * np.abs(yref), what="down 5120x17408 prefill + residual")
 
 
-@pytest.mark.parametrize("M,in_place", [(17000, True), (16999, False)])
+@pytest.mark.parametrize("M,in_place", [(17000, True), (16999, False), (16998, True)])
 def test_q2_gemm_residual_one_split_ragged(M, in_place):
     """A residual on a product that takes no K split (63 row tiles x 3 token
     tiles), ragged in rows and tokens, in place and not, with M % 4 == 0 (16-byte
