@@ -182,10 +182,9 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
   // Per tile an exact int32 accumulator for the current scale group and the
   // f32 sum over closed groups.  A group's first MFMA starts from 0; closing
   // the group is one convert and one FMA per output.  A group is closed
-  // during the next group's first unit, tile by
-  // tile just before the tile's accumulator restarts; its scales are read
-  // into registers at the end of its last unit, before the ring reuses the
-  // stage.
+  // during the next group's first unit, tile by tile just before the tile's
+  // accumulator restarts; its scales are read into registers at the end of
+  // its last unit, before the ring reuses the stage.
   constexpr int kTiles = kOBW * kBB + 1;
   i32x4 acc[kTiles];
   float facc[kTiles][4];
@@ -260,9 +259,8 @@ __global__ __launch_bounds__(kThreads, 1) void q2_gemm_kernel(
 
   // K loop over the ring, one window of two units per barrier: after the
   // barrier that makes the loads of units u, u + 1 (stage buffers B0,
-  // B0 + 1) visible, the loads of
-  // u + 2, u + 3 go out into the buffers the previous window used, and u,
-  // u + 1 are multiplied.
+  // B0 + 1) visible, the loads of u + 2, u + 3 go out into the buffers the
+  // previous window used, and u, u + 1 are multiplied.
   for (int u = u_lo; u < u_hi; u += 2) {
     const int B0 = (u - u_lo) & 2;
     __builtin_amdgcn_s_waitcnt(0x0070);
