@@ -352,9 +352,10 @@ def test_einval_paths_in_launch_quantiser():
     # auto split of the in-launch form: every (tile, split) workgroup in one round
     assert L.qgemv_q2_x_auto_split(5120, 17408, 128) == 3      # 80 tiles x 3 = 240 workgroups
     assert L.qgemv_q2_x_auto_split(17408, 5120, 128) == 1      # 272 tiles fill the GPU
-    assert L.qgemv_q2_x_auto_split(4096, 4096, 64) == 4        # 64 tiles x 4 = 256
+    assert L.qgemv_q2_x_auto_split(4096, 4096, 64) == 1        # 74 KB per row tile: no split
     assert L.qgemv_q2_x_auto_split(64, 512, 64) == 1           # 8 groups: no split
-    assert L.qgemv_q2_x_auto_split(64, 1024, 64) == 2
+    assert L.qgemv_q2_x_auto_split(64, 1024, 64) == 1          # 18 KB per row tile
+    assert L.qgemv_q2_x_auto_split(64, 16384, 64) == 4         # 295 KB: 4 pieces of 74 KB
     assert L.qgemv_q2_x_auto_split(1, 65536, 64) == 16
     assert L.qgemv_q2_x_ws_bytes(5120, 17408, 128, 0) == 128 * 4 + 3 * 5120 * 4
     # qgemv_q2_x

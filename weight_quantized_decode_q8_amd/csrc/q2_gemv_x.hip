@@ -373,15 +373,18 @@ int q2x_auto_split(int64_t M, int64_t K, int group) {
   // The split costs no launch here, only a handshake per row tile, so K is
   // split whenever the row tiles cannot fill the CUs: the largest split that
   // still runs every (tile, split) workgroup in one round (one 16-wave
-  // workgroup per CU), keeping at least 8 scale groups per split.  Measured
-  // on the 5120 x 17408 g128 down projection inside the decode step: S = 3
-  // (240 workgroups) 216.7-217.2 us, S = 2 217.4-218.2, S = 4 (320, two
-  // rounds) 220.6-221.2, S = 1 219.9-220.6.
+  // workgroup per CU), keeping at least 8 scale groups and 64 KiB of weights
+  // per split.  Measured on the 5120 x 17408 g128 down projection inside the
+  // decode step: S = 3 (240 workgroups, 99 KB each) 216.7-217.2 us, S = 2
+  // 217.4-218.2, S = 4 (320, two rounds) 220.6-221.2, S = 1 219.9-220.6; on
+  // the 4096 x 4096 g64 matrix, one per launch, HBM-cold: S = 1 (74 KB per
+  // workgroup) 5.98 us, S = 2 6.85, S = 4 7.61, S = 8 11.7.
   const int64_t tiles = (M + 63) / 64;
   const int64_t ngroups = K / group;
   if (tiles >= 128) return 1;
+  const int64_t tile_bytes = 64 * (K / 4 + 2 * ngroups);  // codes and scales of a row tile
   int S = 1;
-  while (S < kMaxSplit && tiles * (S + 1) <= 256 && ngroups / (S + 1) >= 8) S++;
+  while (S < kMaxSplit && tiles * (S + 1) <= 256 && ngroups / (S + 1) >= 8 && tile_bytes / (S + 1) >= 65536) S++;
   return S;
 }
 
