@@ -438,7 +438,8 @@ qg_status qgemv_q2_batch(const qg_q2_job *jobs, int njobs, void *stream);
 /* Split factor qgemv_q2_x uses for split_k = 0 (auto) on this shape: 1
  * when the row tiles fill the GPU (M >= 8192), else the largest split whose
  * workgroups still all run at once on the 256 CUs (the split costs no
- * launch here).                                                           */
+ * launch here) while each keeps at least 8 scale groups and 64 KiB of
+ * weights (5120 x 17408 g128: 3; 4096 x 4096 g64: 1).                     */
 int qgemv_q2_x_auto_split(int64_t M, int64_t K, int group);
 
 /* Bytes of workspace qgemv_q2_x needs for this shape and split (split_k 0 =
