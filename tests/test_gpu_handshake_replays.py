@@ -1,6 +1,6 @@
-"""The in-launch handshakes of the decode FFN launches (split-K partials and
-the gate|up halves meeting through device-scope atomics and per-tile arrival
-counters) over many calls: the benched decode shapes (gate|up 2 x 17408 x
+"""The in-launch handshakes (split-K partials, the gate|up halves and the
+lm_head's split tail meeting through device-scope atomics and per-tile
+arrival counters) over many calls.  The decode FFN launches: the benched decode shapes (gate|up 2 x 17408 x
 5120 with the quantiser inside, the 5120 x 17408 down projection with its
 split 3 inside, and the fused form with the RMSNorm, the SiLU gate, the tile
 maxima and the residual), 20,000 steps replayed from one graph. Every step's
@@ -79,3 +79,41 @@ def test_decode_ffn_launches_identical_over_20000_graph_steps():
         assert not bool(diff.any()), f"replay {r}: steps {torch.nonzero(diff).flatten().tolist()[:8]} differ"
         for w in (wsd, wsg, wsd2):
             assert int(torch.count_nonzero(w).item()) == 0, f"replay {r}: a workspace is not left zero"
+
+
+def test_balanced_q8row_split_tail_identical_over_20000_graph_calls():
+    """qgemv_q8row_balanced with 296 row tiles (40 past the full round, each
+    split 7 ways along K like the 248320-row lm_head's tail, the pieces
+    meeting through arrival counters): 20,000 calls from one graph, every
+    call's output kept and equal to the first eager call bit for bit, the
+    workspace zero after each replay."""
+    import torch
+    import weight_quantized_decode_q8_amd as qg
+    M, K = 64 * 296, 5120
+    q, rs, xs = synth.q8row_inputs(M, K, seed=91)
+    W = qg.Q8RowWeight.from_host(q, rs)
+    x = torch.from_numpy(xs).cuda()
+    y = torch.empty(M, device="cuda")
+    ws = W.workspace("cuda")
+    assert ws is not None and ws.numel() > 0
+    W.gemv_balanced(x, y, ws)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    slots = torch.empty(STEPS_PER_GRAPH, M, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for k in range(STEPS_PER_GRAPH):
+                W.gemv_balanced(x, y, ws, stream=torch.cuda.current_stream())
+                slots[k].copy_(y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        slots.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        diff = (slots != ref.unsqueeze(0)).any(dim=1)
+        assert not bool(diff.any()), f"replay {r}: calls {torch.nonzero(diff).flatten().tolist()[:8]} differ"
+        assert int(torch.count_nonzero(ws).item()) == 0, f"replay {r}: the workspace is not left zero"
