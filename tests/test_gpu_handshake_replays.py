@@ -1,12 +1,13 @@
 """The in-launch handshakes (split-K partials, the gate|up halves and the
 lm_head's split tail meeting through device-scope atomics and per-tile
-arrival counters) over many calls.  The decode FFN launches: the benched decode shapes (gate|up 2 x 17408 x
-5120 with the quantiser inside, the 5120 x 17408 down projection with its
-split 3 inside, and the fused form with the RMSNorm, the SiLU gate, the tile
-maxima and the residual), 20,000 steps replayed from one graph. Every step's
-outputs are kept in a slot of their own and must equal the first eager run
-bit for bit, and every workspace must be zero after each replay (a missed or
-doubled arrival would leave a count or a partial behind)."""
+arrival counters) over many calls from one graph.  Every call's outputs are
+kept in a slot of their own and must equal the first eager run bit for bit,
+and every workspace must be zero after each replay (a missed or doubled
+arrival would leave a count or a partial behind).  The decode FFN launches
+run at the benched decode shapes: gate|up 2 x 17408 x 5120 with the
+quantiser inside, the 5120 x 17408 down projection with its split 3 inside,
+and the fused form with the RMSNorm, the SiLU gate, the tile maxima and the
+residual."""
 import numpy as np
 import pytest
 
